@@ -1,0 +1,367 @@
+// CPU oracle for one GPU's share of a Mixture-of-Experts layer.
+//
+// TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+// call this file: only the tests, the smoke check and the benchmark's CPU
+// baseline use it.  It shares no code, header, table or helper with the HIP
+// library; the two meet only through the seeded inputs.
+//
+// What it computes (the plain definitions, written as literal loops):
+//   * router: a small linear layer producing per-expert logits, turned into a
+//     probability distribution; the top-K experts by score are selected and
+//     their router-derived weights kept
+//     ("Efficient and portable mixture-of-experts communication", Introduction);
+//   * dispatch: per-expert token counts and an expert-contiguous copy of the
+//     routed tokens, plus the source-index records that tell the combine where
+//     each row goes back (same page, Dispatch section).  Unlike the pages'
+//     receive kernels, whose slot order is non-deterministic, rows here are
+//     ordered by expert, then token index, so the layout has one answer;
+//   * expert MLP: each expert a small SiLU-gated MLP (same page, Introduction:
+//     experts are small MLPs evaluated by a grouped GEMM, Dispatch section);
+//   * combine: the weighted sum of the selected experts' outputs, written to a
+//     caller-owned tensor (same page, Introduction and Combine section);
+//   * the dual-microbatch split: the token range cut at the midpoint of the
+//     padded token count ("Dual Batch Overlap", UBatchRunner), each half run on
+//     its own and the results concatenated.
+//
+// Arithmetic: every value is read exactly (bf16 and fp32 inputs are exact in
+// fp64), every sum is accumulated in fp64 in ascending index order, compiled
+// with -ffp-contract=off and without fast-math.  OpenMP, when enabled, only
+// splits independent output rows between threads, so results do not depend on
+// the thread count.
+//
+// Parity status: every function below is pinned by the CPU tests against
+// closed forms, brute force on tiny inputs, textbook special cases and
+// invariants; none is "parity unpinned".
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+namespace {
+
+enum { ODT_F32 = 0, ODT_BF16 = 1, ODT_F64 = 2 };
+enum { OSCORE_SOFTMAX = 0, OSCORE_SIGMOID = 1 };
+
+// Exact value of element i of a typed array.
+inline double value_at(const void* p, size_t i, int dt) {
+  if (dt == ODT_F32) return static_cast<double>(static_cast<const float*>(p)[i]);
+  if (dt == ODT_BF16) {
+    uint32_t bits = static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16;
+    float f;
+    std::memcpy(&f, &bits, 4);
+    return static_cast<double>(f);
+  }
+  return static_cast<const double*>(p)[i];
+}
+
+inline size_t dtype_bytes(int dt) { return dt == ODT_F32 ? 4 : (dt == ODT_BF16 ? 2 : 8); }
+
+double silu(double z) { return z / (1.0 + std::exp(-z)); }
+
+// Score of one logit given the full logit row (softmax needs all of it).
+// Softmax: p_e = exp(z_e - max z) / sum_j exp(z_j - max z); sigmoid: 1/(1+exp(-z)).
+void scores_of_row(const double* z, int E, int score, double* s) {
+  if (score == OSCORE_SIGMOID) {
+    for (int e = 0; e < E; ++e) s[e] = 1.0 / (1.0 + std::exp(-z[e]));
+    return;
+  }
+  double m = z[0];
+  for (int e = 1; e < E; ++e) m = std::max(m, z[e]);
+  double denom = 0.0;
+  for (int e = 0; e < E; ++e) denom += std::exp(z[e] - m);
+  for (int e = 0; e < E; ++e) s[e] = std::exp(z[e] - m) / denom;
+}
+
+// Select the K largest keys of one row: repeated maximum search, a strictly
+// greater key replaces the candidate, so equal keys go to the lower expert id;
+// slots come out in descending key order.
+void topk_of_row(const double* key, int E, int K, int32_t* ids) {
+  std::vector<char> taken(E, 0);
+  for (int k = 0; k < K; ++k) {
+    int best = -1;
+    for (int e = 0; e < E; ++e) {
+      if (taken[e]) continue;
+      if (best < 0 || key[e] > key[best]) best = e;
+    }
+    taken[best] = 1;
+    ids[k] = best;
+  }
+}
+
+void weights_of_row(const double* s, const int32_t* ids, int K, int renorm, double* w) {
+  double total = 0.0;
+  for (int k = 0; k < K; ++k) total += s[ids[k]];
+  for (int k = 0; k < K; ++k) w[k] = renorm ? s[ids[k]] / total : s[ids[k]];
+}
+
+}  // namespace
+
+extern "C" {
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+// Router logits: z[t,e] = sum_i x[t,i] * w_router[e,i] (+ bias[e]).
+// x [T,d] and w_router [E,d] of dtype dt; bias [E] fp32 or NULL; z [T,E] fp64.
+void oracle_router_logits(int T, int d, int E, int dt, const void* x, const void* w_router,
+                          const float* bias, double* z) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int i = 0; i < d; ++i)
+        acc += value_at(x, (size_t)t * d + i, dt) * value_at(w_router, (size_t)e * d + i, dt);
+      if (bias) acc += static_cast<double>(bias[e]);
+      z[(size_t)t * E + e] = acc;
+    }
+  }
+}
+
+// Top-K selection and weights from given logits z [T,E] (dtype dt_z).
+// Selection is on the logits themselves: both score functions are increasing,
+// so the K largest logits are the K largest scores.  Weights are the selected
+// scores, divided by their sum when renorm is set.
+void oracle_topk(int T, int E, int K, int dt_z, const void* z, int score, int renorm,
+                 int32_t* ids, double* weights) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    std::vector<double> key(E), s(E);
+    for (int e = 0; e < E; ++e) key[e] = value_at(z, (size_t)t * E + e, dt_z);
+    scores_of_row(key.data(), E, score, s.data());
+    topk_of_row(key.data(), E, K, ids + (size_t)t * K);
+    weights_of_row(s.data(), ids + (size_t)t * K, K, renorm, weights + (size_t)t * K);
+  }
+}
+
+// Full router step: logits then top-K.  logits_out may be NULL.
+void oracle_route(int T, int d, int E, int K, int dt, const void* x, const void* w_router,
+                  const float* bias, int score, int renorm, int32_t* ids, double* weights,
+                  double* logits_out) {
+  std::vector<double> z((size_t)T * E);
+  oracle_router_logits(T, d, E, dt, x, w_router, bias, z.data());
+  oracle_topk(T, E, K, ODT_F64, z.data(), score, renorm, ids, weights);
+  if (logits_out) std::memcpy(logits_out, z.data(), sizeof(double) * z.size());
+}
+
+// Dispatch layout.  counts[e] over all E experts (ids outside [0,E) are not
+// counted but tallied in *n_invalid); offsets [E_loc+1] is the exclusive scan
+// of the local experts' counts; rows are filled expert by expert (ascending),
+// token by token (ascending): src_index[row] = t*K + k, row_of[t*K+k] = row,
+// and row_of = -1 for assignments to non-local or invalid experts.
+// If x is not NULL, x_sorted[row] is a byte copy of x[t] (row_bytes each).
+// Returns the number of local rows.
+int oracle_dispatch(int T, int E, int K, int e_begin, int e_end, const int32_t* ids,
+                    int32_t* counts, int32_t* offsets, int32_t* src_index, int32_t* row_of,
+                    int32_t* n_invalid, const void* x, void* x_sorted, long long row_bytes) {
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  int bad = 0;
+  for (int a = 0; a < T * K; ++a) {
+    int e = ids[a];
+    if (e < 0 || e >= E) ++bad;
+    else ++counts[e];
+  }
+  if (n_invalid) *n_invalid = bad;
+  const int n_loc = e_end - e_begin;
+  offsets[0] = 0;
+  for (int j = 0; j < n_loc; ++j) offsets[j + 1] = offsets[j] + counts[e_begin + j];
+  for (int a = 0; a < T * K; ++a) row_of[a] = -1;
+  int row = 0;
+  for (int e = e_begin; e < e_end; ++e) {
+    for (int t = 0; t < T; ++t) {
+      for (int k = 0; k < K; ++k) {
+        if (ids[(size_t)t * K + k] != e) continue;
+        src_index[row] = t * K + k;
+        row_of[(size_t)t * K + k] = row;
+        if (x && x_sorted)
+          std::memcpy(static_cast<char*>(x_sorted) + (size_t)row * row_bytes,
+                      static_cast<const char*>(x) + (size_t)t * row_bytes, (size_t)row_bytes);
+        ++row;
+      }
+    }
+  }
+  return row;
+}
+
+// SiLU-gated expert MLP on a list of rows.  Row r uses expert row_expert[r]
+// (an index into the weight stacks, i.e. local expert number).
+//   h[j]   = SiLU(sum_i x[r,i] * w_gate[e,j,i]) * (sum_i x[r,i] * w_up[e,j,i])
+//   y[r,c] = sum_j h[j] * w_down[e,c,j]
+// x_rows [n,d] dtype dt_x; w_gate, w_up [E_loc,I,d] and w_down [E_loc,d,I]
+// dtype dt_w; y [n,d] fp64.  h stays in fp64.
+void oracle_expert_mlp(int n_rows, int d, int I, int dt_x, const void* x_rows,
+                       const int32_t* row_expert, int dt_w, const void* w_gate,
+                       const void* w_up, const void* w_down, double* y) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int r = 0; r < n_rows; ++r) {
+    const size_t e = (size_t)row_expert[r];
+    std::vector<double> xr(d), h(I);
+    for (int i = 0; i < d; ++i) xr[i] = value_at(x_rows, (size_t)r * d + i, dt_x);
+    for (int j = 0; j < I; ++j) {
+      double g = 0.0, u = 0.0;
+      const size_t base = (e * I + j) * (size_t)d;
+      for (int i = 0; i < d; ++i) {
+        g += xr[i] * value_at(w_gate, base + i, dt_w);
+        u += xr[i] * value_at(w_up, base + i, dt_w);
+      }
+      h[j] = silu(g) * u;
+    }
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      const size_t base = (e * d + c) * (size_t)I;
+      for (int j = 0; j < I; ++j) acc += h[j] * value_at(w_down, base + j, dt_w);
+      y[(size_t)r * d + c] = acc;
+    }
+  }
+}
+
+// Weighted-sum combine for the tokens listed in `tokens` (n_tok of them):
+//   out[i,c] = sum_{k ascending, row_of[t,k] >= 0} w[t,k] * y_sorted[row_of[t,k], c]
+//            + sum_{s ascending} y_shared[s, t, c]
+// with t = tokens[i].  y_sorted [*,d] dtype dt_y; weights [T,K] dtype dt_w;
+// y_shared [n_shared,T,d] dtype dt_y or NULL; out [n_tok,d] fp64.
+void oracle_combine_tokens(int n_tok, const int32_t* tokens, int T, int d, int K, int dt_y,
+                           const void* y_sorted, const int32_t* row_of, int dt_w,
+                           const void* weights, int n_shared, const void* y_shared,
+                           double* out) {
+#pragma omp parallel for schedule(static)
+  for (int i = 0; i < n_tok; ++i) {
+    const size_t t = (size_t)tokens[i];
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k) {
+        const int32_t r = row_of[t * K + k];
+        if (r < 0) continue;
+        acc += value_at(weights, t * K + k, dt_w) * value_at(y_sorted, (size_t)r * d + c, dt_y);
+      }
+      for (int s = 0; s < n_shared; ++s)
+        acc += value_at(y_shared, ((size_t)s * T + t) * d + c, dt_y);
+      out[(size_t)i * d + c] = acc;
+    }
+  }
+}
+
+void oracle_combine(int T, int d, int K, int dt_y, const void* y_sorted, const int32_t* row_of,
+                    int dt_w, const void* weights, int n_shared, const void* y_shared,
+                    double* out) {
+  std::vector<int32_t> all(T);
+  for (int t = 0; t < T; ++t) all[t] = t;
+  oracle_combine_tokens(T, all.data(), T, d, K, dt_y, y_sorted, row_of, dt_w, weights,
+                        n_shared, y_shared, out);
+}
+
+// Whole layer on tokens [0,T): route, dispatch, routed experts, shared
+// experts (applied to every token with weight one), combine.  All
+// intermediates stay fp64.  x [T,d] dtype dt; w_router [E,d] dtype dt;
+// bias fp32 [E] or NULL; routed weights [E_loc,...] dtype dt; shared weights
+// [n_shared,...] dtype dt or NULL.  Outputs: out [T,d] fp64; ids [T,K];
+// weights_out [T,K] fp64; counts [E] (any of the last three may be NULL).
+// Returns the number of local rows.
+int oracle_forward(int T, int d, int E, int K, int I, int e_begin, int e_end, int n_shared,
+                   int score, int renorm, int dt, const void* x, const void* w_router,
+                   const float* bias, const void* w_gate, const void* w_up, const void* w_down,
+                   const void* ws_gate, const void* ws_up, const void* ws_down, double* out,
+                   int32_t* ids_out, double* weights_out, int32_t* counts_out) {
+  const int n_loc = e_end - e_begin;
+  std::vector<int32_t> ids((size_t)T * K), counts(E), offsets(n_loc + 1),
+      src((size_t)T * K), row_of((size_t)T * K);
+  std::vector<double> w((size_t)T * K);
+  oracle_route(T, d, E, K, dt, x, w_router, bias, score, renorm, ids.data(), w.data(), nullptr);
+  int32_t bad = 0;
+  const size_t rb = (size_t)d * dtype_bytes(dt);
+  std::vector<char> xs((size_t)T * K * rb);
+  const int n_rows = oracle_dispatch(T, E, K, e_begin, e_end, ids.data(), counts.data(),
+                                     offsets.data(), src.data(), row_of.data(), &bad, x,
+                                     xs.data(), (long long)rb);
+  std::vector<int32_t> row_expert(std::max(n_rows, 1));
+  for (int j = 0; j < n_loc; ++j)
+    for (int r = offsets[j]; r < offsets[j + 1]; ++r) row_expert[r] = j;
+  std::vector<double> y((size_t)std::max(n_rows, 1) * d);
+  if (n_rows > 0)
+    oracle_expert_mlp(n_rows, d, I, dt, xs.data(), row_expert.data(), dt, w_gate, w_up,
+                      w_down, y.data());
+  std::vector<double> ysh;
+  if (n_shared > 0) {
+    ysh.resize((size_t)n_shared * T * d);
+    std::vector<int32_t> sh_expert(T);
+    for (int s = 0; s < n_shared; ++s) {
+      for (int t = 0; t < T; ++t) sh_expert[t] = s;
+      oracle_expert_mlp(T, d, I, dt, x, sh_expert.data(), dt, ws_gate, ws_up, ws_down,
+                        ysh.data() + (size_t)s * T * d);
+    }
+  }
+  oracle_combine(T, d, K, ODT_F64, y.data(), row_of.data(), ODT_F64, w.data(), n_shared,
+                 n_shared > 0 ? ysh.data() : nullptr, out);
+  if (ids_out) std::memcpy(ids_out, ids.data(), sizeof(int32_t) * ids.size());
+  if (weights_out) std::memcpy(weights_out, w.data(), sizeof(double) * w.size());
+  if (counts_out) std::memcpy(counts_out, counts.data(), sizeof(int32_t) * counts.size());
+  return n_rows;
+}
+
+// Split point of the dual-microbatch forward: the token count padded up to a
+// multiple of `pad`, halved.  Microbatch 0 is [0, min(mid,T)), microbatch 1 is
+// [mid, T) and may be empty.
+int oracle_split_point(int T, int pad) {
+  const int t_pad = (T + pad - 1) / pad * pad;
+  return t_pad / 2;
+}
+
+// Dual-microbatch forward: the layer run separately on the two token ranges,
+// outputs concatenated in token order.
+void oracle_forward_split(int T, int d, int E, int K, int I, int e_begin, int e_end,
+                          int n_shared, int score, int renorm, int dt, const void* x,
+                          const void* w_router, const float* bias, const void* w_gate,
+                          const void* w_up, const void* w_down, const void* ws_gate,
+                          const void* ws_up, const void* ws_down, int pad, double* out) {
+  const int mid = oracle_split_point(T, pad);
+  const int t0 = std::min(mid, T);
+  const size_t rb = (size_t)d * dtype_bytes(dt);
+  if (t0 > 0)
+    oracle_forward(t0, d, E, K, I, e_begin, e_end, n_shared, score, renorm, dt, x, w_router,
+                   bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, out, nullptr, nullptr,
+                   nullptr);
+  if (T > mid)
+    oracle_forward(T - mid, d, E, K, I, e_begin, e_end, n_shared, score, renorm, dt,
+                   static_cast<const char*>(x) + (size_t)mid * rb, w_router, bias, w_gate,
+                   w_up, w_down, ws_gate, ws_up, ws_down, out + (size_t)mid * d, nullptr,
+                   nullptr, nullptr);
+}
+
+// Round fp64 values to bf16 bit patterns, to nearest, ties to even, directly
+// from fp64 (no intermediate fp32 rounding).  Finite inputs within the bf16
+// range only.
+void oracle_round_bf16(long long n, const double* in, uint16_t* out) {
+  for (long long i = 0; i < n; ++i) {
+    const double v = in[i];
+    double r = 0.0;
+    if (v != 0.0) {
+      int ex;
+      std::frexp(v, &ex);                   // v = f * 2^ex, 0.5 <= |f| < 1
+      const int q = std::max(ex - 8, -133);  // bf16 keeps 8 significant bits
+      r = std::ldexp(std::nearbyint(std::ldexp(v, -q)), q);
+    }
+    const float f = static_cast<float>(r);  // exact: r has at most 8 significant bits
+    uint32_t bits;
+    std::memcpy(&bits, &f, 4);
+    out[i] = static_cast<uint16_t>(bits >> 16);
+  }
+}
+
+}  // extern "C"

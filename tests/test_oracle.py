@@ -1,0 +1,454 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+hand-derived worked examples, closed forms, brute force on tiny inputs,
+textbook special cases (checked with numpy/scipy, which the oracle does not
+use) and invariants.  All CPU-only.
+
+Definitions: "Efficient and portable mixture-of-experts communication"
+(Introduction: router distribution, top-K, weighted sum; Dispatch: per-expert
+counts, contiguous per-expert rows with source records; Combine: weighted sum
+into a caller-owned tensor) and "Dual Batch Overlap" (UBatchRunner: split at
+the midpoint of the padded token count).
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from combine_router_softmax_top_amd import workloads as W
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")))
+
+
+def _silu_np(z):
+    return z * scipy.special.expit(z)
+
+
+def _bf16_exact(t):
+    return t.to(torch.bfloat16)
+
+
+# ---------------------------------------------------------------- worked examples
+
+@pytest.mark.parametrize("case", GOLDEN["route_cases"], ids=lambda c: c["name"])
+def test_route_worked_examples(case):
+    z = torch.tensor([case["logits"]], dtype=torch.float64)
+    ids, w = oracle.topk(z, case["K"], case["score"], case["renorm"])
+    assert ids[0].tolist() == case["ids"]
+    np.testing.assert_allclose(w[0].numpy(), case["weights"], rtol=0, atol=1e-12)
+
+
+def test_dispatch_worked_example():
+    c = GOLDEN["dispatch_case"]
+    ids = torch.tensor(c["ids"], dtype=torch.int32)
+    r = oracle.dispatch(ids, c["E"], c["expert_begin"], c["expert_end"])
+    assert r["counts"].tolist() == c["counts"]
+    assert r["offsets"].tolist() == c["offsets"]
+    assert r["src_index"].tolist() == c["src_index"]
+    assert r["row_of"].tolist() == c["row_of"]
+    assert r["n_invalid"] == 0
+
+
+def test_mlp_worked_example():
+    c = GOLDEN["mlp_case"]
+    f = lambda v, *s: torch.tensor(v, dtype=torch.float64).reshape(*s)
+    y = oracle.expert_mlp(f(c["x"], 1, c["d"]), torch.zeros(1, dtype=torch.int32),
+                          f(c["w_gate"], 1, c["I"], c["d"]), f(c["w_up"], 1, c["I"], c["d"]),
+                          f(c["w_down"], 1, c["d"], c["I"]))
+    np.testing.assert_allclose(y.flatten().numpy(), c["y"], rtol=1e-15, atol=0)
+
+
+def test_combine_worked_example():
+    c = GOLDEN["combine_case"]
+    y = torch.tensor(c["y_sorted"], dtype=torch.float64)
+    out = oracle.combine(y, torch.tensor(c["row_of"], dtype=torch.int32),
+                         torch.tensor(c["weights"], dtype=torch.float64), c["T"], c["K"])
+    np.testing.assert_array_equal(out.numpy(), np.array(c["out"]))
+
+
+# ---------------------------------------------------------------- router
+
+def test_softmax_matches_scipy_and_sums_to_one():
+    g = torch.Generator().manual_seed(1)
+    z = torch.randn(50, 16, generator=g, dtype=torch.float64) * 3
+    ids, w = oracle.topk(z, 16, "softmax", False)
+    p = scipy.special.softmax(z.numpy(), axis=1)
+    got = np.zeros_like(p)
+    np.put_along_axis(got, ids.numpy().astype(np.int64), w.numpy(), axis=1)
+    np.testing.assert_allclose(got, p, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(w.sum(1).numpy(), 1.0, atol=1e-12)
+
+
+def test_sigmoid_matches_scipy():
+    g = torch.Generator().manual_seed(2)
+    z = torch.randn(40, 12, generator=g, dtype=torch.float64) * 4
+    ids, w = oracle.topk(z, 5, "sigmoid", False)
+    s = scipy.special.expit(z.numpy())
+    np.testing.assert_allclose(w.numpy(), np.take_along_axis(s, ids.numpy().astype(np.int64), 1),
+                               rtol=1e-14)
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+def test_renormalised_weights_sum_to_one(score):
+    g = torch.Generator().manual_seed(3)
+    z = torch.randn(64, 32, generator=g, dtype=torch.float64)
+    _, w = oracle.topk(z, 6, score, True)
+    np.testing.assert_allclose(w.sum(1).numpy(), 1.0, atol=1e-14)
+
+
+def test_renormalised_softmax_equals_softmax_over_selected():
+    # Renormalising the top-K of a softmax over all experts equals a softmax over
+    # the K selected logits alone (the common factor cancels).
+    g = torch.Generator().manual_seed(4)
+    z = torch.randn(30, 10, generator=g, dtype=torch.float64) * 2
+    ids, w = oracle.topk(z, 3, "softmax", True)
+    sel = np.take_along_axis(z.numpy(), ids.numpy().astype(np.int64), 1)
+    np.testing.assert_allclose(w.numpy(), scipy.special.softmax(sel, axis=1), rtol=1e-13)
+
+
+@pytest.mark.parametrize("E,K", [(4, 1), (5, 2), (6, 3), (8, 3), (8, 8)])
+def test_topk_bruteforce(E, K):
+    g = torch.Generator().manual_seed(10 * E + K)
+    z = torch.randn(8, E, generator=g, dtype=torch.float64)
+    ids, _ = oracle.topk(z, K, "softmax", True)
+    for t in range(8):
+        best = max(itertools.combinations(range(E), K), key=lambda s: sum(z[t, list(s)].tolist()))
+        assert sorted(ids[t].tolist()) == sorted(best)
+        keys = z[t, ids[t].long()].tolist()
+        assert all(keys[i] > keys[i + 1] for i in range(K - 1)), "slots must be in descending key order"
+
+
+def test_topk_ties_go_to_lower_id():
+    z = torch.tensor([[0.5] * 8, [1.0, 3.0, 3.0, 3.0, 0.0, 3.0, 2.0, 2.0]], dtype=torch.float64)
+    ids, _ = oracle.topk(z, 4, "sigmoid", True)
+    assert ids[0].tolist() == [0, 1, 2, 3]
+    assert ids[1].tolist() == [1, 2, 3, 5]
+
+
+def test_topk_selects_on_logits_not_rounded_scores():
+    # exp(-800) and exp(-801) both underflow to zero in fp64, yet the logits differ:
+    # selection must keep the larger logit.
+    z = torch.tensor([[0.0, -801.0, -800.0]], dtype=torch.float64)
+    ids, _ = oracle.topk(z, 2, "softmax", False)
+    assert ids[0].tolist() == [0, 2]
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_router_logits_match_numpy(dt):
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(17, 48, generator=g).to(dt)
+    wr = (torch.randn(6, 48, generator=g) * 0.2).to(dt)
+    b = torch.randn(6, generator=g)
+    z = oracle.router_logits(x, wr, b)
+    ref = x.double().numpy() @ wr.double().numpy().T + b.double().numpy()
+    np.testing.assert_allclose(z.numpy(), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_route_equals_logits_then_topk():
+    cfg = W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=20, hidden=64)
+    x = W.make_tokens(cfg)
+    wr, b = W.make_router(cfg)
+    ids, w, z = oracle.route(x, wr, b, cfg.top_k, cfg.score, cfg.renormalize)
+    ref = x.double().numpy() @ wr.double().numpy().T + b.double().numpy()
+    np.testing.assert_allclose(z.numpy(), ref, rtol=1e-12, atol=1e-12)
+    ids2, w2 = oracle.topk(torch.from_numpy(ref), cfg.top_k, cfg.score, cfg.renormalize)
+    assert torch.equal(ids, ids2)
+    np.testing.assert_allclose(w.numpy(), w2.numpy(), atol=1e-14)
+
+
+# ---------------------------------------------------------------- dispatch
+
+def _dispatch_bruteforce(ids, E, eb, ee):
+    """Independent statement of the layout: sort local (expert, token, slot) triples."""
+    T, K = ids.shape
+    idl = ids.tolist()
+    counts = [0] * E
+    for t in range(T):
+        for k in range(K):
+            if 0 <= idl[t][k] < E:
+                counts[idl[t][k]] += 1
+    trip = sorted((idl[t][k], t, k) for t in range(T) for k in range(K) if eb <= idl[t][k] < ee)
+    src = [t * K + k for (_, t, k) in trip]
+    row_of = [-1] * (T * K)
+    for r, a in enumerate(src):
+        row_of[a] = r
+    offsets = [0]
+    for e in range(eb, ee):
+        offsets.append(offsets[-1] + counts[e])
+    return counts, offsets, src, row_of
+
+
+@pytest.mark.parametrize("T,E,K,eb,ee", [(1, 1, 1, 0, 1), (5, 4, 2, 0, 4), (7, 6, 3, 2, 5),
+                                         (9, 8, 8, 0, 8), (33, 16, 4, 4, 12)])
+def test_dispatch_bruteforce(T, E, K, eb, ee):
+    ids = W.random_ids(T, E, K, seed=T + E)
+    r = oracle.dispatch(ids, E, eb, ee)
+    counts, offsets, src, row_of = _dispatch_bruteforce(ids, E, eb, ee)
+    assert r["counts"].tolist() == counts
+    assert r["offsets"].tolist() == offsets
+    assert r["src_index"].tolist() == src
+    assert r["row_of"].tolist() == row_of
+
+
+def test_dispatch_invariants_with_invalid_ids():
+    T, E, K, eb, ee = 300, 64, 6, 8, 40
+    ids = W.random_ids(T, E, K, seed=7, invalid_frac=0.05)
+    x = torch.randn(T, 24).to(torch.bfloat16)
+    r = oracle.dispatch(ids, E, eb, ee, x=x)
+    n_bad = int(((ids < 0) | (ids >= E)).sum())
+    assert n_bad > 0 and r["n_invalid"] == n_bad
+    assert int(r["counts"].sum()) == T * K - n_bad
+    # counts agree with a histogram
+    valid = ids[(ids >= 0) & (ids < E)].long()
+    assert r["counts"].tolist() == torch.bincount(valid, minlength=E).tolist()
+    off, src, row_of = r["offsets"], r["src_index"], r["row_of"]
+    assert int(off[-1]) == r["n_rows"] == int(((ids >= eb) & (ids < ee)).sum())
+    # src_index and row_of are mutual inverses over local assignments
+    assert torch.equal(row_of[src.long()], torch.arange(r["n_rows"], dtype=torch.int32))
+    local = ((ids >= eb) & (ids < ee)).flatten()
+    assert bool((row_of[~local] == -1).all())
+    # rows of one expert hold that expert, in strictly increasing token order
+    flat = ids.flatten()
+    for j in range(ee - eb):
+        seg = src[off[j]:off[j + 1]].long()
+        assert bool((flat[seg] == eb + j).all())
+        assert bool(((seg[1:] // K) > (seg[:-1] // K)).all())
+    # copied rows are bit copies of their source tokens
+    assert torch.equal(r["x_sorted"].view(torch.int16), x[src.long() // K].view(torch.int16))
+
+
+def test_dispatch_counts_sum_to_TK_on_a_layer_config():
+    cfg = W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=256, hidden=64)
+    x = W.make_tokens(cfg)
+    wr, b = W.make_router(cfg)
+    ids, _, _ = oracle.route(x, wr, b, cfg.top_k, cfg.score, cfg.renormalize)
+    r = oracle.dispatch(ids, cfg.num_experts, cfg.expert_begin, cfg.expert_end)
+    assert int(r["counts"].sum()) == cfg.num_tokens * cfg.top_k
+    # the Zipf bias makes the low expert ids the popular ones
+    c = r["counts"]
+    assert int(c[:32].sum()) > int(c[32:64].sum()) > int(c[224:].sum())
+
+
+# ---------------------------------------------------------------- expert MLP
+
+def _dense_mlp_np(x, wg, wu, wd):
+    x = x.double().numpy()
+    return (_silu_np(x @ wg.double().numpy().T) * (x @ wu.double().numpy().T)) @ wd.double().numpy().T
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_expert_mlp_single_expert_is_dense_silu_mlp(dt):
+    # I != d so that a transposed weight would not even have the right shape.
+    g = torch.Generator().manual_seed(11)
+    n, d, I = 9, 40, 24
+    x = torch.randn(n, d, generator=g).to(dt)
+    wg = (torch.randn(1, I, d, generator=g) * 0.3).to(dt)
+    wu = (torch.randn(1, I, d, generator=g) * 0.3).to(dt)
+    wd = (torch.randn(1, d, I, generator=g) * 0.3).to(dt)
+    y = oracle.expert_mlp(x, torch.zeros(n, dtype=torch.int32), wg, wu, wd)
+    np.testing.assert_allclose(y.numpy(), _dense_mlp_np(x, wg[0], wu[0], wd[0]), rtol=1e-11, atol=1e-12)
+
+
+def test_expert_mlp_picks_each_rows_expert():
+    g = torch.Generator().manual_seed(12)
+    n, d, I, E = 12, 16, 8, 3
+    x = torch.randn(n, d, generator=g)
+    wg, wu = torch.randn(E, I, d, generator=g), torch.randn(E, I, d, generator=g)
+    wd = torch.randn(E, d, I, generator=g)
+    re = torch.tensor([2, 0, 1, 1, 0, 2, 2, 0, 1, 0, 0, 2], dtype=torch.int32)
+    y = oracle.expert_mlp(x, re, wg, wu, wd)
+    for r in range(n):
+        e = int(re[r])
+        np.testing.assert_allclose(y[r].numpy(), _dense_mlp_np(x[r:r + 1], wg[e], wu[e], wd[e])[0],
+                                   rtol=1e-11, atol=1e-11)
+
+
+def test_expert_mlp_linear_in_down_projection():
+    g = torch.Generator().manual_seed(13)
+    x = torch.randn(5, 32, generator=g)
+    wg, wu, wd = (torch.randn(2, 16, 32, generator=g), torch.randn(2, 16, 32, generator=g),
+                  torch.randn(2, 32, 16, generator=g))
+    re = torch.tensor([0, 1, 0, 1, 1], dtype=torch.int32)
+    y1 = oracle.expert_mlp(x, re, wg, wu, wd)
+    y2 = oracle.expert_mlp(x, re, wg, wu, wd * 4)
+    assert torch.equal(y2, y1 * 4)  # power-of-two scaling is exact
+
+
+def test_silu_special_values():
+    d = torch.ones(1, 1, 1, dtype=torch.float64)
+    x0 = torch.zeros(1, 1, dtype=torch.float64)
+    assert oracle.expert_mlp(x0, torch.zeros(1, dtype=torch.int32), d, d, d).item() == 0.0
+    # large positive gate: SiLU(z) -> z; large negative: -> 0
+    xb = torch.full((1, 1), 40.0, dtype=torch.float64)
+    assert oracle.expert_mlp(xb, torch.zeros(1, dtype=torch.int32), d, d, d).item() == pytest.approx(1600.0, rel=1e-15)
+    xn = torch.full((1, 1), -40.0, dtype=torch.float64)
+    assert abs(oracle.expert_mlp(xn, torch.zeros(1, dtype=torch.int32), d, d, d).item()) < 1e-13
+
+
+# ---------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_identity_round_trip_renormalised(dt):
+    # Identity experts (y_sorted = x_sorted) with renormalised weights give back x.
+    T, E, K, d = 200, 16, 4, 32
+    g = torch.Generator().manual_seed(14)
+    x = torch.randn(T, d, generator=g).to(dt)
+    z = torch.randn(T, E, generator=g, dtype=torch.float64)
+    ids, w = oracle.topk(z, K, "softmax", True)
+    r = oracle.dispatch(ids, E, 0, E, x=x)
+    out = oracle.combine(r["x_sorted"], r["row_of"], w, T, K)
+    if dt == torch.bfloat16:
+        assert torch.equal(oracle.round_bf16(out).view(torch.int16), x.view(torch.int16))
+    else:
+        np.testing.assert_allclose(out.numpy(), x.double().numpy(), rtol=1e-14, atol=0)
+
+
+def test_identity_round_trip_not_renormalised_and_partial():
+    # Not renormalised: out = x * (sum of weights).  With only experts [eb,ee) local,
+    # out = x * (sum of the weights of the local slots).
+    T, E, K, d = 120, 12, 3, 16
+    g = torch.Generator().manual_seed(15)
+    x = torch.randn(T, d, generator=g, dtype=torch.float64)
+    z = torch.randn(T, E, generator=g, dtype=torch.float64)
+    ids, w = oracle.topk(z, K, "softmax", False)
+    for eb, ee in [(0, E), (3, 7)]:
+        r = oracle.dispatch(ids, E, eb, ee, x=x)
+        out = oracle.combine(r["x_sorted"], r["row_of"], w, T, K)
+        local = ((ids >= eb) & (ids < ee)).double()
+        np.testing.assert_allclose(out.numpy(), (x * (w * local).sum(1, keepdim=True)).numpy(),
+                                   rtol=1e-14, atol=1e-15)
+
+
+def test_combine_adds_shared_rows():
+    T, K, d = 6, 2, 4
+    y = torch.zeros(T * K, d, dtype=torch.float64)
+    row_of = torch.full((T * K,), -1, dtype=torch.int32)
+    w = torch.zeros(T, K, dtype=torch.float64)
+    ysh = torch.arange(2 * T * d, dtype=torch.float64).reshape(2, T, d)
+    out = oracle.combine(y, row_of, w, T, K, y_shared=ysh)
+    np.testing.assert_array_equal(out.numpy(), (ysh[0] + ysh[1]).numpy())
+    sub = oracle.combine(y, row_of, w, T, K, y_shared=ysh, tokens=[4, 1])
+    np.testing.assert_array_equal(sub.numpy(), (ysh[0] + ysh[1])[[4, 1]].numpy())
+
+
+# ---------------------------------------------------------------- whole layer
+
+def _small(cfg_name, **kw):
+    return W.CONFIGS[cfg_name].replace(**kw)
+
+
+def test_forward_all_experts_selected_is_dense_mixture():
+    # K = E with renormalised softmax weights: the layer is the dense softmax-weighted
+    # mixture of every expert's MLP.
+    cfg = _small("tiny_f32", num_tokens=24, hidden=32, num_experts=4, top_k=4, intermediate=16,
+                 expert_end=4)
+    inp = W.make_inputs(cfg)
+    out, _, _, counts = oracle.forward(cfg, inp)
+    assert counts.tolist() == [24] * 4
+    x = inp["x"].double().numpy()
+    p = scipy.special.softmax(x @ inp["w_router"].double().numpy().T, axis=1)
+    ref = sum(p[:, e:e + 1] * _dense_mlp_np(inp["x"], inp["w_gate"][e], inp["w_up"][e],
+                                            inp["w_down"][e]) for e in range(4))
+    np.testing.assert_allclose(out.numpy(), ref, rtol=1e-10, atol=1e-13)
+
+
+def test_forward_top1_is_argmax_expert_mlp():
+    # K = 1 renormalised: each token goes through exactly its argmax expert with weight 1.
+    cfg = _small("tiny_f32", num_tokens=40, hidden=32, num_experts=4, top_k=1, intermediate=24,
+                 expert_end=4)
+    inp = W.make_inputs(cfg)
+    out, ids, w, _ = oracle.forward(cfg, inp)
+    x = inp["x"].double().numpy()
+    am = np.argmax(x @ inp["w_router"].double().numpy().T, axis=1)
+    assert ids[:, 0].tolist() == am.tolist()
+    assert bool((w == 1.0).all())
+    for t in range(40):
+        e = int(am[t])
+        ref = _dense_mlp_np(inp["x"][t:t + 1], inp["w_gate"][e], inp["w_up"][e], inp["w_down"][e])
+        np.testing.assert_allclose(out[t].numpy(), ref[0], rtol=1e-11, atol=1e-14)
+
+
+def test_forward_shared_experts_alone_are_dense_mlps():
+    # With every routed expert's down projection zero, only the shared experts remain:
+    # out = sum_s MLP_s(x), each a plain dense SiLU-gated MLP.
+    cfg = _small("dsv2lite_decode", num_tokens=10, hidden=32, num_experts=8, top_k=3,
+                 intermediate=16, expert_end=8)
+    inp = W.make_inputs(cfg)
+    inp["w_down"] = torch.zeros_like(inp["w_down"])
+    out, _, _, _ = oracle.forward(cfg, inp)
+    ref = sum(_dense_mlp_np(inp["x"], inp["ws_gate"][s], inp["ws_up"][s], inp["ws_down"][s])
+              for s in range(2))
+    np.testing.assert_allclose(out.numpy(), ref, rtol=1e-9, atol=1e-12)
+
+
+def test_forward_expert_shares_sum_to_unsharded_layer():
+    # Splitting the experts into disjoint local ranges (one per GPU of an expert-parallel
+    # group) and summing the partial outputs gives the layer with every expert local.
+    base = _small("dsv3_prefill_ep", num_tokens=48, hidden=32, num_experts=16, top_k=4,
+                  intermediate=16, expert_begin=0, expert_end=16)
+    full_inp = W.make_inputs(base)
+    full, ids, _, counts = oracle.forward(base, full_inp)
+    acc = torch.zeros_like(full)
+    for eb in range(0, 16, 4):
+        cfg = base.replace(expert_begin=eb, expert_end=eb + 4)
+        inp = dict(full_inp)
+        for k in ("w_gate", "w_up", "w_down"):
+            inp[k] = full_inp[k][eb:eb + 4].contiguous()
+        part, ids_p, _, counts_p = oracle.forward(cfg, inp)
+        assert torch.equal(ids_p, ids) and torch.equal(counts_p, counts)
+        acc += part
+    np.testing.assert_allclose(acc.numpy(), full.numpy(), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("T", [1, 100, 256, 300, 512, 777])
+def test_split_point(T):
+    mid = oracle.split_point(T, 256)
+    t_pad = -(-T // 256) * 256
+    assert mid == t_pad // 2
+    assert mid % 128 == 0
+
+
+def test_split_forward_equals_unsplit():
+    cfg = _small("dsv3_dual_microbatch", num_tokens=300, hidden=32, num_experts=16, top_k=4,
+                 intermediate=16, expert_end=8)
+    inp = W.make_inputs(cfg)
+    full, _, _, _ = oracle.forward(cfg, inp)
+    split = oracle.forward_split(cfg, inp)
+    assert torch.equal(split, full)
+    # T=100 pads to 256, mid = 128 >= T: the second microbatch is empty.
+    cfg2 = cfg.replace(num_tokens=100)
+    inp2 = W.make_inputs(cfg2)
+    assert torch.equal(oracle.forward_split(cfg2, inp2), oracle.forward(cfg2, inp2)[0])
+
+
+def test_round_bf16_against_torch_and_ties():
+    g = torch.Generator().manual_seed(16)
+    v = torch.randn(10000, generator=g, dtype=torch.float32) * 100
+    # fp32 values are exact in fp64, so direct rounding must agree with torch's fp32->bf16
+    assert torch.equal(oracle.round_bf16(v.double()).view(torch.int16),
+                       v.to(torch.bfloat16).view(torch.int16))
+    one = 1.0
+    vals = torch.tensor([one + 2 ** -8, one + 3 * 2 ** -8, -(one + 2 ** -8), one + 2 ** -8 + 2 ** -40],
+                        dtype=torch.float64)
+    got = oracle.round_bf16(vals).double().tolist()
+    assert got == [1.0, 1.0 + 2 ** -6, -1.0, 1.0 + 2 ** -7]
+
+
+def test_threads_do_not_change_results():
+    cfg = _small("dsv2lite_decode", num_tokens=32, hidden=64, num_experts=8, top_k=3,
+                 intermediate=32, expert_end=8)
+    inp = W.make_inputs(cfg)
+    n0 = oracle.num_threads()
+    try:
+        oracle.set_threads(1)
+        a = oracle.forward(cfg, inp)[0]
+        oracle.set_threads(max(2, n0))
+        b = oracle.forward(cfg, inp)[0]
+    finally:
+        oracle.set_threads(n0)
+    assert torch.equal(a, b)
