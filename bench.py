@@ -1,0 +1,224 @@
+"""Benchmark of the MoE layer hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic tokens:
+moe_route -> moe_dispatch -> moe_expert_mlp -> moe_combine, each a C-ABI call
+on one HIP stream, inputs and weights resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is whole-layer tokens/s (tokens per step /
+step time).  The per-stage figures the metric names are reported beside it:
+dispatch+combine tokens/s and HBM GB/s against the 8 TB/s peak, and the
+expert GEMM's TFLOP/s against the 2.5 PFLOP/s dense bf16 MFMA peak.  The
+`roofline` object is for the expert MLP (the dominant kernel pair), timed with
+HIP events recorded on its own stream around every call inside the timed
+region.  `cpu_baseline` is the fp64 CPU oracle timed on a bounded sample of
+the same workload's tokens.
+
+Usage: python bench.py [--gpus 1] [--steps 30] [--warmup 5] [--workload dsv3_prefill_ep]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+_ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, _ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_VALU_PEAK_TFLOPS = 157.3
+TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "expert_mlp_traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="dsv3_prefill_ep")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    src = os.path.join(_ROOT, "combine_router_softmax_top_amd", "csrc", "expert_mlp.hip")
+    with open(src, "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(cfg, n_loc: int, t_touch: int) -> dict:
+    """Minimum HBM bytes / flops of each stage (per call)."""
+    T, d, E, K, I, b = (cfg.num_tokens, cfg.hidden, cfg.num_experts, cfg.top_k,
+                        cfg.intermediate, cfg.elem_bytes)
+    S = cfg.num_shared
+    route = T * d * b + E * d * b + T * K * 8 + (E * 4 if cfg.zipf_s is not None else 0)
+    dispatch = t_touch * d * b + n_loc * d * b + n_loc * 4 + 2 * T * K * 4 + 2 * E * 4
+    combine = n_loc * d * b + T * K * 8 + T * d * b + S * T * d * b
+    flops = 6.0 * n_loc * d * I + 6.0 * S * T * d * I
+    n_touched_experts = None
+    return dict(route=route, dispatch=dispatch, combine=combine, gemm_flops=flops)
+
+
+def cpu_baseline(cfg, inp, target_s: float) -> dict:
+    import torch
+
+    import oracle
+    threads = oracle.num_threads()
+    n = 8
+    while True:
+        sub = cfg.with_tokens(n)
+        sub_inp = dict(inp)
+        sub_inp["x"] = inp["x"][:n].contiguous()
+        t0 = time.perf_counter()
+        oracle.forward(sub, sub_inp)
+        dt = time.perf_counter() - t0
+        if dt >= target_s * 0.5 or n >= cfg.num_tokens:
+            break
+        n = min(cfg.num_tokens, max(n * 2, int(n * target_s / max(dt, 1e-3))))
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of the {cfg.num_tokens} tokens of the same workload, whole "
+                      f"layer (route, dispatch, expert MLP, combine) in fp64, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from combine_router_softmax_top_amd import binding as B
+    from combine_router_softmax_top_amd import workloads as W
+    from combine_router_softmax_top_amd.layer import MoELayer
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    B.lib()
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        bb = torch.empty_like(a)
+        for _ in range(3):
+            bb.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+
+    cfg = W.CONFIGS[args.workload]
+    t_gen = time.perf_counter()
+    inp = W.make_inputs(cfg, seed=0)
+    t_gen = time.perf_counter() - t_gen
+    layer = MoELayer(cfg, inp, device="cuda:0")
+    stream = torch.cuda.Stream()
+
+    def step(evs=None):
+        with torch.cuda.stream(stream):
+            if evs is not None:
+                evs[0].record(stream)
+            layer.route(stream, with_logits=False)
+            if evs is not None:
+                evs[1].record(stream)
+            layer.dispatch(stream)
+            if evs is not None:
+                evs[2].record(stream)
+            layer.expert_mlp(stream)
+            if evs is not None:
+                evs[3].record(stream)
+            layer.combine(stream)
+            if evs is not None:
+                evs[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    n_loc = layer.n_rows()
+    ids = layer.topk_ids
+    local = (ids >= cfg.expert_begin) & (ids < cfg.expert_end)
+    t_touch = int(local.any(1).sum())
+    alg = algorithmic(cfg, n_loc, t_touch)
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = {"route": 0.0, "dispatch": 0.0, "expert_mlp": 0.0, "combine": 0.0}
+    names = list(stage)
+    for ev in events:
+        for j, nm in enumerate(names):
+            stage[nm] += ev[j].elapsed_time(ev[j + 1]) / args.steps  # ms
+    ms_per_step = wall * 1e3 / args.steps
+    T = cfg.num_tokens
+
+    def gbs(nbytes, ms):
+        return nbytes / (ms * 1e-3) / 1e9
+
+    dc_ms = stage["dispatch"] + stage["combine"]
+    dc_bytes = alg["dispatch"] + alg["combine"]
+    bf16 = cfg.dtype == "bf16"
+    peak = BF16_MFMA_PEAK_TFLOPS if bf16 else FP32_VALU_PEAK_TFLOPS
+    gemm_tflops = alg["gemm_flops"] / (stage["expert_mlp"] * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("source_digest") == source_digest() and rec.get("workload") == cfg.name:
+            traffic = rec.get("hbm_bytes_per_launch")
+    result = {
+        "metric": "dispatch+combine tokens/s & HBM GB/s (% peak); expert GEMM % MFMA peak",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s (whole layer step)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) expert weights, random router)",
+        "config": {"workload": cfg.name, "tokens": T, "hidden": cfg.hidden,
+                   "experts": cfg.num_experts,
+                   "local_experts": f"{cfg.expert_begin}-{cfg.expert_end - 1}",
+                   "top_k": cfg.top_k, "intermediate": cfg.intermediate,
+                   "shared_experts": cfg.num_shared, "local_rows": n_loc,
+                   "tokens_touching_local_experts": t_touch, "parallelism": "none (1 GPU)"},
+        "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
+        "dispatch_combine": {
+            "tokens_per_s": T / (dc_ms * 1e-3),
+            "GB_per_s": gbs(dc_bytes, dc_ms),
+            "frac_hbm_peak": gbs(dc_bytes, dc_ms) / HBM_PEAK_GBS,
+            "dispatch_GB_per_s": gbs(alg["dispatch"], stage["dispatch"]),
+            "combine_GB_per_s": gbs(alg["combine"], stage["combine"]),
+            "algorithmic_bytes": dc_bytes},
+        "route": {"GB_per_s": gbs(alg["route"], stage["route"]),
+                  "frac_hbm_peak": gbs(alg["route"], stage["route"]) / HBM_PEAK_GBS,
+                  "algorithmic_bytes": alg["route"]},
+        "expert_gemm": {"TFLOP_per_s": gemm_tflops, "frac_mfma_peak": gemm_tflops / peak,
+                        "flops": alg["gemm_flops"]},
+        "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": gemm_tflops, "peak": peak,
+                     "unit": "TFLOP/s", "frac": gemm_tflops / peak, "traffic": traffic,
+                     "kernel": "moe_expert_mlp (gate/up SiLU GEMM + down GEMM)",
+                     "avg_launch_us": stage["expert_mlp"] * 1e3},
+        "input_generation_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

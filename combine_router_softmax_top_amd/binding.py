@@ -1,0 +1,250 @@
+"""Thin Python binding of libmoe.so (the C ABI declared in include/moe.h).
+
+Argument marshalling only: torch tensors supply device memory (data_ptr) and
+streams (cuda_stream); every step of the layer runs in the HIP kernels behind
+the C ABI.  There is no fallback: if libmoe.so is missing or cannot be loaded
+the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+from .workloads import MoEConfig
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_WS_DISPATCH, MOE_WS_EXPERT_MLP, MOE_WS_FORWARD, MOE_WS_FORWARD_DBO = range(4)
+
+EXPORTED = ["moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_forward",
+            "moe_forward_dbo", "moe_workspace_bytes", "moe_dbo_split_point", "moe_status_string"]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+class ConfigStruct(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_tokens", "hidden", "num_experts", "top_k", "intermediate", "expert_begin",
+        "expert_end", "num_shared", "score", "renormalize", "dtype")]
+
+
+class LayerTensorsStruct(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "x", "w_router", "bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down",
+        "out", "topk_ids", "topk_weights")]
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libmoe.so")
+
+
+def lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built: run __graft_entry__.build() "
+                               "(the MoE path has no non-HIP fallback)")
+        L = ctypes.CDLL(path)
+        P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        C = ctypes.POINTER(ConfigStruct)
+        LT = ctypes.POINTER(LayerTensorsStruct)
+        sigs = {
+            "moe_route": [C, P, P, P, P, P, P, P],
+            "moe_dispatch": [C, P, P, P, P, P, P, P, P, SZ, P],
+            "moe_expert_mlp": [C, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+            "moe_combine": [C, P, P, P, P, P, P],
+            "moe_forward": [C, LT, P, SZ, P],
+            "moe_forward_dbo": [C, LT, P, SZ, I32, P, P],
+        }
+        for name, args in sigs.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = ctypes.c_int
+        L.moe_workspace_bytes.argtypes = [C, I32]
+        L.moe_workspace_bytes.restype = SZ
+        L.moe_dbo_split_point.argtypes = [I32]
+        L.moe_dbo_split_point.restype = I32
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        _LIB = L
+    return _LIB
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def config_struct(cfg: MoEConfig, num_tokens: Optional[int] = None) -> ConfigStruct:
+    return ConfigStruct(
+        int(cfg.num_tokens if num_tokens is None else num_tokens), cfg.hidden, cfg.num_experts,
+        cfg.top_k, cfg.intermediate, cfg.expert_begin, cfg.expert_end, cfg.num_shared,
+        MOE_SCORE_SIGMOID if cfg.score == "sigmoid" else MOE_SCORE_SOFTMAX,
+        int(cfg.renormalize), MOE_BF16 if cfg.dtype == "bf16" else MOE_F32)
+
+
+def _cs(cfg) -> ConfigStruct:
+    return cfg if isinstance(cfg, ConfigStruct) else config_struct(cfg)
+
+
+def _p(t: Optional[torch.Tensor], what: str = "", shape=None, dtype=None) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what}: must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if shape is not None and t.numel() < _prod(shape):
+        raise ValueError(f"{what}: {tuple(t.shape)} smaller than {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _prod(s):
+    n = 1
+    for v in s:
+        n *= int(v)
+    return n
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoEError(fn, status)
+
+
+def _act(cfg):
+    return torch.bfloat16 if cfg.dtype == MOE_BF16 else torch.float32
+
+
+def workspace_bytes(cfg, kind: int) -> int:
+    c = _cs(cfg)
+    return int(lib().moe_workspace_bytes(ctypes.byref(c), int(kind)))
+
+
+def dbo_split_point(num_tokens: int) -> int:
+    return int(lib().moe_dbo_split_point(int(num_tokens)))
+
+
+def moe_route(cfg, x, w_router, bias, topk_ids, topk_weights, logits=None, stream=None):
+    c = _cs(cfg)
+    T, d, E, K, dt = c.num_tokens, c.hidden, c.num_experts, c.top_k, _act(c)
+    st = lib().moe_route(ctypes.byref(c), _p(x, "x", (T, d), dt),
+                         _p(w_router, "w_router", (E, d), dt),
+                         _p(bias, "bias", (E,), torch.float32),
+                         _p(topk_ids, "topk_ids", (T, K), torch.int32),
+                         _p(topk_weights, "topk_weights", (T, K), torch.float32),
+                         _p(logits, "logits", (T, E), torch.float32), _stream(stream))
+    _check("moe_route", st)
+
+
+def moe_dispatch(cfg, x, topk_ids, expert_counts, expert_offsets, x_sorted, src_index, row_of,
+                 workspace, stream=None):
+    c = _cs(cfg)
+    T, d, E, K, dt = c.num_tokens, c.hidden, c.num_experts, c.top_k, _act(c)
+    n_loc = c.expert_end - c.expert_begin
+    st = lib().moe_dispatch(ctypes.byref(c), _p(x, "x", (T, d), dt),
+                            _p(topk_ids, "topk_ids", (T, K), torch.int32),
+                            _p(expert_counts, "expert_counts", (E,), torch.int32),
+                            _p(expert_offsets, "expert_offsets", (n_loc + 1,), torch.int32),
+                            _p(x_sorted, "x_sorted", (T * K, d), dt),
+                            _p(src_index, "src_index", (T * K,), torch.int32),
+                            _p(row_of, "row_of", (T * K,), torch.int32),
+                            _p(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+                            _stream(stream))
+    _check("moe_dispatch", st)
+
+
+def moe_expert_mlp(cfg, x_sorted, expert_offsets, w_gate, w_up, w_down, y_sorted, x=None,
+                   ws_gate=None, ws_up=None, ws_down=None, y_shared=None, workspace=None,
+                   stream=None):
+    c = _cs(cfg)
+    T, d, K, I, S, dt = c.num_tokens, c.hidden, c.top_k, c.intermediate, c.num_shared, _act(c)
+    n_loc = c.expert_end - c.expert_begin
+    st = lib().moe_expert_mlp(
+        ctypes.byref(c), _p(x_sorted, "x_sorted", (T * K, d), dt),
+        _p(expert_offsets, "expert_offsets", (n_loc + 1,), torch.int32),
+        _p(w_gate, "w_gate", (n_loc, I, d), dt), _p(w_up, "w_up", (n_loc, I, d), dt),
+        _p(w_down, "w_down", (n_loc, d, I), dt), _p(y_sorted, "y_sorted", (T * K, d), dt),
+        _p(x, "x", (T, d), dt), _p(ws_gate, "ws_gate", (S, I, d), dt),
+        _p(ws_up, "ws_up", (S, I, d), dt), _p(ws_down, "ws_down", (S, d, I), dt),
+        _p(y_shared, "y_shared", (S, T, d), dt), _p(workspace, "workspace"),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check("moe_expert_mlp", st)
+
+
+def moe_combine(cfg, y_sorted, row_of, topk_weights, y_shared, out, stream=None):
+    c = _cs(cfg)
+    T, d, K, S, dt = c.num_tokens, c.hidden, c.top_k, c.num_shared, _act(c)
+    st = lib().moe_combine(ctypes.byref(c), _p(y_sorted, "y_sorted", (T * K, d), dt),
+                           _p(row_of, "row_of", (T * K,), torch.int32),
+                           _p(topk_weights, "topk_weights", (T, K), torch.float32),
+                           _p(y_shared, "y_shared", (S, T, d), dt), _p(out, "out", (T, d), dt),
+                           _stream(stream))
+    _check("moe_combine", st)
+
+
+def layer_tensors(cfg, t: dict) -> LayerTensorsStruct:
+    c = _cs(cfg)
+    T, d, E, K, I, S, dt = (c.num_tokens, c.hidden, c.num_experts, c.top_k, c.intermediate,
+                            c.num_shared, _act(c))
+    n_loc = c.expert_end - c.expert_begin
+    return LayerTensorsStruct(
+        _p(t["x"], "x", (T, d), dt), _p(t["w_router"], "w_router", (E, d), dt),
+        _p(t.get("bias"), "bias", (E,), torch.float32),
+        _p(t["w_gate"], "w_gate", (n_loc, I, d), dt), _p(t["w_up"], "w_up", (n_loc, I, d), dt),
+        _p(t["w_down"], "w_down", (n_loc, d, I), dt),
+        _p(t.get("ws_gate"), "ws_gate", (S, I, d), dt), _p(t.get("ws_up"), "ws_up", (S, I, d), dt),
+        _p(t.get("ws_down"), "ws_down", (S, d, I), dt), _p(t["out"], "out", (T, d), dt),
+        _p(t["topk_ids"], "topk_ids", (T, K), torch.int32),
+        _p(t["topk_weights"], "topk_weights", (T, K), torch.float32))
+
+
+def moe_forward(cfg, tensors: dict, workspace, stream=None):
+    c = _cs(cfg)
+    lt = layer_tensors(c, tensors)
+    st = lib().moe_forward(ctypes.byref(c), ctypes.byref(lt), _p(workspace, "workspace"),
+                           workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("moe_forward", st)
+
+
+def moe_forward_dbo(cfg, tensors: dict, workspace, min_tokens_to_split: int = 0, compute=None,
+                    comm=None):
+    c = _cs(cfg)
+    lt = layer_tensors(c, tensors)
+    cs = _stream(compute)
+    ms = cs if comm is None else _stream(comm)
+    st = lib().moe_forward_dbo(ctypes.byref(c), ctypes.byref(lt), _p(workspace, "workspace"),
+                               workspace.numel() * workspace.element_size(),
+                               int(min_tokens_to_split), cs, ms)
+    _check("moe_forward_dbo", st)
+
+
+def alloc_workspace(cfg, kind: int, device="cuda") -> torch.Tensor:
+    n = workspace_bytes(cfg, kind)
+    if n == 0:
+        raise MoEError("moe_workspace_bytes", MOE_ERR_INVALID_ARGUMENT)
+    # torch's caching allocator returns 256-byte (or larger) aligned blocks.
+    return torch.empty(n, dtype=torch.uint8, device=device)

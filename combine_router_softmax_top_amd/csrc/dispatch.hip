@@ -1,0 +1,207 @@
+// Dispatch: per-expert counts, expert offsets and a stable scatter of the
+// routed tokens into expert-contiguous rows.
+//
+// Operation ("Efficient and portable mixture-of-experts communication",
+// Dispatch): count the tokens bound for each expert, copy the tokens into a
+// contiguous per-expert buffer that feeds the grouped GEMM, and record for
+// each row where it came from so that the combine can send it back.  The
+// pages' receive side fills slots in arbitrary order; here the order is fixed
+// (expert ascending, then token ascending), so the layout has one answer.
+//
+// Three kernels, no host synchronisation and no memset:
+//  1. count: one workgroup per chunk of 256 tokens.  Each expert gets a
+//     256-bit token mask in LDS (64-bit LDS atomic OR per assignment).  The
+//     rank of an assignment inside its chunk is the popcount of the mask bits
+//     below its token; the per-chunk count of an expert is the popcount of its
+//     whole mask.  Invalid ids are tallied into an extra histogram column.
+//  2. scan: one workgroup turns the chunk histograms into global counts,
+//     exclusive offsets over the local experts and per-(chunk, expert) row
+//     bases.
+//  3. scatter: one wave per token; the token row is read once (16-byte
+//     loads) and written to each of its local rows; the row maps are
+//     written alongside.  Tokens with no local expert are not read at all.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kCH = kDispatchChunk;
+constexpr int kWords = kCH / 64;
+
+__global__ __launch_bounds__(kCH) void dispatch_count_kernel(
+    const int32_t* __restrict__ ids, int T, int K, int E, int eb, int ee,
+    int32_t* __restrict__ hist /*[n_chunks][E+1]*/, int32_t* __restrict__ rank /*[T*K]*/) {
+  extern __shared__ unsigned long long mask[];  // [E][kWords]
+  __shared__ int bad_total;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * kWords; i += kCH) mask[i] = 0ull;
+  if (tid == 0) bad_total = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kCH + tid;
+  const int word = tid >> 6;
+  const unsigned long long bit = 1ull << (tid & 63);
+  int bad = 0;
+  if (t < T) {
+    for (int k = 0; k < K; ++k) {
+      const int e = ids[(size_t)t * K + k];
+      if (e >= 0 && e < E) atomicOr(&mask[e * kWords + word], bit);
+      else ++bad;
+    }
+  }
+  if (bad) atomicAdd(&bad_total, bad);
+  __syncthreads();
+  if (t < T) {
+    for (int k = 0; k < K; ++k) {
+      const int e = ids[(size_t)t * K + k];
+      int r = -1;
+      if (e >= eb && e < ee) {
+        const unsigned long long* m = mask + e * kWords;
+        r = __popcll(m[word] & (bit - 1ull));
+        for (int w = 0; w < word; ++w) r += __popcll(m[w]);
+      }
+      rank[(size_t)t * K + k] = r;
+    }
+  }
+  int32_t* h = hist + (size_t)blockIdx.x * (E + 1);
+  for (int e = tid; e < E; e += kCH) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kWords; ++w) c += __popcll(mask[e * kWords + w]);
+    h[e] = c;
+  }
+  if (tid == 0) h[E] = bad_total;
+}
+
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
+    const int32_t* __restrict__ hist, int n_chunks, int E, int eb, int ee,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ base,
+    int32_t* __restrict__ n_invalid) {
+  __shared__ int32_t loc[MOE_MAX_EXPERTS];
+  __shared__ int32_t scan[2][MOE_MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  const int n_loc = ee - eb;
+  for (int e = tid; e <= E; e += kScanThreads) {
+    int s = 0;
+    for (int c = 0; c < n_chunks; ++c) s += hist[(size_t)c * (E + 1) + e];
+    if (e == E) *n_invalid = s;
+    else {
+      counts[e] = s;
+      if (e >= eb && e < ee) loc[e - eb] = s;
+    }
+  }
+  __syncthreads();
+  // Inclusive Hillis-Steele scan over the local experts' counts.
+  int cur = 0;
+  for (int j = tid; j < n_loc; j += kScanThreads) scan[0][j] = loc[j];
+  __syncthreads();
+  for (int off = 1; off < n_loc; off <<= 1) {
+    for (int j = tid; j < n_loc; j += kScanThreads)
+      scan[cur ^ 1][j] = scan[cur][j] + (j >= off ? scan[cur][j - off] : 0);
+    cur ^= 1;
+    __syncthreads();
+  }
+  if (tid == 0) offsets[0] = 0;
+  for (int j = tid; j < n_loc; j += kScanThreads) offsets[j + 1] = scan[cur][j];
+  // Row base of (chunk c, local expert j) = offset of j + rows of j in earlier chunks.
+  for (int j = tid; j < n_loc; j += kScanThreads) {
+    int run = scan[cur][j] - loc[j];
+    for (int c = 0; c < n_chunks; ++c) {
+      base[(size_t)c * n_loc + j] = run;
+      run += hist[(size_t)c * (E + 1) + eb + j];
+    }
+  }
+}
+
+constexpr int kUnroll = 4;
+
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ ids,
+    const int32_t* __restrict__ rank, const int32_t* __restrict__ base, int T, int K, int eb,
+    int n_loc, int row_vecs, uint4* __restrict__ x_sorted, int32_t* __restrict__ src_index,
+    int32_t* __restrict__ row_of) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int chunk = t / kCH;
+  int myrow = -1;
+  if (lane < K) {
+    const int a = t * K + lane;
+    const int r = rank[a];
+    if (r >= 0) {
+      myrow = base[(size_t)chunk * n_loc + (ids[a] - eb)] + r;
+      src_index[myrow] = a;
+    }
+    row_of[a] = myrow;
+  }
+  // Any local row at all?  (wave-uniform)
+  const unsigned long long any = __ballot(myrow >= 0);
+  if (any == 0ull) return;
+  const uint4* src = x + (size_t)t * row_vecs;
+  for (int v0 = 0; v0 < row_vecs; v0 += kWave * kUnroll) {
+    uint4 buf[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int v = v0 + u * kWave + lane;
+      if (v < row_vecs) buf[u] = src[v];
+    }
+    for (int k = 0; k < K; ++k) {
+      const int rk = __builtin_amdgcn_readlane(myrow, k);
+      if (rk < 0) continue;
+      uint4* dst = x_sorted + (size_t)rk * row_vecs;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int v = v0 + u * kWave + lane;
+        if (v < row_vecs) dst[v] = buf[u];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// Workspace: [n_invalid (256 B)] [hist n_chunks*(E+1)] [rank T*K] [base n_chunks*E_loc]
+size_t dispatch_workspace_bytes(const moe_config_t& c) {
+  const size_t n_chunks = (size_t)ceil_div(c.num_tokens, kCH);
+  const size_t n_loc = (size_t)(c.expert_end - c.expert_begin);
+  size_t b = 256;
+  b += align_up(n_chunks * (c.num_experts + 1) * 4, 256);
+  b += align_up((size_t)c.num_tokens * c.top_k * 4, 256);
+  b += align_up(n_chunks * n_loc * 4, 256);
+  return b;
+}
+
+hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* ids,
+                           int32_t* counts, int32_t* offsets, void* x_sorted, int32_t* src_index,
+                           int32_t* row_of, void* workspace, hipStream_t s) {
+  const int T = c.num_tokens, K = c.top_k, E = c.num_experts;
+  const int eb = c.expert_begin, ee = c.expert_end, n_loc = ee - eb;
+  const int n_chunks = ceil_div(T, kCH);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* n_invalid = reinterpret_cast<int32_t*>(ws);
+  ws += 256;
+  int32_t* hist = reinterpret_cast<int32_t*>(ws);
+  ws += align_up((size_t)n_chunks * (E + 1) * 4, 256);
+  int32_t* rank = reinterpret_cast<int32_t*>(ws);
+  ws += align_up((size_t)T * K * 4, 256);
+  int32_t* base = reinterpret_cast<int32_t*>(ws);
+
+  const size_t lds = (size_t)E * kWords * sizeof(unsigned long long);
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(n_chunks), dim3(kCH), lds, s, ids, T, K, E, eb,
+                     ee, hist, rank);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, hist, n_chunks, E,
+                     eb, ee, counts, offsets, base, n_invalid);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int elem = c.dtype == MOE_BF16 ? 2 : 4;
+  const int row_vecs = c.hidden * elem / 16;
+  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(ceil_div(T, 4)), dim3(256), 0, s,
+                     static_cast<const uint4*>(x), ids, rank, base, T, K, eb, n_loc, row_vecs,
+                     static_cast<uint4*>(x_sorted), src_index, row_of);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,398 @@
+// Grouped SiLU-gated expert MLP over expert-contiguous rows.
+//
+// Operation ("Efficient and portable mixture-of-experts communication",
+// Introduction: each expert is a small MLP; Dispatch: the contiguous
+// per-expert buffer is the input of a downstream grouped GEMM):
+//     h = SiLU(X_e W_gate[e]^T) * (X_e W_up[e]^T),   y = h W_down[e]^T
+// for the rows X_e of each local expert e, and the same MLP applied to every
+// token for the shared experts.
+//
+// bf16 path (gfx950 MFMA, fp32 accumulation):
+//   * one 256-thread workgroup computes a 256x256 output tile (gate/up pass:
+//     256 rows x (128 gate + 128 up) columns, multiplied together in the
+//     epilogue, so h is written once, in bf16); four waves in a 2x2 grid,
+//     each a 128x128 sub-tile of 4x4 v_mfma_f32_32x32x16_bf16 blocks;
+//   * 64-deep k-tiles staged through LDS, double-buffered: the next tile's
+//     global loads are in flight while the current one feeds the MFMAs; rows
+//     are 128 B in LDS with the 16-byte chunk index XORed with (row & 7), so
+//     both the staging writes and the fragment reads are bank-conflict free;
+//   * ragged groups: the tile list (expert, row tile, column tile) is derived
+//     on the device from the expert offsets; the grid is the host's upper
+//     bound and surplus workgroups exit at once (no host synchronisation);
+//   * workgroup ids are remapped so that each XCD (ids are dealt round-robin
+//     over the 8 XCDs) walks a contiguous stretch of tiles, and within an
+//     expert tiles go in groups of 4 row tiles, keeping shared operands in
+//     that XCD's L2;
+//   * the k order of every output is fixed (64-wide tiles ascending, MFMA
+//     k-blocks of 16 ascending) and independent of the row tiling, so a row's
+//     result does not depend on which other rows share its call.
+// fp32 path: a plain LDS-tiled VALU kernel (64x64 tiles, 4x4 per thread).
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// ------------------------------------------------------------------ tiles
+
+struct Tile {
+  int row0;     // first row of the group in A / C
+  int rows;     // rows of the group
+  int group;    // expert (weight stack index)
+  int m_tile;   // row tile inside the group
+  int n_tile;   // column tile
+};
+
+constexpr int kGroupM = 4;
+
+// Maps a linear tile id onto (group, row tile, column tile).  Groups are the
+// local experts (from the device offsets) or, with offsets == nullptr, a single
+// group of fixed_rows rows.  Returns false for ids past the last tile.
+__device__ __forceinline__ bool find_tile(int tile, const int32_t* __restrict__ offsets,
+                                          int n_groups, int fixed_rows, int BM, int nN,
+                                          Tile& out) {
+  int row0 = 0, rows = fixed_rows, group = 0;
+  int mt = (rows + BM - 1) / BM;
+  if (offsets != nullptr) {
+    bool found = false;
+    for (int j = 0; j < n_groups; ++j) {
+      const int a = offsets[j], b = offsets[j + 1];
+      const int m = (b - a + BM - 1) / BM;
+      const int cnt = m * nN;
+      if (tile < cnt) {
+        row0 = a; rows = b - a; group = j; mt = m; found = true;
+        break;
+      }
+      tile -= cnt;
+    }
+    if (!found) return false;
+  } else if (tile >= mt * nN) {
+    return false;
+  }
+  const int gsize = kGroupM * nN;
+  const int g = tile / gsize;
+  const int first_m = g * kGroupM;
+  const int gm = min(kGroupM, mt - first_m);
+  const int in = tile - g * gsize;
+  out.row0 = row0;
+  out.rows = rows;
+  out.group = group;
+  out.m_tile = first_m + in % gm;
+  out.n_tile = in / gm;
+  return true;
+}
+
+// Workgroup id -> logical tile id: XCD x (ids x, x+8, ...) gets the x-th
+// contiguous eighth of the tile range.  gridDim.x is a multiple of 8.
+__device__ __forceinline__ int xcd_tile_id() {
+  const int per = gridDim.x >> 3;
+  return (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+}
+
+// ------------------------------------------------------------------ bf16 MFMA GEMM
+
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kRowBytes = kBK * 2;                        // 128 B per staged row
+constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 64 KB
+constexpr int kLoadsPerThread = kBM * (kRowBytes / 16) / 256;  // 8 chunks of A, 8 of B
+
+enum { EPI_STORE = 0, EPI_SILU_GLU = 1 };
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.f + __expf(-z)); }
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
+    const uint16_t* __restrict__ A, int lda, long long strideA_batch,
+    const uint16_t* __restrict__ B0,
+    const uint16_t* __restrict__ B1, long long strideB_group, long long strideB_batch,
+    uint16_t* __restrict__ C, int ldc, long long strideC_batch,
+    const int32_t* __restrict__ offsets, int n_groups, int fixed_rows, int N, int Kdim) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
+
+  // Output columns per tile: EPI_STORE 256, EPI_SILU_GLU 128 (gate and up 128 each).
+  constexpr int kNOut = EPI == EPI_SILU_GLU ? kBN / 2 : kBN;
+  const int nN = (N + kNOut - 1) / kNOut;
+  Tile tl;
+  if (!find_tile(xcd_tile_id(), offsets, n_groups, fixed_rows, kBM, nN, tl)) return;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = tl.m_tile * kBM;
+  const int n0 = tl.n_tile * kNOut;
+  const long long zb = (long long)blockIdx.z * strideB_batch;
+  A += (long long)blockIdx.z * strideA_batch;
+  const uint16_t* bg = B0 + zb + (long long)tl.group * strideB_group;
+  const uint16_t* bu = EPI == EPI_SILU_GLU ? B1 + zb + (long long)tl.group * strideB_group : bg;
+  uint16_t* Cz = C + (long long)blockIdx.z * strideC_batch;
+
+  // Staging assignment: chunk c = tid & 7 of rows r_j = tid/8 + 32 j.
+  const int c = tid & 7;
+  const int swz = (tid >> 3) & 7;
+  const uint16_t* pa[kLoadsPerThread];
+  const uint16_t* pb[kLoadsPerThread];
+#pragma unroll
+  for (int j = 0; j < kLoadsPerThread; ++j) {
+    const int r = (tid >> 3) + 32 * j;
+    const int am = min(m0 + r, tl.rows - 1);
+    pa[j] = A + (long long)(tl.row0 + am) * lda + c * 8;
+    int brow;
+    const uint16_t* bbase;
+    if (EPI == EPI_SILU_GLU) {
+      bbase = r < kNOut ? bg : bu;
+      brow = min(n0 + (r & (kNOut - 1)), N - 1);
+    } else {
+      bbase = bg;
+      brow = min(n0 + r, N - 1);
+    }
+    pb[j] = bbase + (long long)brow * Kdim + c * 8;
+  }
+  const int st_off = ((tid >> 3) * kRowBytes) + ((c ^ swz) * 16);
+
+  uint4 ra[kLoadsPerThread], rb[kLoadsPerThread];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < kLoadsPerThread; ++j) {
+      ra[j] = *reinterpret_cast<const uint4*>(pa[j] + k0);
+      rb[j] = *reinterpret_cast<const uint4*>(pb[j] + k0);
+    }
+  };
+  auto lstore = [&](int stage) {
+    uint8_t* s = lds + stage * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < kLoadsPerThread; ++j) {
+      *reinterpret_cast<uint4*>(s + st_off + j * 32 * kRowBytes) = ra[j];
+      *reinterpret_cast<uint4*>(s + kBM * kRowBytes + st_off + j * 32 * kRowBytes) = rb[j];
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Fragment rows: A rows wm*128 + i*32 + (lane & 31); B rows per sub-tile.
+  int b_row[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (EPI == EPI_SILU_GLU)
+      b_row[j] = (j < 2 ? 0 : kNOut) + wn * 64 + (j & 1) * 32 + (lane & 31);
+    else
+      b_row[j] = wn * 128 + j * 32 + (lane & 31);
+  }
+  const int a_row0 = wm * 128 + (lane & 31);
+  const int kgrp = lane >> 5;
+  const int lsw = lane & 7;
+
+  const int nk = Kdim / kBK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * kBK);
+    const uint8_t* sa = lds + cur * kStageBytes;
+    const uint8_t* sb = sa + kBM * kRowBytes;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int pc = ((ks * 2 + kgrp) ^ lsw) * 16;
+      bf16x8 af[4], bf[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        af[i] = *reinterpret_cast<const bf16x8*>(sa + (a_row0 + i * 32) * kRowBytes + pc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bf[j] = *reinterpret_cast<const bf16x8*>(sb + b_row[j] * kRowBytes + pc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue.  Accumulator element r of lane l in a 32x32 block holds
+  // row (r/4)*8 + (l/32)*4 + r%4, column l%32.
+  const int col_l = lane & 31;
+  const int row_l = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
+      if (m >= tl.rows) continue;
+      uint16_t* crow = Cz + (long long)(tl.row0 + m) * ldc;
+      if (EPI == EPI_SILU_GLU) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = n0 + wn * 64 + j * 32 + col_l;
+          if (n < N) crow[n] = f32_to_bf16_bits(silu_f(acc[i][j][r]) * acc[i][j + 2][r]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + wn * 128 + j * 32 + col_l;
+          if (n < N) crow[n] = f32_to_bf16_bits(acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fp32 VALU GEMM
+
+constexpr int kFM = 64, kFN = 64, kFK = 16;
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(
+    const float* __restrict__ A, int lda, long long strideA_batch, const float* __restrict__ B0,
+    const float* __restrict__ B1, long long strideB_group, long long strideB_batch,
+    float* __restrict__ C, int ldc, long long strideC_batch, const int32_t* __restrict__ offsets,
+    int n_groups, int fixed_rows, int N, int Kdim) {
+  __shared__ float sa[kFK][kFM + 1];
+  __shared__ float sg[kFK][kFN + 1];
+  __shared__ float su[kFK][kFN + 1];
+  const int nN = (N + kFN - 1) / kFN;
+  Tile tl;
+  if (!find_tile(xcd_tile_id(), offsets, n_groups, fixed_rows, kFM, nN, tl)) return;
+  const int tid = threadIdx.x;
+  const int tx = tid & 15, ty = tid >> 4;
+  const int m0 = tl.m_tile * kFM, n0 = tl.n_tile * kFN;
+  const long long zb = (long long)blockIdx.z * strideB_batch;
+  A += (long long)blockIdx.z * strideA_batch;
+  const float* bg = B0 + zb + (long long)tl.group * strideB_group;
+  const float* bu = EPI == EPI_SILU_GLU ? B1 + zb + (long long)tl.group * strideB_group : bg;
+  float* Cz = C + (long long)blockIdx.z * strideC_batch;
+  float ag[4][4] = {}, au[4][4] = {};
+  for (int k0 = 0; k0 < Kdim; k0 += kFK) {
+    // 64 rows x 16 k per operand: each thread stages 4 elements of each.
+    for (int q = tid; q < kFM * kFK; q += 256) {
+      const int r = q / kFK, kk = q % kFK;
+      const int am = min(m0 + r, tl.rows - 1);
+      sa[kk][r] = A[(long long)(tl.row0 + am) * lda + k0 + kk];
+      const int bn = min(n0 + r, N - 1);
+      sg[kk][r] = bg[(long long)bn * Kdim + k0 + kk];
+      if (EPI == EPI_SILU_GLU) su[kk][r] = bu[(long long)bn * Kdim + k0 + kk];
+    }
+    __syncthreads();
+    for (int kk = 0; kk < kFK; ++kk) {
+      float a[4], g[4], u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = sa[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        g[j] = sg[kk][tx * 4 + j];
+        u[j] = EPI == EPI_SILU_GLU ? su[kk][tx * 4 + j] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ag[i][j] = fmaf(a[i], g[j], ag[i][j]);
+          if (EPI == EPI_SILU_GLU) au[i][j] = fmaf(a[i], u[j], au[i][j]);
+        }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m >= tl.rows) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx * 4 + j;
+      if (n >= N) continue;
+      const float v = EPI == EPI_SILU_GLU ? silu_f(ag[i][j]) * au[i][j] : ag[i][j];
+      Cz[(long long)(tl.row0 + m) * ldc + n] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch helpers
+
+struct GemmArgs {
+  const void* A; int lda; long long strideA_batch;
+  const void* B0; const void* B1; long long strideB_group; long long strideB_batch;
+  void* C; int ldc; long long strideC_batch;
+  const int32_t* offsets; int n_groups; int fixed_rows; int max_row_tiles_bound;
+  int N; int Kdim; int batch;
+};
+
+inline int grid_for(int row_tiles, int col_tiles) {
+  const int g = row_tiles * col_tiles;
+  return (g + 7) / 8 * 8;
+}
+
+template <int EPI>
+hipError_t run_gemm(int dtype, const GemmArgs& g, hipStream_t s) {
+  if (dtype == MOE_BF16) {
+    constexpr int nout = EPI == EPI_SILU_GLU ? kBN / 2 : kBN;
+    const int rt = g.offsets ? g.max_row_tiles_bound : ceil_div(g.fixed_rows, kBM);
+    const dim3 grid(grid_for(rt, ceil_div(g.N, nout)), 1, g.batch);
+    hipLaunchKernelGGL(gemm_bf16_kernel<EPI>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(g.A), g.lda, g.strideA_batch,
+                       static_cast<const uint16_t*>(g.B0), static_cast<const uint16_t*>(g.B1),
+                       g.strideB_group, g.strideB_batch, static_cast<uint16_t*>(g.C), g.ldc,
+                       g.strideC_batch, g.offsets, g.n_groups, g.fixed_rows, g.N, g.Kdim);
+  } else {
+    const int rt = g.offsets ? g.max_row_tiles_bound : ceil_div(g.fixed_rows, kFM);
+    const dim3 grid(grid_for(rt, ceil_div(g.N, kFN)), 1, g.batch);
+    hipLaunchKernelGGL(gemm_f32_kernel<EPI>, grid, dim3(256), 0, s,
+                       static_cast<const float*>(g.A), g.lda, g.strideA_batch,
+                       static_cast<const float*>(g.B0),
+                       static_cast<const float*>(g.B1), g.strideB_group, g.strideB_batch,
+                       static_cast<float*>(g.C), g.ldc, g.strideC_batch, g.offsets, g.n_groups,
+                       g.fixed_rows, g.N, g.Kdim);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Workspace: h for the routed rows [T*K, I] and for the shared experts [S, T, I].
+size_t mlp_workspace_bytes(const moe_config_t& c) {
+  const size_t elem = c.dtype == MOE_BF16 ? 2 : 4;
+  size_t b = align_up((size_t)c.num_tokens * c.top_k * c.intermediate * elem, 256);
+  b += align_up((size_t)c.num_shared * c.num_tokens * c.intermediate * elem, 256);
+  return b;
+}
+
+hipError_t launch_expert_mlp(const moe_config_t& c, const void* x_sorted, const int32_t* offsets,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             void* y_sorted, const void* x, const void* ws_gate,
+                             const void* ws_up, const void* ws_down, void* y_shared,
+                             void* workspace, hipStream_t s) {
+  const int T = c.num_tokens, K = c.top_k, d = c.hidden, I = c.intermediate;
+  const int n_loc = c.expert_end - c.expert_begin;
+  const size_t elem = c.dtype == MOE_BF16 ? 2 : 4;
+  char* ws = static_cast<char*>(workspace);
+  void* h = ws;
+  void* h_sh = ws + align_up((size_t)T * K * I * elem, 256);
+  const int bm = c.dtype == MOE_BF16 ? kBM : kFM;
+  const int row_bound = ceil_div(T * K, bm) + n_loc;
+
+  GemmArgs up{x_sorted, d, 0, w_gate, w_up, (long long)I * d, 0, h, I, 0,
+              offsets, n_loc, 0, row_bound, I, d, 1};
+  hipError_t err = run_gemm<EPI_SILU_GLU>(c.dtype, up, s);
+  if (err != hipSuccess) return err;
+  GemmArgs down{h, I, 0, w_down, nullptr, (long long)d * I, 0, y_sorted, d, 0,
+                offsets, n_loc, 0, row_bound, d, I, 1};
+  err = run_gemm<EPI_STORE>(c.dtype, down, s);
+  if (err != hipSuccess || c.num_shared == 0) return err;
+
+  GemmArgs sup{x, d, 0, ws_gate, ws_up, 0, (long long)I * d, h_sh, I, (long long)T * I,
+               nullptr, 1, T, 0, I, d, c.num_shared};
+  err = run_gemm<EPI_SILU_GLU>(c.dtype, sup, s);
+  if (err != hipSuccess) return err;
+  GemmArgs sdown{h_sh, I, (long long)T * I, ws_down, nullptr, 0, (long long)d * I, y_shared, d, (long long)T * d,
+                 nullptr, 1, T, 0, d, I, c.num_shared};
+  return run_gemm<EPI_STORE>(c.dtype, sdown, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,336 @@
+// C ABI of the MoE hot path: argument validation (pure host code, run before
+// any HIP call), workspace carving, kernel launches, and the two-stream
+// dual-microbatch forward.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+using moe::align_up;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+moe_status_t check_config(const moe_config_t* c) {
+  if (!c) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->num_tokens < 1 || c->hidden < 1 || c->intermediate < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->num_experts < 1 || c->num_experts > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->top_k < 1 || c->top_k > MOE_MAX_TOPK || c->top_k > c->num_experts)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (c->expert_begin < 0 || c->expert_end > c->num_experts || c->expert_begin >= c->expert_end)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (c->num_shared < 0 || c->num_shared > MOE_MAX_SHARED) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->score != MOE_SCORE_SOFTMAX && c->score != MOE_SCORE_SIGMOID)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)c->num_tokens * c->top_k >= (int64_t(1) << 31)) return MOE_ERR_INVALID_ARGUMENT;
+  const int q = c->dtype == MOE_BF16 ? 64 : 16;
+  if (c->hidden % q != 0 || c->intermediate % q != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Intermediates of one whole-layer call, carved from a workspace.
+struct LayerScratch {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* src_index;
+  int32_t* row_of;
+  void* x_sorted;
+  void* y_sorted;
+  void* y_shared;
+  void* dispatch_ws;
+  void* mlp_ws;
+};
+
+size_t layer_scratch(const moe_config_t& c, void* base, LayerScratch* out) {
+  const size_t T = c.num_tokens, K = c.top_k, d = c.hidden;
+  const size_t elem = c.dtype == MOE_BF16 ? 2 : 4;
+  const size_t n_loc = c.expert_end - c.expert_begin;
+  const size_t sizes[9] = {
+      align_up(c.num_experts * 4, 256),
+      align_up((n_loc + 1) * 4, 256),
+      align_up(T * K * 4, 256),
+      align_up(T * K * 4, 256),
+      align_up(T * K * d * elem, 256),
+      align_up(T * K * d * elem, 256),
+      align_up((size_t)c.num_shared * T * d * elem, 256),
+      align_up(moe::dispatch_workspace_bytes(c), 256),
+      align_up(moe::mlp_workspace_bytes(c), 256)};
+  size_t off[9];
+  size_t total = 0;
+  for (int i = 0; i < 9; ++i) {
+    off[i] = total;
+    total += sizes[i];
+  }
+  if (out) {
+    char* b = static_cast<char*>(base);
+    out->counts = reinterpret_cast<int32_t*>(b + off[0]);
+    out->offsets = reinterpret_cast<int32_t*>(b + off[1]);
+    out->src_index = reinterpret_cast<int32_t*>(b + off[2]);
+    out->row_of = reinterpret_cast<int32_t*>(b + off[3]);
+    out->x_sorted = b + off[4];
+    out->y_sorted = b + off[5];
+    out->y_shared = c.num_shared > 0 ? b + off[6] : nullptr;
+    out->dispatch_ws = b + off[7];
+    out->mlp_ws = b + off[8];
+  }
+  return total;
+}
+
+moe_status_t check_layer_tensors(const moe_config_t& c, const moe_layer_tensors_t* t) {
+  if (!t) return MOE_ERR_INVALID_ARGUMENT;
+  if (!t->x || !t->w_router || !t->w_gate || !t->w_up || !t->w_down || !t->out ||
+      !t->topk_ids || !t->topk_weights)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const bool sh = c.num_shared > 0;
+  if (sh != (t->ws_gate != nullptr) || sh != (t->ws_up != nullptr) ||
+      sh != (t->ws_down != nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(t->x, 16) || !aligned(t->out, 16) || !aligned(t->w_router, 16) ||
+      !aligned(t->w_gate, 16) || !aligned(t->w_up, 16) || !aligned(t->w_down, 16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return MOE_OK;
+}
+
+moe_config_t with_tokens(const moe_config_t& c, int32_t t) {
+  moe_config_t r = c;
+  r.num_tokens = t;
+  return r;
+}
+
+// Launch the four steps of one layer call on the given streams, recording the
+// events between steps when two streams are used.
+moe_status_t enqueue_layer(const moe_config_t& c, const moe_layer_tensors_t& t, void* ws,
+                           hipStream_t s) {
+  LayerScratch sc;
+  layer_scratch(c, ws, &sc);
+  hipError_t e = moe::launch_route(c, t.x, t.w_router, t.bias, t.topk_ids, t.topk_weights,
+                                   nullptr, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_dispatch(c, t.x, t.topk_ids, sc.counts, sc.offsets, sc.x_sorted, sc.src_index,
+                           sc.row_of, sc.dispatch_ws, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_expert_mlp(c, sc.x_sorted, sc.offsets, t.w_gate, t.w_up, t.w_down, sc.y_sorted,
+                             t.x, t.ws_gate, t.ws_up, t.ws_down, sc.y_shared, sc.mlp_ws, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_combine(c, sc.y_sorted, sc.row_of, t.topk_weights, sc.y_shared, t.out, s);
+  return hip_status(e);
+}
+
+// The tensors of microbatch [t0, t0 + n) of a layer call.
+moe_layer_tensors_t slice(const moe_config_t& c, const moe_layer_tensors_t& t, int32_t t0) {
+  const size_t rb = (size_t)c.hidden * (c.dtype == MOE_BF16 ? 2 : 4);
+  moe_layer_tensors_t r = t;
+  r.x = static_cast<const char*>(t.x) + (size_t)t0 * rb;
+  r.out = static_cast<char*>(t.out) + (size_t)t0 * rb;
+  r.topk_ids = t.topk_ids + (size_t)t0 * c.top_k;
+  r.topk_weights = t.topk_weights + (size_t)t0 * c.top_k;
+  return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int32_t moe_dbo_split_point(int32_t num_tokens) {
+  if (num_tokens < 0) return 0;
+  const int64_t t_pad = ((int64_t)num_tokens + 255) / 256 * 256;
+  return (int32_t)(t_pad / 2);
+}
+
+size_t moe_workspace_bytes(const moe_config_t* cfg, int32_t kind) {
+  if (check_config(cfg) != MOE_OK) return 0;
+  switch (kind) {
+    case MOE_WS_DISPATCH: return moe::dispatch_workspace_bytes(*cfg);
+    case MOE_WS_EXPERT_MLP: return moe::mlp_workspace_bytes(*cfg);
+    case MOE_WS_FORWARD: return layer_scratch(*cfg, nullptr, nullptr);
+    case MOE_WS_FORWARD_DBO: {
+      const int32_t mid = moe_dbo_split_point(cfg->num_tokens);
+      const int32_t n0 = std::min(mid, cfg->num_tokens);
+      // Two microbatch scratches (microbatch 0 is the larger), or the unsplit one.
+      const size_t split = 2 * layer_scratch(with_tokens(*cfg, n0), nullptr, nullptr);
+      return std::max(split, layer_scratch(*cfg, nullptr, nullptr));
+    }
+    default: return 0;
+  }
+}
+
+moe_status_t moe_route(const moe_config_t* cfg, const void* x, const void* w_router,
+                       const float* bias, int32_t* topk_ids, float* topk_weights, float* logits,
+                       moe_stream_t stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !topk_ids || !topk_weights) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(w_router, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(moe::launch_route(*cfg, x, w_router, bias, topk_ids, topk_weights, logits,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_dispatch(const moe_config_t* cfg, const void* x, const int32_t* topk_ids,
+                          int32_t* expert_counts, int32_t* expert_offsets, void* x_sorted,
+                          int32_t* src_index, int32_t* row_of, void* workspace,
+                          size_t workspace_bytes, moe_stream_t stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!x || !topk_ids || !expert_counts || !expert_offsets || !x_sorted || !src_index ||
+      !row_of || !workspace)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(x_sorted, 16) || !aligned(workspace, 256))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < moe::dispatch_workspace_bytes(*cfg)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(moe::launch_dispatch(*cfg, x, topk_ids, expert_counts, expert_offsets,
+                                         x_sorted, src_index, row_of, workspace,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expert_mlp(const moe_config_t* cfg, const void* x_sorted,
+                            const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                            const void* w_down, void* y_sorted, const void* x,
+                            const void* ws_gate, const void* ws_up, const void* ws_down,
+                            void* y_shared, void* workspace, size_t workspace_bytes,
+                            moe_stream_t stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!x_sorted || !expert_offsets || !w_gate || !w_up || !w_down || !y_sorted || !workspace)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const bool sh = cfg->num_shared > 0;
+  if (sh != (x != nullptr) || sh != (ws_gate != nullptr) || sh != (ws_up != nullptr) ||
+      sh != (ws_down != nullptr) || sh != (y_shared != nullptr))
+    return MOE_ERR_INVALID_ARGUMENT;
+  for (const void* p : {x_sorted, w_gate, w_up, w_down, (const void*)y_sorted})
+    if (!aligned(p, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (sh)
+    for (const void* p : {x, ws_gate, ws_up, ws_down, (const void*)y_shared})
+      if (!aligned(p, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < moe::mlp_workspace_bytes(*cfg)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(moe::launch_expert_mlp(*cfg, x_sorted, expert_offsets, w_gate, w_up, w_down,
+                                           y_sorted, x, ws_gate, ws_up, ws_down, y_shared,
+                                           workspace, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_combine(const moe_config_t* cfg, const void* y_sorted, const int32_t* row_of,
+                         const float* topk_weights, const void* y_shared, void* out,
+                         moe_stream_t stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!y_sorted || !row_of || !topk_weights || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if ((cfg->num_shared > 0) != (y_shared != nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(y_sorted, 16) || !aligned(out, 16) || (y_shared && !aligned(y_shared, 16)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(moe::launch_combine(*cfg, y_sorted, row_of, topk_weights, y_shared, out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_forward(const moe_config_t* cfg, const moe_layer_tensors_t* tensors,
+                         void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  st = check_layer_tensors(*cfg, tensors);
+  if (st != MOE_OK) return st;
+  if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < layer_scratch(*cfg, nullptr, nullptr)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return enqueue_layer(*cfg, *tensors, workspace, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_forward_dbo(const moe_config_t* cfg, const moe_layer_tensors_t* tensors,
+                             void* workspace, size_t workspace_bytes,
+                             int32_t min_tokens_to_split, moe_stream_t compute,
+                             moe_stream_t comm) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  st = check_layer_tensors(*cfg, tensors);
+  if (st != MOE_OK) return st;
+  if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < moe_workspace_bytes(cfg, MOE_WS_FORWARD_DBO))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t cs = static_cast<hipStream_t>(compute);
+  hipStream_t ms = static_cast<hipStream_t>(comm);
+  const int32_t T = cfg->num_tokens;
+  const int32_t mid = moe_dbo_split_point(T);
+  if (T < min_tokens_to_split || mid >= T) return enqueue_layer(*cfg, *tensors, workspace, cs);
+
+  const moe_config_t c0 = with_tokens(*cfg, mid), c1 = with_tokens(*cfg, T - mid);
+  const moe_layer_tensors_t t0 = slice(*cfg, *tensors, 0), t1 = slice(*cfg, *tensors, mid);
+  LayerScratch s0, s1;
+  const size_t half = layer_scratch(c0, nullptr, nullptr);
+  layer_scratch(c0, workspace, &s0);
+  layer_scratch(c1, static_cast<char*>(workspace) + half, &s1);
+
+  if (cs == ms) {
+    st = enqueue_layer(c0, t0, workspace, cs);
+    if (st != MOE_OK) return st;
+    return enqueue_layer(c1, t1, static_cast<char*>(workspace) + half, cs);
+  }
+
+  enum { EV_START, EV_R0, EV_R1, EV_D0, EV_D1, EV_M0, EV_M1, EV_DONE, EV_N };
+  hipEvent_t ev[EV_N] = {};
+  moe_status_t result = MOE_OK;
+  for (int i = 0; i < EV_N; ++i)
+    if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) {
+      for (int j = 0; j < i; ++j) hipEventDestroy(ev[j]);
+      return MOE_ERR_HIP;
+    }
+  auto ok = [&](hipError_t e) {
+    if (e != hipSuccess) result = MOE_ERR_HIP;
+    return e == hipSuccess;
+  };
+  // The comm stream must see the caller's earlier work on the compute stream.
+  bool good = ok(hipEventRecord(ev[EV_START], cs)) && ok(hipStreamWaitEvent(ms, ev[EV_START], 0));
+  // compute: route both microbatches.
+  good = good && ok(moe::launch_route(c0, t0.x, t0.w_router, t0.bias, t0.topk_ids,
+                                      t0.topk_weights, nullptr, cs)) &&
+         ok(hipEventRecord(ev[EV_R0], cs)) &&
+         ok(moe::launch_route(c1, t1.x, t1.w_router, t1.bias, t1.topk_ids, t1.topk_weights,
+                              nullptr, cs)) &&
+         ok(hipEventRecord(ev[EV_R1], cs));
+  // comm: dispatch both as their routes finish.
+  good = good && ok(hipStreamWaitEvent(ms, ev[EV_R0], 0)) &&
+         ok(moe::launch_dispatch(c0, t0.x, t0.topk_ids, s0.counts, s0.offsets, s0.x_sorted,
+                                 s0.src_index, s0.row_of, s0.dispatch_ws, ms)) &&
+         ok(hipEventRecord(ev[EV_D0], ms)) && ok(hipStreamWaitEvent(ms, ev[EV_R1], 0)) &&
+         ok(moe::launch_dispatch(c1, t1.x, t1.topk_ids, s1.counts, s1.offsets, s1.x_sorted,
+                                 s1.src_index, s1.row_of, s1.dispatch_ws, ms)) &&
+         ok(hipEventRecord(ev[EV_D1], ms));
+  // compute: experts of microbatch 0 (overlapping dispatch 1), then of microbatch 1.
+  good = good && ok(hipStreamWaitEvent(cs, ev[EV_D0], 0)) &&
+         ok(moe::launch_expert_mlp(c0, s0.x_sorted, s0.offsets, t0.w_gate, t0.w_up, t0.w_down,
+                                   s0.y_sorted, t0.x, t0.ws_gate, t0.ws_up, t0.ws_down,
+                                   s0.y_shared, s0.mlp_ws, cs)) &&
+         ok(hipEventRecord(ev[EV_M0], cs)) && ok(hipStreamWaitEvent(cs, ev[EV_D1], 0)) &&
+         ok(moe::launch_expert_mlp(c1, s1.x_sorted, s1.offsets, t1.w_gate, t1.w_up, t1.w_down,
+                                   s1.y_sorted, t1.x, t1.ws_gate, t1.ws_up, t1.ws_down,
+                                   s1.y_shared, s1.mlp_ws, cs)) &&
+         ok(hipEventRecord(ev[EV_M1], cs));
+  // comm: combine 0 (overlapping experts of microbatch 1), then combine 1.
+  good = good && ok(hipStreamWaitEvent(ms, ev[EV_M0], 0)) &&
+         ok(moe::launch_combine(c0, s0.y_sorted, s0.row_of, t0.topk_weights, s0.y_shared, t0.out,
+                                ms)) &&
+         ok(hipStreamWaitEvent(ms, ev[EV_M1], 0)) &&
+         ok(moe::launch_combine(c1, s1.y_sorted, s1.row_of, t1.topk_weights, s1.y_shared, t1.out,
+                                ms)) &&
+         ok(hipEventRecord(ev[EV_DONE], ms)) && ok(hipStreamWaitEvent(cs, ev[EV_DONE], 0));
+  (void)good;
+  for (int i = 0; i < EV_N; ++i) hipEventDestroy(ev[i]);
+  return result;
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer.
+// Written for CDNA4 (gfx950): 64-lane wavefronts, bf16 MFMA, 160 KB LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+// Tokens per dispatch chunk: one workgroup counts and ranks one chunk.
+constexpr int kDispatchChunk = 256;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- launchers (each returns the launch status) ----
+hipError_t launch_route(const moe_config_t& c, const void* x, const void* w_router,
+                        const float* bias, int32_t* ids, float* weights, float* logits,
+                        hipStream_t s);
+
+size_t dispatch_workspace_bytes(const moe_config_t& c);
+hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* ids,
+                           int32_t* counts, int32_t* offsets, void* x_sorted, int32_t* src_index,
+                           int32_t* row_of, void* workspace, hipStream_t s);
+
+size_t mlp_workspace_bytes(const moe_config_t& c);
+hipError_t launch_expert_mlp(const moe_config_t& c, const void* x_sorted, const int32_t* offsets,
+                             const void* w_gate, const void* w_up, const void* w_down,
+                             void* y_sorted, const void* x, const void* ws_gate,
+                             const void* ws_up, const void* ws_down, void* y_shared,
+                             void* workspace, hipStream_t s);
+
+hipError_t launch_combine(const moe_config_t& c, const void* y_sorted, const int32_t* row_of,
+                          const float* weights, const void* y_shared, void* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,97 @@
+"""Device buffers of one MoE layer call and stage-by-stage calls of the C ABI.
+
+Plumbing only: it allocates torch device memory for inputs, outputs and
+workspaces and calls the binding; every step runs in the HIP library.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import binding as B
+from .workloads import MoEConfig
+
+
+class MoELayer:
+    def __init__(self, cfg: MoEConfig, host_inputs: dict, device: str = "cuda"):
+        self.cfg = cfg
+        self.cs = B.config_struct(cfg)
+        dev = torch.device(device)
+        self.device = dev
+        T, d, E, K = cfg.num_tokens, cfg.hidden, cfg.num_experts, cfg.top_k
+        S, n_loc, dt = cfg.num_shared, cfg.num_local, cfg.torch_dtype
+
+        def to_dev(t):
+            return None if t is None else t.to(dev, non_blocking=False).contiguous()
+
+        self.x = to_dev(host_inputs["x"])
+        self.w_router = to_dev(host_inputs["w_router"])
+        self.bias = to_dev(host_inputs.get("bias"))
+        self.w_gate = to_dev(host_inputs.get("w_gate"))
+        self.w_up = to_dev(host_inputs.get("w_up"))
+        self.w_down = to_dev(host_inputs.get("w_down"))
+        self.ws_gate = to_dev(host_inputs.get("ws_gate"))
+        self.ws_up = to_dev(host_inputs.get("ws_up"))
+        self.ws_down = to_dev(host_inputs.get("ws_down"))
+
+        self.topk_ids = torch.empty(T, K, dtype=torch.int32, device=dev)
+        self.topk_weights = torch.empty(T, K, dtype=torch.float32, device=dev)
+        self.logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(n_loc + 1, dtype=torch.int32, device=dev)
+        self.x_sorted = torch.empty(T * K, d, dtype=dt, device=dev)
+        self.src_index = torch.empty(T * K, dtype=torch.int32, device=dev)
+        self.row_of = torch.empty(T * K, dtype=torch.int32, device=dev)
+        self.y_sorted = torch.empty(T * K, d, dtype=dt, device=dev)
+        self.y_shared = torch.empty(S, T, d, dtype=dt, device=dev) if S > 0 else None
+        self.out = torch.empty(T, d, dtype=dt, device=dev)
+        self.ws_dispatch = B.alloc_workspace(self.cs, B.MOE_WS_DISPATCH, dev)
+        self.ws_mlp = B.alloc_workspace(self.cs, B.MOE_WS_EXPERT_MLP, dev)
+        self._ws_forward: Optional[torch.Tensor] = None
+        self._ws_dbo: Optional[torch.Tensor] = None
+
+    # ---- stages -------------------------------------------------------------
+    def route(self, stream=None, with_logits: bool = True):
+        B.moe_route(self.cs, self.x, self.w_router, self.bias, self.topk_ids, self.topk_weights,
+                    self.logits if with_logits else None, stream)
+
+    def dispatch(self, stream=None, topk_ids: Optional[torch.Tensor] = None):
+        B.moe_dispatch(self.cs, self.x, self.topk_ids if topk_ids is None else topk_ids,
+                       self.counts, self.offsets, self.x_sorted, self.src_index, self.row_of,
+                       self.ws_dispatch, stream)
+
+    def expert_mlp(self, stream=None):
+        B.moe_expert_mlp(self.cs, self.x_sorted, self.offsets, self.w_gate, self.w_up,
+                         self.w_down, self.y_sorted, self.x if self.cfg.num_shared else None,
+                         self.ws_gate, self.ws_up, self.ws_down, self.y_shared, self.ws_mlp,
+                         stream)
+
+    def combine(self, stream=None, out: Optional[torch.Tensor] = None):
+        B.moe_combine(self.cs, self.y_sorted, self.row_of, self.topk_weights, self.y_shared,
+                      self.out if out is None else out, stream)
+
+    def n_invalid(self) -> int:
+        return int(self.ws_dispatch[:4].view(torch.int32).item())
+
+    # ---- whole layer --------------------------------------------------------
+    def tensors(self, out: Optional[torch.Tensor] = None) -> dict:
+        return dict(x=self.x, w_router=self.w_router, bias=self.bias, w_gate=self.w_gate,
+                    w_up=self.w_up, w_down=self.w_down, ws_gate=self.ws_gate, ws_up=self.ws_up,
+                    ws_down=self.ws_down, out=self.out if out is None else out,
+                    topk_ids=self.topk_ids, topk_weights=self.topk_weights)
+
+    def forward(self, stream=None, out: Optional[torch.Tensor] = None):
+        if self._ws_forward is None:
+            self._ws_forward = B.alloc_workspace(self.cs, B.MOE_WS_FORWARD, self.device)
+        B.moe_forward(self.cs, self.tensors(out), self._ws_forward, stream)
+
+    def forward_dbo(self, compute=None, comm=None, min_tokens_to_split: int = 0,
+                    out: Optional[torch.Tensor] = None):
+        if self._ws_dbo is None:
+            self._ws_dbo = B.alloc_workspace(self.cs, B.MOE_WS_FORWARD_DBO, self.device)
+        B.moe_forward_dbo(self.cs, self.tensors(out), self._ws_dbo, min_tokens_to_split,
+                          compute, comm)
+
+    def n_rows(self) -> int:
+        return int(self.offsets[-1].item())

@@ -1,0 +1,263 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) Mixture-of-Experts layer hot path:
+ * router + top-K, sparse dispatch, grouped SiLU-gated expert MLP, weighted
+ * combine, and a two-microbatch overlapped forward.
+ *
+ * Sources of the operations (page titles and sections):
+ *   [PPLX] "Efficient and portable mixture-of-experts communication"
+ *          (Perplexity, 2025-04-02): Introduction, Sharding and Parallelism,
+ *          Portable Kernels, Dispatch, Combine.
+ *   [DBO]  "Dual Batch Overlap" (vLLM design doc): Introduction (overlap
+ *          schedule), UBatchRunner (midpoint split), Interfaces (compute and
+ *          communication streams).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer (HBM of the current HIP
+ *     device) unless marked "host".  The library never allocates, frees or
+ *     keeps device memory: inputs, outputs and workspaces are caller-owned and
+ *     may be reused from call to call (as the pages' buffers are reused across
+ *     layers, [PPLX] Portable Kernels).
+ *   - All matrices are dense row-major.  Expert weights use the [out, in]
+ *     layout, so both operands of every product are contiguous along the
+ *     reduction dimension.
+ *   - Calls are asynchronous: the host validates arguments, then only enqueues
+ *     kernels on the given stream; pointers must stay valid until that work has
+ *     completed.  No call synchronises with the host or reads device data on
+ *     the host.
+ *   - On any status other than MOE_OK nothing has been enqueued (except
+ *     MOE_ERR_HIP, returned when a launch itself fails).
+ *   - Results are deterministic: no floating-point atomics, fixed reduction
+ *     orders, a stable dispatch order.  Repeated calls give identical bits.
+ *   - Stateless and re-entrant; calls on different streams are independent as
+ *     long as their buffers do not overlap.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,   /* NULL pointer, bad size, bad expert range   */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 2,
+  MOE_ERR_UNSUPPORTED = 3,        /* valid but not implemented (dtype, shape)  */
+  MOE_ERR_HIP = 4                 /* a HIP runtime call or launch failed       */
+} moe_status_t;
+
+/* Element types of activations and weights. */
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+/* Router score functions. */
+enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+/* Workspace kinds for moe_workspace_bytes. */
+enum { MOE_WS_DISPATCH = 0, MOE_WS_EXPERT_MLP = 1, MOE_WS_FORWARD = 2, MOE_WS_FORWARD_DBO = 3 };
+
+#define MOE_MAX_EXPERTS 512
+#define MOE_MAX_TOPK 16
+#define MOE_MAX_SHARED 4
+
+/* One layer's shape.  Limits (else MOE_ERR_INVALID_ARGUMENT):
+ *   1 <= num_tokens, num_tokens * top_k < 2^31;
+ *   1 <= num_experts <= MOE_MAX_EXPERTS; 1 <= top_k <= min(num_experts, MOE_MAX_TOPK);
+ *   0 <= expert_begin < expert_end <= num_experts;
+ *   0 <= num_shared <= MOE_MAX_SHARED; score in MOE_SCORE_*; dtype in MOE_F32/MOE_BF16;
+ *   hidden and intermediate >= 1.
+ * Shapes the kernels do not cover return MOE_ERR_UNSUPPORTED:
+ *   bf16: hidden and intermediate multiples of 64;  f32: multiples of 4. */
+typedef struct moe_config {
+  int32_t num_tokens;    /* T: tokens in this call                                    */
+  int32_t hidden;        /* d: model width                                            */
+  int32_t num_experts;   /* E: routed experts of the whole layer (all GPUs)           */
+  int32_t top_k;         /* K: experts chosen per token                               */
+  int32_t intermediate;  /* I: expert MLP width                                       */
+  int32_t expert_begin;  /* this GPU hosts experts [expert_begin, expert_end)         */
+  int32_t expert_end;
+  int32_t num_shared;    /* always-applied shared experts, each of width I            */
+  int32_t score;         /* MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID                    */
+  int32_t renormalize;   /* 1: weights = selected scores / their sum; 0: raw scores   */
+  int32_t dtype;         /* MOE_F32 or MOE_BF16, for activations and weights          */
+} moe_config_t;
+
+/* A hipStream_t handle; NULL means the default (null) stream. */
+typedef void* moe_stream_t;
+
+/*
+ * moe_route -- router projection, scoring and top-K selection.
+ * [PPLX] Introduction: the router is a small linear layer whose output is a
+ * probability distribution over experts; the K best-scoring experts are kept
+ * and weighted by values derived from that distribution.
+ *
+ *   z[t,e] = sum_i x[t,i] * w_router[e,i] + (bias ? bias[e] : 0)   (fp32 accumulate)
+ *   score  = softmax over all E of z[t,:]  (MOE_SCORE_SOFTMAX)
+ *          | 1 / (1 + exp(-z[t,e]))       (MOE_SCORE_SIGMOID)
+ *   topk_ids[t,:]     = the K experts with the largest z (both scores are
+ *                       increasing in z), in descending order of z; equal z
+ *                       go to the lower expert id first;
+ *   topk_weights[t,k] = score of topk_ids[t,k], divided by the sum of the K
+ *                       selected scores when cfg->renormalize is set.
+ * Arguments:
+ *   x            [T, d]  dtype            tokens
+ *   w_router     [E, d]  dtype            router weight ([out, in])
+ *   bias         [E]     fp32 or NULL     added to the logits (used for selection and score)
+ *   topk_ids     [T, K]  int32  (out)
+ *   topk_weights [T, K]  fp32   (out)
+ *   logits       [T, E]  fp32   (out, optional: NULL to skip) the z above
+ */
+moe_status_t moe_route(const moe_config_t* cfg, const void* x, const void* w_router,
+                       const float* bias, int32_t* topk_ids, float* topk_weights,
+                       float* logits, moe_stream_t stream);
+
+/*
+ * moe_dispatch -- count tokens per expert and copy routed tokens into
+ * expert-contiguous rows, recording where each row came from.
+ * [PPLX] Dispatch: per-destination-expert token counts; tokens unpacked into a
+ * contiguous per-expert buffer that feeds the grouped GEMM; source indices
+ * stored in a buffer shared with the combine.  Unlike the pages' receive
+ * kernel, the row order here is stable (expert ascending, then token
+ * ascending), so the layout is unique and deterministic.
+ *
+ *   expert_counts[e]  = #{(t,k) : topk_ids[t,k] == e}  for all E experts
+ *   expert_offsets[j] = sum of expert_counts[expert_begin + i] for i < j,
+ *                       j = 0..E_loc (so expert_offsets[E_loc] = N_loc, the local rows)
+ *   for local expert e (ascending), token t (ascending) with topk_ids[t,k] == e:
+ *       row = expert_offsets[e - expert_begin] + (rank of t among such tokens)
+ *       x_sorted[row,:] = x[t,:] (bit copy); src_index[row] = t*K + k; row_of[t*K+k] = row
+ *   row_of[t*K+k] = -1 for assignments to non-local or invalid experts.
+ * Ids outside [0, E) are skipped and counted into the int32 at the start of
+ * the workspace ("n_invalid", valid after the stream reaches this point).
+ * Arguments:
+ *   x              [T, d]     dtype
+ *   topk_ids       [T, K]     int32
+ *   expert_counts  [E]        int32 (out)
+ *   expert_offsets [E_loc+1]  int32 (out)
+ *   x_sorted       [T*K, d]   dtype (out; rows >= N_loc untouched)
+ *   src_index      [T*K]      int32 (out; entries >= N_loc untouched)
+ *   row_of         [T*K]      int32 (out)
+ *   workspace      >= moe_workspace_bytes(cfg, MOE_WS_DISPATCH) bytes, 256-byte aligned
+ */
+moe_status_t moe_dispatch(const moe_config_t* cfg, const void* x, const int32_t* topk_ids,
+                          int32_t* expert_counts, int32_t* expert_offsets, void* x_sorted,
+                          int32_t* src_index, int32_t* row_of, void* workspace,
+                          size_t workspace_bytes, moe_stream_t stream);
+
+/*
+ * moe_expert_mlp -- grouped SiLU-gated MLP over the expert-contiguous rows,
+ * plus optional shared experts over all tokens.
+ * [PPLX] Introduction (experts are small MLPs), Dispatch (the contiguous
+ * buffer feeds a downstream grouped GEMM); [DBO] Introduction (shared
+ * expert "S" in the overlap schedule).
+ *
+ *   for local expert j, rows r in [expert_offsets[j], expert_offsets[j+1]):
+ *     h[r,:]        = SiLU(x_sorted[r,:] . w_gate[j]^T) * (x_sorted[r,:] . w_up[j]^T)
+ *     y_sorted[r,:] = h[r,:] . w_down[j]^T,         SiLU(z) = z / (1 + exp(-z))
+ *   for shared expert s < num_shared: the same MLP on every token of x,
+ *     weights ws_*[s], result in y_shared[s].
+ * fp32 accumulation; bf16 configs keep h in bf16 and write bf16 outputs.
+ * Row counts are read on the device from expert_offsets (no host sync).
+ * Arguments:
+ *   x_sorted       [T*K, d]      dtype   (from moe_dispatch)
+ *   expert_offsets [E_loc+1]     int32   (from moe_dispatch)
+ *   w_gate, w_up   [E_loc, I, d] dtype
+ *   w_down         [E_loc, d, I] dtype
+ *   y_sorted       [T*K, d]      dtype (out; rows >= N_loc untouched)
+ *   x              [T, d]        dtype, shared experts' input (NULL iff num_shared == 0)
+ *   ws_gate, ws_up [num_shared, I, d], ws_down [num_shared, d, I]  (NULL iff num_shared == 0)
+ *   y_shared       [num_shared, T, d] dtype (out; NULL iff num_shared == 0)
+ *   workspace      >= moe_workspace_bytes(cfg, MOE_WS_EXPERT_MLP) bytes, 256-byte aligned
+ */
+moe_status_t moe_expert_mlp(const moe_config_t* cfg, const void* x_sorted,
+                            const int32_t* expert_offsets, const void* w_gate, const void* w_up,
+                            const void* w_down, void* y_sorted, const void* x,
+                            const void* ws_gate, const void* ws_up, const void* ws_down,
+                            void* y_shared, void* workspace, size_t workspace_bytes,
+                            moe_stream_t stream);
+
+/*
+ * moe_combine -- weighted sum of each token's expert outputs, back in token order.
+ * [PPLX] Introduction (output = weighted sum of the selected experts'
+ * outputs), Sharding and Parallelism (the accumulation fused into the gather),
+ * Combine (router weights applied on the receiving side; the result written to
+ * an externally allocated tensor).
+ *
+ *   out[t,:] = round( sum_{k=0..K-1, row_of[t*K+k] >= 0} topk_weights[t,k] * y_sorted[row_of[t*K+k],:]
+ *                     + sum_{s=0..num_shared-1} y_shared[s,t,:] )
+ * accumulated in fp32 in exactly that order, rounded once to dtype.
+ * Assignments with row_of = -1 (experts hosted elsewhere) contribute nothing:
+ * out is this GPU's partial sum.
+ * Arguments:
+ *   y_sorted     [T*K, d]           dtype
+ *   row_of       [T*K]              int32 (from moe_dispatch)
+ *   topk_weights [T, K]             fp32  (from moe_route)
+ *   y_shared     [num_shared, T, d] dtype, or NULL iff num_shared == 0
+ *   out          [T, d]             dtype (out)
+ */
+moe_status_t moe_combine(const moe_config_t* cfg, const void* y_sorted, const int32_t* row_of,
+                         const float* topk_weights, const void* y_shared, void* out,
+                         moe_stream_t stream);
+
+/* Tensors of a whole-layer call (moe_forward, moe_forward_dbo). */
+typedef struct moe_layer_tensors {
+  const void* x;             /* [T, d] dtype                                     */
+  const void* w_router;      /* [E, d] dtype                                     */
+  const float* bias;         /* [E] fp32 or NULL                                 */
+  const void* w_gate;        /* [E_loc, I, d] dtype                              */
+  const void* w_up;          /* [E_loc, I, d] dtype                              */
+  const void* w_down;        /* [E_loc, d, I] dtype                              */
+  const void* ws_gate;       /* [num_shared, I, d] dtype or NULL                 */
+  const void* ws_up;         /* [num_shared, I, d] dtype or NULL                 */
+  const void* ws_down;       /* [num_shared, d, I] dtype or NULL                 */
+  void* out;                 /* [T, d] dtype (out)                               */
+  int32_t* topk_ids;         /* [T, K] int32 (out)                               */
+  float* topk_weights;       /* [T, K] fp32 (out)                                */
+} moe_layer_tensors_t;
+
+/*
+ * moe_forward -- the whole layer on one stream: moe_route, moe_dispatch,
+ * moe_expert_mlp, moe_combine, with every intermediate (x_sorted, y_sorted,
+ * maps, counts, h, y_shared) carved from the caller's workspace of at least
+ * moe_workspace_bytes(cfg, MOE_WS_FORWARD) bytes (256-byte aligned).
+ */
+moe_status_t moe_forward(const moe_config_t* cfg, const moe_layer_tensors_t* tensors,
+                         void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/*
+ * moe_forward_dbo -- the layer as two microbatches on two streams of one GPU.
+ * [DBO] UBatchRunner: the token count is padded up to a multiple of 256 and
+ * split at the midpoint: microbatch 0 = tokens [0, min(mid, T)), microbatch 1
+ * = [mid, T) (no work when empty).  [DBO] Introduction and Interfaces: one
+ * microbatch's dispatch/combine runs on the communication stream while the
+ * other microbatch's expert compute runs on the compute stream:
+ *     compute: route0, route1, mlp0, mlp1
+ *     comm:    dispatch0, dispatch1, combine0, combine1
+ * with events ordering each microbatch's steps, so dispatch1 overlaps mlp0
+ * and combine0 overlaps mlp1.  Every output row depends only on its own
+ * token, so the result is bitwise equal to moe_forward's.
+ * If T < min_tokens_to_split (or microbatch 1 is empty) the unsplit forward
+ * runs on `compute`.  On return, work enqueued later on `compute` waits for
+ * both microbatches; `comm` may be the same stream as `compute`.
+ * workspace >= moe_workspace_bytes(cfg, MOE_WS_FORWARD_DBO) bytes.
+ */
+moe_status_t moe_forward_dbo(const moe_config_t* cfg, const moe_layer_tensors_t* tensors,
+                             void* workspace, size_t workspace_bytes,
+                             int32_t min_tokens_to_split, moe_stream_t compute,
+                             moe_stream_t comm);
+
+/* Bytes of workspace needed by a call of the given kind (MOE_WS_*), or 0 for
+ * an invalid configuration.  Pure host function. */
+size_t moe_workspace_bytes(const moe_config_t* cfg, int32_t kind);
+
+/* Token index at which moe_forward_dbo splits T tokens (pure host function). */
+int32_t moe_dbo_split_point(int32_t num_tokens);
+
+/* Static description of a status code (host). */
+const char* moe_status_string(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

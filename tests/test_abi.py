@@ -1,0 +1,102 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from combine_router_softmax_top_amd import binding as B
+from combine_router_softmax_top_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(moe_[a-z_]+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return B.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ["moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_forward_dbo"]:
+        assert n in names
+    assert sorted(B.EXPORTED) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert B.status_string(B.MOE_OK) == "ok"
+    assert "workspace" in B.status_string(B.MOE_ERR_WORKSPACE_TOO_SMALL)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("top_k", 0, B.MOE_ERR_INVALID_ARGUMENT),
+    ("top_k", 17, B.MOE_ERR_INVALID_ARGUMENT),
+    ("num_experts", 513, B.MOE_ERR_INVALID_ARGUMENT),
+    ("num_tokens", 0, B.MOE_ERR_INVALID_ARGUMENT),
+    ("expert_end", 257, B.MOE_ERR_INVALID_ARGUMENT),
+    ("expert_begin", 32, B.MOE_ERR_INVALID_ARGUMENT),
+    ("num_shared", 5, B.MOE_ERR_INVALID_ARGUMENT),
+    ("score", 7, B.MOE_ERR_INVALID_ARGUMENT),
+    ("dtype", 9, B.MOE_ERR_INVALID_ARGUMENT),
+    ("hidden", 7000, B.MOE_ERR_UNSUPPORTED),
+    ("intermediate", 100, B.MOE_ERR_UNSUPPORTED),
+])
+def test_config_validation_on_host(lib, field, value, status):
+    cs = B.config_struct(W.CONFIGS["dsv3_prefill_ep"])
+    setattr(cs, field, value)
+    P = ctypes.c_void_p
+    st = lib.moe_route(ctypes.byref(cs), P(16), P(16), None, P(16), P(16), None, None)
+    assert st == status
+    assert lib.moe_workspace_bytes(ctypes.byref(cs), B.MOE_WS_FORWARD) == 0
+
+
+def test_null_pointers_and_small_workspace_rejected_on_host(lib):
+    cs = B.config_struct(W.CONFIGS["dsv3_prefill_ep"])
+    P = ctypes.c_void_p
+    assert lib.moe_route(ctypes.byref(cs), None, P(16), None, P(16), P(16), None, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_route(ctypes.byref(cs), P(8), P(16), None, P(16), P(16), None, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT  # misaligned activations
+    need = lib.moe_workspace_bytes(ctypes.byref(cs), B.MOE_WS_DISPATCH)
+    st = lib.moe_dispatch(ctypes.byref(cs), P(256), P(256), P(256), P(256), P(256), P(256),
+                          P(256), P(256), need - 1, None)
+    assert st == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    # shared-expert pointers must be given iff num_shared > 0
+    assert lib.moe_combine(ctypes.byref(cs), P(256), P(256), P(256), P(256), P(256), None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    cs3 = B.config_struct(W.CONFIGS["dsv2lite_decode"])
+    assert lib.moe_combine(ctypes.byref(cs3), P(256), P(256), P(256), None, P(256), None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    ws = lib.moe_workspace_bytes(ctypes.byref(cs3), B.MOE_WS_EXPERT_MLP)
+    assert lib.moe_expert_mlp(ctypes.byref(cs3), P(256), P(256), P(256), P(256), P(256), P(256),
+                              None, None, None, None, None, P(256), ws, None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_sizes_grow_with_tokens(lib):
+    cfg = W.CONFIGS["dsv3_prefill_ep"]
+    small = B.workspace_bytes(cfg.with_tokens(128), B.MOE_WS_FORWARD)
+    big = B.workspace_bytes(cfg, B.MOE_WS_FORWARD)
+    assert 0 < small < big
+    dbo = B.workspace_bytes(W.CONFIGS["dsv3_dual_microbatch"], B.MOE_WS_FORWARD_DBO)
+    assert dbo >= 2 * B.workspace_bytes(cfg, B.MOE_WS_FORWARD) * 0.99
+
+
+@pytest.mark.parametrize("T,mid", [(8192, 4096), (100, 128), (300, 256), (256, 128), (1, 128)])
+def test_dbo_split_point(lib, T, mid):
+    assert B.dbo_split_point(T) == mid
