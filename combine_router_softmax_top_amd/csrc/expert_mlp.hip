@@ -150,23 +150,6 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
   }
   const int st_off = ((tid >> 3) * kRowBytes) + ((c ^ swz) * 16);
 
-  uint4 ra[kLoadsPerThread], rb[kLoadsPerThread];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < kLoadsPerThread; ++j) {
-      ra[j] = *reinterpret_cast<const uint4*>(pa[j] + k0);
-      rb[j] = *reinterpret_cast<const uint4*>(pb[j] + k0);
-    }
-  };
-  auto lstore = [&](int stage) {
-    uint8_t* s = lds + stage * kStageBytes;
-#pragma unroll
-    for (int j = 0; j < kLoadsPerThread; ++j) {
-      *reinterpret_cast<uint4*>(s + st_off + j * 32 * kRowBytes) = ra[j];
-      *reinterpret_cast<uint4*>(s + kBM * kRowBytes + st_off + j * 32 * kRowBytes) = rb[j];
-    }
-  };
-
   f32x16 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -189,12 +172,29 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
   const int lsw = lane & 7;
 
   const int nk = Kdim / kBK;
-  gload(0);
-  lstore(0);
+  u32x4 ra[kLoadsPerThread], rb[kLoadsPerThread];
+#pragma unroll
+  for (int j = 0; j < kLoadsPerThread; ++j) {
+    ra[j] = *reinterpret_cast<const u32x4*>(pa[j]);
+    rb[j] = *reinterpret_cast<const u32x4*>(pb[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < kLoadsPerThread; ++j) {
+    *reinterpret_cast<u32x4*>(lds + st_off + j * 32 * kRowBytes) = ra[j];
+    *reinterpret_cast<u32x4*>(lds + kBM * kRowBytes + st_off + j * 32 * kRowBytes) = rb[j];
+  }
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
+    const bool more = kt + 1 < nk;
+    if (more) {
+      const int k0 = (kt + 1) * kBK;
+#pragma unroll
+      for (int j = 0; j < kLoadsPerThread; ++j) {
+        ra[j] = *reinterpret_cast<const u32x4*>(pa[j] + k0);
+        rb[j] = *reinterpret_cast<const u32x4*>(pb[j] + k0);
+      }
+    }
     const uint8_t* sa = lds + cur * kStageBytes;
     const uint8_t* sb = sa + kBM * kRowBytes;
 #pragma unroll
@@ -213,7 +213,14 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
+    if (more) {
+      uint8_t* st = lds + (cur ^ 1) * kStageBytes;
+#pragma unroll
+      for (int j = 0; j < kLoadsPerThread; ++j) {
+        *reinterpret_cast<u32x4*>(st + st_off + j * 32 * kRowBytes) = ra[j];
+        *reinterpret_cast<u32x4*>(st + kBM * kRowBytes + st_off + j * 32 * kRowBytes) = rb[j];
+      }
+    }
     __syncthreads();
   }
 
