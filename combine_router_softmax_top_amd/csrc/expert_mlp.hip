@@ -12,10 +12,11 @@
 //     256 rows x (128 gate + 128 up) columns, multiplied together in the
 //     epilogue, so h is written once, in bf16); four waves in a 2x2 grid,
 //     each a 128x128 sub-tile of 4x4 v_mfma_f32_32x32x16_bf16 blocks;
-//   * 64-deep k-tiles staged through LDS, double-buffered: the next tile's
-//     global loads are in flight while the current one feeds the MFMAs; rows
-//     are 128 B in LDS with the 16-byte chunk index XORed with (row & 7), so
-//     both the staging writes and the fragment reads are bank-conflict free;
+//   * 32-deep k-tiles move straight from global memory into a ring of four
+//     LDS stages (global_load_lds, 16 B per lane), issued three tiles ahead,
+//     so HBM latency hides behind the MFMAs of the tiles in between; the
+//     rows are XOR-swizzled in 16-byte chunks so the fragment reads are free
+//     of bank conflicts;
 //   * ragged groups: the tile list (expert, row tile, column tile) is derived
 //     on the device from the expert offsets; the grid is the host's upper
 //     bound and surplus workgroups exit at once (no host synchronisation);
@@ -92,23 +93,91 @@ __device__ __forceinline__ int xcd_tile_id() {
 
 // ------------------------------------------------------------------ bf16 MFMA GEMM
 
-constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kRowBytes = kBK * 2;                        // 128 B per staged row
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 64 KB
-constexpr int kLoadsPerThread = kBM * (kRowBytes / 16) / 256;  // 8 chunks of A, 8 of B
+constexpr int kBM = 256, kBN = 256, kBK = 32;
+constexpr int kThreads = 512;                             // 8 waves, 2 per SIMD
+constexpr int kRowBytes = kBK * 2;                        // 64 B per staged row
+constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 32 KB
+constexpr int kStages = 4;                                // 128 KB of LDS
+constexpr int kDmaPerTile = kStageBytes / (kThreads * 16);  // 4 x 16 B per thread
+constexpr int kDmaA = kDmaPerTile / 2;
 
 enum { EPI_STORE = 0, EPI_SILU_GLU = 1 };
 
 __device__ __forceinline__ float silu_f(float z) { return z / (1.f + __expf(-z)); }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS tile layout: 64-byte rows (32 bf16 of k) of four 16-byte chunks; row R
+// keeps logical chunk c in physical slot c ^ swz(R), swz(R) = ((R>>1)^(R>>3)) & 3.
+// A 64-lane ds_read_b128 of 32 consecutive rows at one logical chunk then hits
+// distinct 16-byte slots within every 8-lane (128 B) and 16-lane (256 B)
+// service group, i.e. no bank conflicts.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+// One wave's share of staging a k-tile (A then B, 32 KB per workgroup) with
+// direct global->LDS loads: instruction j of wave w fills 1 KB of LDS = rows
+// (8j + w)*16 .. +16 of the A (j < 2) or B (j >= 2) tile; lane l covers row
+// +l/4, physical chunk l%4, so its source is logical chunk (l%4) ^ swz(row).
+__device__ __forceinline__ void stage_tile(uint8_t* stage, const uint8_t* a_tile,
+                                           const uint8_t* b_lo, const uint8_t* b_hi,
+                                           const uint32_t (&off)[kDmaPerTile], int wave,
+                                           int kbytes) {
+#pragma unroll
+  for (int j = 0; j < kDmaPerTile; ++j) {
+    const uint8_t* src = j < kDmaA ? a_tile : (j < kDmaA + kDmaA / 2 ? b_lo : b_hi);
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + kbytes + off[j]),
+                                     (lds_ptr_t)(stage + (j * 8 + wave) * 1024), 16, 0, 0);
+  }
+}
+
+struct Frags {
+  bf16x8 a[4], b[2];
+};
+
+// Fragments of k-step ks (16 deep) of a staged tile: A rows a_row0 + 32i,
+// B rows b_row[j]; xa/xb hold (lane's k-group) ^ swz(row).
+__device__ __forceinline__ void load_frags(const uint8_t* stage, int ks, int a_row0,
+                                           const int (&b_row)[2], const int (&xa)[4],
+                                           const int (&xb)[2], Frags& f) {
+  const uint8_t* sa = stage;
+  const uint8_t* sb = stage + kBM * kRowBytes;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.a[i] = *reinterpret_cast<const bf16x8*>(sa + (a_row0 + i * 32) * kRowBytes +
+                                              (((2 * ks) ^ xa[i]) << 4));
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    f.b[j] = *reinterpret_cast<const bf16x8*>(sb + b_row[j] * kRowBytes +
+                                              (((2 * ks) ^ xb[j]) << 4));
+}
+
+__device__ __forceinline__ void mma_step(const Frags& f, f32x16 (&acc)[4][2]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Wait until this wave's loads of the oldest in-flight stage have landed (two
+// later tiles' loads may stay in flight: loads complete in issue order) and
+// its LDS reads have returned; then a workgroup barrier without a memory
+// fence, so the later stages' loads stay in flight across it.
+__device__ __forceinline__ void wait_stage_and_barrier() {
+  static_assert(kStages == 4 && kDmaPerTile == 4, "vmcnt immediate assumes 4 stages x 4 loads");
+  asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ A, int lda, long long strideA_batch,
     const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, long long strideB_group, long long strideB_batch,
     uint16_t* __restrict__ C, int ldc, long long strideC_batch,
     const int32_t* __restrict__ offsets, int n_groups, int fixed_rows, int N, int Kdim) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
 
   // Output columns per tile: EPI_STORE 256, EPI_SILU_GLU 128 (gate and up 128 each).
   constexpr int kNOut = EPI == EPI_SILU_GLU ? kBN / 2 : kBN;
@@ -117,8 +186,9 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
   if (!find_tile(xcd_tile_id(), offsets, n_groups, fixed_rows, kBM, nN, tl)) return;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3;   // 2 x 4 waves, each 128 rows x 64 columns
   const int m0 = tl.m_tile * kBM;
   const int n0 = tl.n_tile * kNOut;
   const long long zb = (long long)blockIdx.z * strideB_batch;
@@ -127,102 +197,83 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
   const uint16_t* bu = EPI == EPI_SILU_GLU ? B1 + zb + (long long)tl.group * strideB_group : bg;
   uint16_t* Cz = C + (long long)blockIdx.z * strideC_batch;
 
-  // Staging assignment: chunk c = tid & 7 of rows r_j = tid/8 + 32 j.
-  const int c = tid & 7;
-  const int swz = (tid >> 3) & 7;
-  const uint16_t* pa[kLoadsPerThread];
-  const uint16_t* pb[kLoadsPerThread];
+  // Per-lane byte offsets of the staged rows inside the tile's operand blocks.
+  // B rows 0..127 come from b_lo, rows 128..255 from b_hi (the up weights in
+  // the gate/up pass, the next 128 rows of the same weights otherwise).
+  const uint8_t* a_tile = reinterpret_cast<const uint8_t*>(A + (long long)(tl.row0 + m0) * lda);
+  const uint8_t* b_lo = reinterpret_cast<const uint8_t*>(bg + (long long)n0 * Kdim);
+  const uint8_t* b_hi = EPI == EPI_SILU_GLU
+                            ? reinterpret_cast<const uint8_t*>(bu + (long long)n0 * Kdim)
+                            : b_lo;
+  const int a_last = tl.rows - 1 - m0;
+  const int b_last = N - 1 - n0;
+  uint32_t off[kDmaPerTile];
 #pragma unroll
-  for (int j = 0; j < kLoadsPerThread; ++j) {
-    const int r = (tid >> 3) + 32 * j;
-    const int am = min(m0 + r, tl.rows - 1);
-    pa[j] = A + (long long)(tl.row0 + am) * lda + c * 8;
-    int brow;
-    const uint16_t* bbase;
-    if (EPI == EPI_SILU_GLU) {
-      bbase = r < kNOut ? bg : bu;
-      brow = min(n0 + (r & (kNOut - 1)), N - 1);
+  for (int j = 0; j < kDmaPerTile; ++j) {
+    const int r = ((j % kDmaA) * 8 + wave) * 16 + (lane >> 2);  // row within A or B tile
+    const int lchunk = (lane & 3) ^ swz(r);
+    if (j < kDmaA) {
+      off[j] = (uint32_t)(min(r, a_last) * lda * 2 + lchunk * 16);
     } else {
-      bbase = bg;
-      brow = min(n0 + r, N - 1);
+      // r is the B-tile row; rows 128.. come from b_hi
+      const int br = EPI == EPI_SILU_GLU ? (r & (kNOut - 1)) : r;
+      off[j] = (uint32_t)(min(br, b_last) * Kdim * 2 + lchunk * 16);
     }
-    pb[j] = bbase + (long long)brow * Kdim + c * 8;
   }
-  const int st_off = ((tid >> 3) * kRowBytes) + ((c ^ swz) * 16);
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // Fragment rows: A rows wm*128 + i*32 + (lane & 31); B rows per sub-tile.
-  int b_row[4];
+  // Fragment rows: A rows wm*128 + i*32 + (lane & 31); B rows: the wave's 64
+  // output columns (gate/up pass: 32 gate rows and the matching 32 up rows).
+  int b_row[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     if (EPI == EPI_SILU_GLU)
-      b_row[j] = (j < 2 ? 0 : kNOut) + wn * 64 + (j & 1) * 32 + (lane & 31);
+      b_row[j] = j * kNOut + wn * 32 + (lane & 31);
     else
-      b_row[j] = wn * 128 + j * 32 + (lane & 31);
+      b_row[j] = wn * 64 + j * 32 + (lane & 31);
   }
   const int a_row0 = wm * 128 + (lane & 31);
   const int kgrp = lane >> 5;
-  const int lsw = lane & 7;
+  int xa[4], xb[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xa[i] = kgrp ^ swz(a_row0 + i * 32);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) xb[j] = kgrp ^ swz(b_row[j]);
 
+  // A ring of kStages LDS stages: k-tile t lives in stage t % kStages and its
+  // loads are issued kStages-1 tiles ahead of its use.  Per tile (two
+  // k-steps): the loads of tile t+3 and the second k-step's fragment reads
+  // are interleaved with the first k-step's MFMAs; the stage wait and barrier
+  // come before the second k-step's MFMAs, which then overlap the fragment
+  // reads of tile t+1.  The body has no branches: every iteration issues one
+  // tile of loads, past the last tile re-reading the last tile into a stage
+  // that is never read again, and reads next-tile fragments that the last
+  // iteration never uses.
   const int nk = Kdim / kBK;
-  u32x4 ra[kLoadsPerThread], rb[kLoadsPerThread];
-#pragma unroll
-  for (int j = 0; j < kLoadsPerThread; ++j) {
-    ra[j] = *reinterpret_cast<const u32x4*>(pa[j]);
-    rb[j] = *reinterpret_cast<const u32x4*>(pb[j]);
-  }
-#pragma unroll
-  for (int j = 0; j < kLoadsPerThread; ++j) {
-    *reinterpret_cast<u32x4*>(lds + st_off + j * 32 * kRowBytes) = ra[j];
-    *reinterpret_cast<u32x4*>(lds + kBM * kRowBytes + st_off + j * 32 * kRowBytes) = rb[j];
-  }
-  __syncthreads();
+  for (int t = 0; t < kStages - 1; ++t)
+    stage_tile(lds + t * kStageBytes, a_tile, b_lo, b_hi, off, wave, min(t, nk - 1) * kRowBytes);
+  wait_stage_and_barrier();
+  Frags f0, f1;
+  load_frags(lds, 0, a_row0, b_row, xa, xb, f0);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = (kt + 1) * kBK;
-#pragma unroll
-      for (int j = 0; j < kLoadsPerThread; ++j) {
-        ra[j] = *reinterpret_cast<const u32x4*>(pa[j] + k0);
-        rb[j] = *reinterpret_cast<const u32x4*>(pb[j] + k0);
-      }
-    }
-    const uint8_t* sa = lds + cur * kStageBytes;
-    const uint8_t* sb = sa + kBM * kRowBytes;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int pc = ((ks * 2 + kgrp) ^ lsw) * 16;
-      bf16x8 af[4], bf[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(sa + (a_row0 + i * 32) * kRowBytes + pc);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const bf16x8*>(sb + b_row[j] * kRowBytes + pc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      uint8_t* st = lds + (cur ^ 1) * kStageBytes;
-#pragma unroll
-      for (int j = 0; j < kLoadsPerThread; ++j) {
-        *reinterpret_cast<u32x4*>(st + st_off + j * 32 * kRowBytes) = ra[j];
-        *reinterpret_cast<u32x4*>(st + kBM * kRowBytes + st_off + j * 32 * kRowBytes) = rb[j];
-      }
-    }
-    __syncthreads();
+    const uint8_t* cur = lds + (kt % kStages) * kStageBytes;
+    const int tn = kt + kStages - 1;
+    stage_tile(lds + (tn % kStages) * kStageBytes, a_tile, b_lo, b_hi, off, wave,
+               min(tn, nk - 1) * kRowBytes);
+    load_frags(cur, 1, a_row0, b_row, xa, xb, f1);
+    mma_step(f0, acc);
+    wait_stage_and_barrier();
+    load_frags(lds + ((kt + 1) % kStages) * kStageBytes, 0, a_row0, b_row, xa, xb, f0);
+    mma_step(f1, acc);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // Epilogue.  Accumulator element r of lane l in a 32x32 block holds
   // row (r/4)*8 + (l/32)*4 + r%4, column l%32.
@@ -236,15 +287,12 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(
       if (m >= tl.rows) continue;
       uint16_t* crow = Cz + (long long)(tl.row0 + m) * ldc;
       if (EPI == EPI_SILU_GLU) {
+        const int n = n0 + wn * 32 + col_l;
+        if (n < N) crow[n] = f32_to_bf16_bits(silu_f(acc[i][0][r]) * acc[i][1][r]);
+      } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int n = n0 + wn * 64 + j * 32 + col_l;
-          if (n < N) crow[n] = f32_to_bf16_bits(silu_f(acc[i][j][r]) * acc[i][j + 2][r]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = n0 + wn * 128 + j * 32 + col_l;
           if (n < N) crow[n] = f32_to_bf16_bits(acc[i][j][r]);
         }
       }
@@ -342,7 +390,7 @@ hipError_t run_gemm(int dtype, const GemmArgs& g, hipStream_t s) {
     constexpr int nout = EPI == EPI_SILU_GLU ? kBN / 2 : kBN;
     const int rt = g.offsets ? g.max_row_tiles_bound : ceil_div(g.fixed_rows, kBM);
     const dim3 grid(grid_for(rt, ceil_div(g.N, nout)), 1, g.batch);
-    hipLaunchKernelGGL(gemm_bf16_kernel<EPI>, grid, dim3(256), 0, s,
+    hipLaunchKernelGGL(gemm_bf16_kernel<EPI>, grid, dim3(kThreads), 0, s,
                        static_cast<const uint16_t*>(g.A), g.lda, g.strideA_batch,
                        static_cast<const uint16_t*>(g.B0), static_cast<const uint16_t*>(g.B1),
                        g.strideB_group, g.strideB_batch, static_cast<uint16_t*>(g.C), g.ldc,
