@@ -21,7 +21,7 @@ _LIB = None
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
-MOE_WS_DISPATCH, MOE_WS_EXPERT_MLP, MOE_WS_FORWARD, MOE_WS_FORWARD_DBO = range(4)
+MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_EXPERT_MLP, MOE_WS_FORWARD, MOE_WS_FORWARD_DBO = range(5)
 
 EXPORTED = ["moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_forward",
             "moe_forward_dbo", "moe_workspace_bytes", "moe_dbo_split_point", "moe_status_string"]
@@ -61,7 +61,7 @@ def lib() -> ctypes.CDLL:
         C = ctypes.POINTER(ConfigStruct)
         LT = ctypes.POINTER(LayerTensorsStruct)
         sigs = {
-            "moe_route": [C, P, P, P, P, P, P, P],
+            "moe_route": [C, P, P, P, P, P, P, P, SZ, P],
             "moe_dispatch": [C, P, P, P, P, P, P, P, P, SZ, P],
             "moe_expert_mlp": [C, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
             "moe_combine": [C, P, P, P, P, P, P],
@@ -147,7 +147,8 @@ def dbo_split_point(num_tokens: int) -> int:
     return int(lib().moe_dbo_split_point(int(num_tokens)))
 
 
-def moe_route(cfg, x, w_router, bias, topk_ids, topk_weights, logits=None, stream=None):
+def moe_route(cfg, x, w_router, bias, topk_ids, topk_weights, logits=None, workspace=None,
+              stream=None):
     c = _cs(cfg)
     T, d, E, K, dt = c.num_tokens, c.hidden, c.num_experts, c.top_k, _act(c)
     st = lib().moe_route(ctypes.byref(c), _p(x, "x", (T, d), dt),
@@ -155,7 +156,9 @@ def moe_route(cfg, x, w_router, bias, topk_ids, topk_weights, logits=None, strea
                          _p(bias, "bias", (E,), torch.float32),
                          _p(topk_ids, "topk_ids", (T, K), torch.int32),
                          _p(topk_weights, "topk_weights", (T, K), torch.float32),
-                         _p(logits, "logits", (T, E), torch.float32), _stream(stream))
+                         _p(logits, "logits", (T, E), torch.float32), _p(workspace, "workspace"),
+                         0 if workspace is None else workspace.numel() * workspace.element_size(),
+                         _stream(stream))
     _check("moe_route", st)
 
 
@@ -242,9 +245,11 @@ def moe_forward_dbo(cfg, tensors: dict, workspace, min_tokens_to_split: int = 0,
     _check("moe_forward_dbo", st)
 
 
-def alloc_workspace(cfg, kind: int, device="cuda") -> torch.Tensor:
+def alloc_workspace(cfg, kind: int, device="cuda") -> Optional[torch.Tensor]:
     n = workspace_bytes(cfg, kind)
     if n == 0:
+        if kind == MOE_WS_ROUTE:
+            return None  # fp32 layers need no router workspace
         raise MoEError("moe_workspace_bytes", MOE_ERR_INVALID_ARGUMENT)
     # torch's caching allocator returns 256-byte (or larger) aligned blocks.
     return torch.empty(n, dtype=torch.uint8, device=device)

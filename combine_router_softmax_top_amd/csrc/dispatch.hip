@@ -73,18 +73,27 @@ __global__ __launch_bounds__(kCH) void dispatch_count_kernel(
 }
 
 constexpr int kScanThreads = 1024;
+constexpr int kScanLdsInts = 12288;  // chunk histograms staged in LDS when they fit (48 KB)
 
 __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     const int32_t* __restrict__ hist, int n_chunks, int E, int eb, int ee,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ base,
     int32_t* __restrict__ n_invalid) {
+  __shared__ int32_t hs[kScanLdsInts];
   __shared__ int32_t loc[MOE_MAX_EXPERTS];
   __shared__ int32_t scan[2][MOE_MAX_EXPERTS];
   const int tid = threadIdx.x;
   const int n_loc = ee - eb;
+  const int n_hist = n_chunks * (E + 1);
+  // One coalesced pass over the histograms into LDS (else read them in place).
+  const bool staged = n_hist <= kScanLdsInts;
+  if (staged)
+    for (int i = tid; i < n_hist; i += kScanThreads) hs[i] = hist[i];
+  __syncthreads();
+  const int32_t* h = staged ? hs : hist;
   for (int e = tid; e <= E; e += kScanThreads) {
     int s = 0;
-    for (int c = 0; c < n_chunks; ++c) s += hist[(size_t)c * (E + 1) + e];
+    for (int c = 0; c < n_chunks; ++c) s += h[(size_t)c * (E + 1) + e];
     if (e == E) *n_invalid = s;
     else {
       counts[e] = s;
@@ -109,7 +118,7 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     int run = scan[cur][j] - loc[j];
     for (int c = 0; c < n_chunks; ++c) {
       base[(size_t)c * n_loc + j] = run;
-      run += hist[(size_t)c * (E + 1) + eb + j];
+      run += h[(size_t)c * (E + 1) + eb + j];
     }
   }
 }

@@ -38,6 +38,7 @@ moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ER
 
 // Intermediates of one whole-layer call, carved from a workspace.
 struct LayerScratch {
+  void* route_ws;
   int32_t* counts;
   int32_t* offsets;
   int32_t* src_index;
@@ -53,7 +54,8 @@ size_t layer_scratch(const moe_config_t& c, void* base, LayerScratch* out) {
   const size_t T = c.num_tokens, K = c.top_k, d = c.hidden;
   const size_t elem = c.dtype == MOE_BF16 ? 2 : 4;
   const size_t n_loc = c.expert_end - c.expert_begin;
-  const size_t sizes[9] = {
+  const size_t sizes[10] = {
+      align_up(moe::route_workspace_bytes(c), 256),
       align_up(c.num_experts * 4, 256),
       align_up((n_loc + 1) * 4, 256),
       align_up(T * K * 4, 256),
@@ -63,23 +65,24 @@ size_t layer_scratch(const moe_config_t& c, void* base, LayerScratch* out) {
       align_up((size_t)c.num_shared * T * d * elem, 256),
       align_up(moe::dispatch_workspace_bytes(c), 256),
       align_up(moe::mlp_workspace_bytes(c), 256)};
-  size_t off[9];
+  size_t off[10];
   size_t total = 0;
-  for (int i = 0; i < 9; ++i) {
+  for (int i = 0; i < 10; ++i) {
     off[i] = total;
     total += sizes[i];
   }
   if (out) {
     char* b = static_cast<char*>(base);
-    out->counts = reinterpret_cast<int32_t*>(b + off[0]);
-    out->offsets = reinterpret_cast<int32_t*>(b + off[1]);
-    out->src_index = reinterpret_cast<int32_t*>(b + off[2]);
-    out->row_of = reinterpret_cast<int32_t*>(b + off[3]);
-    out->x_sorted = b + off[4];
-    out->y_sorted = b + off[5];
-    out->y_shared = c.num_shared > 0 ? b + off[6] : nullptr;
-    out->dispatch_ws = b + off[7];
-    out->mlp_ws = b + off[8];
+    out->route_ws = b + off[0];
+    out->counts = reinterpret_cast<int32_t*>(b + off[1]);
+    out->offsets = reinterpret_cast<int32_t*>(b + off[2]);
+    out->src_index = reinterpret_cast<int32_t*>(b + off[3]);
+    out->row_of = reinterpret_cast<int32_t*>(b + off[4]);
+    out->x_sorted = b + off[5];
+    out->y_sorted = b + off[6];
+    out->y_shared = c.num_shared > 0 ? b + off[7] : nullptr;
+    out->dispatch_ws = b + off[8];
+    out->mlp_ws = b + off[9];
   }
   return total;
 }
@@ -112,7 +115,7 @@ moe_status_t enqueue_layer(const moe_config_t& c, const moe_layer_tensors_t& t, 
   LayerScratch sc;
   layer_scratch(c, ws, &sc);
   hipError_t e = moe::launch_route(c, t.x, t.w_router, t.bias, t.topk_ids, t.topk_weights,
-                                   nullptr, s);
+                                   nullptr, sc.route_ws, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_dispatch(c, t.x, t.topk_ids, sc.counts, sc.offsets, sc.x_sorted, sc.src_index,
                            sc.row_of, sc.dispatch_ws, s);
@@ -159,6 +162,7 @@ int32_t moe_dbo_split_point(int32_t num_tokens) {
 size_t moe_workspace_bytes(const moe_config_t* cfg, int32_t kind) {
   if (check_config(cfg) != MOE_OK) return 0;
   switch (kind) {
+    case MOE_WS_ROUTE: return moe::route_workspace_bytes(*cfg);
     case MOE_WS_DISPATCH: return moe::dispatch_workspace_bytes(*cfg);
     case MOE_WS_EXPERT_MLP: return moe::mlp_workspace_bytes(*cfg);
     case MOE_WS_FORWARD: return layer_scratch(*cfg, nullptr, nullptr);
@@ -175,13 +179,16 @@ size_t moe_workspace_bytes(const moe_config_t* cfg, int32_t kind) {
 
 moe_status_t moe_route(const moe_config_t* cfg, const void* x, const void* w_router,
                        const float* bias, int32_t* topk_ids, float* topk_weights, float* logits,
-                       moe_stream_t stream) {
+                       void* workspace, size_t workspace_bytes, moe_stream_t stream) {
   moe_status_t st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (!x || !w_router || !topk_ids || !topk_weights) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(w_router, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = moe::route_workspace_bytes(*cfg);
+  if (need > 0 && (!workspace || !aligned(workspace, 256))) return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
   return hip_status(moe::launch_route(*cfg, x, w_router, bias, topk_ids, topk_weights, logits,
-                                      static_cast<hipStream_t>(stream)));
+                                      workspace, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_dispatch(const moe_config_t* cfg, const void* x, const int32_t* topk_ids,
@@ -297,10 +304,10 @@ moe_status_t moe_forward_dbo(const moe_config_t* cfg, const moe_layer_tensors_t*
   bool good = ok(hipEventRecord(ev[EV_START], cs)) && ok(hipStreamWaitEvent(ms, ev[EV_START], 0));
   // compute: route both microbatches.
   good = good && ok(moe::launch_route(c0, t0.x, t0.w_router, t0.bias, t0.topk_ids,
-                                      t0.topk_weights, nullptr, cs)) &&
+                                      t0.topk_weights, nullptr, s0.route_ws, cs)) &&
          ok(hipEventRecord(ev[EV_R0], cs)) &&
          ok(moe::launch_route(c1, t1.x, t1.w_router, t1.bias, t1.topk_ids, t1.topk_weights,
-                              nullptr, cs)) &&
+                              nullptr, s1.route_ws, cs)) &&
          ok(hipEventRecord(ev[EV_R1], cs));
   // comm: dispatch both as their routes finish.
   good = good && ok(hipStreamWaitEvent(ms, ev[EV_R0], 0)) &&

@@ -33,9 +33,10 @@ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---- launchers (each returns the launch status) ----
+size_t route_workspace_bytes(const moe_config_t& c);
 hipError_t launch_route(const moe_config_t& c, const void* x, const void* w_router,
                         const float* bias, int32_t* ids, float* weights, float* logits,
-                        hipStream_t s);
+                        void* workspace, hipStream_t s);
 
 size_t dispatch_workspace_bytes(const moe_config_t& c);
 hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* ids,

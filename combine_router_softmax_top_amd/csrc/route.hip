@@ -7,10 +7,9 @@
 // the logit, so the K experts are chosen on the logits directly; equal logits
 // go to the lower expert id; slots come out in descending order.
 //
-// bf16: one workgroup = 16 tokens x all experts.  The four waves split the
-// reduction dimension (wave w takes 32-wide slices w, w+4, ...), each running
-// 16x16x32 bf16 MFMAs into fp32 accumulators held for all expert tiles; the
-// four partial sums are then added in LDS in fixed wave order (deterministic).
+// bf16: a logits GEMM (16x16x32 bf16 MFMA, fp32 accumulation) over tiles of
+// 64 tokens x up to 256 experts x one slice of the reduction dimension, then
+// a selection kernel that adds the slices in a fixed order (deterministic).
 // fp32: each wave takes 4 tokens and reduces every dot product across its 64
 // lanes with a butterfly.
 // Selection: one wave per token, E/64 candidates per lane in registers, K
@@ -93,66 +92,131 @@ __device__ __forceinline__ void select_topk(float (&v)[NV], int E, int K, int sc
   }
 }
 
+// ---- bf16: logits GEMM with a fixed k-split, then selection ----
+//
+// route_logits_kernel<NT>: workgroup = 64 tokens x NT*16 experts x one slice
+// of the reduction dimension.  Each of its 4 waves owns 16 tokens and all
+// NT*16 experts (NT blocks of 16x16x32 MFMA).  Router rows are staged in
+// 64-wide k-chunks through LDS (double-buffered, shared by the 4 waves);
+// token fragments come straight from global memory.  Partial logits of slice
+// s go to part[s][t][e] (fp32) and the select kernel adds the slices in
+// ascending s.  The number of slices depends only on d and E, never on the
+// token count, so a token's logits do not depend on how the batch is split.
+constexpr int kRtTok = 64, kRtKc = 64;
+
+// LDS rows of 128 B (64 bf16): logical 16-byte chunk c of row r sits in slot
+// c ^ rsw(r); 16 lanes reading rows r..r+15 at one logical chunk then touch
+// distinct slots in every 256-byte window (no bank conflicts).
+__device__ __forceinline__ int rsw(int r) { return (r ^ (r >> 3)) & 7; }
+
 template <int NT>
-__global__ __launch_bounds__(256) void route_bf16_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-    const float* __restrict__ bias, int T, int d, int E, int K, int score, int renorm,
-    int32_t* __restrict__ ids, float* __restrict__ weights, float* __restrict__ logits) {
-  constexpr int EP = NT * 16;
-  constexpr int NV = EP >= kWave ? EP / kWave : 1;
-  __shared__ float zs[kTokTile][EP];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t0 = blockIdx.x * kTokTile;
-  const int arow = min(t0 + (lane & 15), T - 1);
-  const int koff = (lane >> 4) * 8;
-  const uint16_t* ap = x + (size_t)arow * d + koff;
+__global__ __launch_bounds__(256) void route_logits_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E,
+    int e_pad, int k_slice, float* __restrict__ part) {
+  constexpr int NE = NT * 16;
+  constexpr int kStage = NE * 128;
+  constexpr int kPer = (NE * 8 + 255) / 256;  // 16-byte staging chunks per thread
+  __shared__ __attribute__((aligned(16))) uint8_t wt[2 * kStage];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int t0 = blockIdx.x * kRtTok + wave * 16;
+  const int e0 = blockIdx.y * NE;
+  const int k0 = blockIdx.z * k_slice;
+  const int kgrp = lane >> 4;
+  const uint16_t* ap = x + (size_t)min(t0 + (lane & 15), T - 1) * d + k0 + kgrp * 8;
+
+  // staging chunk q = tid + 256 i: router row q/8, 16-byte chunk q%8
+  const uint16_t* src[kPer];
+  int dst[kPer];
+  bool live[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int q = tid + 256 * i;
+    live[i] = q < NE * 8;
+    const int row = (q >> 3) % NE, c = q & 7;
+    const int e = min(e0 + row, E - 1);
+    src[i] = wr + (size_t)e * d + k0 + c * 8;
+    dst[i] = row * 128 + ((c ^ rsw(row)) << 4);
+  }
+  u32x4 stg[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (live[i]) stg[i] = *reinterpret_cast<const u32x4*>(src[i]);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i)
+    if (live[i]) *reinterpret_cast<u32x4*>(wt + dst[i]) = stg[i];
+  __syncthreads();
 
   f32x4 acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const uint16_t* bp[NT];
-  bool bok[NT];
+  int boff[NT][2];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    const int e = j * 16 + (lane & 15);
-    bok[j] = e < E;
-    bp[j] = wr + (size_t)(bok[j] ? e : 0) * d + koff;
-  }
-  const int n_kc = d / 32;
-  for (int kc = wave; kc < n_kc; kc += 4) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(ap + kc * 32);
+    const int row = j * 16 + (lane & 15);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      bf16x8 b = *reinterpret_cast<const bf16x8*>(bp[j] + kc * 32);
-      if (!bok[j]) b = bf16x8{};
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+    for (int s = 0; s < 2; ++s) boff[j][s] = row * 128 + (((s * 4 + kgrp) ^ rsw(row)) << 4);
+  }
+  const int nkc = k_slice / kRtKc;
+  for (int kc = 0; kc < nkc; ++kc) {
+    const uint8_t* cur = wt + (kc & 1) * kStage;
+    uint8_t* nxt = wt + ((kc + 1) & 1) * kStage;
+    const bool more = kc + 1 < nkc;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (live[i]) stg[i] = *reinterpret_cast<const u32x4*>(src[i] + (kc + 1) * kRtKc);
     }
-  }
-  // Fixed-order sum of the four waves' partial logits: ((w0 + w1) + w2) + w3.
-  for (int w = 0; w < 4; ++w) {
-    if (wave == w) {
+    bf16x8 a[2];
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
+    for (int s = 0; s < 2; ++s) a[s] = *reinterpret_cast<const bf16x8*>(ap + kc * kRtKc + s * 32);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = (lane >> 4) * 4 + i, e = j * 16 + (lane & 15);
-          zs[tok][e] = (w == 0) ? acc[j][i] : zs[tok][e] + acc[j][i];
-        }
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(cur + boff[j][s]);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b, acc[j], 0, 0, 0);
+      }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (live[i]) *reinterpret_cast<u32x4*>(nxt + dst[i]) = stg[i];
     }
     __syncthreads();
   }
-  for (int tt = wave * 4; tt < wave * 4 + 4; ++tt) {
-    const int t = t0 + tt;
-    if (t >= T) break;
-    float v[NV];
+  // lane holds tokens (lane/16)*4 + i, expert lane%16 of each 16-wide block;
+  // experts past E hold partial sums of a clamped row and are never read.
+  float* out = part + (size_t)blockIdx.z * T * e_pad;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = lane + kWave * i;
-      v[i] = e < E ? zs[tt][e] + (bias ? bias[e] : 0.f) : -INFINITY;
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + (lane >> 4) * 4 + i;
+      if (t < T) out[(size_t)t * e_pad + e0 + j * 16 + (lane & 15)] = acc[j][i];
     }
-    select_topk<NV>(v, E, K, score, renorm, t, ids, weights, logits, lane);
+}
+
+// One wave per token: logits = sum of the k-slice partials (ascending) + bias.
+template <int NV>
+__global__ __launch_bounds__(256) void route_select_kernel(
+    const float* __restrict__ part, int n_slices, int e_pad, const float* __restrict__ bias,
+    int T, int E, int K, int score, int renorm, int32_t* __restrict__ ids,
+    float* __restrict__ weights, float* __restrict__ logits) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + kWave * i;
+    if (e < E) {
+      float z = part[(size_t)t * e_pad + e];
+      for (int s = 1; s < n_slices; ++s) z += part[((size_t)s * T + t) * e_pad + e];
+      v[i] = z + (bias ? bias[e] : 0.f);
+    } else {
+      v[i] = -INFINITY;
+    }
   }
+  select_topk<NV>(v, E, K, score, renorm, t, ids, weights, logits, lane);
 }
 
 template <int NV>
@@ -184,15 +248,69 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
   }
 }
 
-template <int NT>
-hipError_t launch_bf16(const moe_config_t& c, const void* x, const void* wr, const float* bias,
-                       int32_t* ids, float* w, float* logits, hipStream_t s) {
-  const dim3 grid(ceil_div(c.num_tokens, kTokTile)), block(256);
-  hipLaunchKernelGGL(route_bf16_kernel<NT>, grid, block, 0, s,
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr), bias,
-                     c.num_tokens, c.hidden, c.num_experts, c.top_k, c.score, c.renormalize, ids,
-                     w, logits);
+// Router tile width: NT blocks of 16 experts, NT a power of two <= 16.
+int route_nt(const moe_config_t& c) {
+  int nt = 1;
+  while (nt < 16 && nt * 16 < c.num_experts) nt *= 2;
+  return nt;
+}
+
+int route_e_pad(const moe_config_t& c) {
+  const int ne = route_nt(c) * 16;
+  return ceil_div(c.num_experts, ne) * ne;
+}
+
+// Slices of the reduction dimension: a function of d and E only (never of
+// the token count, so splitting a batch does not change any token's sum
+// order).  At most d / (4 E_pad) slices, so the fp32 partials stay a small
+// fraction of the token traffic, and at most 8; slices are 64-multiples.
+int route_k_slices(const moe_config_t& c) {
+  const int e_pad = route_e_pad(c);
+  int ks = 1;
+  while (ks < 8 && 2 * ks <= c.hidden / (4 * e_pad) && c.hidden % (2 * ks * kRtKc) == 0) ks *= 2;
+  return ks;
+}
+
+size_t route_partial_floats(const moe_config_t& c) {
+  return (size_t)route_k_slices(c) * c.num_tokens * route_e_pad(c);
+}
+
+template <int NV>
+hipError_t launch_select(const moe_config_t& c, const float* part, int ks, int e_pad,
+                         const float* bias, int32_t* ids, float* w, float* logits, hipStream_t s) {
+  hipLaunchKernelGGL(route_select_kernel<NV>, dim3(ceil_div(c.num_tokens, 4)), dim3(256), 0, s,
+                     part, ks, e_pad, bias, c.num_tokens, c.num_experts, c.top_k, c.score,
+                     c.renormalize, ids, w, logits);
   return hipGetLastError();
+}
+
+template <int NT>
+void launch_logits(const moe_config_t& c, const void* x, const void* wr, int e_pad, int ks,
+                   float* part, hipStream_t s) {
+  const dim3 grid(ceil_div(c.num_tokens, kRtTok), e_pad / (NT * 16), ks);
+  hipLaunchKernelGGL(route_logits_kernel<NT>, grid, dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr),
+                     c.num_tokens, c.hidden, c.num_experts, e_pad, c.hidden / ks, part);
+}
+
+hipError_t launch_bf16(const moe_config_t& c, const void* x, const void* wr, const float* bias,
+                       int32_t* ids, float* w, float* logits, float* part, hipStream_t s) {
+  const int ks = route_k_slices(c);
+  const int e_pad = route_e_pad(c);
+  switch (route_nt(c)) {
+    case 1: launch_logits<1>(c, x, wr, e_pad, ks, part, s); break;
+    case 2: launch_logits<2>(c, x, wr, e_pad, ks, part, s); break;
+    case 4: launch_logits<4>(c, x, wr, e_pad, ks, part, s); break;
+    case 8: launch_logits<8>(c, x, wr, e_pad, ks, part, s); break;
+    default: launch_logits<16>(c, x, wr, e_pad, ks, part, s); break;
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int nv = ceil_div(c.num_experts, kWave);
+  if (nv <= 1) return launch_select<1>(c, part, ks, e_pad, bias, ids, w, logits, s);
+  if (nv <= 2) return launch_select<2>(c, part, ks, e_pad, bias, ids, w, logits, s);
+  if (nv <= 4) return launch_select<4>(c, part, ks, e_pad, bias, ids, w, logits, s);
+  return launch_select<8>(c, part, ks, e_pad, bias, ids, w, logits, s);
 }
 
 template <int NV>
@@ -207,18 +325,16 @@ hipError_t launch_f32(const moe_config_t& c, const void* x, const void* wr, cons
 
 }  // namespace
 
+size_t route_workspace_bytes(const moe_config_t& c) {
+  return c.dtype == MOE_BF16 ? align_up(route_partial_floats(c) * sizeof(float), 256) : 0;
+}
+
 hipError_t launch_route(const moe_config_t& c, const void* x, const void* w_router,
                         const float* bias, int32_t* ids, float* weights, float* logits,
-                        hipStream_t s) {
-  if (c.dtype == MOE_BF16) {
-    const int nt = ceil_div(c.num_experts, 16);
-    if (nt <= 1) return launch_bf16<1>(c, x, w_router, bias, ids, weights, logits, s);
-    if (nt <= 2) return launch_bf16<2>(c, x, w_router, bias, ids, weights, logits, s);
-    if (nt <= 4) return launch_bf16<4>(c, x, w_router, bias, ids, weights, logits, s);
-    if (nt <= 8) return launch_bf16<8>(c, x, w_router, bias, ids, weights, logits, s);
-    if (nt <= 16) return launch_bf16<16>(c, x, w_router, bias, ids, weights, logits, s);
-    return launch_bf16<32>(c, x, w_router, bias, ids, weights, logits, s);
-  }
+                        void* workspace, hipStream_t s) {
+  if (c.dtype == MOE_BF16)
+    return launch_bf16(c, x, w_router, bias, ids, weights, logits,
+                       static_cast<float*>(workspace), s);
   const int nv = ceil_div(c.num_experts, kWave);
   if (nv <= 1) return launch_f32<1>(c, x, w_router, bias, ids, weights, logits, s);
   if (nv <= 2) return launch_f32<2>(c, x, w_router, bias, ids, weights, logits, s);

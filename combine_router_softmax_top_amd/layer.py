@@ -46,6 +46,7 @@ class MoELayer:
         self.y_sorted = torch.empty(T * K, d, dtype=dt, device=dev)
         self.y_shared = torch.empty(S, T, d, dtype=dt, device=dev) if S > 0 else None
         self.out = torch.empty(T, d, dtype=dt, device=dev)
+        self.ws_route = B.alloc_workspace(self.cs, B.MOE_WS_ROUTE, dev)
         self.ws_dispatch = B.alloc_workspace(self.cs, B.MOE_WS_DISPATCH, dev)
         self.ws_mlp = B.alloc_workspace(self.cs, B.MOE_WS_EXPERT_MLP, dev)
         self._ws_forward: Optional[torch.Tensor] = None
@@ -54,7 +55,7 @@ class MoELayer:
     # ---- stages -------------------------------------------------------------
     def route(self, stream=None, with_logits: bool = True):
         B.moe_route(self.cs, self.x, self.w_router, self.bias, self.topk_ids, self.topk_weights,
-                    self.logits if with_logits else None, stream)
+                    self.logits if with_logits else None, self.ws_route, stream)
 
     def dispatch(self, stream=None, topk_ids: Optional[torch.Tensor] = None):
         B.moe_dispatch(self.cs, self.x, self.topk_ids if topk_ids is None else topk_ids,

@@ -54,7 +54,8 @@ enum { MOE_F32 = 0, MOE_BF16 = 1 };
 /* Router score functions. */
 enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 /* Workspace kinds for moe_workspace_bytes. */
-enum { MOE_WS_DISPATCH = 0, MOE_WS_EXPERT_MLP = 1, MOE_WS_FORWARD = 2, MOE_WS_FORWARD_DBO = 3 };
+enum { MOE_WS_ROUTE = 0, MOE_WS_DISPATCH = 1, MOE_WS_EXPERT_MLP = 2, MOE_WS_FORWARD = 3,
+       MOE_WS_FORWARD_DBO = 4 };
 
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_TOPK 16
@@ -106,10 +107,13 @@ typedef void* moe_stream_t;
  *   topk_ids     [T, K]  int32  (out)
  *   topk_weights [T, K]  fp32   (out)
  *   logits       [T, E]  fp32   (out, optional: NULL to skip) the z above
+ *   workspace    >= moe_workspace_bytes(cfg, MOE_WS_ROUTE) bytes, 256-byte aligned
+ *                (that size is 0 for fp32 layers, where workspace may be NULL)
  */
 moe_status_t moe_route(const moe_config_t* cfg, const void* x, const void* w_router,
                        const float* bias, int32_t* topk_ids, float* topk_weights,
-                       float* logits, moe_stream_t stream);
+                       float* logits, void* workspace, size_t workspace_bytes,
+                       moe_stream_t stream);
 
 /*
  * moe_dispatch -- count tokens per expert and copy routed tokens into

@@ -60,7 +60,7 @@ def test_config_validation_on_host(lib, field, value, status):
     cs = B.config_struct(W.CONFIGS["dsv3_prefill_ep"])
     setattr(cs, field, value)
     P = ctypes.c_void_p
-    st = lib.moe_route(ctypes.byref(cs), P(16), P(16), None, P(16), P(16), None, None)
+    st = lib.moe_route(ctypes.byref(cs), P(16), P(16), None, P(16), P(16), None, P(256), 1 << 30, None)
     assert st == status
     assert lib.moe_workspace_bytes(ctypes.byref(cs), B.MOE_WS_FORWARD) == 0
 
@@ -68,9 +68,9 @@ def test_config_validation_on_host(lib, field, value, status):
 def test_null_pointers_and_small_workspace_rejected_on_host(lib):
     cs = B.config_struct(W.CONFIGS["dsv3_prefill_ep"])
     P = ctypes.c_void_p
-    assert lib.moe_route(ctypes.byref(cs), None, P(16), None, P(16), P(16), None, None) == \
+    assert lib.moe_route(ctypes.byref(cs), None, P(16), None, P(16), P(16), None, P(256), 1 << 30, None) == \
         B.MOE_ERR_INVALID_ARGUMENT
-    assert lib.moe_route(ctypes.byref(cs), P(8), P(16), None, P(16), P(16), None, None) == \
+    assert lib.moe_route(ctypes.byref(cs), P(8), P(16), None, P(16), P(16), None, P(256), 1 << 30, None) == \
         B.MOE_ERR_INVALID_ARGUMENT  # misaligned activations
     need = lib.moe_workspace_bytes(ctypes.byref(cs), B.MOE_WS_DISPATCH)
     st = lib.moe_dispatch(ctypes.byref(cs), P(256), P(256), P(256), P(256), P(256), P(256),
