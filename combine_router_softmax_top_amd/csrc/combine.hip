@@ -21,31 +21,31 @@ struct Vec;
 template <>
 struct Vec<uint16_t> {  // bf16: 8 per 16 bytes
   static constexpr int N = 8;
-  __device__ static void load(const uint4& v, float (&f)[8]) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  __device__ static void load(const u32x4& v, float (&f)[8]) {
+    const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f[2 * i] = __uint_as_float(w[i] << 16);
       f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
-  __device__ static uint4 store(const float (&f)[8]) {
+  __device__ static u32x4 store(const float (&f)[8]) {
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       w[i] = (uint32_t)f32_to_bf16_bits(f[2 * i]) | ((uint32_t)f32_to_bf16_bits(f[2 * i + 1]) << 16);
-    return uint4{w[0], w[1], w[2], w[3]};
+    return u32x4{w[0], w[1], w[2], w[3]};
   }
 };
 template <>
 struct Vec<float> {  // fp32: 4 per 16 bytes
   static constexpr int N = 4;
-  __device__ static void load(const uint4& v, float (&f)[4]) {
-    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
-    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  __device__ static void load(const u32x4& v, float (&f)[4]) {
+    f[0] = __uint_as_float(v[0]); f[1] = __uint_as_float(v[1]);
+    f[2] = __uint_as_float(v[2]); f[3] = __uint_as_float(v[3]);
   }
-  __device__ static uint4 store(const float (&f)[4]) {
-    return uint4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+  __device__ static u32x4 store(const float (&f)[4]) {
+    return u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
                  __float_as_uint(f[3])};
   }
 };
@@ -54,9 +54,9 @@ constexpr int kPieces = 2;  // 16-byte pieces per lane per iteration
 
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(
-    const uint4* __restrict__ y_sorted, const int32_t* __restrict__ row_of,
-    const float* __restrict__ weights, const uint4* __restrict__ y_shared, int num_tokens, int K,
-    int n_shared, int row_vecs, uint4* __restrict__ out) {
+    const u32x4* __restrict__ y_sorted, const int32_t* __restrict__ row_of,
+    const float* __restrict__ weights, const u32x4* __restrict__ y_shared, int num_tokens, int K,
+    int n_shared, int row_vecs, u32x4* __restrict__ out) {
   constexpr int N = Vec<T>::N;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
       const int rk = __builtin_amdgcn_readlane(myrow, k);
       if (rk < 0) continue;
       const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myw), k));
-      const uint4* src = y_sorted + (size_t)rk * row_vecs;
+      const u32x4* src = y_sorted + (size_t)rk * row_vecs;
 #pragma unroll
       for (int p = 0; p < kPieces; ++p) {
         const int v = v0 + p * kWave + lane;
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
       }
     }
     for (int s = 0; s < n_shared; ++s) {
-      const uint4* src = y_shared + ((size_t)s * num_tokens + t) * row_vecs;
+      const u32x4* src = y_shared + ((size_t)s * num_tokens + t) * row_vecs;
 #pragma unroll
       for (int p = 0; p < kPieces; ++p) {
         const int v = v0 + p * kWave + lane;
@@ -120,14 +120,14 @@ hipError_t launch_combine(const moe_config_t& c, const void* y_sorted, const int
   const int n_sh = y_shared ? c.num_shared : 0;
   if (c.dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, block, 0, s,
-                       static_cast<const uint4*>(y_sorted), row_of, weights,
-                       static_cast<const uint4*>(y_shared), c.num_tokens, c.top_k, n_sh, row_vecs,
-                       static_cast<uint4*>(out));
+                       static_cast<const u32x4*>(y_sorted), row_of, weights,
+                       static_cast<const u32x4*>(y_shared), c.num_tokens, c.top_k, n_sh, row_vecs,
+                       static_cast<u32x4*>(out));
   else
     hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, s,
-                       static_cast<const uint4*>(y_sorted), row_of, weights,
-                       static_cast<const uint4*>(y_shared), c.num_tokens, c.top_k, n_sh, row_vecs,
-                       static_cast<uint4*>(out));
+                       static_cast<const u32x4*>(y_sorted), row_of, weights,
+                       static_cast<const u32x4*>(y_shared), c.num_tokens, c.top_k, n_sh, row_vecs,
+                       static_cast<u32x4*>(out));
   return hipGetLastError();
 }
 

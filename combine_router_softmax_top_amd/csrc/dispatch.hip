@@ -126,9 +126,9 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
 constexpr int kUnroll = 4;
 
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
-    const uint4* __restrict__ x, const int32_t* __restrict__ ids,
+    const u32x4* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ base, int T, int K, int eb,
-    int n_loc, int row_vecs, uint4* __restrict__ x_sorted, int32_t* __restrict__ src_index,
+    int n_loc, int row_vecs, u32x4* __restrict__ x_sorted, int32_t* __restrict__ src_index,
     int32_t* __restrict__ row_of) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -147,9 +147,9 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   // Any local row at all?  (wave-uniform)
   const unsigned long long any = __ballot(myrow >= 0);
   if (any == 0ull) return;
-  const uint4* src = x + (size_t)t * row_vecs;
+  const u32x4* src = x + (size_t)t * row_vecs;
   for (int v0 = 0; v0 < row_vecs; v0 += kWave * kUnroll) {
-    uint4 buf[kUnroll];
+    u32x4 buf[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int v = v0 + u * kWave + lane;
@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     for (int k = 0; k < K; ++k) {
       const int rk = __builtin_amdgcn_readlane(myrow, k);
       if (rk < 0) continue;
-      uint4* dst = x_sorted + (size_t)rk * row_vecs;
+      u32x4* dst = x_sorted + (size_t)rk * row_vecs;
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int v = v0 + u * kWave + lane;
@@ -208,8 +208,8 @@ hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* 
   const int elem = c.dtype == MOE_BF16 ? 2 : 4;
   const int row_vecs = c.hidden * elem / 16;
   hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(ceil_div(T, 4)), dim3(256), 0, s,
-                     static_cast<const uint4*>(x), ids, rank, base, T, K, eb, n_loc, row_vecs,
-                     static_cast<uint4*>(x_sorted), src_index, row_of);
+                     static_cast<const u32x4*>(x), ids, rank, base, T, K, eb, n_loc, row_vecs,
+                     static_cast<u32x4*>(x_sorted), src_index, row_of);
   return hipGetLastError();
 }
 
