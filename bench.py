@@ -30,7 +30,7 @@ sys.path.insert(0, _ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 FP32_VALU_PEAK_TFLOPS = 157.3
-TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "expert_mlp_traffic.json")
+TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "expert_mlp_dsv3_prefill_ep_traffic.json")
 
 
 def parse():
@@ -64,7 +64,6 @@ def algorithmic(cfg, n_loc: int, t_touch: int) -> dict:
     dispatch = t_touch * d * b + n_loc * d * b + n_loc * 4 + 2 * T * K * 4 + 2 * E * 4
     combine = n_loc * d * b + T * K * 8 + T * d * b + S * T * d * b
     flops = 6.0 * n_loc * d * I + 6.0 * S * T * d * I
-    n_touched_experts = None
     return dict(route=route, dispatch=dispatch, combine=combine, gemm_flops=flops)
 
 
