@@ -12,11 +12,11 @@
 //     256 rows x (128 gate + 128 up) columns, multiplied together in the
 //     epilogue, so h is written once, in bf16); four waves in a 2x2 grid,
 //     each a 128x128 sub-tile of 4x4 v_mfma_f32_32x32x16_bf16 blocks;
-//   * 32-deep k-tiles move straight from global memory into a ring of four
-//     LDS stages (global_load_lds, 16 B per lane), issued three tiles ahead,
-//     so HBM latency hides behind the MFMAs of the tiles in between; the
-//     rows are XOR-swizzled in 16-byte chunks so the fragment reads are free
-//     of bank conflicts;
+//   * 64-deep k-tiles (full 128-byte row segments) move straight from global
+//     memory into two LDS stages (global_load_lds, 16 B per lane), the next
+//     tile loading while the current one feeds the MFMAs; the rows are
+//     XOR-swizzled in 16-byte chunks so the fragment reads are free of bank
+//     conflicts;
 //   * ragged groups: the tile list (expert, row tile, column tile) is derived
 //     on the device from the expert offsets; the grid is the host's upper
 //     bound and surplus workgroups exit at once (no host synchronisation);
@@ -93,13 +93,14 @@ __device__ __forceinline__ int xcd_tile_id() {
 
 // ------------------------------------------------------------------ bf16 MFMA GEMM
 
-constexpr int kBM = 256, kBN = 256, kBK = 32;
+constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kThreads = 512;                             // 8 waves, 2 per SIMD
-constexpr int kRowBytes = kBK * 2;                        // 64 B per staged row
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 32 KB
-constexpr int kStages = 4;                                // 128 KB of LDS
-constexpr int kDmaPerTile = kStageBytes / (kThreads * 16);  // 4 x 16 B per thread
+constexpr int kRowBytes = kBK * 2;                        // 128 B per staged row
+constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 64 KB
+constexpr int kStages = 2;                                // 128 KB of LDS
+constexpr int kDmaPerTile = kStageBytes / (kThreads * 16);  // 8 x 16 B per thread
 constexpr int kDmaA = kDmaPerTile / 2;
+constexpr int kRowsPerDma = 1024 / kRowBytes;             // rows filled by one wave instruction
 
 enum { EPI_STORE = 0, EPI_SILU_GLU = 1 };
 
@@ -107,17 +108,17 @@ __device__ __forceinline__ float silu_f(float z) { return z / (1.f + __expf(-z))
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// LDS tile layout: 64-byte rows (32 bf16 of k) of four 16-byte chunks; row R
-// keeps logical chunk c in physical slot c ^ swz(R), swz(R) = ((R>>1)^(R>>3)) & 3.
+// LDS tile layout: 128-byte rows (64 bf16 of k) of eight 16-byte chunks; row
+// R keeps logical chunk c in physical slot c ^ swz(R), swz(R) = (R ^ (R>>3)) & 7.
 // A 64-lane ds_read_b128 of 32 consecutive rows at one logical chunk then hits
 // distinct 16-byte slots within every 8-lane (128 B) and 16-lane (256 B)
 // service group, i.e. no bank conflicts.
-__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// One wave's share of staging a k-tile (A then B, 32 KB per workgroup) with
+// One wave's share of staging a k-tile (A then B, 64 KB per workgroup) with
 // direct global->LDS loads: instruction j of wave w fills 1 KB of LDS = rows
-// (8j + w)*16 .. +16 of the A (j < 2) or B (j >= 2) tile; lane l covers row
-// +l/4, physical chunk l%4, so its source is logical chunk (l%4) ^ swz(row).
+// (8j + w)*8 .. +8 of the A (j < 4) or B (j >= 4) tile; lane l covers row
+// +l/8, physical chunk l%8, so its source is logical chunk (l%8) ^ swz(row).
 __device__ __forceinline__ void stage_tile(uint8_t* stage, const uint8_t* a_tile,
                                            const uint8_t* b_lo, const uint8_t* b_hi,
                                            const uint32_t (&off)[kDmaPerTile], int wave,
@@ -159,13 +160,11 @@ __device__ __forceinline__ void mma_step(const Frags& f, f32x16 (&acc)[4][2]) {
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-// Wait until this wave's loads of the oldest in-flight stage have landed (two
-// later tiles' loads may stay in flight: loads complete in issue order) and
-// its LDS reads have returned; then a workgroup barrier without a memory
-// fence, so the later stages' loads stay in flight across it.
+// Wait until this wave's loads of the next stage have landed and its LDS
+// reads have returned; then a workgroup barrier (without a memory fence:
+// the waits above are the only ones needed).
 __device__ __forceinline__ void wait_stage_and_barrier() {
-  static_assert(kStages == 4 && kDmaPerTile == 4, "vmcnt immediate assumes 4 stages x 4 loads");
-  asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -210,8 +209,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
   uint32_t off[kDmaPerTile];
 #pragma unroll
   for (int j = 0; j < kDmaPerTile; ++j) {
-    const int r = ((j % kDmaA) * 8 + wave) * 16 + (lane >> 2);  // row within A or B tile
-    const int lchunk = (lane & 3) ^ swz(r);
+    const int r = ((j % kDmaA) * 8 + wave) * kRowsPerDma + lane / (kRowBytes / 16);
+    const int lchunk = (lane % (kRowBytes / 16)) ^ swz(r);
     if (j < kDmaA) {
       off[j] = (uint32_t)(min(r, a_last) * lda * 2 + lchunk * 16);
     } else {
@@ -247,30 +246,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 #pragma unroll
   for (int j = 0; j < 2; ++j) xb[j] = kgrp ^ swz(b_row[j]);
 
-  // A ring of kStages LDS stages: k-tile t lives in stage t % kStages and its
-  // loads are issued kStages-1 tiles ahead of its use.  Per tile (two
-  // k-steps): the loads of tile t+3 and the second k-step's fragment reads
-  // are interleaved with the first k-step's MFMAs; the stage wait and barrier
-  // come before the second k-step's MFMAs, which then overlap the fragment
-  // reads of tile t+1.  The body has no branches: every iteration issues one
-  // tile of loads, past the last tile re-reading the last tile into a stage
-  // that is never read again, and reads next-tile fragments that the last
-  // iteration never uses.
+  // Two LDS stages: tile t+1 is loaded (direct to LDS) while tile t feeds the
+  // MFMAs.  Fragments are double-buffered across the four k-steps of a tile;
+  // the stage wait and barrier come before the last k-step's MFMAs, which
+  // then overlap the fragment reads of the next tile.  The body has no
+  // branches: past the last tile the loads re-read the last tile into the
+  // free stage and the next-tile fragments are never used.
   const int nk = Kdim / kBK;
-  for (int t = 0; t < kStages - 1; ++t)
-    stage_tile(lds + t * kStageBytes, a_tile, b_lo, b_hi, off, wave, min(t, nk - 1) * kRowBytes);
+  stage_tile(lds, a_tile, b_lo, b_hi, off, wave, 0);
   wait_stage_and_barrier();
   Frags f0, f1;
   load_frags(lds, 0, a_row0, b_row, xa, xb, f0);
   for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t* cur = lds + (kt % kStages) * kStageBytes;
-    const int tn = kt + kStages - 1;
-    stage_tile(lds + (tn % kStages) * kStageBytes, a_tile, b_lo, b_hi, off, wave,
-               min(tn, nk - 1) * kRowBytes);
+    const uint8_t* cur = lds + (kt & 1) * kStageBytes;
+    uint8_t* nxt = lds + ((kt + 1) & 1) * kStageBytes;
+    stage_tile(nxt, a_tile, b_lo, b_hi, off, wave, min(kt + 1, nk - 1) * kRowBytes);
     load_frags(cur, 1, a_row0, b_row, xa, xb, f1);
     mma_step(f0, acc);
+    load_frags(cur, 2, a_row0, b_row, xa, xb, f0);
+    mma_step(f1, acc);
+    load_frags(cur, 3, a_row0, b_row, xa, xb, f1);
+    mma_step(f0, acc);
     wait_stage_and_barrier();
-    load_frags(lds + ((kt + 1) % kStages) * kStageBytes, 0, a_row0, b_row, xa, xb, f0);
+    load_frags(nxt, 0, a_row0, b_row, xa, xb, f0);
     mma_step(f1, acc);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
