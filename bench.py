@@ -44,7 +44,46 @@ def parse():
                    help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--dbo", action="store_true",
+                   help="time the two-microbatch forward (moe_forward_dbo, compute + comm "
+                        "streams) against the unsplit moe_forward on the same tokens")
     return p.parse_args()
+
+
+def bench_dbo(args, cfg, layer, torch) -> dict:
+    """Whole-layer time of moe_forward_dbo vs moe_forward (same inputs, same outputs)."""
+    from combine_router_softmax_top_amd import binding as B
+    compute, comm = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(compute)
+        for _ in range(args.steps):
+            fn()
+        ev1.record(compute)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / args.steps
+
+    unsplit = timed(lambda: layer.forward(stream=compute))
+    ref = layer.out.clone()
+    split = timed(lambda: layer.forward_dbo(compute=compute, comm=comm))
+    torch.cuda.synchronize()
+    same = bool(torch.equal(layer.out.view(torch.int16), ref.view(torch.int16)))
+    one_stream = timed(lambda: layer.forward_dbo(compute=compute, comm=compute))
+    T = cfg.num_tokens
+    return {"metric": "dual-microbatch layer tokens/s (moe_forward_dbo, two HIP streams)",
+            "value": T / (split * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": split, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+            "data": "synthetic (seeded)",
+            "config": {"workload": cfg.name, "tokens": T, "microbatches": [
+                B.dbo_split_point(T), T - B.dbo_split_point(T)]},
+            "unsplit_ms": unsplit, "split_two_streams_ms": split, "split_one_stream_ms": one_stream,
+            "overlap_gain": unsplit / split - 1.0, "bitwise_equal_to_unsplit": same}
 
 
 def source_digest() -> str:
@@ -120,6 +159,9 @@ def main():
     inp = W.make_inputs(cfg, seed=0)
     t_gen = time.perf_counter() - t_gen
     layer = MoELayer(cfg, inp, device="cuda:0")
+    if args.dbo:
+        print(json.dumps(bench_dbo(args, cfg, layer, torch)), flush=True)
+        return
     stream = torch.cuda.Stream()
 
     def step(evs=None):

@@ -8,10 +8,12 @@
 // token for the shared experts.
 //
 // bf16 path (gfx950 MFMA, fp32 accumulation):
-//   * one 256-thread workgroup computes a 256x256 output tile (gate/up pass:
+//   * one 512-thread workgroup computes a 256x256 output tile (gate/up pass:
 //     256 rows x (128 gate + 128 up) columns, multiplied together in the
-//     epilogue, so h is written once, in bf16); four waves in a 2x2 grid,
-//     each a 128x128 sub-tile of 4x4 v_mfma_f32_32x32x16_bf16 blocks;
+//     epilogue, so h is written once, in bf16); eight waves (two per SIMD)
+//     in a 2x4 grid, each a 128x64 sub-tile of 4x2 v_mfma_f32_32x32x16_bf16
+//     blocks; an expert's last row tile with at most 128 rows runs as a
+//     half-height tile (each wave 64x64);
 //   * 64-deep k-tiles (full 128-byte row segments) move straight from global
 //     memory into two LDS stages (global_load_lds, 16 B per lane), the next
 //     tile loading while the current one feeds the MFMAs; the rows are
@@ -115,16 +117,19 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // service group, i.e. no bank conflicts.
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// One wave's share of staging a k-tile (A then B, 64 KB per workgroup) with
-// direct global->LDS loads: instruction j of wave w fills 1 KB of LDS = rows
-// (8j + w)*8 .. +8 of the A (j < 4) or B (j >= 4) tile; lane l covers row
-// +l/8, physical chunk l%8, so its source is logical chunk (l%8) ^ swz(row).
+// One wave's share of staging a k-tile (A then B, up to 64 KB per workgroup)
+// with direct global->LDS loads: instruction j of wave w fills 1 KB of LDS =
+// rows (8j + w)*8 .. +8 of the A (j < 4) or B (j >= 4) tile; lane l covers
+// row +l/8, physical chunk l%8, so its source is logical chunk (l%8) ^ swz(row).
+// NA = A instructions per wave: 4 for a 256-row tile, 2 for a 128-row tile.
+template <int NA>
 __device__ __forceinline__ void stage_tile(uint8_t* stage, const uint8_t* a_tile,
                                            const uint8_t* b_lo, const uint8_t* b_hi,
                                            const uint32_t (&off)[kDmaPerTile], int wave,
                                            int kbytes) {
 #pragma unroll
   for (int j = 0; j < kDmaPerTile; ++j) {
+    if (j >= NA && j < kDmaA) continue;
     const uint8_t* src = j < kDmaA ? a_tile : (j < kDmaA + kDmaA / 2 ? b_lo : b_hi);
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + kbytes + off[j]),
                                      (lds_ptr_t)(stage + (j * 8 + wave) * 1024), 16, 0, 0);
@@ -135,15 +140,17 @@ struct Frags {
   bf16x8 a[4], b[2];
 };
 
-// Fragments of k-step ks (16 deep) of a staged tile: A rows a_row0 + 32i,
-// B rows b_row[j]; xa/xb hold (lane's k-group) ^ swz(row).
+// Fragments of k-step ks (16 deep) of a staged tile: NFA A fragments (rows
+// a_row0 + 32i) and 2 B fragments (rows b_row[j]); xa/xb hold (lane's
+// k-group) ^ swz(row).
+template <int NFA>
 __device__ __forceinline__ void load_frags(const uint8_t* stage, int ks, int a_row0,
                                            const int (&b_row)[2], const int (&xa)[4],
                                            const int (&xb)[2], Frags& f) {
   const uint8_t* sa = stage;
   const uint8_t* sb = stage + kBM * kRowBytes;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NFA; ++i)
     f.a[i] = *reinterpret_cast<const bf16x8*>(sa + (a_row0 + i * 32) * kRowBytes +
                                               (((2 * ks) ^ xa[i]) << 4));
 #pragma unroll
@@ -152,9 +159,10 @@ __device__ __forceinline__ void load_frags(const uint8_t* stage, int ks, int a_r
                                               (((2 * ks) ^ xb[j]) << 4));
 }
 
+template <int NFA>
 __device__ __forceinline__ void mma_step(const Frags& f, f32x16 (&acc)[4][2]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NFA; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
@@ -167,6 +175,135 @@ __device__ __forceinline__ void wait_stage_and_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+struct TileArgs {
+  const uint16_t* A;
+  int lda;
+  const uint16_t* bg;
+  const uint16_t* bu;
+  uint16_t* C;
+  int ldc;
+  int row0, rows, m0, n0, N, Kdim;
+};
+
+// One output tile.  NFA = 4: 256 rows, the 8 waves as 2 x 4, each 128 rows x
+// 64 columns.  NFA = 2: the last row tile of an expert with at most 128 rows,
+// each wave 64 rows x 64 columns (half the A staging and half the MFMAs).
+// The k order of every output element is the same in both.
+template <int EPI, int NFA>
+__device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
+  constexpr int kNOut = EPI == EPI_SILU_GLU ? kBN / 2 : kBN;
+  constexpr int kWaveRows = NFA * 32;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int m0 = ta.m0, n0 = ta.n0, N = ta.N, Kdim = ta.Kdim;
+
+  // Per-lane byte offsets of the staged rows inside the tile's operand blocks.
+  // B rows 0..127 come from b_lo, rows 128..255 from b_hi (the up weights in
+  // the gate/up pass, the next 128 rows of the same weights otherwise).
+  const uint8_t* a_tile =
+      reinterpret_cast<const uint8_t*>(ta.A + (long long)(ta.row0 + m0) * ta.lda);
+  const uint8_t* b_lo = reinterpret_cast<const uint8_t*>(ta.bg + (long long)n0 * Kdim);
+  const uint8_t* b_hi = EPI == EPI_SILU_GLU
+                            ? reinterpret_cast<const uint8_t*>(ta.bu + (long long)n0 * Kdim)
+                            : b_lo;
+  const int a_last = ta.rows - 1 - m0;
+  const int b_last = N - 1 - n0;
+  uint32_t off[kDmaPerTile];
+#pragma unroll
+  for (int j = 0; j < kDmaPerTile; ++j) {
+    const int r = ((j % kDmaA) * 8 + wave) * kRowsPerDma + lane / (kRowBytes / 16);
+    const int lchunk = (lane % (kRowBytes / 16)) ^ swz(r);
+    if (j < kDmaA) {
+      off[j] = (uint32_t)(min(r, a_last) * ta.lda * 2 + lchunk * 16);
+    } else {
+      // r is the B-tile row; rows 128.. come from b_hi
+      const int br = EPI == EPI_SILU_GLU ? (r & (kNOut - 1)) : r;
+      off[j] = (uint32_t)(min(br, b_last) * Kdim * 2 + lchunk * 16);
+    }
+  }
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Fragment rows: A rows wm*kWaveRows + i*32 + (lane & 31); B rows: the
+  // wave's 64 output columns (gate/up pass: 32 gate rows and the matching 32
+  // up rows).
+  int b_row[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (EPI == EPI_SILU_GLU)
+      b_row[j] = j * kNOut + wn * 32 + (lane & 31);
+    else
+      b_row[j] = wn * 64 + j * 32 + (lane & 31);
+  }
+  const int a_row0 = wm * kWaveRows + (lane & 31);
+  const int kgrp = lane >> 5;
+  int xa[4], xb[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) xa[i] = kgrp ^ swz(a_row0 + i * 32);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) xb[j] = kgrp ^ swz(b_row[j]);
+
+  // Two LDS stages: tile t+1 is loaded (direct to LDS) while tile t feeds the
+  // MFMAs.  Fragments are double-buffered across the four k-steps of a tile;
+  // the stage wait and barrier come before the last k-step's MFMAs, which
+  // then overlap the fragment reads of the next tile.  The body has no
+  // branches: past the last tile the loads re-read the last tile into the
+  // free stage and the next-tile fragments are never used.
+  constexpr int NA = NFA == 4 ? kDmaA : kDmaA / 2;
+  const int nk = Kdim / kBK;
+  stage_tile<NA>(lds, a_tile, b_lo, b_hi, off, wave, 0);
+  wait_stage_and_barrier();
+  Frags f0, f1;
+  load_frags<NFA>(lds, 0, a_row0, b_row, xa, xb, f0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint8_t* cur = lds + (kt & 1) * kStageBytes;
+    uint8_t* nxt = lds + ((kt + 1) & 1) * kStageBytes;
+    stage_tile<NA>(nxt, a_tile, b_lo, b_hi, off, wave, min(kt + 1, nk - 1) * kRowBytes);
+    load_frags<NFA>(cur, 1, a_row0, b_row, xa, xb, f1);
+    mma_step<NFA>(f0, acc);
+    load_frags<NFA>(cur, 2, a_row0, b_row, xa, xb, f0);
+    mma_step<NFA>(f1, acc);
+    load_frags<NFA>(cur, 3, a_row0, b_row, xa, xb, f1);
+    mma_step<NFA>(f0, acc);
+    wait_stage_and_barrier();
+    load_frags<NFA>(nxt, 0, a_row0, b_row, xa, xb, f0);
+    mma_step<NFA>(f1, acc);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // Epilogue.  Accumulator element r of lane l in a 32x32 block holds
+  // row (r/4)*8 + (l/32)*4 + r%4, column l%32.
+  const int col_l = lane & 31;
+  const int row_l = (lane >> 5) * 4;
+#pragma unroll
+  for (int i = 0; i < NFA; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * kWaveRows + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
+      if (m >= ta.rows) continue;
+      uint16_t* crow = ta.C + (long long)(ta.row0 + m) * ta.ldc;
+      if (EPI == EPI_SILU_GLU) {
+        const int n = n0 + wn * 32 + col_l;
+        if (n < N) crow[n] = f32_to_bf16_bits(silu_f(acc[i][0][r]) * acc[i][1][r]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int n = n0 + wn * 64 + j * 32 + col_l;
+          if (n < N) crow[n] = f32_to_bf16_bits(acc[i][j][r]);
+        }
+      }
+    }
+  }
 }
 
 template <int EPI>
@@ -184,118 +321,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
   Tile tl;
   if (!find_tile(xcd_tile_id(), offsets, n_groups, fixed_rows, kBM, nN, tl)) return;
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int wm = wave >> 2, wn = wave & 3;   // 2 x 4 waves, each 128 rows x 64 columns
-  const int m0 = tl.m_tile * kBM;
-  const int n0 = tl.n_tile * kNOut;
   const long long zb = (long long)blockIdx.z * strideB_batch;
-  A += (long long)blockIdx.z * strideA_batch;
-  const uint16_t* bg = B0 + zb + (long long)tl.group * strideB_group;
-  const uint16_t* bu = EPI == EPI_SILU_GLU ? B1 + zb + (long long)tl.group * strideB_group : bg;
-  uint16_t* Cz = C + (long long)blockIdx.z * strideC_batch;
-
-  // Per-lane byte offsets of the staged rows inside the tile's operand blocks.
-  // B rows 0..127 come from b_lo, rows 128..255 from b_hi (the up weights in
-  // the gate/up pass, the next 128 rows of the same weights otherwise).
-  const uint8_t* a_tile = reinterpret_cast<const uint8_t*>(A + (long long)(tl.row0 + m0) * lda);
-  const uint8_t* b_lo = reinterpret_cast<const uint8_t*>(bg + (long long)n0 * Kdim);
-  const uint8_t* b_hi = EPI == EPI_SILU_GLU
-                            ? reinterpret_cast<const uint8_t*>(bu + (long long)n0 * Kdim)
-                            : b_lo;
-  const int a_last = tl.rows - 1 - m0;
-  const int b_last = N - 1 - n0;
-  uint32_t off[kDmaPerTile];
-#pragma unroll
-  for (int j = 0; j < kDmaPerTile; ++j) {
-    const int r = ((j % kDmaA) * 8 + wave) * kRowsPerDma + lane / (kRowBytes / 16);
-    const int lchunk = (lane % (kRowBytes / 16)) ^ swz(r);
-    if (j < kDmaA) {
-      off[j] = (uint32_t)(min(r, a_last) * lda * 2 + lchunk * 16);
-    } else {
-      // r is the B-tile row; rows 128.. come from b_hi
-      const int br = EPI == EPI_SILU_GLU ? (r & (kNOut - 1)) : r;
-      off[j] = (uint32_t)(min(br, b_last) * Kdim * 2 + lchunk * 16);
-    }
-  }
-
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  // Fragment rows: A rows wm*128 + i*32 + (lane & 31); B rows: the wave's 64
-  // output columns (gate/up pass: 32 gate rows and the matching 32 up rows).
-  int b_row[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (EPI == EPI_SILU_GLU)
-      b_row[j] = j * kNOut + wn * 32 + (lane & 31);
-    else
-      b_row[j] = wn * 64 + j * 32 + (lane & 31);
-  }
-  const int a_row0 = wm * 128 + (lane & 31);
-  const int kgrp = lane >> 5;
-  int xa[4], xb[2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) xa[i] = kgrp ^ swz(a_row0 + i * 32);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) xb[j] = kgrp ^ swz(b_row[j]);
-
-  // Two LDS stages: tile t+1 is loaded (direct to LDS) while tile t feeds the
-  // MFMAs.  Fragments are double-buffered across the four k-steps of a tile;
-  // the stage wait and barrier come before the last k-step's MFMAs, which
-  // then overlap the fragment reads of the next tile.  The body has no
-  // branches: past the last tile the loads re-read the last tile into the
-  // free stage and the next-tile fragments are never used.
-  const int nk = Kdim / kBK;
-  stage_tile(lds, a_tile, b_lo, b_hi, off, wave, 0);
-  wait_stage_and_barrier();
-  Frags f0, f1;
-  load_frags(lds, 0, a_row0, b_row, xa, xb, f0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t* cur = lds + (kt & 1) * kStageBytes;
-    uint8_t* nxt = lds + ((kt + 1) & 1) * kStageBytes;
-    stage_tile(nxt, a_tile, b_lo, b_hi, off, wave, min(kt + 1, nk - 1) * kRowBytes);
-    load_frags(cur, 1, a_row0, b_row, xa, xb, f1);
-    mma_step(f0, acc);
-    load_frags(cur, 2, a_row0, b_row, xa, xb, f0);
-    mma_step(f1, acc);
-    load_frags(cur, 3, a_row0, b_row, xa, xb, f1);
-    mma_step(f0, acc);
-    wait_stage_and_barrier();
-    load_frags(nxt, 0, a_row0, b_row, xa, xb, f0);
-    mma_step(f1, acc);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  // Epilogue.  Accumulator element r of lane l in a 32x32 block holds
-  // row (r/4)*8 + (l/32)*4 + r%4, column l%32.
-  const int col_l = lane & 31;
-  const int row_l = (lane >> 5) * 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
-      if (m >= tl.rows) continue;
-      uint16_t* crow = Cz + (long long)(tl.row0 + m) * ldc;
-      if (EPI == EPI_SILU_GLU) {
-        const int n = n0 + wn * 32 + col_l;
-        if (n < N) crow[n] = f32_to_bf16_bits(silu_f(acc[i][0][r]) * acc[i][1][r]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = n0 + wn * 64 + j * 32 + col_l;
-          if (n < N) crow[n] = f32_to_bf16_bits(acc[i][j][r]);
-        }
-      }
-    }
-  }
+  TileArgs ta;
+  ta.A = A + (long long)blockIdx.z * strideA_batch;
+  ta.lda = lda;
+  ta.bg = B0 + zb + (long long)tl.group * strideB_group;
+  ta.bu = EPI == EPI_SILU_GLU ? B1 + zb + (long long)tl.group * strideB_group : ta.bg;
+  ta.C = C + (long long)blockIdx.z * strideC_batch;
+  ta.ldc = ldc;
+  ta.row0 = tl.row0;
+  ta.rows = tl.rows;
+  ta.m0 = tl.m_tile * kBM;
+  ta.n0 = tl.n_tile * kNOut;
+  ta.N = N;
+  ta.Kdim = Kdim;
+  if (tl.rows - ta.m0 <= kBM / 2)
+    gemm_tile<EPI, 2>(ta, lds);
+  else
+    gemm_tile<EPI, 4>(ta, lds);
 }
 
 // ------------------------------------------------------------------ fp32 VALU GEMM
