@@ -15,8 +15,9 @@
 //     blocks; an expert's last row tile with at most 128 rows runs as a
 //     half-height tile (each wave 64x64);
 //   * 64-deep k-tiles (full 128-byte row segments) move straight from global
-//     memory into two LDS stages (global_load_lds, 16 B per lane), the next
-//     tile loading while the current one feeds the MFMAs; the rows are
+//     memory into LDS (global_load_lds, 16 B per lane): the activations in a
+//     ring of two slots (one tile ahead), the weights in a ring of three (two
+//     tiles ahead, they miss L2 more often), 160 KB in all; the rows are
 //     XOR-swizzled in 16-byte chunks so the fragment reads are free of bank
 //     conflicts;
 //   * ragged groups: the tile list (expert, row tile, column tile) is derived
@@ -98,9 +99,9 @@ __device__ __forceinline__ int xcd_tile_id() {
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kThreads = 512;                             // 8 waves, 2 per SIMD
 constexpr int kRowBytes = kBK * 2;                        // 128 B per staged row
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;      // 64 KB
-constexpr int kStages = 2;                                // 128 KB of LDS
-constexpr int kDmaPerTile = kStageBytes / (kThreads * 16);  // 8 x 16 B per thread
+constexpr int kSlotBytes = kBM * kRowBytes;               // 32 KB: one operand of one k-tile
+constexpr int kAStages = 2, kBStages = 3;                 // 5 slots = 160 KB of LDS
+constexpr int kDmaPerTile = 2 * kSlotBytes / (kThreads * 16);  // 8 x 16 B per thread
 constexpr int kDmaA = kDmaPerTile / 2;
 constexpr int kRowsPerDma = 1024 / kRowBytes;             // rows filled by one wave instruction
 
@@ -117,23 +118,29 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // service group, i.e. no bank conflicts.
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// One wave's share of staging a k-tile (A then B, up to 64 KB per workgroup)
-// with direct global->LDS loads: instruction j of wave w fills 1 KB of LDS =
-// rows (8j + w)*8 .. +8 of the A (j < 4) or B (j >= 4) tile; lane l covers
-// row +l/8, physical chunk l%8, so its source is logical chunk (l%8) ^ swz(row).
-// NA = A instructions per wave: 4 for a 256-row tile, 2 for a 128-row tile.
+// Staging one operand of a k-tile (32 KB per workgroup) with direct
+// global->LDS loads: instruction j of wave w fills 1 KB of the slot = rows
+// (8j + w)*8 .. +8; lane l covers row +l/8, physical chunk l%8, so its source
+// is logical chunk (l%8) ^ swz(row).  NA = A instructions per wave (4 for a
+// 256-row tile, 2 for a 128-row tile); B always takes 4 (rows 0..127 from
+// b_lo, 128..255 from b_hi).
 template <int NA>
-__device__ __forceinline__ void stage_tile(uint8_t* stage, const uint8_t* a_tile,
-                                           const uint8_t* b_lo, const uint8_t* b_hi,
-                                           const uint32_t (&off)[kDmaPerTile], int wave,
-                                           int kbytes) {
+__device__ __forceinline__ void stage_a(uint8_t* slot, const uint8_t* a_tile,
+                                        const uint32_t (&off)[kDmaPerTile], int wave,
+                                        int kbytes) {
 #pragma unroll
-  for (int j = 0; j < kDmaPerTile; ++j) {
-    if (j >= NA && j < kDmaA) continue;
-    const uint8_t* src = j < kDmaA ? a_tile : (j < kDmaA + kDmaA / 2 ? b_lo : b_hi);
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + kbytes + off[j]),
-                                     (lds_ptr_t)(stage + (j * 8 + wave) * 1024), 16, 0, 0);
-  }
+  for (int j = 0; j < NA; ++j)
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(a_tile + kbytes + off[j]),
+                                     (lds_ptr_t)(slot + (j * 8 + wave) * 1024), 16, 0, 0);
+}
+__device__ __forceinline__ void stage_b(uint8_t* slot, const uint8_t* b_lo, const uint8_t* b_hi,
+                                        const uint32_t (&off)[kDmaPerTile], int wave,
+                                        int kbytes) {
+#pragma unroll
+  for (int j = 0; j < kDmaA; ++j)
+    __builtin_amdgcn_global_load_lds(
+        static_cast<const void*>((j < kDmaA / 2 ? b_lo : b_hi) + kbytes + off[kDmaA + j]),
+        (lds_ptr_t)(slot + (j * 8 + wave) * 1024), 16, 0, 0);
 }
 
 struct Frags {
@@ -144,11 +151,9 @@ struct Frags {
 // a_row0 + 32i) and 2 B fragments (rows b_row[j]); xa/xb hold (lane's
 // k-group) ^ swz(row).
 template <int NFA>
-__device__ __forceinline__ void load_frags(const uint8_t* stage, int ks, int a_row0,
-                                           const int (&b_row)[2], const int (&xa)[4],
-                                           const int (&xb)[2], Frags& f) {
-  const uint8_t* sa = stage;
-  const uint8_t* sb = stage + kBM * kRowBytes;
+__device__ __forceinline__ void load_frags(const uint8_t* sa, const uint8_t* sb, int ks,
+                                           int a_row0, const int (&b_row)[2],
+                                           const int (&xa)[4], const int (&xb)[2], Frags& f) {
 #pragma unroll
   for (int i = 0; i < NFA; ++i)
     f.a[i] = *reinterpret_cast<const bf16x8*>(sa + (a_row0 + i * 32) * kRowBytes +
@@ -168,11 +173,14 @@ __device__ __forceinline__ void mma_step(const Frags& f, f32x16 (&acc)[4][2]) {
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
-// Wait until this wave's loads of the next stage have landed and its LDS
-// reads have returned; then a workgroup barrier (without a memory fence:
-// the waits above are the only ones needed).
+// Wait until this wave's loads of the next k-tile have landed -- only the
+// B loads of the tile after it (the last kDmaA loads issued) may still be in
+// flight; loads complete in issue order -- and its LDS reads have returned;
+// then a workgroup barrier without a memory fence, so those B loads stay in
+// flight across it.
 __device__ __forceinline__ void wait_stage_and_barrier() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  static_assert(kDmaA == 4, "vmcnt immediate assumes 4 B loads per k-tile");
+  asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -253,30 +261,39 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) xb[j] = kgrp ^ swz(b_row[j]);
 
-  // Two LDS stages: tile t+1 is loaded (direct to LDS) while tile t feeds the
-  // MFMAs.  Fragments are double-buffered across the four k-steps of a tile;
-  // the stage wait and barrier come before the last k-step's MFMAs, which
-  // then overlap the fragment reads of the next tile.  The body has no
-  // branches: past the last tile the loads re-read the last tile into the
-  // free stage and the next-tile fragments are never used.
+  // LDS: A k-tiles in a ring of 2 slots, B k-tiles in a ring of 3 (the
+  // weights miss L2 more often, so they are loaded two tiles ahead, A one).
+  // Fragments are double-buffered across the four k-steps of a tile; the
+  // stage wait and barrier come before the last k-step's MFMAs, which then
+  // overlap the fragment reads of the next tile.  The body has no branches:
+  // past the last tile the loads re-read the last tile into free slots and
+  // the next-tile fragments are never used.
   constexpr int NA = NFA == 4 ? kDmaA : kDmaA / 2;
+  uint8_t* a_slots = lds;
+  uint8_t* b_slots = lds + kAStages * kSlotBytes;
   const int nk = Kdim / kBK;
-  stage_tile<NA>(lds, a_tile, b_lo, b_hi, off, wave, 0);
+  stage_a<NA>(a_slots, a_tile, off, wave, 0);
+  stage_b(b_slots, b_lo, b_hi, off, wave, 0);
+  stage_b(b_slots + kSlotBytes, b_lo, b_hi, off, wave, min(1, nk - 1) * kRowBytes);
   wait_stage_and_barrier();
   Frags f0, f1;
-  load_frags<NFA>(lds, 0, a_row0, b_row, xa, xb, f0);
+  load_frags<NFA>(a_slots, b_slots, 0, a_row0, b_row, xa, xb, f0);
   for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t* cur = lds + (kt & 1) * kStageBytes;
-    uint8_t* nxt = lds + ((kt + 1) & 1) * kStageBytes;
-    stage_tile<NA>(nxt, a_tile, b_lo, b_hi, off, wave, min(kt + 1, nk - 1) * kRowBytes);
-    load_frags<NFA>(cur, 1, a_row0, b_row, xa, xb, f1);
+    const uint8_t* sa = a_slots + (kt & 1) * kSlotBytes;
+    const uint8_t* sb = b_slots + (kt % kBStages) * kSlotBytes;
+    uint8_t* na = a_slots + ((kt + 1) & 1) * kSlotBytes;
+    const uint8_t* nb = b_slots + ((kt + 1) % kBStages) * kSlotBytes;
+    stage_a<NA>(na, a_tile, off, wave, min(kt + 1, nk - 1) * kRowBytes);
+    stage_b(b_slots + ((kt + 2) % kBStages) * kSlotBytes, b_lo, b_hi, off, wave,
+            min(kt + 2, nk - 1) * kRowBytes);
+    load_frags<NFA>(sa, sb, 1, a_row0, b_row, xa, xb, f1);
     mma_step<NFA>(f0, acc);
-    load_frags<NFA>(cur, 2, a_row0, b_row, xa, xb, f0);
+    load_frags<NFA>(sa, sb, 2, a_row0, b_row, xa, xb, f0);
     mma_step<NFA>(f1, acc);
-    load_frags<NFA>(cur, 3, a_row0, b_row, xa, xb, f1);
+    load_frags<NFA>(sa, sb, 3, a_row0, b_row, xa, xb, f1);
     mma_step<NFA>(f0, acc);
     wait_stage_and_barrier();
-    load_frags<NFA>(nxt, 0, a_row0, b_row, xa, xb, f0);
+    load_frags<NFA>(na, nb, 0, a_row0, b_row, xa, xb, f0);
     mma_step<NFA>(f1, acc);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -313,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ B1, long long strideB_group, long long strideB_batch,
     uint16_t* __restrict__ C, int ldc, long long strideC_batch,
     const int32_t* __restrict__ offsets, int n_groups, int fixed_rows, int N, int Kdim) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[(kAStages + kBStages) * kSlotBytes];
 
   // Output columns per tile: EPI_STORE 256, EPI_SILU_GLU 128 (gate and up 128 each).
   constexpr int kNOut = EPI == EPI_SILU_GLU ? kBN / 2 : kBN;
