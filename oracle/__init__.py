@@ -30,7 +30,9 @@ _LL = ctypes.c_longlong
 def lib():
     global _LIB
     if _LIB is None:
-        path = _build.library_path()
+        # ORACLE_LIBRARY: an alternative build of moe_oracle.cpp (the mutation
+        # test points the pins at deliberately broken copies).
+        path = os.environ.get("ORACLE_LIBRARY") or _build.library_path()
         if not os.path.exists(path):
             _build.build()
         L = ctypes.CDLL(path)
