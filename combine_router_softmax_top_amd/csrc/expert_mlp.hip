@@ -23,10 +23,10 @@
 //   * ragged groups: the tile list (expert, row tile, column tile) is derived
 //     on the device from the expert offsets; the grid is the host's upper
 //     bound and surplus workgroups exit at once (no host synchronisation);
-//   * workgroup ids are remapped so that each XCD (ids are dealt round-robin
-//     over the 8 XCDs) walks a contiguous stretch of tiles, and within an
-//     expert tiles go in groups of 4 row tiles, keeping shared operands in
-//     that XCD's L2;
+//   * the valid tiles are counted on the device and dealt to the 8 XCDs (ids
+//     go round-robin over them) in contiguous stretches of equal length, and
+//     within an expert tiles go in groups of 4 row tiles, keeping shared
+//     operands in that XCD's L2;
 //   * the k order of every output is fixed (64-wide tiles ascending, MFMA
 //     k-blocks of 16 ascending) and independent of the row tiling, so a row's
 //     result does not depend on which other rows share its call.
@@ -50,30 +50,71 @@ struct Tile {
 
 constexpr int kGroupM = 4;
 
-// Maps a linear tile id onto (group, row tile, column tile).  Groups are the
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int u = __shfl_up(v, d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// Tiles of group j (lane-parallel over groups; lanes past n_groups give 0).
+__device__ __forceinline__ int group_tiles(const int32_t* __restrict__ offsets, int n_groups,
+                                           int j, int BM, int nN, int& a, int& b) {
+  a = b = 0;
+  if (j >= n_groups) return 0;
+  a = offsets[j];
+  b = offsets[j + 1];
+  return (b - a + BM - 1) / BM * nN;
+}
+
+// Maps this workgroup onto (group, row tile, column tile).  Groups are the
 // local experts (from the device offsets) or, with offsets == nullptr, a single
-// group of fixed_rows rows.  Returns false for ids past the last tile.
-__device__ __forceinline__ bool find_tile(int tile, const int32_t* __restrict__ offsets,
-                                          int n_groups, int fixed_rows, int BM, int nN,
-                                          Tile& out) {
+// group of fixed_rows rows.  The valid tiles are counted first and dealt to the
+// 8 XCDs in contiguous stretches of equal length (workgroup ids go round-robin
+// over the XCDs, so XCD x runs ids x, x+8, ...): the grid is only an upper
+// bound, and splitting the bound instead would leave the last XCDs with the
+// surplus ids.  Within a group, tiles go in groups of kGroupM row tiles that
+// sweep the column tiles.  Returns false for surplus workgroups.
+__device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int n_groups,
+                                          int fixed_rows, int BM, int nN, Tile& out) {
+  const int lane = threadIdx.x & 63;
   int row0 = 0, rows = fixed_rows, group = 0;
-  int mt = (rows + BM - 1) / BM;
+  int total;
   if (offsets != nullptr) {
-    bool found = false;
-    for (int j = 0; j < n_groups; ++j) {
-      const int a = offsets[j], b = offsets[j + 1];
-      const int m = (b - a + BM - 1) / BM;
-      const int cnt = m * nN;
-      if (tile < cnt) {
-        row0 = a; rows = b - a; group = j; mt = m; found = true;
+    total = 0;
+    for (int base = 0; base < n_groups; base += 64) {
+      int a, b;
+      const int cnt = group_tiles(offsets, n_groups, base + lane, BM, nN, a, b);
+      total += __shfl(wave_inclusive_sum(cnt), 63, 64);
+    }
+  } else {
+    total = (rows + BM - 1) / BM * nN;
+  }
+  const int per = (total + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  int tile = (blockIdx.x & 7) * per + slot;
+  if (slot >= per || tile >= total) return false;
+  if (offsets != nullptr) {
+    for (int base = 0;; base += 64) {
+      int a, b;
+      const int cnt = group_tiles(offsets, n_groups, base + lane, BM, nN, a, b);
+      const int incl = wave_inclusive_sum(cnt);
+      const int chunk = __shfl(incl, 63, 64);
+      if (tile < chunk) {
+        const int L = __builtin_ctzll(__ballot(incl > tile));
+        row0 = __shfl(a, L, 64);
+        rows = __shfl(b, L, 64) - row0;
+        group = base + L;
+        tile -= __shfl(incl - cnt, L, 64);
         break;
       }
-      tile -= cnt;
+      tile -= chunk;
     }
-    if (!found) return false;
-  } else if (tile >= mt * nN) {
-    return false;
   }
+  const int mt = (rows + BM - 1) / BM;
   const int gsize = kGroupM * nN;
   const int g = tile / gsize;
   const int first_m = g * kGroupM;
@@ -85,13 +126,6 @@ __device__ __forceinline__ bool find_tile(int tile, const int32_t* __restrict__ 
   out.m_tile = first_m + in % gm;
   out.n_tile = in / gm;
   return true;
-}
-
-// Workgroup id -> logical tile id: XCD x (ids x, x+8, ...) gets the x-th
-// contiguous eighth of the tile range.  gridDim.x is a multiple of 8.
-__device__ __forceinline__ int xcd_tile_id() {
-  const int per = gridDim.x >> 3;
-  return (blockIdx.x & 7) * per + (blockIdx.x >> 3);
 }
 
 // ------------------------------------------------------------------ bf16 MFMA GEMM
@@ -336,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
   constexpr int kNOut = EPI == EPI_SILU_GLU ? kBN / 2 : kBN;
   const int nN = (N + kNOut - 1) / kNOut;
   Tile tl;
-  if (!find_tile(xcd_tile_id(), offsets, n_groups, fixed_rows, kBM, nN, tl)) return;
+  if (!find_tile(offsets, n_groups, fixed_rows, kBM, nN, tl)) return;
 
   const long long zb = (long long)blockIdx.z * strideB_batch;
   TileArgs ta;
@@ -373,7 +407,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
   __shared__ float su[kFK][kFN + 1];
   const int nN = (N + kFN - 1) / kFN;
   Tile tl;
-  if (!find_tile(xcd_tile_id(), offsets, n_groups, fixed_rows, kFM, nN, tl)) return;
+  if (!find_tile(offsets, n_groups, fixed_rows, kFM, nN, tl)) return;
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
   const int m0 = tl.m_tile * kFM, n0 = tl.n_tile * kFN;
