@@ -219,6 +219,32 @@ __device__ __forceinline__ void wait_stage_and_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Scheduling of one k-step (one basic block between sched_barriers): the
+// k-step's NM MFMAs, each of the first ones followed by two of the ND LDS
+// reads of the next k-step's fragments, the later ones by the NV global->LDS
+// loads (the loads follow the reads in program order: they write LDS the
+// compiler cannot tell apart from what the reads read).  The reads thus
+// have most of the k-step to land.  Without this the compiler sinks each
+// fragment read to just before its MFMA and waits on it there.
+template <int NM, int ND, int NV, int I = 0>
+__device__ __forceinline__ void pin_kstep_schedule() {
+  if constexpr (I == NM) {
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    constexpr int kWithReads = (ND + 1) / 2;
+    constexpr int kRest = NM - kWithReads;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (I < kWithReads) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * I + 2 <= ND ? 2 : 1, 0);  // DS read
+    } else if constexpr (NV > 0) {
+      constexpr int j = I - kWithReads;
+      constexpr int n = NV * (j + 1) / kRest - NV * j / kRest;
+      if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x020, n, 0);  // VMEM
+    }
+    pin_kstep_schedule<NM, ND, NV, I + 1>();
+  }
+}
+
 struct TileArgs {
   const uint16_t* A;
   int lda;
@@ -303,6 +329,7 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
   // past the last tile the loads re-read the last tile into free slots and
   // the next-tile fragments are never used.
   constexpr int NA = NFA == 4 ? kDmaA : kDmaA / 2;
+  constexpr int kMfma = NFA * 2, kReads = NFA + 2;  // per k-step
   uint8_t* a_slots = lds;
   uint8_t* b_slots = lds + kAStages * kSlotBytes;
   const int nk = Kdim / kBK;
@@ -317,18 +344,22 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
     const uint8_t* sb = b_slots + (kt % kBStages) * kSlotBytes;
     uint8_t* na = a_slots + ((kt + 1) & 1) * kSlotBytes;
     const uint8_t* nb = b_slots + ((kt + 1) % kBStages) * kSlotBytes;
+    load_frags<NFA>(sa, sb, 1, a_row0, b_row, xa, xb, f1);
     stage_a<NA>(na, a_tile, off, wave, min(kt + 1, nk - 1) * kRowBytes);
     stage_b(b_slots + ((kt + 2) % kBStages) * kSlotBytes, b_lo, b_hi, off, wave,
             min(kt + 2, nk - 1) * kRowBytes);
-    load_frags<NFA>(sa, sb, 1, a_row0, b_row, xa, xb, f1);
     mma_step<NFA>(f0, acc);
+    pin_kstep_schedule<kMfma, kReads, NA + kDmaA>();
     load_frags<NFA>(sa, sb, 2, a_row0, b_row, xa, xb, f0);
     mma_step<NFA>(f1, acc);
+    pin_kstep_schedule<kMfma, kReads, 0>();
     load_frags<NFA>(sa, sb, 3, a_row0, b_row, xa, xb, f1);
     mma_step<NFA>(f0, acc);
+    pin_kstep_schedule<kMfma, kReads, 0>();
     wait_stage_and_barrier();
     load_frags<NFA>(na, nb, 0, a_row0, b_row, xa, xb, f0);
     mma_step<NFA>(f1, acc);
+    pin_kstep_schedule<kMfma, kReads, 0>();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
