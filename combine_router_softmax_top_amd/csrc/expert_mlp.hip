@@ -23,10 +23,10 @@
 //   * ragged groups: the tile list (expert, row tile, column tile) is derived
 //     on the device from the expert offsets; the grid is the host's upper
 //     bound and surplus workgroups exit at once (no host synchronisation);
-//   * the valid tiles are counted on the device and dealt to the 8 XCDs (ids
-//     go round-robin over them) in contiguous stretches of equal length, and
-//     within an expert tiles go in groups of 4 row tiles, keeping shared
-//     operands in that XCD's L2;
+//   * the row tiles of all experts form bands of 16; the 8 XCDs work on the
+//     same band at once, each on an eighth of its columns, so a weight tile
+//     streams from HBM once per band and the activations shared by the XCDs
+//     come from the Infinity Cache;
 //   * the k order of every output is fixed (64-wide tiles ascending, MFMA
 //     k-blocks of 16 ascending) and independent of the row tiling, so a row's
 //     result does not depend on which other rows share its call.
@@ -48,8 +48,6 @@ struct Tile {
   int n_tile;   // column tile
 };
 
-constexpr int kGroupM = 4;
-
 __device__ __forceinline__ int wave_inclusive_sum(int v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -70,61 +68,75 @@ __device__ __forceinline__ int group_tiles(const int32_t* __restrict__ offsets, 
   return (b - a + BM - 1) / BM * nN;
 }
 
+constexpr int kBandRows = 16;  // row tiles per band
+
 // Maps this workgroup onto (group, row tile, column tile).  Groups are the
 // local experts (from the device offsets) or, with offsets == nullptr, a single
-// group of fixed_rows rows.  The valid tiles are counted first and dealt to the
-// 8 XCDs in contiguous stretches of equal length (workgroup ids go round-robin
-// over the XCDs, so XCD x runs ids x, x+8, ...): the grid is only an upper
-// bound, and splitting the bound instead would leave the last XCDs with the
-// surplus ids.  Within a group, tiles go in groups of kGroupM row tiles that
-// sweep the column tiles.  Returns false for surplus workgroups.
+// group of fixed_rows rows.  The row tiles of all groups, in order, form one
+// list cut into bands of kBandRows row tiles; the 8 XCDs (workgroup ids go
+// round-robin over them, XCD x running ids x, x+8, ...) all work on the same
+// band at a time, each on an eighth of the band's tiles taken column-major, so
+// an XCD holds a couple of weight column tiles across all the band's rows.
+// A weight tile then streams from HBM once per band, and the activation rows,
+// shared by the 8 XCDs at the same time, come from the Infinity Cache after
+// the first read.  Returns false for surplus workgroups.
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int n_groups,
                                           int fixed_rows, int BM, int nN, Tile& out) {
   const int lane = threadIdx.x & 63;
-  int row0 = 0, rows = fixed_rows, group = 0;
-  int total;
+  int n_rt;  // row tiles in all groups
   if (offsets != nullptr) {
-    total = 0;
+    n_rt = 0;
     for (int base = 0; base < n_groups; base += 64) {
       int a, b;
-      const int cnt = group_tiles(offsets, n_groups, base + lane, BM, nN, a, b);
-      total += __shfl(wave_inclusive_sum(cnt), 63, 64);
+      const int cnt = group_tiles(offsets, n_groups, base + lane, BM, 1, a, b);
+      n_rt += __shfl(wave_inclusive_sum(cnt), 63, 64);
     }
   } else {
-    total = (rows + BM - 1) / BM * nN;
+    n_rt = (fixed_rows + BM - 1) / BM;
   }
-  const int per = (total + 7) >> 3;
-  const int slot = blockIdx.x >> 3;
-  int tile = (blockIdx.x & 7) * per + slot;
-  if (slot >= per || tile >= total) return false;
+  const int xcd = blockIdx.x & 7;
+  int slot = blockIdx.x >> 3;
+  const int full_bands = n_rt / kBandRows;
+  const int per_full = 2 * nN;  // kBandRows * nN / 8 tiles of a full band per XCD
+  int band, band_rows, t;
+  if (slot < full_bands * per_full) {
+    band = slot / per_full;
+    band_rows = kBandRows;
+    t = xcd * per_full + slot % per_full;
+  } else {
+    slot -= full_bands * per_full;
+    band = full_bands;
+    band_rows = n_rt - full_bands * kBandRows;
+    const int tiles = band_rows * nN;
+    const int first = xcd * tiles / 8, end = (xcd + 1) * tiles / 8;
+    if (band_rows == 0 || slot >= end - first) return false;
+    t = first + slot;
+  }
+  const int n_tile = t / band_rows;
+  int rt = band * kBandRows + t % band_rows;  // global row tile
+  int row0 = 0, rows = fixed_rows, group = 0;
   if (offsets != nullptr) {
     for (int base = 0;; base += 64) {
       int a, b;
-      const int cnt = group_tiles(offsets, n_groups, base + lane, BM, nN, a, b);
+      const int cnt = group_tiles(offsets, n_groups, base + lane, BM, 1, a, b);
       const int incl = wave_inclusive_sum(cnt);
       const int chunk = __shfl(incl, 63, 64);
-      if (tile < chunk) {
-        const int L = __builtin_ctzll(__ballot(incl > tile));
+      if (rt < chunk) {
+        const int L = __builtin_ctzll(__ballot(incl > rt));
         row0 = __shfl(a, L, 64);
         rows = __shfl(b, L, 64) - row0;
         group = base + L;
-        tile -= __shfl(incl - cnt, L, 64);
+        rt -= __shfl(incl - cnt, L, 64);
         break;
       }
-      tile -= chunk;
+      rt -= chunk;
     }
   }
-  const int mt = (rows + BM - 1) / BM;
-  const int gsize = kGroupM * nN;
-  const int g = tile / gsize;
-  const int first_m = g * kGroupM;
-  const int gm = min(kGroupM, mt - first_m);
-  const int in = tile - g * gsize;
   out.row0 = row0;
   out.rows = rows;
   out.group = group;
-  out.m_tile = first_m + in % gm;
-  out.n_tile = in / gm;
+  out.m_tile = rt;
+  out.n_tile = n_tile;
   return true;
 }
 
@@ -198,23 +210,25 @@ __device__ __forceinline__ void load_frags(const uint8_t* sa, const uint8_t* sb,
                                               (((2 * ks) ^ xb[j]) << 4));
 }
 
+// The weights go in the MFMA's first (row) operand, so each 32x32 block holds
+// the transposed output: a lane keeps one output row and runs of 4 adjacent
+// output columns, which the epilogue stores 8 bytes at a time.
 template <int NFA>
 __device__ __forceinline__ void mma_step(const Frags& f, f32x16 (&acc)[4][2]) {
 #pragma unroll
   for (int i = 0; i < NFA; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
-// Wait until this wave's loads of the next k-tile have landed -- only the
-// B loads of the tile after it (the last kDmaA loads issued) may still be in
-// flight; loads complete in issue order -- and its LDS reads have returned;
-// then a workgroup barrier without a memory fence, so those B loads stay in
-// flight across it.
-__device__ __forceinline__ void wait_stage_and_barrier() {
-  static_assert(kDmaA == 4, "vmcnt immediate assumes 4 B loads per k-tile");
-  asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+// Wait until at most VM of this wave's global->LDS loads are in flight (loads
+// complete in issue order, so every older load has landed) and its LDS reads
+// have returned; then a workgroup barrier without a memory fence, so the
+// younger loads stay in flight across it.
+template <int VM>
+__device__ __forceinline__ void wait_loads_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(VM) : "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
@@ -243,6 +257,15 @@ __device__ __forceinline__ void pin_kstep_schedule() {
     }
     pin_kstep_schedule<NM, ND, NV, I + 1>();
   }
+}
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Four floats rounded to bf16 and written as one 8-byte store.
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, const float (&v)[4]) {
+  const u32x2 w = {(uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16),
+                   (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16)};
+  *reinterpret_cast<u32x2*>(dst) = w;
 }
 
 struct TileArgs {
@@ -321,67 +344,85 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) xb[j] = kgrp ^ swz(b_row[j]);
 
-  // LDS: A k-tiles in a ring of 2 slots, B k-tiles in a ring of 3 (the
-  // weights miss L2 more often, so they are loaded two tiles ahead, A one).
-  // Fragments are double-buffered across the four k-steps of a tile; the
-  // stage wait and barrier come before the last k-step's MFMAs, which then
-  // overlap the fragment reads of the next tile.  The body has no branches:
-  // past the last tile the loads re-read the last tile into free slots and
-  // the next-tile fragments are never used.
+  // LDS: A k-tiles in a ring of 2 slots, B k-tiles in a ring of 3.  Right
+  // after the barrier that ends the reads of tile kt (its last k-step's
+  // fragments are already in registers) the slots of tile kt take A(kt+2)
+  // and B(kt+3): the activations are in flight for five k-steps before they
+  // are needed, the weights (which miss L2 more often) for nine.  The wait
+  // before that barrier needs tile kt+1, so only the B(kt+2) loads issued
+  // after A(kt+1) may still be in flight.  Fragments are double-buffered
+  // across the four k-steps; the barrier comes before the last k-step's
+  // MFMAs, which overlap the next tile's first fragment reads and the new
+  // loads.  The body has no branches: past the last tile the loads re-read
+  // the last tile into free slots and the next-tile fragments go unused.
   constexpr int NA = NFA == 4 ? kDmaA : kDmaA / 2;
   constexpr int kMfma = NFA * 2, kReads = NFA + 2;  // per k-step
   uint8_t* a_slots = lds;
   uint8_t* b_slots = lds + kAStages * kSlotBytes;
   const int nk = Kdim / kBK;
+  const int last = (nk - 1) * kRowBytes;
   stage_a<NA>(a_slots, a_tile, off, wave, 0);
   stage_b(b_slots, b_lo, b_hi, off, wave, 0);
-  stage_b(b_slots + kSlotBytes, b_lo, b_hi, off, wave, min(1, nk - 1) * kRowBytes);
-  wait_stage_and_barrier();
+  stage_a<NA>(a_slots + kSlotBytes, a_tile, off, wave, min(kRowBytes, last));
+  stage_b(b_slots + kSlotBytes, b_lo, b_hi, off, wave, min(kRowBytes, last));
+  stage_b(b_slots + 2 * kSlotBytes, b_lo, b_hi, off, wave, min(2 * kRowBytes, last));
+  wait_loads_and_barrier<NA + 2 * kDmaA>();  // tile 0 landed
   Frags f0, f1;
   load_frags<NFA>(a_slots, b_slots, 0, a_row0, b_row, xa, xb, f0);
   for (int kt = 0; kt < nk; ++kt) {
-    const uint8_t* sa = a_slots + (kt & 1) * kSlotBytes;
-    const uint8_t* sb = b_slots + (kt % kBStages) * kSlotBytes;
-    uint8_t* na = a_slots + ((kt + 1) & 1) * kSlotBytes;
+    uint8_t* sa = a_slots + (kt & 1) * kSlotBytes;
+    uint8_t* sb = b_slots + (kt % kBStages) * kSlotBytes;
+    const uint8_t* na = a_slots + ((kt + 1) & 1) * kSlotBytes;
     const uint8_t* nb = b_slots + ((kt + 1) % kBStages) * kSlotBytes;
     load_frags<NFA>(sa, sb, 1, a_row0, b_row, xa, xb, f1);
-    stage_a<NA>(na, a_tile, off, wave, min(kt + 1, nk - 1) * kRowBytes);
-    stage_b(b_slots + ((kt + 2) % kBStages) * kSlotBytes, b_lo, b_hi, off, wave,
-            min(kt + 2, nk - 1) * kRowBytes);
     mma_step<NFA>(f0, acc);
-    pin_kstep_schedule<kMfma, kReads, NA + kDmaA>();
+    pin_kstep_schedule<kMfma, kReads, 0>();
     load_frags<NFA>(sa, sb, 2, a_row0, b_row, xa, xb, f0);
     mma_step<NFA>(f1, acc);
     pin_kstep_schedule<kMfma, kReads, 0>();
     load_frags<NFA>(sa, sb, 3, a_row0, b_row, xa, xb, f1);
     mma_step<NFA>(f0, acc);
     pin_kstep_schedule<kMfma, kReads, 0>();
-    wait_stage_and_barrier();
+    wait_loads_and_barrier<kDmaA>();  // tile kt+1 landed; tile kt's slots free
     load_frags<NFA>(na, nb, 0, a_row0, b_row, xa, xb, f0);
+    stage_a<NA>(sa, a_tile, off, wave, min((kt + 2) * kRowBytes, last));
+    stage_b(sb, b_lo, b_hi, off, wave, min((kt + 3) * kRowBytes, last));
     mma_step<NFA>(f1, acc);
-    pin_kstep_schedule<kMfma, kReads, 0>();
+    pin_kstep_schedule<kMfma, kReads, NA + kDmaA>();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // Epilogue.  Accumulator element r of lane l in a 32x32 block holds
-  // row (r/4)*8 + (l/32)*4 + r%4, column l%32.
-  const int col_l = lane & 31;
-  const int row_l = (lane >> 5) * 4;
+  // Epilogue.  Element r of lane l in a (transposed) 32x32 block is output
+  // row l%32, column (r/4)*8 + (l/32)*4 + r%4: four adjacent bf16 per
+  // (lane, r/4), stored as one 8-byte write.  N is a multiple of 64, so a
+  // group of four columns is either wholly inside or wholly past N.
+  const int row_l = lane & 31;
+  const int col_l = (lane >> 5) * 4;
 #pragma unroll
   for (int i = 0; i < NFA; ++i) {
+    const int m = m0 + wm * kWaveRows + i * 32 + row_l;
+    if (m >= ta.rows) continue;
+    uint16_t* crow = ta.C + (long long)(ta.row0 + m) * ta.ldc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * kWaveRows + i * 32 + (r >> 2) * 8 + row_l + (r & 3);
-      if (m >= ta.rows) continue;
-      uint16_t* crow = ta.C + (long long)(ta.row0 + m) * ta.ldc;
+    for (int g = 0; g < 4; ++g) {
       if (EPI == EPI_SILU_GLU) {
-        const int n = n0 + wn * 32 + col_l;
-        if (n < N) crow[n] = f32_to_bf16_bits(silu_f(acc[i][0][r]) * acc[i][1][r]);
+        const int n = n0 + wn * 32 + g * 8 + col_l;
+        if (n < N) {
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = silu_f(acc[i][0][4 * g + q]) * acc[i][1][4 * g + q];
+          store_bf16x4(crow + n, v);
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int n = n0 + wn * 64 + j * 32 + col_l;
-          if (n < N) crow[n] = f32_to_bf16_bits(acc[i][j][r]);
+          const int n = n0 + wn * 64 + j * 32 + g * 8 + col_l;
+          if (n < N) {
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q];
+            store_bf16x4(crow + n, v);
+          }
         }
       }
     }
@@ -502,9 +543,11 @@ struct GemmArgs {
   int N; int Kdim; int batch;
 };
 
+// Workgroups for an upper bound of row tiles: a multiple of 8, with room for
+// the uneven split of the last band over the XCDs.
 inline int grid_for(int row_tiles, int col_tiles) {
   const int g = row_tiles * col_tiles;
-  return (g + 7) / 8 * 8;
+  return (g + 7) / 8 * 8 + 8;
 }
 
 template <int EPI>
