@@ -44,6 +44,10 @@ def parse():
                    help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--write-traffic-record", metavar="DIR", default=None,
+                   help="no GPU work: read the rocprofv3 counter CSVs under DIR (pmc_FETCH_SIZE, "
+                        "pmc_WRITE_SIZE, pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE) and write the "
+                        "expert-MLP HBM traffic record for the current kernel source")
     p.add_argument("--dbo", action="store_true",
                    help="time the two-microbatch forward (moe_forward_dbo, compute + comm "
                         "streams) against the unsplit moe_forward on the same tokens")
@@ -127,8 +131,52 @@ def cpu_baseline(cfg, inp, target_s: float) -> dict:
                       f"layer (route, dispatch, expert MLP, combine) in fp64, {dt:.1f} s"}
 
 
+def write_traffic_record(d: str, out_path: str = TRAFFIC_FILE) -> dict:
+    """HBM bytes per expert-MLP call from FETCH_SIZE / WRITE_SIZE counter runs.
+
+    Each counter (KiB per dispatch, averaged over dispatches) is scaled by what
+    the same counter reads for a plain device copy of 1 GiB (which reads and
+    writes 1 GiB), so the result is in real bytes.
+    """
+    import csv
+    import glob
+    import re
+
+    def per_kernel(sub):
+        f = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)
+        if not f:
+            raise SystemExit(f"no counter CSV under {os.path.join(d, sub)}")
+        acc = {}
+        for r in csv.DictReader(open(f[0])):
+            m = re.search(r"(\w+_kernel(<[^>]*>)?|__amd_rocclr_copyBuffer)", r["Kernel_Name"])
+            if m:
+                acc.setdefault(m.group(1), []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch, write = per_kernel("pmc_FETCH_SIZE"), per_kernel("pmc_WRITE_SIZE")
+    copy_kib = float(1 << 20)
+    ff = copy_kib / per_kernel("pmc_copy_FETCH_SIZE")["__amd_rocclr_copyBuffer"]
+    fw = copy_kib / per_kernel("pmc_copy_WRITE_SIZE")["__amd_rocclr_copyBuffer"]
+    g1 = (fetch["gemm_bf16_kernel<1>"] * ff + write["gemm_bf16_kernel<1>"] * fw) * 1024
+    g0 = (fetch["gemm_bf16_kernel<0>"] * ff + write["gemm_bf16_kernel<0>"] * fw) * 1024
+    rec = {"workload": "dsv3_prefill_ep", "source_digest": source_digest(),
+           "hbm_bytes_per_launch": g1 + g0, "gate_up_bytes": g1, "down_bytes": g0,
+           "fetch_factor": ff, "write_factor": fw,
+           "per_kernel_hbm_mb": {k: {"read": fetch[k] * ff * 1024 / 1e6,
+                                     "write": write.get(k, 0.0) * fw * 1024 / 1e6}
+                                 for k in fetch if k != "__amd_rocclr_copyBuffer"},
+           "note": "FETCH_SIZE/WRITE_SIZE per dispatch of the two expert-MLP kernels, "
+                   "scaled by a 1 GiB device copy"}
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
 def main():
     args = parse()
+    if args.write_traffic_record:
+        print(json.dumps(write_traffic_record(args.write_traffic_record)), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
               "multi-GPU path", file=sys.stderr)

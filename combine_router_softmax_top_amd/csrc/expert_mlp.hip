@@ -23,10 +23,12 @@
 //   * ragged groups: the tile list (expert, row tile, column tile) is derived
 //     on the device from the expert offsets; the grid is the host's upper
 //     bound and surplus workgroups exit at once (no host synchronisation);
-//   * the row tiles of all experts form bands of 16; the 8 XCDs work on the
-//     same band at once, each on an eighth of its columns, so a weight tile
-//     streams from HBM once per band and the activations shared by the XCDs
-//     come from the Infinity Cache;
+//   * the row tiles of all experts (full-height first, the half-height last
+//     tiles at the end) form bands of 16; the 8 XCDs work on the same band at
+//     once as a 2 x 4 grid (8 rows x a quarter of the columns each), so a
+//     weight tile streams from memory at most twice per band and an
+//     activation tile is shared by 4 XCDs, the repeats served by the
+//     Infinity Cache;
 //   * the k order of every output is fixed (64-wide tiles ascending, MFMA
 //     k-blocks of 16 ascending) and independent of the row tiling, so a row's
 //     result does not depend on which other rows share its call.
@@ -58,75 +60,108 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
   return v;
 }
 
-// Tiles of group j (lane-parallel over groups; lanes past n_groups give 0).
-__device__ __forceinline__ int group_tiles(const int32_t* __restrict__ offsets, int n_groups,
-                                           int j, int BM, int nN, int& a, int& b) {
-  a = b = 0;
-  if (j >= n_groups) return 0;
+// Row tiles of group j (lane-parallel over groups; lanes past n_groups give
+// 0): `full` tiles computed at full height (BM rows, including a last tile of
+// more than BM/2 rows) and `half` (0 or 1) for a last tile of at most BM/2
+// rows, which runs at half height.
+__device__ __forceinline__ void group_row_tiles(const int32_t* __restrict__ offsets, int n_groups,
+                                                int j, int BM, int& a, int& full, int& half) {
+  a = 0;
+  full = half = 0;
+  if (j >= n_groups) return;
   a = offsets[j];
-  b = offsets[j + 1];
-  return (b - a + BM - 1) / BM * nN;
+  const int rows = offsets[j + 1] - a;
+  const int rem = rows % BM;
+  full = rows / BM + (rem > BM / 2 ? 1 : 0);
+  half = (rem > 0 && rem <= BM / 2) ? 1 : 0;
 }
 
 constexpr int kBandRows = 16;  // row tiles per band
 
+// XCD row groups of a band: the 8 XCDs form a grid of row groups x column
+// groups over each band (2 x 4; 8 x 1 when there are fewer than 4 column
+// tiles, so every XCD gets work).
+__host__ __device__ inline int xcd_row_groups(int nN) { return nN >= 4 ? 2 : 8; }
+
+// Upper bound of the tiles one XCD gets, for a bound of row tiles.
+__host__ __device__ inline int tiles_per_xcd_bound(int row_tiles, int nN) {
+  const int rx = xcd_row_groups(nN), cx = 8 / rx;
+  return (nN + cx - 1) / cx * ((row_tiles + rx - 1) / rx + 1);
+}
+
 // Maps this workgroup onto (group, row tile, column tile).  Groups are the
 // local experts (from the device offsets) or, with offsets == nullptr, a single
-// group of fixed_rows rows.  The row tiles of all groups, in order, form one
-// list cut into bands of kBandRows row tiles; the 8 XCDs (workgroup ids go
-// round-robin over them, XCD x running ids x, x+8, ...) all work on the same
-// band at a time, each on an eighth of the band's tiles taken column-major, so
-// an XCD holds a couple of weight column tiles across all the band's rows.
-// A weight tile then streams from HBM once per band, and the activation rows,
-// shared by the 8 XCDs at the same time, come from the Infinity Cache after
-// the first read.  Returns false for surplus workgroups.
+// group of fixed_rows rows.  The row tiles form one list -- every group's
+// full-height tiles in group order, then the half-height last tiles -- cut
+// into bands of kBandRows row tiles.  The 8 XCDs (workgroup ids go round-robin
+// over them, XCD x running ids x, x+8, ...) all work on the same band at a
+// time: they form a grid of row groups x column groups over it, and XCD x
+// takes its block of the band column by column.  An XCD thus holds a few
+// weight column tiles across half the band's rows: a weight tile streams
+// from memory once or twice per band, an activation row tile is shared by
+// the few XCDs of its row group (the Infinity Cache serves the repeats), and
+// within an XCD both operands are reused from L2.  The cheap half-height
+// tiles come last, where the final round of tiles is only partly filled.
+// Returns false for surplus workgroups.
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int n_groups,
                                           int fixed_rows, int BM, int nN, Tile& out) {
   const int lane = threadIdx.x & 63;
-  int n_rt;  // row tiles in all groups
+  int n_full = 0, n_half = 0;
   if (offsets != nullptr) {
-    n_rt = 0;
     for (int base = 0; base < n_groups; base += 64) {
-      int a, b;
-      const int cnt = group_tiles(offsets, n_groups, base + lane, BM, 1, a, b);
-      n_rt += __shfl(wave_inclusive_sum(cnt), 63, 64);
+      int a, f, h;
+      group_row_tiles(offsets, n_groups, base + lane, BM, a, f, h);
+      n_full += __shfl(wave_inclusive_sum(f), 63, 64);
+      n_half += __shfl(wave_inclusive_sum(h), 63, 64);
     }
   } else {
-    n_rt = (fixed_rows + BM - 1) / BM;
+    const int rem = fixed_rows % BM;
+    n_full = fixed_rows / BM + (rem > BM / 2 ? 1 : 0);
+    n_half = (rem > 0 && rem <= BM / 2) ? 1 : 0;
   }
+  const int n_rt = n_full + n_half;
   const int xcd = blockIdx.x & 7;
   int slot = blockIdx.x >> 3;
+  const int rx = xcd_row_groups(nN), cx = 8 / rx;
+  const int rg = xcd / cx, cg = xcd % cx;
+  const int c0 = cg * nN / cx, nc = (cg + 1) * nN / cx - c0;  // this XCD's columns
   const int full_bands = n_rt / kBandRows;
-  const int per_full = 2 * nN;  // kBandRows * nN / 8 tiles of a full band per XCD
-  int band, band_rows, t;
+  int r0 = rg * kBandRows / rx, nr = (rg + 1) * kBandRows / rx - r0;  // its rows of a band
+  const int per_full = nr * nc;
+  int band;
   if (slot < full_bands * per_full) {
     band = slot / per_full;
-    band_rows = kBandRows;
-    t = xcd * per_full + slot % per_full;
+    slot -= band * per_full;
   } else {
     slot -= full_bands * per_full;
     band = full_bands;
-    band_rows = n_rt - full_bands * kBandRows;
-    const int tiles = band_rows * nN;
-    const int first = xcd * tiles / 8, end = (xcd + 1) * tiles / 8;
-    if (band_rows == 0 || slot >= end - first) return false;
-    t = first + slot;
+    const int rows_b = n_rt - full_bands * kBandRows;
+    r0 = rg * rows_b / rx;
+    nr = (rg + 1) * rows_b / rx - r0;
+    if (slot >= nr * nc) return false;
   }
-  const int n_tile = t / band_rows;
-  int rt = band * kBandRows + t % band_rows;  // global row tile
-  int row0 = 0, rows = fixed_rows, group = 0;
-  if (offsets != nullptr) {
+  const int n_tile = c0 + slot / nr;
+  int rt = band * kBandRows + r0 + slot % nr;  // index in the row-tile list
+  int row0 = 0, rows = fixed_rows, group = 0, m_tile;
+  if (offsets == nullptr) {
+    m_tile = rt;
+  } else {
+    // Full-height tiles: the rt-th in group order; half-height: the
+    // (rt - n_full)-th group that has one, which is its last row tile.
+    const bool is_half = rt >= n_full;
+    if (is_half) rt -= n_full;
     for (int base = 0;; base += 64) {
-      int a, b;
-      const int cnt = group_tiles(offsets, n_groups, base + lane, BM, 1, a, b);
+      int a, f, h;
+      group_row_tiles(offsets, n_groups, base + lane, BM, a, f, h);
+      const int cnt = is_half ? h : f;
       const int incl = wave_inclusive_sum(cnt);
       const int chunk = __shfl(incl, 63, 64);
       if (rt < chunk) {
         const int L = __builtin_ctzll(__ballot(incl > rt));
         row0 = __shfl(a, L, 64);
-        rows = __shfl(b, L, 64) - row0;
         group = base + L;
-        rt -= __shfl(incl - cnt, L, 64);
+        rows = offsets[group + 1] - row0;
+        m_tile = is_half ? __shfl(f, L, 64) : rt - __shfl(incl - cnt, L, 64);
         break;
       }
       rt -= chunk;
@@ -135,7 +170,7 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
   out.row0 = row0;
   out.rows = rows;
   out.group = group;
-  out.m_tile = rt;
+  out.m_tile = m_tile;
   out.n_tile = n_tile;
   return true;
 }
@@ -143,13 +178,18 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
 // ------------------------------------------------------------------ bf16 MFMA GEMM
 
 constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kThreads = 512;                             // 8 waves, 2 per SIMD
-constexpr int kRowBytes = kBK * 2;                        // 128 B per staged row
-constexpr int kSlotBytes = kBM * kRowBytes;               // 32 KB: one operand of one k-tile
-constexpr int kAStages = 2, kBStages = 3;                 // 5 slots = 160 KB of LDS
-constexpr int kDmaPerTile = 2 * kSlotBytes / (kThreads * 16);  // 8 x 16 B per thread
-constexpr int kDmaA = kDmaPerTile / 2;
+constexpr int kWaves = 8;                                 // 2 x 4 wave grid, 2 waves per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWN = kWaves / 2;                           // waves along the columns
+constexpr int kBF = kBN / kWN / 32;                       // B fragments (32 columns) per wave
+constexpr int kRowBytes = kBK * 2;                        // bytes per staged row
+constexpr int kChunks = kRowBytes / 16;                   // 16-byte chunks per row
+constexpr int kSlotBytes = kBM * kRowBytes;               // one operand of one k-tile
+// Ring slots per operand (160 KB of LDS in all).
+constexpr int kAStages = 2, kBStages = 3;
+constexpr int kDmaB = kSlotBytes / 1024 / kWaves;         // 1-KB loads per wave per operand
 constexpr int kRowsPerDma = 1024 / kRowBytes;             // rows filled by one wave instruction
+static_assert(kAStages * kSlotBytes + kBStages * kSlotBytes == 160 * 1024, "LDS budget");
 
 enum { EPI_STORE = 0, EPI_SILU_GLU = 1 };
 
@@ -172,25 +212,25 @@ __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 // b_lo, 128..255 from b_hi).
 template <int NA>
 __device__ __forceinline__ void stage_a(uint8_t* slot, const uint8_t* a_tile,
-                                        const uint32_t (&off)[kDmaPerTile], int wave,
+                                        const uint32_t (&off)[2 * kDmaB], int wave,
                                         int kbytes) {
 #pragma unroll
   for (int j = 0; j < NA; ++j)
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(a_tile + kbytes + off[j]),
-                                     (lds_ptr_t)(slot + (j * 8 + wave) * 1024), 16, 0, 0);
+                                     (lds_ptr_t)(slot + (j * kWaves + wave) * 1024), 16, 0, 0);
 }
 __device__ __forceinline__ void stage_b(uint8_t* slot, const uint8_t* b_lo, const uint8_t* b_hi,
-                                        const uint32_t (&off)[kDmaPerTile], int wave,
+                                        const uint32_t (&off)[2 * kDmaB], int wave,
                                         int kbytes) {
 #pragma unroll
-  for (int j = 0; j < kDmaA; ++j)
+  for (int j = 0; j < kDmaB; ++j)
     __builtin_amdgcn_global_load_lds(
-        static_cast<const void*>((j < kDmaA / 2 ? b_lo : b_hi) + kbytes + off[kDmaA + j]),
-        (lds_ptr_t)(slot + (j * 8 + wave) * 1024), 16, 0, 0);
+        static_cast<const void*>((j < kDmaB / 2 ? b_lo : b_hi) + kbytes + off[kDmaB + j]),
+        (lds_ptr_t)(slot + (j * kWaves + wave) * 1024), 16, 0, 0);
 }
 
 struct Frags {
-  bf16x8 a[4], b[2];
+  bf16x8 a[4], b[kBF];
 };
 
 // Fragments of k-step ks (16 deep) of a staged tile: NFA A fragments (rows
@@ -198,14 +238,14 @@ struct Frags {
 // k-group) ^ swz(row).
 template <int NFA>
 __device__ __forceinline__ void load_frags(const uint8_t* sa, const uint8_t* sb, int ks,
-                                           int a_row0, const int (&b_row)[2],
-                                           const int (&xa)[4], const int (&xb)[2], Frags& f) {
+                                           int a_row0, const int (&b_row)[kBF],
+                                           const int (&xa)[4], const int (&xb)[kBF], Frags& f) {
 #pragma unroll
   for (int i = 0; i < NFA; ++i)
     f.a[i] = *reinterpret_cast<const bf16x8*>(sa + (a_row0 + i * 32) * kRowBytes +
                                               (((2 * ks) ^ xa[i]) << 4));
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < kBF; ++j)
     f.b[j] = *reinterpret_cast<const bf16x8*>(sb + b_row[j] * kRowBytes +
                                               (((2 * ks) ^ xb[j]) << 4));
 }
@@ -214,11 +254,11 @@ __device__ __forceinline__ void load_frags(const uint8_t* sa, const uint8_t* sb,
 // the transposed output: a lane keeps one output row and runs of 4 adjacent
 // output columns, which the epilogue stores 8 bytes at a time.
 template <int NFA>
-__device__ __forceinline__ void mma_step(const Frags& f, f32x16 (&acc)[4][2]) {
+__device__ __forceinline__ void mma_step(const Frags& f, f32x16 (&acc)[4][kBF]) {
 #pragma unroll
   for (int i = 0; i < NFA; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kBF; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
@@ -289,7 +329,8 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / kWN, wn = wave % kWN;
+  constexpr int kWaveCols = kNOut / kWN;  // output (or h) columns per wave
   const int m0 = ta.m0, n0 = ta.n0, N = ta.N, Kdim = ta.Kdim;
 
   // Per-lane byte offsets of the staged rows inside the tile's operand blocks.
@@ -303,12 +344,12 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
                             : b_lo;
   const int a_last = ta.rows - 1 - m0;
   const int b_last = N - 1 - n0;
-  uint32_t off[kDmaPerTile];
+  uint32_t off[2 * kDmaB];
 #pragma unroll
-  for (int j = 0; j < kDmaPerTile; ++j) {
-    const int r = ((j % kDmaA) * 8 + wave) * kRowsPerDma + lane / (kRowBytes / 16);
-    const int lchunk = (lane % (kRowBytes / 16)) ^ swz(r);
-    if (j < kDmaA) {
+  for (int j = 0; j < 2 * kDmaB; ++j) {
+    const int r = ((j % kDmaB) * kWaves + wave) * kRowsPerDma + lane / kChunks;
+    const int lchunk = (lane % kChunks) ^ swz(r);
+    if (j < kDmaB) {
       off[j] = (uint32_t)(min(r, a_last) * ta.lda * 2 + lchunk * 16);
     } else {
       // r is the B-tile row; rows 128.. come from b_hi
@@ -317,62 +358,67 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
     }
   }
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][kBF];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kBF; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   // Fragment rows: A rows wm*kWaveRows + i*32 + (lane & 31); B rows: the
   // wave's 64 output columns (gate/up pass: 32 gate rows and the matching 32
   // up rows).
-  int b_row[2];
+  int b_row[kBF];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (EPI == EPI_SILU_GLU)
-      b_row[j] = j * kNOut + wn * 32 + (lane & 31);
+  for (int j = 0; j < kBF; ++j) {
+    if (EPI == EPI_SILU_GLU)  // gate rows for j < kBF/2, the matching up rows after
+      b_row[j] = (j / (kBF / 2)) * kNOut + wn * kWaveCols + (j % (kBF / 2)) * 32 + (lane & 31);
     else
-      b_row[j] = wn * 64 + j * 32 + (lane & 31);
+      b_row[j] = wn * kWaveCols + j * 32 + (lane & 31);
   }
   const int a_row0 = wm * kWaveRows + (lane & 31);
   const int kgrp = lane >> 5;
-  int xa[4], xb[2];
+  int xa[4], xb[kBF];
 #pragma unroll
   for (int i = 0; i < 4; ++i) xa[i] = kgrp ^ swz(a_row0 + i * 32);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) xb[j] = kgrp ^ swz(b_row[j]);
+  for (int j = 0; j < kBF; ++j) xb[j] = kgrp ^ swz(b_row[j]);
 
-  // LDS: A k-tiles in a ring of 2 slots, B k-tiles in a ring of 3.  Right
-  // after the barrier that ends the reads of tile kt (its last k-step's
-  // fragments are already in registers) the slots of tile kt take A(kt+2)
-  // and B(kt+3): the activations are in flight for five k-steps before they
-  // are needed, the weights (which miss L2 more often) for nine.  The wait
-  // before that barrier needs tile kt+1, so only the B(kt+2) loads issued
-  // after A(kt+1) may still be in flight.  Fragments are double-buffered
-  // across the four k-steps; the barrier comes before the last k-step's
-  // MFMAs, which overlap the next tile's first fragment reads and the new
-  // loads.  The body has no branches: past the last tile the loads re-read
-  // the last tile into free slots and the next-tile fragments go unused.
-  constexpr int NA = NFA == 4 ? kDmaA : kDmaA / 2;
-  constexpr int kMfma = NFA * 2, kReads = NFA + 2;  // per k-step
+  // LDS: A k-tiles in a ring of kAStages slots, B k-tiles in a ring of
+  // kBStages.  Right after the barrier that ends the reads of tile kt (its
+  // last k-step's fragments are already in registers) the slots of tile kt
+  // take A(kt+kAStages) and B(kt+kBStages), so each load is in flight for
+  // about stages-1 k-tiles before the barrier that needs it.  Loads complete
+  // in issue order; the wait before barrier kt needs tile kt+1 and leaves the
+  // younger loads in flight (kVmBarrier).  Fragments are double-buffered
+  // across the k-steps; the barrier comes before the last k-step's MFMAs,
+  // which overlap the next tile's first fragment reads and the new loads.
+  // The body has no branches: past the last tile the loads re-read the last
+  // tile into free slots and the next-tile fragments go unused.
+  constexpr int NA = NFA == 4 ? kDmaB : kDmaB / 2;
+  constexpr int kMfma = NFA * kBF, kReads = NFA + kBF;  // per k-step
+  constexpr int kMaxStages = kAStages > kBStages ? kAStages : kBStages;
+  // Loads issued after tile 0's in the prologue; after tile kt+1's by barrier kt.
+  constexpr int kVmPrologue = (kAStages - 1) * NA + (kBStages - 1) * kDmaB;
+  constexpr int kVmBarrier = kDmaB;  // the B(kt+2) loads issued after A(kt+1)
+  static_assert(kAStages == 2 && kBStages == 3 && kVmPrologue < 64, "vmcnt immediates");
   uint8_t* a_slots = lds;
   uint8_t* b_slots = lds + kAStages * kSlotBytes;
   const int nk = Kdim / kBK;
   const int last = (nk - 1) * kRowBytes;
-  stage_a<NA>(a_slots, a_tile, off, wave, 0);
-  stage_b(b_slots, b_lo, b_hi, off, wave, 0);
-  stage_a<NA>(a_slots + kSlotBytes, a_tile, off, wave, min(kRowBytes, last));
-  stage_b(b_slots + kSlotBytes, b_lo, b_hi, off, wave, min(kRowBytes, last));
-  stage_b(b_slots + 2 * kSlotBytes, b_lo, b_hi, off, wave, min(2 * kRowBytes, last));
-  wait_loads_and_barrier<NA + 2 * kDmaA>();  // tile 0 landed
+#pragma unroll
+  for (int t = 0; t < kMaxStages; ++t) {
+    if (t < kAStages) stage_a<NA>(a_slots + t * kSlotBytes, a_tile, off, wave, min(t * kRowBytes, last));
+    if (t < kBStages) stage_b(b_slots + t * kSlotBytes, b_lo, b_hi, off, wave, min(t * kRowBytes, last));
+  }
+  wait_loads_and_barrier<kVmPrologue>();  // tile 0 landed
   Frags f0, f1;
   load_frags<NFA>(a_slots, b_slots, 0, a_row0, b_row, xa, xb, f0);
   for (int kt = 0; kt < nk; ++kt) {
-    uint8_t* sa = a_slots + (kt & 1) * kSlotBytes;
+    uint8_t* sa = a_slots + (kt % kAStages) * kSlotBytes;
     uint8_t* sb = b_slots + (kt % kBStages) * kSlotBytes;
-    const uint8_t* na = a_slots + ((kt + 1) & 1) * kSlotBytes;
+    const uint8_t* na = a_slots + ((kt + 1) % kAStages) * kSlotBytes;
     const uint8_t* nb = b_slots + ((kt + 1) % kBStages) * kSlotBytes;
     load_frags<NFA>(sa, sb, 1, a_row0, b_row, xa, xb, f1);
     mma_step<NFA>(f0, acc);
@@ -383,12 +429,12 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
     load_frags<NFA>(sa, sb, 3, a_row0, b_row, xa, xb, f1);
     mma_step<NFA>(f0, acc);
     pin_kstep_schedule<kMfma, kReads, 0>();
-    wait_loads_and_barrier<kDmaA>();  // tile kt+1 landed; tile kt's slots free
+    wait_loads_and_barrier<kVmBarrier>();  // tile kt+1 landed; tile kt's slots free
     load_frags<NFA>(na, nb, 0, a_row0, b_row, xa, xb, f0);
-    stage_a<NA>(sa, a_tile, off, wave, min((kt + 2) * kRowBytes, last));
-    stage_b(sb, b_lo, b_hi, off, wave, min((kt + 3) * kRowBytes, last));
+    stage_a<NA>(sa, a_tile, off, wave, min((kt + kAStages) * kRowBytes, last));
+    stage_b(sb, b_lo, b_hi, off, wave, min((kt + kBStages) * kRowBytes, last));
     mma_step<NFA>(f1, acc);
-    pin_kstep_schedule<kMfma, kReads, NA + kDmaA>();
+    pin_kstep_schedule<kMfma, kReads, NA + kDmaB>();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -406,17 +452,21 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       if (EPI == EPI_SILU_GLU) {
-        const int n = n0 + wn * 32 + g * 8 + col_l;
-        if (n < N) {
-          float v[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = silu_f(acc[i][0][4 * g + q]) * acc[i][1][4 * g + q];
-          store_bf16x4(crow + n, v);
+        for (int j = 0; j < kBF / 2; ++j) {
+          const int n = n0 + wn * kWaveCols + j * 32 + g * 8 + col_l;
+          if (n < N) {
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              v[q] = silu_f(acc[i][j][4 * g + q]) * acc[i][j + kBF / 2][4 * g + q];
+            store_bf16x4(crow + n, v);
+          }
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = n0 + wn * 64 + j * 32 + g * 8 + col_l;
+        for (int j = 0; j < kBF; ++j) {
+          const int n = n0 + wn * kWaveCols + j * 32 + g * 8 + col_l;
           if (n < N) {
             float v[4];
 #pragma unroll
@@ -543,11 +593,10 @@ struct GemmArgs {
   int N; int Kdim; int batch;
 };
 
-// Workgroups for an upper bound of row tiles: a multiple of 8, with room for
-// the uneven split of the last band over the XCDs.
+// Workgroups for an upper bound of row tiles: 8 XCDs x the most tiles one
+// XCD can get.
 inline int grid_for(int row_tiles, int col_tiles) {
-  const int g = row_tiles * col_tiles;
-  return (g + 7) / 8 * 8 + 8;
+  return 8 * tiles_per_xcd_bound(row_tiles, col_tiles);
 }
 
 template <int EPI>
