@@ -126,9 +126,19 @@ def cpu_baseline(cfg, inp, target_s: float) -> dict:
         if dt >= target_s * 0.5 or n >= cfg.num_tokens:
             break
         n = min(cfg.num_tokens, max(n * 2, int(n * target_s / max(dt, 1e-3))))
-    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of the {cfg.num_tokens} tokens of the same workload, whole "
-                      f"layer (route, dispatch, expert MLP, combine) in fp64, {dt:.1f} s"}
+    reps = 1
+    if dt < target_s * 0.5:
+        # The whole workload is quick: repeat it until the target CPU time.
+        reps = max(2, int(target_s / max(dt, 1e-4)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.forward(sub, sub_inp)
+        dt = time.perf_counter() - t0
+    what = f"first {n} of the {cfg.num_tokens} tokens" if n < cfg.num_tokens else \
+        f"all {n} tokens" + (f", {reps} times" if reps > 1 else "")
+    return {"value": n * reps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{what} of the same workload, whole layer (route, dispatch, expert MLP, "
+                      f"combine) in fp64, {dt:.1f} s"}
 
 
 def write_traffic_record(d: str, out_path: str = TRAFFIC_FILE) -> dict:
