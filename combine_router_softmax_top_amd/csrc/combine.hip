@@ -9,8 +9,9 @@
 // One wave per token, four tokens per workgroup.  The row maps and weights of
 // the token are read into lanes 0..K-1 and broadcast with readlane (scalar
 // registers).  Each lane owns 16-byte pieces of the output row; for each piece
-// it issues the K gathers, accumulates w_k * y in fp32 in ascending k, adds
-// the shared-expert rows, and rounds once.
+// it issues the gathers of up to 8 expert rows at once (so many rows are in
+// flight per wave), accumulates w_k * y in fp32 in ascending k, adds the
+// shared-expert rows, and rounds once.
 #include "moe_internal.h"
 
 namespace moe {
@@ -50,9 +51,33 @@ struct Vec<float> {  // fp32: 4 per 16 bytes
   }
 };
 
-constexpr int kPieces = 2;  // 16-byte pieces per lane per iteration
+// Accumulates w_j * y[rows[j]] for the NB slots of one batch, in slot order,
+// into acc.
+// rows[j] < 0 marks an empty slot: its load reads the valid row `dummy` and
+// the value is discarded by a select (never multiplied by 0, which could turn
+// a non-finite dummy into NaN).  All loads are issued before the first use.
+template <typename T, int NB>
+__device__ __forceinline__ void gather_batch(const u32x4* __restrict__ base, long long row_stride,
+                                             int v, const int (&rows)[NB], const float (&w)[NB],
+                                             int dummy, float (&acc)[Vec<T>::N]) {
+  constexpr int N = Vec<T>::N;
+  u32x4 buf[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j)
+    buf[j] = base[(long long)(rows[j] >= 0 ? rows[j] : dummy) * row_stride + v];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    float f[N];
+    Vec<T>::load(buf[j], f);
+    const bool ok = rows[j] >= 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = ok ? fmaf(w[j], f[i], acc[i]) : acc[i];
+  }
+}
 
-template <typename T>
+// KB = routed rows gathered per batch (2, 4 or 8: the smallest that holds
+// min(K, 8)); the shared-expert rows (at most 4) form one batch of their own.
+template <typename T, int KB>
 __global__ __launch_bounds__(256) void combine_kernel(
     const u32x4* __restrict__ y_sorted, const int32_t* __restrict__ row_of,
     const float* __restrict__ weights, const u32x4* __restrict__ y_shared, int num_tokens, int K,
@@ -67,67 +92,74 @@ __global__ __launch_bounds__(256) void combine_kernel(
     myrow = row_of[(size_t)t * K + lane];
     myw = weights[(size_t)t * K + lane];
   }
-  for (int v0 = 0; v0 < row_vecs; v0 += kWave * kPieces) {
-    float acc[kPieces][N];
+  // A valid row for the loads of empty slots: the token's first local row,
+  // or (no local row at all) row 0 of the buffer, whose values are unused.
+  const unsigned long long has = __ballot(myrow >= 0);
+  const int dummy = has ? __shfl(myrow, __builtin_ctzll(has), 64) : 0;
+  for (int v0 = 0; v0 < row_vecs; v0 += kWave) {
+    const int v = min(v0 + lane, row_vecs - 1);  // lanes past the row re-read its end
+    float acc[N];
 #pragma unroll
-    for (int p = 0; p < kPieces; ++p)
+    for (int i = 0; i < N; ++i) acc[i] = 0.f;
+    for (int k0 = 0; has && k0 < K; k0 += KB) {
+      int rows[KB];
+      float w[KB];
 #pragma unroll
-      for (int i = 0; i < N; ++i) acc[p][i] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      const int rk = __builtin_amdgcn_readlane(myrow, k);
-      if (rk < 0) continue;
-      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myw), k));
-      const u32x4* src = y_sorted + (size_t)rk * row_vecs;
-#pragma unroll
-      for (int p = 0; p < kPieces; ++p) {
-        const int v = v0 + p * kWave + lane;
-        if (v < row_vecs) {
-          float f[N];
-          Vec<T>::load(src[v], f);
-#pragma unroll
-          for (int i = 0; i < N; ++i) acc[p][i] = fmaf(wk, f[i], acc[p][i]);
-        }
+      for (int j = 0; j < KB; ++j) {  // lanes >= K hold row -1
+        rows[j] = __builtin_amdgcn_readlane(myrow, k0 + j);
+        w[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myw), k0 + j));
       }
+      gather_batch<T, KB>(y_sorted, row_vecs, v, rows, w, dummy, acc);
     }
-    for (int s = 0; s < n_shared; ++s) {
-      const u32x4* src = y_shared + ((size_t)s * num_tokens + t) * row_vecs;
+    if (n_shared > 0) {
+      constexpr int SB = MOE_MAX_SHARED;
+      int rows[SB];
+      float w[SB];
 #pragma unroll
-      for (int p = 0; p < kPieces; ++p) {
-        const int v = v0 + p * kWave + lane;
-        if (v < row_vecs) {
-          float f[N];
-          Vec<T>::load(src[v], f);
-#pragma unroll
-          for (int i = 0; i < N; ++i) acc[p][i] += f[i];
-        }
+      for (int j = 0; j < SB; ++j) {
+        rows[j] = j < n_shared ? j * num_tokens + t : -1;
+        w[j] = 1.f;
       }
+      // Unit weights: fmaf(1, y, acc) == acc + y exactly.
+      gather_batch<T, SB>(y_shared, row_vecs, v, rows, w, t, acc);
     }
-#pragma unroll
-    for (int p = 0; p < kPieces; ++p) {
-      const int v = v0 + p * kWave + lane;
-      if (v < row_vecs) out[(size_t)t * row_vecs + v] = Vec<T>::store(acc[p]);
-    }
+    if (v0 + lane < row_vecs) out[(size_t)t * row_vecs + v] = Vec<T>::store(acc);
   }
 }
 
 }  // namespace
 
+template <typename T, int KB>
+static void launch_kb(const moe_config_t& c, const void* y_sorted, const int32_t* row_of,
+                      const float* weights, const void* y_shared, int n_sh, int row_vecs,
+                      void* out, hipStream_t s) {
+  hipLaunchKernelGGL((combine_kernel<T, KB>), dim3(ceil_div(c.num_tokens, 4)), dim3(256), 0, s,
+                     static_cast<const u32x4*>(y_sorted), row_of, weights,
+                     static_cast<const u32x4*>(y_shared), c.num_tokens, c.top_k, n_sh, row_vecs,
+                     static_cast<u32x4*>(out));
+}
+
+template <typename T>
+static void launch_t(const moe_config_t& c, const void* y_sorted, const int32_t* row_of,
+                     const float* weights, const void* y_shared, int n_sh, int row_vecs, void* out,
+                     hipStream_t s) {
+  if (c.top_k <= 2)
+    launch_kb<T, 2>(c, y_sorted, row_of, weights, y_shared, n_sh, row_vecs, out, s);
+  else if (c.top_k <= 4)
+    launch_kb<T, 4>(c, y_sorted, row_of, weights, y_shared, n_sh, row_vecs, out, s);
+  else
+    launch_kb<T, 8>(c, y_sorted, row_of, weights, y_shared, n_sh, row_vecs, out, s);
+}
+
 hipError_t launch_combine(const moe_config_t& c, const void* y_sorted, const int32_t* row_of,
                           const float* weights, const void* y_shared, void* out, hipStream_t s) {
   const int elem = c.dtype == MOE_BF16 ? 2 : 4;
   const int row_vecs = c.hidden * elem / 16;
-  const dim3 grid(ceil_div(c.num_tokens, 4)), block(256);
   const int n_sh = y_shared ? c.num_shared : 0;
   if (c.dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, block, 0, s,
-                       static_cast<const u32x4*>(y_sorted), row_of, weights,
-                       static_cast<const u32x4*>(y_shared), c.num_tokens, c.top_k, n_sh, row_vecs,
-                       static_cast<u32x4*>(out));
+    launch_t<uint16_t>(c, y_sorted, row_of, weights, y_shared, n_sh, row_vecs, out, s);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, grid, block, 0, s,
-                       static_cast<const u32x4*>(y_sorted), row_of, weights,
-                       static_cast<const u32x4*>(y_shared), c.num_tokens, c.top_k, n_sh, row_vecs,
-                       static_cast<u32x4*>(out));
+    launch_t<float>(c, y_sorted, row_of, weights, y_shared, n_sh, row_vecs, out, s);
   return hipGetLastError();
 }
 
