@@ -124,26 +124,25 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
   const int kgrp = lane >> 4;
   const uint16_t* ap = x + (size_t)min(t0 + (lane & 15), T - 1) * d + k0 + kgrp * 8;
 
-  // staging chunk q = tid + 256 i: router row q/8, 16-byte chunk q%8
+  // staging chunk q = tid + 256 i: router row q/8, 16-byte chunk q%8.  When
+  // the stage has fewer than 256 chunks, the surplus threads copy an existing
+  // chunk again (same bytes to the same place), which keeps the body free of
+  // branches.
   const uint16_t* src[kPer];
   int dst[kPer];
-  bool live[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int q = tid + 256 * i;
-    live[i] = q < NE * 8;
-    const int row = (q >> 3) % NE, c = q & 7;
+    const int q = (tid + 256 * i) % (NE * 8);
+    const int row = q >> 3, c = q & 7;
     const int e = min(e0 + row, E - 1);
     src[i] = wr + (size_t)e * d + k0 + c * 8;
     dst[i] = row * 128 + ((c ^ rsw(row)) << 4);
   }
   u32x4 stg[kPer];
 #pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    if (live[i]) stg[i] = *reinterpret_cast<const u32x4*>(src[i]);
+  for (int i = 0; i < kPer; ++i) stg[i] = *reinterpret_cast<const u32x4*>(src[i]);
 #pragma unroll
-  for (int i = 0; i < kPer; ++i)
-    if (live[i]) *reinterpret_cast<u32x4*>(wt + dst[i]) = stg[i];
+  for (int i = 0; i < kPer; ++i) *reinterpret_cast<u32x4*>(wt + dst[i]) = stg[i];
   __syncthreads();
 
   f32x4 acc[NT];
@@ -156,32 +155,49 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
 #pragma unroll
     for (int s = 0; s < 2; ++s) boff[j][s] = row * 128 + (((s * 4 + kgrp) ^ rsw(row)) << 4);
   }
+  // Token fragments come straight from global memory (HBM) two chunks ahead,
+  // issued after the next chunk's router-row loads: loads complete in issue
+  // order, so the wait for those rows (before they are written to LDS) leaves
+  // the newest token loads in flight.  The barrier waits for LDS only (a
+  // __syncthreads would also drain the prefetches).
   const int nkc = k_slice / kRtKc;
-  for (int kc = 0; kc < nkc; ++kc) {
+  // One chunk: stage the next chunk's router rows, prefetch the token
+  // fragments of chunk kc+2 into `aload`, multiply chunk kc (`ause`).  The
+  // loop below rotates three fragment buffers by renaming (unrolled by 3), so
+  // no copy ever waits on an in-flight prefetch.
+  auto chunk = [&](int kc, const bf16x8(&ause)[2], bf16x8(&aload)[2]) {
     const uint8_t* cur = wt + (kc & 1) * kStage;
     uint8_t* nxt = wt + ((kc + 1) & 1) * kStage;
-    const bool more = kc + 1 < nkc;
-    if (more) {
+    // past the last chunk the last rows are staged again into the free slot
+    const int kn = min(kc + 1, nkc - 1) * kRtKc;
 #pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (live[i]) stg[i] = *reinterpret_cast<const u32x4*>(src[i] + (kc + 1) * kRtKc);
-    }
-    bf16x8 a[2];
+    for (int i = 0; i < kPer; ++i) stg[i] = *reinterpret_cast<const u32x4*>(src[i] + kn);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) a[s] = *reinterpret_cast<const bf16x8*>(ap + kc * kRtKc + s * 32);
+    for (int s = 0; s < 2; ++s)
+      aload[s] = *reinterpret_cast<const bf16x8*>(ap + min(kc + 2, nkc - 1) * kRtKc + s * 32);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         const bf16x8 b = *reinterpret_cast<const bf16x8*>(cur + boff[j][s]);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], b, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ause[s], b, acc[j], 0, 0, 0);
       }
-    if (more) {
 #pragma unroll
-      for (int i = 0; i < kPer; ++i)
-        if (live[i]) *reinterpret_cast<u32x4*>(nxt + dst[i]) = stg[i];
-    }
-    __syncthreads();
+    for (int i = 0; i < kPer; ++i) *reinterpret_cast<u32x4*>(nxt + dst[i]) = stg[i];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  bf16x8 a0[2], a1[2], a2[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    a0[s] = *reinterpret_cast<const bf16x8*>(ap + s * 32);
+    a1[s] = *reinterpret_cast<const bf16x8*>(ap + min(1, nkc - 1) * kRtKc + s * 32);
+  }
+  for (int kc = 0; kc < nkc; kc += 3) {
+    chunk(kc, a0, a2);
+    if (kc + 1 < nkc) chunk(kc + 1, a1, a0);
+    if (kc + 2 < nkc) chunk(kc + 2, a2, a1);
   }
   // lane holds tokens (lane/16)*4 + i, expert lane%16 of each 16-wide block;
   // experts past E hold partial sums of a clamped row and are never read.
