@@ -60,21 +60,16 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
   return v;
 }
 
-// Row tiles of group j (lane-parallel over groups; lanes past n_groups give
-// 0): `full` tiles computed at full height (BM rows, including a last tile of
-// more than BM/2 rows) and `half` (0 or 1) for a last tile of at most BM/2
-// rows, which runs at half height.
-__device__ __forceinline__ void group_row_tiles(const int32_t* __restrict__ offsets, int n_groups,
-                                                int j, int BM, int& a, int& full, int& half) {
-  a = 0;
-  full = half = 0;
-  if (j >= n_groups) return;
-  a = offsets[j];
-  const int rows = offsets[j + 1] - a;
+// Row tiles of a group of `rows` rows: `full` tiles computed at full height
+// (BM rows, including a last tile of more than BM/2 rows) and `half` (0 or 1)
+// for a last tile of at most BM/2 rows, which runs at half height.
+__device__ __forceinline__ void group_row_tiles(int rows, int BM, int& full, int& half) {
   const int rem = rows % BM;
   full = rows / BM + (rem > BM / 2 ? 1 : 0);
   half = (rem > 0 && rem <= BM / 2) ? 1 : 0;
 }
+
+constexpr int kMaxGroupChunks = MOE_MAX_EXPERTS / 64;  // groups per lane, at most
 
 constexpr int kBandRows = 16;  // row tiles per band
 
@@ -106,18 +101,29 @@ __host__ __device__ inline int tiles_per_xcd_bound(int row_tiles, int nN) {
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int n_groups,
                                           int fixed_rows, int BM, int nN, Tile& out) {
   const int lane = threadIdx.x & 63;
+  // The offsets are read once, all at once: lane l holds group c*64 + l.
+  int g0[kMaxGroupChunks], g1[kMaxGroupChunks];
   int n_full = 0, n_half = 0;
   if (offsets != nullptr) {
-    for (int base = 0; base < n_groups; base += 64) {
-      int a, f, h;
-      group_row_tiles(offsets, n_groups, base + lane, BM, a, f, h);
+#pragma unroll
+    for (int c = 0; c < kMaxGroupChunks; ++c) {
+      const int j = c * 64 + lane;
+      g0[c] = g1[c] = 0;
+      if (c * 64 < n_groups && j < n_groups) {
+        g0[c] = offsets[j];
+        g1[c] = offsets[j + 1];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxGroupChunks; ++c) {
+      if (c * 64 >= n_groups) break;
+      int f, h;
+      group_row_tiles(g1[c] - g0[c], BM, f, h);
       n_full += __shfl(wave_inclusive_sum(f), 63, 64);
       n_half += __shfl(wave_inclusive_sum(h), 63, 64);
     }
   } else {
-    const int rem = fixed_rows % BM;
-    n_full = fixed_rows / BM + (rem > BM / 2 ? 1 : 0);
-    n_half = (rem > 0 && rem <= BM / 2) ? 1 : 0;
+    group_row_tiles(fixed_rows, BM, n_full, n_half);
   }
   const int n_rt = n_full + n_half;
   const int xcd = blockIdx.x & 7;
@@ -142,29 +148,31 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
   }
   const int n_tile = c0 + slot / nr;
   int rt = band * kBandRows + r0 + slot % nr;  // index in the row-tile list
-  int row0 = 0, rows = fixed_rows, group = 0, m_tile;
-  if (offsets == nullptr) {
-    m_tile = rt;
-  } else {
+  int row0 = 0, rows = fixed_rows, group = 0, m_tile = rt;
+  if (offsets != nullptr) {
     // Full-height tiles: the rt-th in group order; half-height: the
     // (rt - n_full)-th group that has one, which is its last row tile.
     const bool is_half = rt >= n_full;
     if (is_half) rt -= n_full;
-    for (int base = 0;; base += 64) {
-      int a, f, h;
-      group_row_tiles(offsets, n_groups, base + lane, BM, a, f, h);
+    bool found = false;
+#pragma unroll
+    for (int c = 0; c < kMaxGroupChunks; ++c) {
+      if (found || c * 64 >= n_groups) break;
+      int f, h;
+      group_row_tiles(g1[c] - g0[c], BM, f, h);
       const int cnt = is_half ? h : f;
       const int incl = wave_inclusive_sum(cnt);
       const int chunk = __shfl(incl, 63, 64);
       if (rt < chunk) {
         const int L = __builtin_ctzll(__ballot(incl > rt));
-        row0 = __shfl(a, L, 64);
-        group = base + L;
-        rows = offsets[group + 1] - row0;
+        row0 = __shfl(g0[c], L, 64);
+        rows = __shfl(g1[c], L, 64) - row0;
+        group = c * 64 + L;
         m_tile = is_half ? __shfl(f, L, 64) : rt - __shfl(incl - cnt, L, 64);
-        break;
+        found = true;
+      } else {
+        rt -= chunk;
       }
-      rt -= chunk;
     }
   }
   out.row0 = row0;
