@@ -25,6 +25,12 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wno-unused-command-line-argument"]
 
 
+# Per-source extra flags.  route.hip: keep MFMA accumulators in VGPRs.  Its
+# logits kernel runs one wave per SIMD; with the accumulators in AGPRs the
+# compiler copied them between the two register files every k-chunk.
+EXTRA_FLAGS = {"route.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def library_path() -> str:
     return os.path.join(_HERE, "libmoe.so")
 
@@ -35,7 +41,8 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(_BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, "-x", "hip", *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, "-x", "hip", *CFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src,
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -8,8 +8,9 @@
 // go to the lower expert id; slots come out in descending order.
 //
 // bf16: a logits GEMM (16x16x32 bf16 MFMA, fp32 accumulation) over tiles of
-// 64 tokens x up to 256 experts x one slice of the reduction dimension, then
-// a selection kernel that adds the slices in a fixed order (deterministic).
+// 64 tokens x up to 256 experts x one slice of the reduction dimension, its
+// operands streamed into LDS four chunks ahead, then a selection kernel that
+// adds the slices in a fixed order (deterministic).
 // fp32: each wave takes 4 tokens and reduces every dot product across its 64
 // lanes with a butterfly.
 // Selection: one wave per token, E/64 candidates per lane in registers, K
@@ -95,120 +96,189 @@ __device__ __forceinline__ void select_topk(float (&v)[NV], int E, int K, int sc
 // ---- bf16: logits GEMM with a fixed k-split, then selection ----
 //
 // route_logits_kernel<NT>: workgroup = 64 tokens x NT*16 experts x one slice
-// of the reduction dimension.  Each of its 4 waves owns 16 tokens and all
-// NT*16 experts (NT blocks of 16x16x32 MFMA).  Router rows are staged in
-// 64-wide k-chunks through LDS (double-buffered, shared by the 4 waves);
-// token fragments come straight from global memory.  Partial logits of slice
-// s go to part[s][t][e] (fp32) and the select kernel adds the slices in
-// ascending s.  The number of slices depends only on d and E, never on the
-// token count, so a token's logits do not depend on how the batch is split.
-constexpr int kRtTok = 64, kRtKc = 64;
+// of the reduction dimension, 4 waves.  With NT >= 4 each wave owns all 64
+// tokens and a quarter of the experts; with fewer expert blocks each wave
+// owns 16 tokens and all the experts.  Token rows and router rows move in
+// 64-deep chunks straight from global memory into LDS (global_load_lds) in a
+// ring of 4 slots: right after the barrier that ends the reads of chunk c its
+// slot takes chunk c+4, so each load has three chunks of MFMA work to land.
+// 16x16x32 bf16 MFMAs, fp32 accumulation.  Partial logits of slice s go to
+// part[s][t][e] (fp32); the select kernel adds the slices in ascending s.
+// The number of slices depends only on d and E, never on the token count, so
+// a token's logits do not depend on how the batch is split.
+constexpr int kRtTok = 64, kRtKc = 64, kRtStages = 4;
 
 // LDS rows of 128 B (64 bf16): logical 16-byte chunk c of row r sits in slot
 // c ^ rsw(r); 16 lanes reading rows r..r+15 at one logical chunk then touch
 // distinct slots in every 256-byte window (no bank conflicts).
 __device__ __forceinline__ int rsw(int r) { return (r ^ (r >> 3)) & 7; }
 
-template <int NT>
-__global__ __launch_bounds__(256) void route_logits_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E,
-    int e_pad, int k_slice, float* __restrict__ part) {
-  constexpr int NE = NT * 16;
-  constexpr int kStage = NE * 128;
-  constexpr int kPer = (NE * 8 + 255) / 256;  // 16-byte staging chunks per thread
-  __shared__ __attribute__((aligned(16))) uint8_t wt[2 * kStage];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int t0 = blockIdx.x * kRtTok + wave * 16;
-  const int e0 = blockIdx.y * NE;
-  const int k0 = blockIdx.z * k_slice;
-  const int kgrp = lane >> 4;
-  const uint16_t* ap = x + (size_t)min(t0 + (lane & 15), T - 1) * d + k0 + kgrp * 8;
+typedef __attribute__((address_space(3))) void* rt_lds_ptr_t;
 
-  // staging chunk q = tid + 256 i: router row q/8, 16-byte chunk q%8.  When
-  // the stage has fewer than 256 chunks, the surplus threads copy an existing
-  // chunk again (same bytes to the same place), which keeps the body free of
-  // branches.
-  const uint16_t* src[kPer];
-  int dst[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int q = (tid + 256 * i) % (NE * 8);
-    const int row = q >> 3, c = q & 7;
-    const int e = min(e0 + row, E - 1);
-    src[i] = wr + (size_t)e * d + k0 + c * 8;
-    dst[i] = row * 128 + ((c ^ rsw(row)) << 4);
-  }
-  u32x4 stg[kPer];
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) stg[i] = *reinterpret_cast<const u32x4*>(src[i]);
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) *reinterpret_cast<u32x4*>(wt + dst[i]) = stg[i];
-  __syncthreads();
-
-  f32x4 acc[NT];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int boff[NT][2];
-#pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int row = j * 16 + (lane & 15);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) boff[j][s] = row * 128 + (((s * 4 + kgrp) ^ rsw(row)) << 4);
-  }
-  // Token fragments come straight from global memory (HBM) two chunks ahead,
-  // issued after the next chunk's router-row loads: loads complete in issue
-  // order, so the wait for those rows (before they are written to LDS) leaves
-  // the newest token loads in flight.  The barrier waits for LDS only (a
-  // __syncthreads would also drain the prefetches).
-  const int nkc = k_slice / kRtKc;
-  // One chunk: stage the next chunk's router rows, prefetch the token
-  // fragments of chunk kc+2 into `aload`, multiply chunk kc (`ause`).  The
-  // loop below rotates three fragment buffers by renaming (unrolled by 3), so
-  // no copy ever waits on an in-flight prefetch.
-  auto chunk = [&](int kc, const bf16x8(&ause)[2], bf16x8(&aload)[2]) {
-    const uint8_t* cur = wt + (kc & 1) * kStage;
-    uint8_t* nxt = wt + ((kc + 1) & 1) * kStage;
-    // past the last chunk the last rows are staged again into the free slot
-    const int kn = min(kc + 1, nkc - 1) * kRtKc;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) stg[i] = *reinterpret_cast<const u32x4*>(src[i] + kn);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      aload[s] = *reinterpret_cast<const bf16x8*>(ap + min(kc + 2, nkc - 1) * kRtKc + s * 32);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(cur + boff[j][s]);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ause[s], b, acc[j], 0, 0, 0);
-      }
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) *reinterpret_cast<u32x4*>(nxt + dst[i]) = stg[i];
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-  bf16x8 a0[2], a1[2], a2[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    a0[s] = *reinterpret_cast<const bf16x8*>(ap + s * 32);
-    a1[s] = *reinterpret_cast<const bf16x8*>(ap + min(1, nkc - 1) * kRtKc + s * 32);
-  }
-  for (int kc = 0; kc < nkc; kc += 3) {
-    chunk(kc, a0, a2);
-    if (kc + 1 < nkc) chunk(kc + 1, a1, a0);
-    if (kc + 2 < nkc) chunk(kc + 2, a2, a1);
-  }
-  // lane holds tokens (lane/16)*4 + i, expert lane%16 of each 16-wide block;
-  // experts past E hold partial sums of a clamped row and are never read.
-  float* out = part + (size_t)blockIdx.z * T * e_pad;
-#pragma unroll
-  for (int j = 0; j < NT; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + (lane >> 4) * 4 + i;
-      if (t < T) out[(size_t)t * e_pad + e0 + j * 16 + (lane & 15)] = acc[j][i];
+// Router-tile schedule of one 32-deep k-step: NM MFMAs, the ND fragment
+// reads of the next k-step two after each of the first MFMAs, and NV
+// global->LDS loads spread over the rest.
+template <int NM, int ND, int NV, int I = 0>
+__device__ __forceinline__ void rt_pin_schedule() {
+  constexpr int kWithReads = (ND + 1) / 2;
+  if constexpr (NM < kWithReads + 1) {
+    __builtin_amdgcn_sched_barrier(0);
+  } else if constexpr (I == NM) {
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    constexpr int kRest = NM - kWithReads;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (I < kWithReads) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * I + 2 <= ND ? 2 : 1, 0);  // DS read
+    } else if constexpr (NV > 0) {
+      constexpr int j = I - kWithReads;
+      constexpr int n = NV * (j + 1) / kRest - NV * j / kRest;
+      if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x020, n, 0);  // VMEM
     }
+    rt_pin_schedule<NM, ND, NV, I + 1>();
+  }
+}
+
+template <int VM>
+__device__ __forceinline__ void rt_wait_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(VM) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup -> (token tile, expert tile, slice): workgroup ids go round-robin
+// over the 8 XCDs; XCD x works on slice x % ks only (ks divides 8), so its L2
+// holds one slice of the router matrix while the token rows stream through.
+template <int NT>
+__global__ __launch_bounds__(256, 1) void route_logits_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int d, int E,
+    int e_pad, int k_slice, int ks, int n_tok_tiles, float* __restrict__ part) {
+  constexpr int NE = NT * 16;
+  constexpr int kBRows = NE < 32 ? 32 : NE;          // staged router rows (>= one load per wave)
+  constexpr int kSlotA = kRtTok * 128;                 // 8 KB
+  constexpr int kSlotB = kBRows * 128;
+  constexpr int kStage = kSlotA + kSlotB;
+  constexpr int NA = kSlotA / 1024 / 4;                // 2 loads per wave
+  constexpr int NB = kSlotB / 1024 / 4;                // 1..8 loads per wave
+  constexpr int AF = NT >= 4 ? 4 : 1;                  // token fragments per wave
+  constexpr int BF = NT >= 4 ? NT / 4 : NT;            // expert fragments per wave
+  constexpr int kLoads = NA + NB;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kRtStages * kStage];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int xcd = blockIdx.x & 7, per = 8 / ks;
+  const int z = xcd % ks;
+  const int pair = xcd / ks + per * (blockIdx.x >> 3);  // (token tile, expert tile)
+  const int n_exp_tiles = e_pad / NE;
+  if (pair >= n_tok_tiles * n_exp_tiles) return;
+  const int t0 = (pair % n_tok_tiles) * kRtTok;
+  const int e0 = (pair / n_tok_tiles) * NE;
+  const int k0 = z * k_slice;
+  const int tok0 = NT >= 4 ? 0 : wave * 16;
+  const int exp0 = NT >= 4 ? wave * BF * 16 : 0;
+
+  // Load j of wave w fills rows (4j + w)*8 .. +8 of a slot; lane l covers row
+  // +l/8, physical chunk l%8, whose source is logical chunk (l%8) ^ rsw(row).
+  // Rows past the last token / expert repeat it.
+  const uint8_t* xa = reinterpret_cast<const uint8_t*>(x + (size_t)t0 * d + k0);
+  const uint8_t* wb = reinterpret_cast<const uint8_t*>(wr + (size_t)e0 * d + k0);
+  uint32_t offa[NA], offb[NB];
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    const int r = (j * 4 + wave) * 8 + lane / 8;
+    offa[j] = (uint32_t)(min(r, T - 1 - t0) * d * 2 + (((lane & 7) ^ rsw(r)) << 4));
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int r = (j * 4 + wave) * 8 + lane / 8;
+    offb[j] = (uint32_t)(min(r, E - 1 - e0) * d * 2 + (((lane & 7) ^ rsw(r)) << 4));
+  }
+  auto stage = [&](int slot, int kbytes) {
+    uint8_t* sa = lds + slot * kStage;
+    uint8_t* sb = sa + kSlotA;
+    const uint8_t* xs = xa + kbytes;  // uniform base, per-lane 32-bit offsets
+    const uint8_t* ws = wb + kbytes;
+#pragma unroll
+    for (int j = 0; j < NA; ++j)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(xs + offa[j]),
+                                       (rt_lds_ptr_t)(sa + (j * 4 + wave) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(ws + offb[j]),
+                                       (rt_lds_ptr_t)(sb + (j * 4 + wave) * 1024), 16, 0, 0);
+  };
+
+  // Fragments of 32-deep k-step ks (0, 1) of a chunk: lane l reads row
+  // base + l%16 at logical chunk 4 ks + l/16.
+  // Per-lane byte offsets of the fragments in a slot for k-step 0; k-step 1
+  // reads logical chunk +4, i.e. the offset ^ 64 (the chunk's bit 2).
+  const int kg = lane >> 4;
+  int fa[AF], fb[BF];
+#pragma unroll
+  for (int i = 0; i < AF; ++i) {
+    const int r = tok0 + i * 16 + (lane & 15);
+    fa[i] = r * 128 + ((kg ^ rsw(r)) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < BF; ++j) {
+    const int r = exp0 + j * 16 + (lane & 15);
+    fb[j] = kSlotA + r * 128 + ((kg ^ rsw(r)) << 4);
+  }
+  struct RFrags {
+    bf16x8 a[AF], b[BF];
+  };
+  auto frags = [&](int slot, int ks, RFrags& f) {
+    const uint8_t* st = lds + slot * kStage;
+    const int x = ks * 64;
+#pragma unroll
+    for (int i = 0; i < AF; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(st + (fa[i] ^ x));
+#pragma unroll
+    for (int j = 0; j < BF; ++j) f.b[j] = *reinterpret_cast<const bf16x8*>(st + (fb[j] ^ x));
+  };
+  f32x4 acc[AF][BF];
+#pragma unroll
+  for (int i = 0; i < AF; ++i)
+#pragma unroll
+    for (int j = 0; j < BF; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const RFrags& f) {
+#pragma unroll
+    for (int i = 0; i < AF; ++i)
+#pragma unroll
+      for (int j = 0; j < BF; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  };
+
+  const int nkc = k_slice / kRtKc;
+  const int last = (nkc - 1) * kRtKc * 2;
+#pragma unroll
+  for (int t = 0; t < kRtStages; ++t) stage(t, min(t * kRtKc * 2, last));
+  rt_wait_and_barrier<(kRtStages - 1) * kLoads>();  // chunk 0 landed
+  RFrags f0, f1;
+  frags(0, 0, f0);
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int slot = kc % kRtStages;
+    frags(slot, 1, f1);
+    mma(f0);
+    rt_pin_schedule<AF * BF, AF + BF, 0>();
+    rt_wait_and_barrier<(kRtStages - 2) * kLoads>();  // chunk kc+1 landed; slot free
+    frags((kc + 1) % kRtStages, 0, f0);
+    stage(slot, min((kc + kRtStages) * kRtKc * 2, last));
+    mma(f1);
+    rt_pin_schedule<AF * BF, AF + BF, kLoads>();
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // lane holds tokens (lane/16)*4 + r and expert lane%16 of each 16 x 16
+  // block; experts past E hold sums of a repeated row and are never read.
+  float* out = part + (size_t)z * T * e_pad;
+#pragma unroll
+  for (int i = 0; i < AF; ++i)
+#pragma unroll
+    for (int j = 0; j < BF; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + tok0 + i * 16 + (lane >> 4) * 4 + r;
+        if (t < T) out[(size_t)t * e_pad + e0 + exp0 + j * 16 + (lane & 15)] = acc[i][j][r];
+      }
 }
 
 // One wave per token: logits = sum of the k-slice partials (ascending) + bias.
@@ -279,7 +349,8 @@ int route_e_pad(const moe_config_t& c) {
 // Slices of the reduction dimension: a function of d and E only (never of
 // the token count, so splitting a batch does not change any token's sum
 // order).  At most d / (4 E_pad) slices, so the fp32 partials stay a small
-// fraction of the token traffic, and at most 8; slices are 64-multiples.
+// fraction of the token traffic, and at most 8 (a power of two, so it
+// divides the 8 XCDs); slices are 64-multiples.
 int route_k_slices(const moe_config_t& c) {
   const int e_pad = route_e_pad(c);
   int ks = 1;
@@ -303,10 +374,13 @@ hipError_t launch_select(const moe_config_t& c, const float* part, int ks, int e
 template <int NT>
 void launch_logits(const moe_config_t& c, const void* x, const void* wr, int e_pad, int ks,
                    float* part, hipStream_t s) {
-  const dim3 grid(ceil_div(c.num_tokens, kRtTok), e_pad / (NT * 16), ks);
+  const int n_tok = ceil_div(c.num_tokens, kRtTok);
+  const int pairs = n_tok * (e_pad / (NT * 16));
+  const int per = 8 / ks;  // XCDs per slice
+  const dim3 grid(8 * ceil_div(pairs, per));
   hipLaunchKernelGGL(route_logits_kernel<NT>, grid, dim3(256), 0, s,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wr),
-                     c.num_tokens, c.hidden, c.num_experts, e_pad, c.hidden / ks, part);
+                     c.num_tokens, c.hidden, c.num_experts, e_pad, c.hidden / ks, ks, n_tok, part);
 }
 
 hipError_t launch_bf16(const moe_config_t& c, const void* x, const void* wr, const float* bias,
