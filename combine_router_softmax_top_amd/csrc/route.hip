@@ -35,6 +35,46 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Selection keys: (logit, expert) packed so that a larger key is a larger
+// logit, and among equal logits the lower expert id.  The high word is the
+// logit's bit pattern made order-preserving as an unsigned integer (flip all
+// bits of a negative, the sign bit of a non-negative); the low word is ~id.
+__device__ __forceinline__ unsigned long long sel_key(float v, int e) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)o << 32) | (uint32_t)~(uint32_t)e;
+}
+__device__ __forceinline__ float key_value(unsigned long long k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int key_expert(unsigned long long k) { return (int)~(uint32_t)k; }
+
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_max(unsigned long long k) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xf, 0xf, false);
+  const unsigned long long o = ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+  return o > k ? o : k;
+}
+__device__ __forceinline__ unsigned long long xor_max(unsigned long long k, int off) {
+  const int lo = __shfl_xor((int)(uint32_t)k, off);
+  const int hi = __shfl_xor((int)(uint32_t)(k >> 32), off);
+  const unsigned long long o = ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+  return o > k ? o : k;
+}
+
+// Largest key of the wave, in every lane: within each row of 16 lanes by DPP
+// (swap neighbours, swap pairs, rotate by 4, rotate by 8), then across rows.
+__device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k) {
+  k = dpp_max<0xB1>(k);   // quad_perm [1,0,3,2]
+  k = dpp_max<0x4E>(k);   // quad_perm [2,3,0,1]
+  k = dpp_max<0x124>(k);  // row_ror 4
+  k = dpp_max<0x128>(k);  // row_ror 8
+  k = xor_max(k, 16);
+  return xor_max(k, 32);
+}
+
 // v[i] holds the logit of expert lane + 64*i (bias included), -inf past E.
 template <int NV>
 __device__ __forceinline__ void select_topk(float (&v)[NV], int E, int K, int score, int renorm,
@@ -60,24 +100,27 @@ __device__ __forceinline__ void select_topk(float (&v)[NV], int E, int K, int sc
       if (lane + kWave * i < E) s += __expf(v[i] - m);
     denom = wave_sum(s);
   }
+  // Candidate keys; experts past E and already chosen ones hold key 0, below
+  // every real key.
+  unsigned long long kv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int e = lane + kWave * i;
+    kv[i] = e < E ? sel_key(v[i], e) : 0ull;
+  }
   int my_e = 0;
   float my_s = 0.f, sum_sel = 0.f;
   for (int k = 0; k < K; ++k) {
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
+    unsigned long long best = kv[0];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      if (v[i] > bv) { bv = v[i]; be = lane + kWave * i; }
-    }
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oe = __shfl_xor(be, off);
-      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-    }
+    for (int i = 1; i < NV; ++i) best = kv[i] > best ? kv[i] : best;
+    best = wave_max_key(best);
+    const int be = key_expert(best);
+    const float bv = key_value(best);
     if ((be & (kWave - 1)) == lane) {
 #pragma unroll
       for (int i = 0; i < NV; ++i)
-        if (i == (be >> 6)) v[i] = -INFINITY;
+        if (i == (be >> 6)) kv[i] = 0ull;
     }
     const float sc = score == MOE_SCORE_SIGMOID ? 1.f / (1.f + __expf(-bv)) : __expf(bv - m);
     sum_sel += sc;
@@ -93,8 +136,6 @@ __device__ __forceinline__ void select_topk(float (&v)[NV], int E, int K, int sc
   }
 }
 
-// ---- bf16: logits GEMM with a fixed k-split, then selection ----
-//
 // route_logits_kernel<NT>: workgroup = 64 tokens x NT*16 experts x one slice
 // of the reduction dimension, 4 waves.  With NT >= 4 each wave owns all 64
 // tokens and a quarter of the experts; with fewer expert blocks each wave
@@ -290,17 +331,25 @@ __global__ __launch_bounds__(256) void route_select_kernel(
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  // All slice loads first (at most 8 slices), then the sums in ascending
+  // slice order.
+  float p[8][NV];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = min(lane + kWave * i, e_pad - 1);
+      p[s][i] = s < n_slices ? part[((size_t)s * T + t) * e_pad + e] : 0.f;
+    }
   float v[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int e = lane + kWave * i;
-    if (e < E) {
-      float z = part[(size_t)t * e_pad + e];
-      for (int s = 1; s < n_slices; ++s) z += part[((size_t)s * T + t) * e_pad + e];
-      v[i] = z + (bias ? bias[e] : 0.f);
-    } else {
-      v[i] = -INFINITY;
-    }
+    float z = p[0][i];
+#pragma unroll
+    for (int s = 1; s < 8; ++s)
+      if (s < n_slices) z += p[s][i];
+    v[i] = e < E ? z + (bias ? bias[e] : 0.f) : -INFINITY;
   }
   select_topk<NV>(v, E, K, score, renorm, t, ids, weights, logits, lane);
 }
