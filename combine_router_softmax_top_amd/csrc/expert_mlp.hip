@@ -524,17 +524,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 
 // ------------------------------------------------------------------ fp32 VALU GEMM
 
-constexpr int kFM = 64, kFN = 64, kFK = 16;
+constexpr int kFM = 64, kFN = 64, kFK = 32;
 
+// fp32 layers: 64 x 64 output tiles, 256 threads with 4 x 4 outputs each (and
+// the matching up outputs in the gate/up pass), 32-deep k-steps through two
+// LDS buffers: the next step's operands are loaded (16-byte loads) while the
+// current one is multiplied.  k runs in ascending order for every output.
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(
     const float* __restrict__ A, int lda, long long strideA_batch, const float* __restrict__ B0,
     const float* __restrict__ B1, long long strideB_group, long long strideB_batch,
     float* __restrict__ C, int ldc, long long strideC_batch, const int32_t* __restrict__ offsets,
     int n_groups, int fixed_rows, int N, int Kdim) {
-  __shared__ float sa[kFK][kFM + 1];
-  __shared__ float sg[kFK][kFN + 1];
-  __shared__ float su[kFK][kFN + 1];
+  constexpr bool kGlu = EPI == EPI_SILU_GLU;
+  __shared__ __attribute__((aligned(16))) float sa[2][kFK][kFM + 4];
+  __shared__ __attribute__((aligned(16))) float sg[2][kFK][kFN + 4];
+  __shared__ __attribute__((aligned(16))) float su[kGlu ? 2 : 1][kFK][kFN + 4];
   const int nN = (N + kFN - 1) / kFN;
   Tile tl;
   if (!find_tile(offsets, n_groups, fixed_rows, kFM, nN, tl)) return;
@@ -544,38 +549,71 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
   const long long zb = (long long)blockIdx.z * strideB_batch;
   A += (long long)blockIdx.z * strideA_batch;
   const float* bg = B0 + zb + (long long)tl.group * strideB_group;
-  const float* bu = EPI == EPI_SILU_GLU ? B1 + zb + (long long)tl.group * strideB_group : bg;
+  const float* bu = kGlu ? B1 + zb + (long long)tl.group * strideB_group : bg;
   float* Cz = C + (long long)blockIdx.z * strideC_batch;
-  float ag[4][4] = {}, au[4][4] = {};
-  for (int k0 = 0; k0 < Kdim; k0 += kFK) {
-    // 64 rows x 16 k per operand: each thread stages 4 elements of each.
-    for (int q = tid; q < kFM * kFK; q += 256) {
-      const int r = q / kFK, kk = q % kFK;
-      const int am = min(m0 + r, tl.rows - 1);
-      sa[kk][r] = A[(long long)(tl.row0 + am) * lda + k0 + kk];
-      const int bn = min(n0 + r, N - 1);
-      sg[kk][r] = bg[(long long)bn * Kdim + k0 + kk];
-      if (EPI == EPI_SILU_GLU) su[kk][r] = bu[(long long)bn * Kdim + k0 + kk];
+
+  // Staging: thread t loads 4 consecutive k (k4 = 4 (t % 8)) of rows t/8 and
+  // t/8 + 32 of each operand; rows past the tile's last one repeat it, k past
+  // Kdim reads as zero (Kdim is a multiple of 16, so a group of 4 is wholly
+  // inside or wholly past).
+  const int k4 = (tid & 7) * 4;
+  const float* pa[2];
+  const float* pg[2];
+  const float* pu[2];
+  int rr[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    rr[j] = (tid >> 3) + 32 * j;
+    pa[j] = A + (long long)(tl.row0 + min(m0 + rr[j], tl.rows - 1)) * lda + k4;
+    const int bn = min(n0 + rr[j], N - 1);
+    pg[j] = bg + (long long)bn * Kdim + k4;
+    pu[j] = bu + (long long)bn * Kdim + k4;
+  }
+  f32x4 ra[2], rg[2], ru[2];
+  auto load = [&](int k0) {
+    const bool in = k0 + k4 < Kdim;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      ra[j] = in ? *reinterpret_cast<const f32x4*>(pa[j] + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
+      rg[j] = in ? *reinterpret_cast<const f32x4*>(pg[j] + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (kGlu) ru[j] = in ? *reinterpret_cast<const f32x4*>(pu[j] + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    __syncthreads();
-    for (int kk = 0; kk < kFK; ++kk) {
-      float a[4], g[4], u[4];
+  };
+  auto store = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = sa[kk][ty * 4 + i];
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        g[j] = sg[kk][tx * 4 + j];
-        u[j] = EPI == EPI_SILU_GLU ? su[kk][tx * 4 + j] : 0.f;
+      for (int c = 0; c < 4; ++c) {
+        sa[buf][k4 + c][rr[j]] = ra[j][c];
+        sg[buf][k4 + c][rr[j]] = rg[j][c];
+        if (kGlu) su[buf][k4 + c][rr[j]] = ru[j][c];
       }
+  };
+  float ag[4][4] = {}, au[4][4] = {};
+  load(0);
+  store(0);
+  __syncthreads();
+  int buf = 0;
+  for (int k0 = 0; k0 < Kdim; k0 += kFK) {
+    const bool more = k0 + kFK < Kdim;
+    if (more) load(k0 + kFK);
+#pragma unroll 8
+    for (int kk = 0; kk < kFK; ++kk) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&sa[buf][kk][ty * 4]);
+      const f32x4 g = *reinterpret_cast<const f32x4*>(&sg[buf][kk][tx * 4]);
+      f32x4 u = {0.f, 0.f, 0.f, 0.f};
+      if (kGlu) u = *reinterpret_cast<const f32x4*>(&su[buf][kk][tx * 4]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           ag[i][j] = fmaf(a[i], g[j], ag[i][j]);
-          if (EPI == EPI_SILU_GLU) au[i][j] = fmaf(a[i], u[j], au[i][j]);
+          if (kGlu) au[i][j] = fmaf(a[i], u[j], au[i][j]);
         }
     }
+    if (more) store(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -585,7 +623,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + tx * 4 + j;
       if (n >= N) continue;
-      const float v = EPI == EPI_SILU_GLU ? silu_f(ag[i][j]) * au[i][j] : ag[i][j];
+      const float v = kGlu ? silu_f(ag[i][j]) * au[i][j] : ag[i][j];
       Cz[(long long)(tl.row0 + m) * ldc + n] = v;
     }
   }

@@ -359,6 +359,7 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ wr, const float* __restrict__ bias,
     int T, int d, int E, int K, int score, int renorm, int32_t* __restrict__ ids,
     float* __restrict__ weights, float* __restrict__ logits) {
+  constexpr int kGrp = 8;  // experts reduced together (independent butterflies)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int tt = wave * 4; tt < wave * 4 + 4; ++tt) {
     const int t = blockIdx.x * kTokTile + tt;
@@ -367,16 +368,31 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = -INFINITY;
     const float* xr = x + (size_t)t * d;
-    for (int e = 0; e < E; ++e) {
-      const float* wrow = wr + (size_t)e * d;
-      float p = 0.f;
-      for (int i = lane; i < d; i += kWave) p = fmaf(xr[i], wrow[i], p);
-      p = wave_sum(p);
-      if (bias) p += bias[e];
-      if ((e & (kWave - 1)) == lane) {
+    for (int e0 = 0; e0 < E; e0 += kGrp) {
+      // lane-partial dot products of kGrp experts, each in ascending i
+      float p[kGrp];
 #pragma unroll
-        for (int i = 0; i < NV; ++i)
-          if (i == (e >> 6)) v[i] = p;
+      for (int g = 0; g < kGrp; ++g) p[g] = 0.f;
+      for (int i = lane; i < d; i += kWave) {
+        const float xv = xr[i];
+#pragma unroll
+        for (int g = 0; g < kGrp; ++g)
+          if (e0 + g < E) p[g] = fmaf(xv, wr[(size_t)(e0 + g) * d + i], p[g]);
+      }
+      // kGrp independent butterfly sums (every lane ends with the same bits)
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+        for (int g = 0; g < kGrp; ++g) p[g] += __shfl_xor(p[g], off);
+#pragma unroll
+      for (int g = 0; g < kGrp; ++g) {
+        const int e = e0 + g;
+        if (e < E && (e & (kWave - 1)) == lane) {
+          const float z = p[g] + (bias ? bias[e] : 0.f);
+#pragma unroll
+          for (int i = 0; i < NV; ++i)
+            if (i == (e >> 6)) v[i] = z;
+        }
       }
     }
     select_topk<NV>(v, E, K, score, renorm, t, ids, weights, logits, lane);
