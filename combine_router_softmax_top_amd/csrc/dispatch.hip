@@ -9,71 +9,64 @@
 // (expert ascending, then token ascending), so the layout has one answer.
 //
 // Three kernels, no host synchronisation and no memset:
-//  1. count: one workgroup per chunk of 256 tokens.  Each expert gets a
-//     256-bit token mask in LDS (64-bit LDS atomic OR per assignment).  The
-//     rank of an assignment inside its chunk is the popcount of the mask bits
-//     below its token; the per-chunk count of an expert is the popcount of its
-//     whole mask.  Invalid ids are tallied into an extra histogram column.
+//  1. count: one workgroup per chunk of 1024 assignments (t*K + k in
+//     ascending order, one per thread).  Each local expert gets a 1024-bit
+//     mask over the chunk's assignment slots in LDS (64-bit LDS atomic OR);
+//     the rank of an assignment inside its chunk is the popcount of the mask
+//     bits below its slot, so a token that names an expert twice gets two
+//     ranks in (t, k) order, like any other pair of assignments.  Every
+//     expert's chunk count goes to a histogram row (LDS atomic add); invalid
+//     ids are tallied into an extra column.
 //  2. scan: one workgroup turns the chunk histograms into global counts,
 //     exclusive offsets over the local experts and per-(chunk, expert) row
 //     bases.
 //  3. scatter: one wave per token; the token row is read once (16-byte
-//     loads) and written to each of its local rows; the row maps are
-//     written alongside.  Tokens with no local expert are not read at all.
+//     loads, held in registers) and written to each of its local rows; the
+//     row maps are written alongside.  Tokens with no local expert are not
+//     read at all.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kCH = kDispatchChunk;
-constexpr int kWords = kCH / 64;
+constexpr int kCA = kDispatchChunk;  // assignments per count chunk = threads per workgroup
+constexpr int kWords = kCA / 64;     // 64-bit mask words per expert and chunk
 
-__global__ __launch_bounds__(kCH) void dispatch_count_kernel(
-    const int32_t* __restrict__ ids, int T, int K, int E, int eb, int ee,
-    int32_t* __restrict__ hist /*[n_chunks][E+1]*/, int32_t* __restrict__ rank /*[T*K]*/) {
-  extern __shared__ unsigned long long mask[];  // [E][kWords]
-  __shared__ int bad_total;
+__global__ __launch_bounds__(kCA) void dispatch_count_kernel(
+    const int32_t* __restrict__ ids, int n_assign, int E, int eb, int ee,
+    int32_t* __restrict__ hist /*[n_chunks][E+1]*/, int32_t* __restrict__ rank /*[n_assign]*/) {
+  __shared__ unsigned long long mask[MOE_MAX_EXPERTS * kWords];  // [local expert][word]
+  __shared__ int cnt[MOE_MAX_EXPERTS + 1];                        // [expert], [E] = invalid
   const int tid = threadIdx.x;
-  for (int i = tid; i < E * kWords; i += kCH) mask[i] = 0ull;
-  if (tid == 0) bad_total = 0;
+  const int n_loc = ee - eb;
+  for (int i = tid; i < n_loc * kWords; i += kCA) mask[i] = 0ull;
+  for (int i = tid; i <= E; i += kCA) cnt[i] = 0;
   __syncthreads();
-  const int t = blockIdx.x * kCH + tid;
+  const long long a = (long long)blockIdx.x * kCA + tid;
+  const bool in = a < n_assign;
   const int word = tid >> 6;
   const unsigned long long bit = 1ull << (tid & 63);
-  int bad = 0;
-  if (t < T) {
-    for (int k = 0; k < K; ++k) {
-      const int e = ids[(size_t)t * K + k];
-      if (e >= 0 && e < E) atomicOr(&mask[e * kWords + word], bit);
-      else ++bad;
-    }
-  }
-  if (bad) atomicAdd(&bad_total, bad);
+  const int e = in ? ids[a] : -1;
+  const bool valid = e >= 0 && e < E;
+  const bool local = in && e >= eb && e < ee;
+  if (in) atomicAdd(&cnt[valid ? e : E], 1);
+  if (local) atomicOr(&mask[(e - eb) * kWords + word], bit);
   __syncthreads();
-  if (t < T) {
-    for (int k = 0; k < K; ++k) {
-      const int e = ids[(size_t)t * K + k];
-      int r = -1;
-      if (e >= eb && e < ee) {
-        const unsigned long long* m = mask + e * kWords;
-        r = __popcll(m[word] & (bit - 1ull));
-        for (int w = 0; w < word; ++w) r += __popcll(m[w]);
-      }
-      rank[(size_t)t * K + k] = r;
+  if (in) {
+    int r = -1;
+    if (local) {
+      const unsigned long long* m = mask + (e - eb) * kWords;
+      r = __popcll(m[word] & (bit - 1ull));
+      for (int w = 0; w < word; ++w) r += __popcll(m[w]);
     }
+    rank[a] = r;
   }
   int32_t* h = hist + (size_t)blockIdx.x * (E + 1);
-  for (int e = tid; e < E; e += kCH) {
-    int c = 0;
-#pragma unroll
-    for (int w = 0; w < kWords; ++w) c += __popcll(mask[e * kWords + w]);
-    h[e] = c;
-  }
-  if (tid == 0) h[E] = bad_total;
+  for (int i = tid; i <= E; i += kCA) h[i] = cnt[i];
 }
 
 constexpr int kScanThreads = 1024;
-constexpr int kScanLdsInts = 12288;  // chunk histograms staged in LDS when they fit (48 KB)
+constexpr int kScanLdsInts = 32768;  // chunk histograms staged in LDS when they fit (128 KB)
 
 __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
     const int32_t* __restrict__ hist, int n_chunks, int E, int eb, int ee,
@@ -123,8 +116,8 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
   }
 }
 
-constexpr int kUnroll = 4;
-
+// NV = 16-byte pieces of the row each lane holds at once.
+template <int NV>
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ base, int T, int K, int eb,
@@ -133,13 +126,12 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const int chunk = t / kCH;
   int myrow = -1;
   if (lane < K) {
     const int a = t * K + lane;
     const int r = rank[a];
     if (r >= 0) {
-      myrow = base[(size_t)chunk * n_loc + (ids[a] - eb)] + r;
+      myrow = base[(size_t)(a / kCA) * n_loc + (ids[a] - eb)] + r;
       src_index[myrow] = a;
     }
     row_of[a] = myrow;
@@ -148,10 +140,10 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   const unsigned long long any = __ballot(myrow >= 0);
   if (any == 0ull) return;
   const u32x4* src = x + (size_t)t * row_vecs;
-  for (int v0 = 0; v0 < row_vecs; v0 += kWave * kUnroll) {
-    u32x4 buf[kUnroll];
+  for (int v0 = 0; v0 < row_vecs; v0 += kWave * NV) {
+    u32x4 buf[NV];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < NV; ++u) {
       const int v = v0 + u * kWave + lane;
       if (v < row_vecs) buf[u] = src[v];
     }
@@ -160,7 +152,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
       if (rk < 0) continue;
       u32x4* dst = x_sorted + (size_t)rk * row_vecs;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < NV; ++u) {
         const int v = v0 + u * kWave + lane;
         if (v < row_vecs) dst[v] = buf[u];
       }
@@ -172,7 +164,7 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 
 // Workspace: [n_invalid (256 B)] [hist n_chunks*(E+1)] [rank T*K] [base n_chunks*E_loc]
 size_t dispatch_workspace_bytes(const moe_config_t& c) {
-  const size_t n_chunks = (size_t)ceil_div(c.num_tokens, kCH);
+  const size_t n_chunks = (size_t)ceil_div(c.num_tokens * c.top_k, kCA);
   const size_t n_loc = (size_t)(c.expert_end - c.expert_begin);
   size_t b = 256;
   b += align_up(n_chunks * (c.num_experts + 1) * 4, 256);
@@ -186,7 +178,8 @@ hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* 
                            int32_t* row_of, void* workspace, hipStream_t s) {
   const int T = c.num_tokens, K = c.top_k, E = c.num_experts;
   const int eb = c.expert_begin, ee = c.expert_end, n_loc = ee - eb;
-  const int n_chunks = ceil_div(T, kCH);
+  const int n_assign = T * K;
+  const int n_chunks = ceil_div(n_assign, kCA);
   char* ws = static_cast<char*>(workspace);
   int32_t* n_invalid = reinterpret_cast<int32_t*>(ws);
   ws += 256;
@@ -196,9 +189,8 @@ hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* 
   ws += align_up((size_t)T * K * 4, 256);
   int32_t* base = reinterpret_cast<int32_t*>(ws);
 
-  const size_t lds = (size_t)E * kWords * sizeof(unsigned long long);
-  hipLaunchKernelGGL(dispatch_count_kernel, dim3(n_chunks), dim3(kCH), lds, s, ids, T, K, E, eb,
-                     ee, hist, rank);
+  hipLaunchKernelGGL(dispatch_count_kernel, dim3(n_chunks), dim3(kCA), 0, s, ids, n_assign, E,
+                     eb, ee, hist, rank);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, hist, n_chunks, E,
@@ -207,7 +199,11 @@ hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* 
   if (err != hipSuccess) return err;
   const int elem = c.dtype == MOE_BF16 ? 2 : 4;
   const int row_vecs = c.hidden * elem / 16;
-  hipLaunchKernelGGL(dispatch_scatter_kernel, dim3(ceil_div(T, 4)), dim3(256), 0, s,
+  const int per_lane = ceil_div(row_vecs, kWave);
+  auto kern = dispatch_scatter_kernel<16>;
+  if (per_lane <= 4) kern = dispatch_scatter_kernel<4>;
+  else if (per_lane <= 8) kern = dispatch_scatter_kernel<8>;
+  hipLaunchKernelGGL(kern, dim3(ceil_div(T, 4)), dim3(256), 0, s,
                      static_cast<const u32x4*>(x), ids, rank, base, T, K, eb, n_loc, row_vecs,
                      static_cast<u32x4*>(x_sorted), src_index, row_of);
   return hipGetLastError();

@@ -10,8 +10,8 @@
 namespace moe {
 
 constexpr int kWave = 64;
-// Tokens per dispatch chunk: one workgroup counts and ranks one chunk.
-constexpr int kDispatchChunk = 256;
+// Assignments (t*K + k) per dispatch chunk: one workgroup counts and ranks one chunk.
+constexpr int kDispatchChunk = 1024;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

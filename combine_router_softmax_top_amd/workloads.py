@@ -170,14 +170,20 @@ def make_inputs(cfg: MoEConfig, seed: int = 0, with_experts: bool = True) -> dic
     return inp
 
 
-def random_ids(T: int, E: int, K: int, seed: int, invalid_frac: float = 0.0) -> torch.Tensor:
+def random_ids(T: int, E: int, K: int, seed: int, invalid_frac: float = 0.0,
+               repeat_pool: int = 0) -> torch.Tensor:
     """Distinct-per-token random expert ids [T, K] int32, for dispatch-only cases.
 
     With ``invalid_frac`` > 0, that fraction of slots is replaced by out-of-range
-    ids (negative or >= E), which the dispatch must skip and count.
+    ids (negative or >= E), which the dispatch must skip and count.  With
+    ``repeat_pool`` > 0 the slots are drawn with replacement from experts
+    [0, repeat_pool) instead, so a token may name an expert more than once.
     """
     g = _gen(seed, 100)
-    ids = torch.argsort(torch.rand(T, E, generator=g), dim=1)[:, :K].to(torch.int32)
+    if repeat_pool > 0:
+        ids = torch.randint(0, min(repeat_pool, E), (T, K), generator=g, dtype=torch.int32)
+    else:
+        ids = torch.argsort(torch.rand(T, E, generator=g), dim=1)[:, :K].to(torch.int32)
     if invalid_frac > 0:
         m = torch.rand(T, K, generator=g) < invalid_frac
         bad = torch.where(torch.rand(T, K, generator=g) < 0.5,

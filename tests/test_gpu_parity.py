@@ -264,6 +264,26 @@ def test_dispatch_invalid_ids_are_skipped_and_counted():
     assert r["n_invalid"] > 0
 
 
+def test_dispatch_repeated_experts_in_a_token():
+    # Slots drawn with replacement: tokens name some experts twice or more;
+    # each such slot gets its own row (token order, then slot order).  5600
+    # assignments span several count chunks and end in a ragged one.
+    cfg = W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=700, hidden=256, intermediate=128)
+    inp = W.make_inputs(cfg, seed=8, with_experts=False)
+    L = MoELayer(cfg, inp)
+    for pool in (40, 3):
+        ids = W.random_ids(cfg.num_tokens, cfg.num_experts, cfg.top_k, seed=9, repeat_pool=pool)
+        L.dispatch(topk_ids=ids.cuda())
+        torch.cuda.synchronize()
+        check_dispatch(cfg, inp, L, ids=ids)
+    # every slot of every token names the same local expert
+    ids = torch.full((cfg.num_tokens, cfg.top_k), 5, dtype=torch.int32)
+    L.dispatch(topk_ids=ids.cuda())
+    torch.cuda.synchronize()
+    check_dispatch(cfg, inp, L, ids=ids)
+    assert L.n_rows() == cfg.num_tokens * cfg.top_k
+
+
 def test_dispatch_skewed_and_all_remote():
     # every token routed to non-local experts: no rows, all row_of = -1, x never read
     cfg = W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=300, hidden=256, intermediate=128)

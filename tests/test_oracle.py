@@ -195,6 +195,20 @@ def test_dispatch_bruteforce(T, E, K, eb, ee):
     assert r["row_of"].tolist() == row_of
 
 
+@pytest.mark.parametrize("T,E,K,eb,ee,pool", [(6, 4, 3, 0, 4, 2), (11, 8, 4, 2, 6, 7),
+                                              (40, 16, 8, 0, 16, 5)])
+def test_dispatch_bruteforce_with_repeated_experts(T, E, K, eb, ee, pool):
+    # A token naming an expert twice gets two rows, in slot order.
+    ids = W.random_ids(T, E, K, seed=T * E + K, repeat_pool=pool)
+    assert any(len(set(r)) < K for r in ids.tolist())
+    r = oracle.dispatch(ids, E, eb, ee)
+    counts, offsets, src, row_of = _dispatch_bruteforce(ids, E, eb, ee)
+    assert r["counts"].tolist() == counts
+    assert r["offsets"].tolist() == offsets
+    assert r["src_index"].tolist() == src
+    assert r["row_of"].tolist() == row_of
+
+
 def test_dispatch_invariants_with_invalid_ids():
     T, E, K, eb, ee = 300, 64, 6, 8, 40
     ids = W.random_ids(T, E, K, seed=7, invalid_frac=0.05)
