@@ -24,6 +24,8 @@
 //     loads, held in registers) and written to each of its local rows; the
 //     row maps are written alongside.  Tokens with no local expert are not
 //     read at all.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -116,37 +118,118 @@ __global__ __launch_bounds__(kScanThreads) void dispatch_scan_kernel(
   }
 }
 
-// NV = 16-byte pieces of the row each lane holds at once.
-template <int NV>
+constexpr int kInlineScanInts = 4096;  // local chunk counts a scatter workgroup stages
+
+// Row numbers for the scatter, computed inside each scatter workgroup (when
+// the local chunk counts fit in kInlineScanInts): the workgroup stages the
+// counts of the local experts in every chunk, totals them per expert, scans
+// the totals into expert offsets, and keeps, for the (at most two) chunks its
+// assignments fall in, offset + rows of the expert in earlier chunks.  The
+// workgroups with the lowest ids also write the global counts, n_invalid and
+// the offsets.  Every thread of the workgroup takes part (barriers).
+struct InlineScan {
+  int32_t hl[kInlineScanInts];         // [chunk][local expert]
+  int32_t sc[2][MOE_MAX_EXPERTS];      // scan ping-pong
+  int32_t base[2][MOE_MAX_EXPERTS];    // row base of chunks c_lo, c_lo + 1
+};
+
+__device__ void inline_scan(InlineScan& L, const int32_t* __restrict__ hist, int n_chunks, int E,
+                            int eb, int n_loc, int c_lo, int32_t* __restrict__ counts,
+                            int32_t* __restrict__ offsets, int32_t* __restrict__ n_invalid) {
+  const int tid = threadIdx.x;
+  // Global counts of all E experts and the invalid column (grid-stride).
+  for (int e = blockIdx.x * 256 + tid; e <= E; e += gridDim.x * 256) {
+    int sum = 0;
+    for (int c = 0; c < n_chunks; ++c) sum += hist[(size_t)c * (E + 1) + e];
+    if (e == E) *n_invalid = sum;
+    else counts[e] = sum;
+  }
+  const int n_h = n_chunks * n_loc;
+  for (int i = tid; i < n_h; i += 256) {
+    const int c = i / n_loc;
+    L.hl[i] = hist[(size_t)c * (E + 1) + eb + (i - c * n_loc)];
+  }
+  __syncthreads();
+  for (int j = tid; j < n_loc; j += 256) {
+    int tot = 0, before = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      const int v = L.hl[c * n_loc + j];
+      before += c < c_lo ? v : 0;
+      tot += v;
+    }
+    L.sc[0][j] = tot;
+    L.base[0][j] = before;
+    L.base[1][j] = before + L.hl[c_lo * n_loc + j];
+  }
+  __syncthreads();
+  // Inclusive Hillis-Steele scan of the totals.
+  int cur = 0;
+  for (int off = 1; off < n_loc; off <<= 1) {
+    for (int j = tid; j < n_loc; j += 256)
+      L.sc[cur ^ 1][j] = L.sc[cur][j] + (j >= off ? L.sc[cur][j - off] : 0);
+    cur ^= 1;
+    __syncthreads();
+  }
+  for (int j = tid; j < n_loc; j += 256) {
+    const int incl = L.sc[cur][j];
+    const int excl = j > 0 ? L.sc[cur][j - 1] : 0;
+    L.base[0][j] += excl;
+    L.base[1][j] += excl;
+    if (blockIdx.x == 0) offsets[j + 1] = incl;
+  }
+  if (blockIdx.x == 0 && tid == 0) offsets[0] = 0;
+  __syncthreads();
+}
+
+// NV = 16-byte pieces of the row each lane holds at once.  INLINE: row
+// numbers from inline_scan (hist), else from the scan kernel (base).
+template <int NV, bool INLINE>
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ ids,
-    const int32_t* __restrict__ rank, const int32_t* __restrict__ base, int T, int K, int eb,
-    int n_loc, int row_vecs, u32x4* __restrict__ x_sorted, int32_t* __restrict__ src_index,
-    int32_t* __restrict__ row_of) {
+    const int32_t* __restrict__ rank, const int32_t* __restrict__ base,
+    const int32_t* __restrict__ hist, int n_chunks, int E, int T, int K, int eb, int n_loc,
+    int row_vecs, u32x4* __restrict__ x_sorted, int32_t* __restrict__ src_index,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ n_invalid) {
+  __shared__ typename std::conditional<INLINE, InlineScan, int>::type lds;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  int myrow = -1;
-  if (lane < K) {
-    const int a = t * K + lane;
-    const int r = rank[a];
-    if (r >= 0) {
-      myrow = base[(size_t)(a / kCA) * n_loc + (ids[a] - eb)] + r;
-      src_index[myrow] = a;
-    }
-    row_of[a] = myrow;
+  const bool tok = t < T;  // wave-uniform
+  int a = -1, r = -1, j = 0;
+  if (tok && lane < K) {
+    a = t * K + lane;
+    r = rank[a];
+    if (r >= 0) j = ids[a] - eb;
   }
-  // Any local row at all?  (wave-uniform)
-  const unsigned long long any = __ballot(myrow >= 0);
-  if (any == 0ull) return;
-  const u32x4* src = x + (size_t)t * row_vecs;
-  for (int v0 = 0; v0 < row_vecs; v0 += kWave * NV) {
-    u32x4 buf[NV];
+  const bool any = __ballot(r >= 0) != 0ull;  // any local row (wave-uniform)
+  // The first piece of the token row does not depend on the row numbers:
+  // its loads go out before the scan.
+  const u32x4* src = x + (size_t)(tok ? t : 0) * row_vecs;
+  u32x4 buf[NV];
+  auto load_piece = [&](int v0) {
 #pragma unroll
     for (int u = 0; u < NV; ++u) {
       const int v = v0 + u * kWave + lane;
       if (v < row_vecs) buf[u] = src[v];
     }
+  };
+  if (tok && any) load_piece(0);
+  int myrow = -1;
+  if constexpr (INLINE) {
+    const int c_lo = blockIdx.x * 4 * K / kCA;  // chunk of the workgroup's first assignment
+    inline_scan(lds, hist, n_chunks, E, eb, n_loc, c_lo, counts, offsets, n_invalid);
+    if (r >= 0) myrow = lds.base[a / kCA - c_lo][j] + r;
+  } else {
+    if (r >= 0) myrow = base[(size_t)(a / kCA) * n_loc + j] + r;
+  }
+  if (!tok) return;
+  if (lane < K) {
+    if (myrow >= 0) src_index[myrow] = a;
+    row_of[a] = myrow;
+  }
+  if (!any) return;
+  for (int v0 = 0; v0 < row_vecs; v0 += kWave * NV) {
+    if (v0 > 0) load_piece(v0);
     for (int k = 0; k < K; ++k) {
       const int rk = __builtin_amdgcn_readlane(myrow, k);
       if (rk < 0) continue;
@@ -158,6 +241,19 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
       }
     }
   }
+}
+
+template <int NV>
+void launch_scatter(bool inl, dim3 grid, hipStream_t s, const void* x, const int32_t* ids,
+                    const int32_t* rank, const int32_t* base, const int32_t* hist, int n_chunks,
+                    int E, int T, int K, int eb, int n_loc, int row_vecs, void* x_sorted,
+                    int32_t* src_index, int32_t* row_of, int32_t* counts, int32_t* offsets,
+                    int32_t* n_invalid) {
+  auto kern = inl ? dispatch_scatter_kernel<NV, true> : dispatch_scatter_kernel<NV, false>;
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, static_cast<const u32x4*>(x), ids, rank, base,
+                     hist, n_chunks, E, T, K, eb, n_loc, row_vecs,
+                     static_cast<u32x4*>(x_sorted), src_index, row_of, counts, offsets,
+                     n_invalid);
 }
 
 }  // namespace
@@ -193,19 +289,27 @@ hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* 
                      eb, ee, hist, rank);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, hist, n_chunks, E,
-                     eb, ee, counts, offsets, base, n_invalid);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  // The scan runs inside the scatter when the local chunk counts fit its LDS.
+  const bool inl = (size_t)n_chunks * n_loc <= (size_t)kInlineScanInts;
+  if (!inl) {
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, hist, n_chunks,
+                       E, eb, ee, counts, offsets, base, n_invalid);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   const int elem = c.dtype == MOE_BF16 ? 2 : 4;
   const int row_vecs = c.hidden * elem / 16;
   const int per_lane = ceil_div(row_vecs, kWave);
-  auto kern = dispatch_scatter_kernel<16>;
-  if (per_lane <= 4) kern = dispatch_scatter_kernel<4>;
-  else if (per_lane <= 8) kern = dispatch_scatter_kernel<8>;
-  hipLaunchKernelGGL(kern, dim3(ceil_div(T, 4)), dim3(256), 0, s,
-                     static_cast<const u32x4*>(x), ids, rank, base, T, K, eb, n_loc, row_vecs,
-                     static_cast<u32x4*>(x_sorted), src_index, row_of);
+  const dim3 grid(ceil_div(T, 4));
+  if (per_lane <= 4)
+    launch_scatter<4>(inl, grid, s, x, ids, rank, base, hist, n_chunks, E, T, K, eb, n_loc,
+                      row_vecs, x_sorted, src_index, row_of, counts, offsets, n_invalid);
+  else if (per_lane <= 8)
+    launch_scatter<8>(inl, grid, s, x, ids, rank, base, hist, n_chunks, E, T, K, eb, n_loc,
+                      row_vecs, x_sorted, src_index, row_of, counts, offsets, n_invalid);
+  else
+    launch_scatter<16>(inl, grid, s, x, ids, rank, base, hist, n_chunks, E, T, K, eb, n_loc,
+                       row_vecs, x_sorted, src_index, row_of, counts, offsets, n_invalid);
   return hipGetLastError();
 }
 

@@ -12,8 +12,8 @@
 //     256 rows x (128 gate + 128 up) columns, multiplied together in the
 //     epilogue, so h is written once, in bf16); eight waves (two per SIMD)
 //     in a 2x4 grid, each a 128x64 sub-tile of 4x2 v_mfma_f32_32x32x16_bf16
-//     blocks; an expert's last row tile with at most 128 rows runs as a
-//     half-height tile (each wave 64x64);
+//     blocks; an expert's last row tile with at most 192 rows runs at the
+//     height of its rows rounded up to 64 (each wave 32, 64 or 96 rows x 64);
 //   * 64-deep k-tiles (full 128-byte row segments) move straight from global
 //     memory into LDS (global_load_lds, 16 B per lane): the activations in a
 //     ring of two slots (one tile ahead), the weights in a ring of three (two
@@ -23,8 +23,8 @@
 //   * ragged groups: the tile list (expert, row tile, column tile) is derived
 //     on the device from the expert offsets; the grid is the host's upper
 //     bound and surplus workgroups exit at once (no host synchronisation);
-//   * the row tiles of all experts (full-height first, the half-height last
-//     tiles at the end) form bands of 16; the 8 XCDs work on the same band at
+//   * the row tiles of all experts (full-height first, then the shorter last
+//     tiles, tallest first) form bands of 16; the 8 XCDs work on the same band at
 //     once as a 2 x 4 grid (8 rows x a quarter of the columns each), so a
 //     weight tile streams from memory at most twice per band and an
 //     activation tile is shared by 4 XCDs, the repeats served by the
@@ -61,12 +61,14 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
 }
 
 // Row tiles of a group of `rows` rows: `full` tiles computed at full height
-// (BM rows, including a last tile of more than BM/2 rows) and `half` (0 or 1)
-// for a last tile of at most BM/2 rows, which runs at half height.
-__device__ __forceinline__ void group_row_tiles(int rows, int BM, int& full, int& half) {
-  const int rem = rows % BM;
-  full = rows / BM + (rem > BM / 2 ? 1 : 0);
-  half = (rem > 0 && rem <= BM / 2) ? 1 : 0;
+// (BM rows, including a last tile of more than 3BM/4 rows) and, when the
+// remainder is at most 3BM/4 rows, one short last tile of q quarters (q = 1..3,
+// its rows rounded up to BM/4), which runs at that height.  q = 0: none.
+__device__ __forceinline__ void group_row_tiles(int rows, int BM, int& full, int& q) {
+  const int qr = BM / 4;
+  const int qq = (rows % BM + qr - 1) / qr;  // 0..4
+  full = rows / BM + (qq == 4 ? 1 : 0);
+  q = qq == 4 ? 0 : qq;
 }
 
 constexpr int kMaxGroupChunks = MOE_MAX_EXPERTS / 64;  // groups per lane, at most
@@ -87,23 +89,24 @@ __host__ __device__ inline int tiles_per_xcd_bound(int row_tiles, int nN) {
 // Maps this workgroup onto (group, row tile, column tile).  Groups are the
 // local experts (from the device offsets) or, with offsets == nullptr, a single
 // group of fixed_rows rows.  The row tiles form one list -- every group's
-// full-height tiles in group order, then the half-height last tiles -- cut
-// into bands of kBandRows row tiles.  The 8 XCDs (workgroup ids go round-robin
+// full-height tiles in group order, then the short last tiles of 3, 2 and 1
+// quarters, each kind in group order -- cut into bands of kBandRows row tiles.  The 8 XCDs (workgroup ids go round-robin
 // over them, XCD x running ids x, x+8, ...) all work on the same band at a
 // time: they form a grid of row groups x column groups over it, and XCD x
 // takes its block of the band column by column.  An XCD thus holds a few
 // weight column tiles across half the band's rows: a weight tile streams
 // from memory once or twice per band, an activation row tile is shared by
 // the few XCDs of its row group (the Infinity Cache serves the repeats), and
-// within an XCD both operands are reused from L2.  The cheap half-height
-// tiles come last, where the final round of tiles is only partly filled.
+// within an XCD both operands are reused from L2.  The cheap short tiles come
+// last, smallest at the very end, where the final round of tiles is only
+// partly filled.
 // Returns false for surplus workgroups.
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int n_groups,
                                           int fixed_rows, int BM, int nN, Tile& out) {
   const int lane = threadIdx.x & 63;
   // The offsets are read once, all at once: lane l holds group c*64 + l.
   int g0[kMaxGroupChunks], g1[kMaxGroupChunks];
-  int n_full = 0, n_half = 0;
+  int n_full = 0, n_part[3] = {0, 0, 0};  // short last tiles of 3, 2, 1 quarters
   if (offsets != nullptr) {
 #pragma unroll
     for (int c = 0; c < kMaxGroupChunks; ++c) {
@@ -117,15 +120,18 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
 #pragma unroll
     for (int c = 0; c < kMaxGroupChunks; ++c) {
       if (c * 64 >= n_groups) break;
-      int f, h;
-      group_row_tiles(g1[c] - g0[c], BM, f, h);
+      int f, q;
+      group_row_tiles(g1[c] - g0[c], BM, f, q);
       n_full += __shfl(wave_inclusive_sum(f), 63, 64);
-      n_half += __shfl(wave_inclusive_sum(h), 63, 64);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) n_part[p] += __shfl(wave_inclusive_sum(q == 3 - p ? 1 : 0), 63, 64);
     }
   } else {
-    group_row_tiles(fixed_rows, BM, n_full, n_half);
+    int q;
+    group_row_tiles(fixed_rows, BM, n_full, q);
+    if (q > 0) n_part[3 - q] = 1;
   }
-  const int n_rt = n_full + n_half;
+  const int n_rt = n_full + n_part[0] + n_part[1] + n_part[2];
   const int xcd = blockIdx.x & 7;
   int slot = blockIdx.x >> 3;
   const int rx = xcd_row_groups(nN), cx = 8 / rx;
@@ -150,17 +156,24 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
   int rt = band * kBandRows + r0 + slot % nr;  // index in the row-tile list
   int row0 = 0, rows = fixed_rows, group = 0, m_tile = rt;
   if (offsets != nullptr) {
-    // Full-height tiles: the rt-th in group order; half-height: the
-    // (rt - n_full)-th group that has one, which is its last row tile.
-    const bool is_half = rt >= n_full;
-    if (is_half) rt -= n_full;
+    // Full-height tiles: the rt-th in group order.  Short tiles of kind p (3 - p
+    // quarters): the rt-th group, past the full tiles and the earlier kinds,
+    // that has one; it is that group's last row tile.
+    const bool is_short = rt >= n_full;
+    int want = -1;  // quarters of the wanted short tile
+    if (is_short) {
+      rt -= n_full;
+      int p = 0;
+      while (p < 2 && rt >= n_part[p]) rt -= n_part[p++];
+      want = 3 - p;
+    }
     bool found = false;
 #pragma unroll
     for (int c = 0; c < kMaxGroupChunks; ++c) {
       if (found || c * 64 >= n_groups) break;
-      int f, h;
-      group_row_tiles(g1[c] - g0[c], BM, f, h);
-      const int cnt = is_half ? h : f;
+      int f, q;
+      group_row_tiles(g1[c] - g0[c], BM, f, q);
+      const int cnt = is_short ? (q == want ? 1 : 0) : f;
       const int incl = wave_inclusive_sum(cnt);
       const int chunk = __shfl(incl, 63, 64);
       if (rt < chunk) {
@@ -168,7 +181,7 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
         row0 = __shfl(g0[c], L, 64);
         rows = __shfl(g1[c], L, 64) - row0;
         group = c * 64 + L;
-        m_tile = is_half ? __shfl(f, L, 64) : rt - __shfl(incl - cnt, L, 64);
+        m_tile = is_short ? __shfl(f, L, 64) : rt - __shfl(incl - cnt, L, 64);
         found = true;
       } else {
         rt -= chunk;
@@ -215,9 +228,9 @@ __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 // Staging one operand of a k-tile (32 KB per workgroup) with direct
 // global->LDS loads: instruction j of wave w fills 1 KB of the slot = rows
 // (8j + w)*8 .. +8; lane l covers row +l/8, physical chunk l%8, so its source
-// is logical chunk (l%8) ^ swz(row).  NA = A instructions per wave (4 for a
-// 256-row tile, 2 for a 128-row tile); B always takes 4 (rows 0..127 from
-// b_lo, 128..255 from b_hi).
+// is logical chunk (l%8) ^ swz(row).  NA = A instructions per wave (one per
+// 64 rows of the tile); B always takes 4 (rows 0..127 from b_lo, 128..255
+// from b_hi).
 template <int NA>
 __device__ __forceinline__ void stage_a(uint8_t* slot, const uint8_t* a_tile,
                                         const uint32_t (&off)[2 * kDmaB], int wave,
@@ -326,10 +339,10 @@ struct TileArgs {
   int row0, rows, m0, n0, N, Kdim;
 };
 
-// One output tile.  NFA = 4: 256 rows, the 8 waves as 2 x 4, each 128 rows x
-// 64 columns.  NFA = 2: the last row tile of an expert with at most 128 rows,
-// each wave 64 rows x 64 columns (half the A staging and half the MFMAs).
-// The k order of every output element is the same in both.
+// One output tile of NFA * 64 rows: the 8 waves as 2 x 4, each NFA * 32 rows
+// x 64 columns.  NFA = 4 for full tiles; 1..3 for the last row tile of an
+// expert with at most 192 rows (that fraction of the A staging and of the
+// MFMAs).  The k order of every output element is the same at every height.
 template <int EPI, int NFA>
 __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
   constexpr int kNOut = EPI == EPI_SILU_GLU ? kBN / 2 : kBN;
@@ -404,7 +417,7 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
   // which overlap the next tile's first fragment reads and the new loads.
   // The body has no branches: past the last tile the loads re-read the last
   // tile into free slots and the next-tile fragments go unused.
-  constexpr int NA = NFA == 4 ? kDmaB : kDmaB / 2;
+  constexpr int NA = NFA;  // A loads per wave: 64 rows each across the 8 waves
   constexpr int kMfma = NFA * kBF, kReads = NFA + kBF;  // per k-step
   constexpr int kMaxStages = kAStages > kBStages ? kAStages : kBStages;
   // Loads issued after tile 0's in the prologue; after tile kt+1's by barrier kt.
@@ -516,10 +529,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
   ta.n0 = tl.n_tile * kNOut;
   ta.N = N;
   ta.Kdim = Kdim;
-  if (tl.rows - ta.m0 <= kBM / 2)
+  // Height of the tile: its rows rounded up to 64 (a full tile when more
+  // than 192), as find_tile classed it.
+  const int left = tl.rows - ta.m0;
+  if (left > 3 * kBM / 4)
+    gemm_tile<EPI, 4>(ta, lds);
+  else if (left > kBM / 2)
+    gemm_tile<EPI, 3>(ta, lds);
+  else if (left > kBM / 4)
     gemm_tile<EPI, 2>(ta, lds);
   else
-    gemm_tile<EPI, 4>(ta, lds);
+    gemm_tile<EPI, 1>(ta, lds);
 }
 
 // ------------------------------------------------------------------ fp32 VALU GEMM

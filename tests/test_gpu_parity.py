@@ -239,6 +239,11 @@ EDGE = [
                                                   num_experts=5, top_k=3, expert_end=5)),
     ("bf16_unaligned_tiles", W.CONFIGS["mixtral_bf16"].replace(num_tokens=515, hidden=320,
                                                                intermediate=448)),
+    # the Zipf bias keeps every token off the least popular experts: no local
+    # rows at all, so the expert MLP has nothing to do and the output is zero
+    ("no_local_rows", W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=64, hidden=256,
+                                                           intermediate=128, expert_begin=248,
+                                                           expert_end=256)),
 ]
 
 
@@ -250,6 +255,8 @@ def test_edge_cases(name, cfg):
     check_dispatch(cfg, inp, L)
     check_mlp(cfg, inp, L)
     check_combine(cfg, L)
+    if name == "no_local_rows":
+        assert L.n_rows() == 0 and not bool(L.out.any())
 
 
 def test_dispatch_invalid_ids_are_skipped_and_counted():
@@ -282,6 +289,20 @@ def test_dispatch_repeated_experts_in_a_token():
     torch.cuda.synchronize()
     check_dispatch(cfg, inp, L, ids=ids)
     assert L.n_rows() == cfg.num_tokens * cfg.top_k
+
+
+def test_dispatch_scan_fallback_for_large_histograms():
+    # 32 chunks x 512 local experts: more per-chunk counts than a scatter
+    # workgroup stages, so the separate scan kernel computes the row numbers.
+    cfg = W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=2048, hidden=64, intermediate=64,
+                                               num_experts=512, top_k=16, expert_begin=0,
+                                               expert_end=512)
+    inp = W.make_inputs(cfg, seed=10, with_experts=False)
+    ids = W.random_ids(cfg.num_tokens, cfg.num_experts, cfg.top_k, seed=11, invalid_frac=0.01)
+    L = MoELayer(cfg, inp)
+    L.dispatch(topk_ids=ids.cuda())
+    torch.cuda.synchronize()
+    check_dispatch(cfg, inp, L, ids=ids)
 
 
 def test_dispatch_skewed_and_all_remote():
