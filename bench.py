@@ -40,6 +40,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="dsv3_prefill_ep")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the graph-replay timing of the whole layer")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -78,6 +80,11 @@ def bench_dbo(args, cfg, layer, torch) -> dict:
     torch.cuda.synchronize()
     same = bool(torch.equal(layer.out.view(torch.int16), ref.view(torch.int16)))
     one_stream = timed(lambda: layer.forward_dbo(compute=compute, comm=compute))
+    graph_ms = None
+    if not args.no_graph:
+        g = layer.capture_forward(dbo=True)
+        graph_ms = timed(lambda: g.launch(compute))
+        g.destroy()
     T = cfg.num_tokens
     return {"metric": "dual-microbatch layer tokens/s (moe_forward_dbo, two HIP streams)",
             "value": T / (split * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -87,7 +94,8 @@ def bench_dbo(args, cfg, layer, torch) -> dict:
             "config": {"workload": cfg.name, "tokens": T, "microbatches": [
                 B.dbo_split_point(T), T - B.dbo_split_point(T)]},
             "unsplit_ms": unsplit, "split_two_streams_ms": split, "split_one_stream_ms": one_stream,
-            "overlap_gain": unsplit / split - 1.0, "bitwise_equal_to_unsplit": same}
+            "overlap_gain": unsplit / split - 1.0, "bitwise_equal_to_unsplit": same,
+            "split_graph_replay_ms": graph_ms}
 
 
 def source_digest() -> str:
@@ -314,9 +322,30 @@ def main():
                      "avg_launch_us": stage["expert_mlp"] * 1e3},
         "input_generation_s": round(t_gen, 1),
     }
+    if not args.no_graph:
+        result["graph_replay"] = graph_replay(args, layer, stream, torch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def graph_replay(args, layer, stream, torch) -> dict:
+    """The whole layer (moe_forward) captured once as a HIP graph and replayed
+    back to back on one stream: the step without per-launch host work."""
+    g = layer.capture_forward()
+    for _ in range(max(args.warmup, 1)):
+        g.launch(stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        g.launch(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    g.destroy()
+    ms = e0.elapsed_time(e1) / args.steps
+    return {"ms_per_step": ms, "tokens_per_s": layer.cfg.num_tokens / (ms * 1e-3),
+            "how": "moe_graph_capture_forward once, moe_graph_launch per step, HIP events"}
 
 
 if __name__ == "__main__":

@@ -24,7 +24,9 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_EXPERT_MLP, MOE_WS_FORWARD, MOE_WS_FORWARD_DBO = range(5)
 
 EXPORTED = ["moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_forward",
-            "moe_forward_dbo", "moe_workspace_bytes", "moe_dbo_split_point", "moe_status_string"]
+            "moe_forward_dbo", "moe_graph_capture_forward", "moe_graph_capture_forward_dbo",
+            "moe_graph_launch", "moe_graph_destroy", "moe_workspace_bytes",
+            "moe_dbo_split_point", "moe_status_string"]
 
 
 class MoEError(RuntimeError):
@@ -67,6 +69,10 @@ def lib() -> ctypes.CDLL:
             "moe_combine": [C, P, P, P, P, P, P],
             "moe_forward": [C, LT, P, SZ, P],
             "moe_forward_dbo": [C, LT, P, SZ, I32, P, P],
+            "moe_graph_capture_forward": [C, LT, P, SZ, ctypes.POINTER(P)],
+            "moe_graph_capture_forward_dbo": [C, LT, P, SZ, I32, ctypes.POINTER(P)],
+            "moe_graph_launch": [P, P],
+            "moe_graph_destroy": [P],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -243,6 +249,47 @@ def moe_forward_dbo(cfg, tensors: dict, workspace, min_tokens_to_split: int = 0,
                                workspace.numel() * workspace.element_size(),
                                int(min_tokens_to_split), cs, ms)
     _check("moe_forward_dbo", st)
+
+
+class Graph:
+    """A captured whole-layer call (moe_graph_capture_forward[_dbo]).  It keeps
+    the tensors whose pointers the graph holds alive until it is destroyed."""
+
+    def __init__(self, handle: int, keep: tuple):
+        self.handle = handle
+        self._keep = keep
+
+    def launch(self, stream=None):
+        _check("moe_graph_launch", lib().moe_graph_launch(self.handle, _stream(stream)))
+
+    def destroy(self):
+        if self.handle:
+            _check("moe_graph_destroy", lib().moe_graph_destroy(self.handle))
+            self.handle = None
+            self._keep = ()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def moe_graph_capture_forward(cfg, tensors: dict, workspace, dbo: bool = False,
+                              min_tokens_to_split: int = 0) -> Graph:
+    c = _cs(cfg)
+    lt = layer_tensors(c, tensors)
+    h = ctypes.c_void_p()
+    nbytes = workspace.numel() * workspace.element_size()
+    if dbo:
+        st = lib().moe_graph_capture_forward_dbo(ctypes.byref(c), ctypes.byref(lt),
+                                                 _p(workspace, "workspace"), nbytes,
+                                                 int(min_tokens_to_split), ctypes.byref(h))
+    else:
+        st = lib().moe_graph_capture_forward(ctypes.byref(c), ctypes.byref(lt),
+                                             _p(workspace, "workspace"), nbytes, ctypes.byref(h))
+    _check("moe_graph_capture_forward" + ("_dbo" if dbo else ""), st)
+    return Graph(h.value, (tuple(v for v in tensors.values() if v is not None), workspace))
 
 
 def alloc_workspace(cfg, kind: int, device="cuda") -> Optional[torch.Tensor]:

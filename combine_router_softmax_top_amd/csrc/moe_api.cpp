@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <new>
 #include <cstdint>
 
 #include "moe.h"
@@ -338,6 +339,104 @@ moe_status_t moe_forward_dbo(const moe_config_t* cfg, const moe_layer_tensors_t*
   (void)good;
   for (int i = 0; i < EV_N; ++i) hipEventDestroy(ev[i]);
   return result;
+}
+
+}  // extern "C"
+
+struct moe_graph {
+  hipGraphExec_t exec;
+};
+
+namespace {
+
+// Runs `enqueue(capture_stream, second_stream)` under stream capture on two
+// private streams and instantiates the result.  The second stream joins the
+// capture through the events the enqueued call records.
+template <typename F>
+moe_status_t capture(F enqueue, moe_graph_t* out) {
+  hipStream_t s0 = nullptr, s1 = nullptr;
+  if (hipStreamCreateWithFlags(&s0, hipStreamNonBlocking) != hipSuccess) return MOE_ERR_HIP;
+  if (hipStreamCreateWithFlags(&s1, hipStreamNonBlocking) != hipSuccess) {
+    hipStreamDestroy(s0);
+    return MOE_ERR_HIP;
+  }
+  moe_status_t st = MOE_OK;
+  hipGraph_t g = nullptr;
+  hipGraphExec_t exec = nullptr;
+  if (hipStreamBeginCapture(s0, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    st = MOE_ERR_HIP;
+  } else {
+    st = enqueue(s0, s1);
+    // End the capture in every case; a failed enqueue discards the graph.
+    const hipError_t e = hipStreamEndCapture(s0, &g);
+    if (st == MOE_OK && (e != hipSuccess || g == nullptr)) st = MOE_ERR_HIP;
+  }
+  if (st == MOE_OK && hipGraphInstantiate(&exec, g, nullptr, nullptr, 0) != hipSuccess)
+    st = MOE_ERR_HIP;
+  if (g) hipGraphDestroy(g);
+  hipStreamDestroy(s1);
+  hipStreamDestroy(s0);
+  if (st != MOE_OK) return st;
+  moe_graph_t h = new (std::nothrow) moe_graph{exec};
+  if (!h) {
+    hipGraphExecDestroy(exec);
+    return MOE_ERR_HIP;
+  }
+  *out = h;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_graph_capture_forward(const moe_config_t* cfg,
+                                       const moe_layer_tensors_t* tensors, void* workspace,
+                                       size_t workspace_bytes, moe_graph_t* graph) {
+  if (!graph) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  st = check_layer_tensors(*cfg, tensors);
+  if (st != MOE_OK) return st;
+  if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < layer_scratch(*cfg, nullptr, nullptr)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return capture(
+      [&](hipStream_t s0, hipStream_t) {
+        return moe_forward(cfg, tensors, workspace, workspace_bytes, s0);
+      },
+      graph);
+}
+
+moe_status_t moe_graph_capture_forward_dbo(const moe_config_t* cfg,
+                                           const moe_layer_tensors_t* tensors, void* workspace,
+                                           size_t workspace_bytes, int32_t min_tokens_to_split,
+                                           moe_graph_t* graph) {
+  if (!graph) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  st = check_layer_tensors(*cfg, tensors);
+  if (st != MOE_OK) return st;
+  if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < moe_workspace_bytes(cfg, MOE_WS_FORWARD_DBO))
+    return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return capture(
+      [&](hipStream_t s0, hipStream_t s1) {
+        return moe_forward_dbo(cfg, tensors, workspace, workspace_bytes, min_tokens_to_split, s0,
+                               s1);
+      },
+      graph);
+}
+
+moe_status_t moe_graph_launch(moe_graph_t graph, moe_stream_t stream) {
+  if (!graph) return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_graph_destroy(moe_graph_t graph) {
+  if (!graph) return MOE_ERR_INVALID_ARGUMENT;
+  const hipError_t e = hipGraphExecDestroy(graph->exec);
+  delete graph;
+  return hip_status(e);
 }
 
 }  // extern "C"

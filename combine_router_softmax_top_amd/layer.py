@@ -94,5 +94,20 @@ class MoELayer:
         B.moe_forward_dbo(self.cs, self.tensors(out), self._ws_dbo, min_tokens_to_split,
                           compute, comm)
 
+    def capture_forward(self, out: Optional[torch.Tensor] = None, dbo: bool = False,
+                        min_tokens_to_split: int = 0) -> B.Graph:
+        """The whole layer (moe_forward, or moe_forward_dbo with dbo=True) captured
+        as a HIP graph over this layer's buffers; replay with .launch(stream)."""
+        if dbo:
+            if self._ws_dbo is None:
+                self._ws_dbo = B.alloc_workspace(self.cs, B.MOE_WS_FORWARD_DBO, self.device)
+            ws = self._ws_dbo
+        else:
+            if self._ws_forward is None:
+                self._ws_forward = B.alloc_workspace(self.cs, B.MOE_WS_FORWARD, self.device)
+            ws = self._ws_forward
+        return B.moe_graph_capture_forward(self.cs, self.tensors(out), ws, dbo=dbo,
+                                           min_tokens_to_split=min_tokens_to_split)
+
     def n_rows(self) -> int:
         return int(self.offsets[-1].item())

@@ -9,14 +9,16 @@
  *          Portable Kernels, Dispatch, Combine.
  *   [DBO]  "Dual Batch Overlap" (vLLM design doc): Introduction (overlap
  *          schedule), UBatchRunner (midpoint split), Interfaces (compute and
- *          communication streams).
+ *          communication streams), Limitations and UBatchWrapper (the
+ *          overlapped forward is captured whole as a graph and replayed).
  *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer (HBM of the current HIP
  *     device) unless marked "host".  The library never allocates, frees or
  *     keeps device memory: inputs, outputs and workspaces are caller-owned and
  *     may be reused from call to call (as the pages' buffers are reused across
- *     layers, [PPLX] Portable Kernels).
+ *     layers, [PPLX] Portable Kernels).  (The graph entry points create a HIP
+ *     graph, whose runtime resources last until moe_graph_destroy.)
  *   - All matrices are dense row-major.  Expert weights use the [out, in]
  *     layout, so both operands of every product are contiguous along the
  *     reduction dimension.
@@ -249,6 +251,35 @@ moe_status_t moe_forward_dbo(const moe_config_t* cfg, const moe_layer_tensors_t*
                              void* workspace, size_t workspace_bytes,
                              int32_t min_tokens_to_split, moe_stream_t compute,
                              moe_stream_t comm);
+
+/*
+ * Graph capture of a whole-layer call.  [DBO] Limitations and UBatchWrapper:
+ * the overlapped forward is captured whole, as one graph, and a captured graph
+ * replays with no host work between its kernels.
+ *
+ * moe_graph_capture_forward / moe_graph_capture_forward_dbo record every
+ * launch of one moe_forward / moe_forward_dbo call (same arguments and
+ * checks) into an executable HIP graph, on private streams of the current
+ * device (created and destroyed inside the call, default priority); nothing
+ * runs during the capture.  The tensor and workspace pointers are fixed in the
+ * graph: each moe_graph_launch recomputes the layer from what those buffers
+ * hold at that time and writes the same outputs, so the buffers must outlive
+ * the graph.  moe_graph_launch enqueues a replay on `stream` (asynchronous;
+ * replays on one stream run in order; replays of one graph must not overlap).
+ * moe_graph_destroy releases the graph (after its replays have completed, or
+ * the runtime defers the release).  *graph is written only on MOE_OK.
+ */
+typedef struct moe_graph* moe_graph_t;
+
+moe_status_t moe_graph_capture_forward(const moe_config_t* cfg,
+                                       const moe_layer_tensors_t* tensors, void* workspace,
+                                       size_t workspace_bytes, moe_graph_t* graph);
+moe_status_t moe_graph_capture_forward_dbo(const moe_config_t* cfg,
+                                           const moe_layer_tensors_t* tensors, void* workspace,
+                                           size_t workspace_bytes, int32_t min_tokens_to_split,
+                                           moe_graph_t* graph);
+moe_status_t moe_graph_launch(moe_graph_t graph, moe_stream_t stream);
+moe_status_t moe_graph_destroy(moe_graph_t graph);
 
 /* Bytes of workspace needed by a call of the given kind (MOE_WS_*), or 0 for
  * an invalid configuration.  Pure host function. */

@@ -100,3 +100,23 @@ def test_workspace_sizes_grow_with_tokens(lib):
 @pytest.mark.parametrize("T,mid", [(8192, 4096), (100, 128), (300, 256), (256, 128), (1, 128)])
 def test_dbo_split_point(lib, T, mid):
     assert B.dbo_split_point(T) == mid
+
+
+def test_graph_entry_points_reject_bad_arguments_on_host(lib):
+    cs = B.config_struct(W.CONFIGS["dsv3_prefill_ep"])
+    h = ctypes.c_void_p()
+    lt = B.LayerTensorsStruct()  # all NULL
+    assert lib.moe_graph_launch(None, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_graph_destroy(None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_graph_capture_forward(ctypes.byref(cs), ctypes.byref(lt), None, 0,
+                                         ctypes.byref(h)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_graph_capture_forward_dbo(ctypes.byref(cs), None, None, 0, 0,
+                                             ctypes.byref(h)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_graph_capture_forward(ctypes.byref(cs), ctypes.byref(lt), None, 0,
+                                         None) == B.MOE_ERR_INVALID_ARGUMENT
+    bad = B.config_struct(W.CONFIGS["dsv3_prefill_ep"])
+    bad.top_k = 0
+    assert lib.moe_graph_capture_forward(ctypes.byref(bad), ctypes.byref(lt), None, 0,
+                                         ctypes.byref(h)) == B.MOE_ERR_INVALID_ARGUMENT
+    assert h.value is None  # nothing written on failure
+

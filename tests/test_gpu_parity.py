@@ -220,6 +220,57 @@ def test_dual_microbatch_equals_unsplit(name):
     assert_close(cfg, ref.cpu(), oracle.forward_split(cfg, inp), "dbo vs oracle split")
 
 
+# ------------------------------------------------------------------ graph capture
+
+@pytest.mark.parametrize("name", ["tiny_f32", "dsv2lite_small", "dsv3_small"])
+def test_graph_replay_equals_eager(name):
+    cfg, inp = inputs_for(name)
+    L = MoELayer(cfg, inp)
+    ref = torch.empty_like(L.out)
+    L.forward(out=ref)
+    torch.cuda.synchronize()
+    got = torch.empty_like(L.out)
+    g = L.capture_forward(out=got)
+    s = torch.cuda.Stream()
+    for rep in range(3):
+        got.zero_()
+        torch.cuda.synchronize()
+        g.launch(s)
+        s.synchronize()
+        assert torch.equal(bits(got), bits(ref)), f"replay {rep} differs from the eager forward"
+        L.forward(out=torch.empty_like(ref))  # eager work between replays
+        torch.cuda.synchronize()
+    # a replay recomputes from what the buffers hold now
+    L.x.copy_(L.x.flip(0))
+    ref2 = torch.empty_like(ref)
+    L.forward(out=ref2)
+    torch.cuda.synchronize()
+    g.launch(s)
+    s.synchronize()
+    assert torch.equal(bits(got), bits(ref2))
+    assert not torch.equal(bits(ref2), bits(ref))
+    g.destroy()
+
+
+def test_graph_replay_dual_microbatch():
+    cfg, inp = inputs_for("dsv3_dbo_small")
+    assert B.dbo_split_point(cfg.num_tokens) < cfg.num_tokens  # the split really happens
+    L = MoELayer(cfg, inp)
+    ref = torch.empty_like(L.out)
+    L.forward(out=ref)
+    torch.cuda.synchronize()
+    got = torch.empty_like(L.out)
+    g = L.capture_forward(out=got, dbo=True)
+    s = torch.cuda.Stream()
+    for rep in range(3):
+        got.zero_()
+        torch.cuda.synchronize()
+        g.launch(s)
+        s.synchronize()
+        assert torch.equal(bits(got), bits(ref)), f"replay {rep} differs from the unsplit forward"
+    g.destroy()
+
+
 # ------------------------------------------------------------------ edge cases
 
 EDGE = [
