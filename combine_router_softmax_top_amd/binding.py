@@ -24,9 +24,10 @@ MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_EXPERT_MLP, MOE_WS_FORWARD, MOE_WS_FORWARD_DBO = range(5)
 
 EXPORTED = ["moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_forward",
-            "moe_forward_dbo", "moe_graph_capture_forward", "moe_graph_capture_forward_dbo",
-            "moe_graph_launch", "moe_graph_destroy", "moe_workspace_bytes",
-            "moe_dbo_split_point", "moe_status_string"]
+            "moe_forward_dbo", "moe_forward_dbo_at", "moe_graph_capture_forward",
+            "moe_graph_capture_forward_dbo", "moe_graph_launch", "moe_graph_destroy",
+            "moe_workspace_bytes", "moe_dbo_split_point", "moe_dbo_plan_split",
+            "moe_status_string"]
 
 
 class MoEError(RuntimeError):
@@ -69,6 +70,7 @@ def lib() -> ctypes.CDLL:
             "moe_combine": [C, P, P, P, P, P, P],
             "moe_forward": [C, LT, P, SZ, P],
             "moe_forward_dbo": [C, LT, P, SZ, I32, P, P],
+            "moe_forward_dbo_at": [C, LT, P, SZ, I32, P, P],
             "moe_graph_capture_forward": [C, LT, P, SZ, ctypes.POINTER(P)],
             "moe_graph_capture_forward_dbo": [C, LT, P, SZ, I32, ctypes.POINTER(P)],
             "moe_graph_launch": [P, P],
@@ -82,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.restype = SZ
         L.moe_dbo_split_point.argtypes = [I32]
         L.moe_dbo_split_point.restype = I32
+        L.moe_dbo_plan_split.argtypes = [I32] * 5
+        L.moe_dbo_plan_split.restype = I32
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         _LIB = L
@@ -290,6 +294,23 @@ def moe_graph_capture_forward(cfg, tensors: dict, workspace, dbo: bool = False,
                                              _p(workspace, "workspace"), nbytes, ctypes.byref(h))
     _check("moe_graph_capture_forward" + ("_dbo" if dbo else ""), st)
     return Graph(h.value, (tuple(v for v in tensors.values() if v is not None), workspace))
+
+
+def moe_forward_dbo_at(cfg, tensors: dict, workspace, split: int, compute=None, comm=None):
+    c = _cs(cfg)
+    lt = layer_tensors(c, tensors)
+    cs = _stream(compute)
+    ms = cs if comm is None else _stream(comm)
+    st = lib().moe_forward_dbo_at(ctypes.byref(c), ctypes.byref(lt), _p(workspace, "workspace"),
+                                  workspace.numel() * workspace.element_size(), int(split), cs,
+                                  ms)
+    _check("moe_forward_dbo_at", st)
+
+
+def dbo_plan_split(num_tokens: int, has_prefill: bool, decode_threshold: int,
+                   prefill_threshold: int, uniform_query_len: int = 1) -> int:
+    return int(lib().moe_dbo_plan_split(int(num_tokens), int(has_prefill), int(decode_threshold),
+                                        int(prefill_threshold), int(uniform_query_len)))
 
 
 def alloc_workspace(cfg, kind: int, device="cuda") -> Optional[torch.Tensor]:

@@ -12,6 +12,8 @@
 
 using moe::align_up;
 
+extern "C" int32_t moe_dbo_split_point(int32_t num_tokens);
+
 namespace {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -128,6 +130,26 @@ moe_status_t enqueue_layer(const moe_config_t& c, const moe_layer_tensors_t& t, 
   return hip_status(e);
 }
 
+// Workspace of a layer call split at `split` (microbatch 1's scratch follows
+// microbatch 0's), or of the unsplit call.
+size_t dbo_workspace(const moe_config_t& c, int32_t split) {
+  if (split <= 0 || split >= c.num_tokens) return layer_scratch(c, nullptr, nullptr);
+  return layer_scratch(with_tokens(c, split), nullptr, nullptr) +
+         layer_scratch(with_tokens(c, c.num_tokens - split), nullptr, nullptr);
+}
+
+// An upper bound of dbo_workspace over every split point: the token-linear
+// parts of the two scratches add up to those of the whole call, the parts
+// that do not depend on the token count (expert counts, offsets, histogram
+// columns) appear twice -- once more than in a one-token call covers -- the
+// chunk counts round up at most once more, and each of the ten 256-byte
+// alignments may add up to 255 bytes per scratch.
+size_t dbo_workspace_bound(const moe_config_t& c) {
+  const size_t whole = layer_scratch(c, nullptr, nullptr);
+  const size_t one = layer_scratch(with_tokens(c, 1), nullptr, nullptr);
+  return std::max(whole, dbo_workspace(c, moe_dbo_split_point(c.num_tokens))) + one + 20 * 256;
+}
+
 // The tensors of microbatch [t0, t0 + n) of a layer call.
 moe_layer_tensors_t slice(const moe_config_t& c, const moe_layer_tensors_t& t, int32_t t0) {
   const size_t rb = (size_t)c.hidden * (c.dtype == MOE_BF16 ? 2 : 4);
@@ -137,6 +159,80 @@ moe_layer_tensors_t slice(const moe_config_t& c, const moe_layer_tensors_t& t, i
   r.topk_ids = t.topk_ids + (size_t)t0 * c.top_k;
   r.topk_weights = t.topk_weights + (size_t)t0 * c.top_k;
   return r;
+}
+
+// The dual-microbatch schedule for a cut at `split` (0: the unsplit layer on
+// `cs`): route on the compute stream, dispatch on the comm stream, the expert
+// MLPs on compute, the combines on comm, with events between; `cs` then waits
+// for both microbatches.
+moe_status_t enqueue_dbo(const moe_config_t& cfg, const moe_layer_tensors_t& tensors,
+                         void* workspace, int32_t split, hipStream_t cs, hipStream_t ms) {
+  const int32_t T = cfg.num_tokens;
+  if (split <= 0 || split >= T) return enqueue_layer(cfg, tensors, workspace, cs);
+
+  const moe_config_t c0 = with_tokens(cfg, split), c1 = with_tokens(cfg, T - split);
+  const moe_layer_tensors_t t0 = slice(cfg, tensors, 0), t1 = slice(cfg, tensors, split);
+  LayerScratch s0, s1;
+  const size_t first = layer_scratch(c0, nullptr, nullptr);
+  layer_scratch(c0, workspace, &s0);
+  layer_scratch(c1, static_cast<char*>(workspace) + first, &s1);
+
+  if (cs == ms) {
+    const moe_status_t st = enqueue_layer(c0, t0, workspace, cs);
+    if (st != MOE_OK) return st;
+    return enqueue_layer(c1, t1, static_cast<char*>(workspace) + first, cs);
+  }
+
+  enum { EV_START, EV_R0, EV_R1, EV_D0, EV_D1, EV_M0, EV_M1, EV_DONE, EV_N };
+  hipEvent_t ev[EV_N] = {};
+  moe_status_t result = MOE_OK;
+  for (int i = 0; i < EV_N; ++i)
+    if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) {
+      for (int j = 0; j < i; ++j) hipEventDestroy(ev[j]);
+      return MOE_ERR_HIP;
+    }
+  auto ok = [&](hipError_t e) {
+    if (e != hipSuccess) result = MOE_ERR_HIP;
+    return e == hipSuccess;
+  };
+  // The comm stream must see the caller's earlier work on the compute stream.
+  bool good = ok(hipEventRecord(ev[EV_START], cs)) && ok(hipStreamWaitEvent(ms, ev[EV_START], 0));
+  // compute: route both microbatches.
+  good = good && ok(moe::launch_route(c0, t0.x, t0.w_router, t0.bias, t0.topk_ids,
+                                      t0.topk_weights, nullptr, s0.route_ws, cs)) &&
+         ok(hipEventRecord(ev[EV_R0], cs)) &&
+         ok(moe::launch_route(c1, t1.x, t1.w_router, t1.bias, t1.topk_ids, t1.topk_weights,
+                              nullptr, s1.route_ws, cs)) &&
+         ok(hipEventRecord(ev[EV_R1], cs));
+  // comm: dispatch both as their routes finish.
+  good = good && ok(hipStreamWaitEvent(ms, ev[EV_R0], 0)) &&
+         ok(moe::launch_dispatch(c0, t0.x, t0.topk_ids, s0.counts, s0.offsets, s0.x_sorted,
+                                 s0.src_index, s0.row_of, s0.dispatch_ws, ms)) &&
+         ok(hipEventRecord(ev[EV_D0], ms)) && ok(hipStreamWaitEvent(ms, ev[EV_R1], 0)) &&
+         ok(moe::launch_dispatch(c1, t1.x, t1.topk_ids, s1.counts, s1.offsets, s1.x_sorted,
+                                 s1.src_index, s1.row_of, s1.dispatch_ws, ms)) &&
+         ok(hipEventRecord(ev[EV_D1], ms));
+  // compute: experts of microbatch 0 (overlapping dispatch 1), then of microbatch 1.
+  good = good && ok(hipStreamWaitEvent(cs, ev[EV_D0], 0)) &&
+         ok(moe::launch_expert_mlp(c0, s0.x_sorted, s0.offsets, t0.w_gate, t0.w_up, t0.w_down,
+                                   s0.y_sorted, t0.x, t0.ws_gate, t0.ws_up, t0.ws_down,
+                                   s0.y_shared, s0.mlp_ws, cs)) &&
+         ok(hipEventRecord(ev[EV_M0], cs)) && ok(hipStreamWaitEvent(cs, ev[EV_D1], 0)) &&
+         ok(moe::launch_expert_mlp(c1, s1.x_sorted, s1.offsets, t1.w_gate, t1.w_up, t1.w_down,
+                                   s1.y_sorted, t1.x, t1.ws_gate, t1.ws_up, t1.ws_down,
+                                   s1.y_shared, s1.mlp_ws, cs)) &&
+         ok(hipEventRecord(ev[EV_M1], cs));
+  // comm: combine 0 (overlapping experts of microbatch 1), then combine 1.
+  good = good && ok(hipStreamWaitEvent(ms, ev[EV_M0], 0)) &&
+         ok(moe::launch_combine(c0, s0.y_sorted, s0.row_of, t0.topk_weights, s0.y_shared, t0.out,
+                                ms)) &&
+         ok(hipStreamWaitEvent(ms, ev[EV_M1], 0)) &&
+         ok(moe::launch_combine(c1, s1.y_sorted, s1.row_of, t1.topk_weights, s1.y_shared, t1.out,
+                                ms)) &&
+         ok(hipEventRecord(ev[EV_DONE], ms)) && ok(hipStreamWaitEvent(cs, ev[EV_DONE], 0));
+  (void)good;
+  for (int i = 0; i < EV_N; ++i) hipEventDestroy(ev[i]);
+  return result;
 }
 
 }  // namespace
@@ -167,13 +263,7 @@ size_t moe_workspace_bytes(const moe_config_t* cfg, int32_t kind) {
     case MOE_WS_DISPATCH: return moe::dispatch_workspace_bytes(*cfg);
     case MOE_WS_EXPERT_MLP: return moe::mlp_workspace_bytes(*cfg);
     case MOE_WS_FORWARD: return layer_scratch(*cfg, nullptr, nullptr);
-    case MOE_WS_FORWARD_DBO: {
-      const int32_t mid = moe_dbo_split_point(cfg->num_tokens);
-      const int32_t n0 = std::min(mid, cfg->num_tokens);
-      // Two microbatch scratches (microbatch 0 is the larger), or the unsplit one.
-      const size_t split = 2 * layer_scratch(with_tokens(*cfg, n0), nullptr, nullptr);
-      return std::max(split, layer_scratch(*cfg, nullptr, nullptr));
-    }
+    case MOE_WS_FORWARD_DBO: return dbo_workspace_bound(*cfg);
     default: return 0;
   }
 }
@@ -270,75 +360,39 @@ moe_status_t moe_forward_dbo(const moe_config_t* cfg, const moe_layer_tensors_t*
   if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < moe_workspace_bytes(cfg, MOE_WS_FORWARD_DBO))
     return MOE_ERR_WORKSPACE_TOO_SMALL;
-  hipStream_t cs = static_cast<hipStream_t>(compute);
-  hipStream_t ms = static_cast<hipStream_t>(comm);
   const int32_t T = cfg->num_tokens;
   const int32_t mid = moe_dbo_split_point(T);
-  if (T < min_tokens_to_split || mid >= T) return enqueue_layer(*cfg, *tensors, workspace, cs);
+  const int32_t split = (T < min_tokens_to_split || mid >= T) ? 0 : mid;
+  return enqueue_dbo(*cfg, *tensors, workspace, split, static_cast<hipStream_t>(compute),
+                     static_cast<hipStream_t>(comm));
+}
 
-  const moe_config_t c0 = with_tokens(*cfg, mid), c1 = with_tokens(*cfg, T - mid);
-  const moe_layer_tensors_t t0 = slice(*cfg, *tensors, 0), t1 = slice(*cfg, *tensors, mid);
-  LayerScratch s0, s1;
-  const size_t half = layer_scratch(c0, nullptr, nullptr);
-  layer_scratch(c0, workspace, &s0);
-  layer_scratch(c1, static_cast<char*>(workspace) + half, &s1);
+moe_status_t moe_forward_dbo_at(const moe_config_t* cfg, const moe_layer_tensors_t* tensors,
+                                void* workspace, size_t workspace_bytes, int32_t split,
+                                moe_stream_t compute, moe_stream_t comm) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  st = check_layer_tensors(*cfg, tensors);
+  if (st != MOE_OK) return st;
+  if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  if (split <= 0 || split >= cfg->num_tokens) split = 0;
+  if (workspace_bytes < dbo_workspace(*cfg, split)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return enqueue_dbo(*cfg, *tensors, workspace, split, static_cast<hipStream_t>(compute),
+                     static_cast<hipStream_t>(comm));
+}
 
-  if (cs == ms) {
-    st = enqueue_layer(c0, t0, workspace, cs);
-    if (st != MOE_OK) return st;
-    return enqueue_layer(c1, t1, static_cast<char*>(workspace) + half, cs);
+int32_t moe_dbo_plan_split(int32_t num_tokens, int32_t has_prefill, int32_t decode_threshold,
+                           int32_t prefill_threshold, int32_t uniform_query_len) {
+  if (num_tokens < 1) return 0;
+  if (num_tokens < (has_prefill ? prefill_threshold : decode_threshold)) return 0;
+  int32_t cut = moe_dbo_split_point(num_tokens);
+  const int32_t q = uniform_query_len;
+  if (!has_prefill && q > 1 && num_tokens % q == 0) {
+    // Nearest request boundary; the lower of two equally near ones.
+    const int32_t r = cut % q;
+    cut = (2 * r <= q) ? cut - r : cut - r + q;
   }
-
-  enum { EV_START, EV_R0, EV_R1, EV_D0, EV_D1, EV_M0, EV_M1, EV_DONE, EV_N };
-  hipEvent_t ev[EV_N] = {};
-  moe_status_t result = MOE_OK;
-  for (int i = 0; i < EV_N; ++i)
-    if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) {
-      for (int j = 0; j < i; ++j) hipEventDestroy(ev[j]);
-      return MOE_ERR_HIP;
-    }
-  auto ok = [&](hipError_t e) {
-    if (e != hipSuccess) result = MOE_ERR_HIP;
-    return e == hipSuccess;
-  };
-  // The comm stream must see the caller's earlier work on the compute stream.
-  bool good = ok(hipEventRecord(ev[EV_START], cs)) && ok(hipStreamWaitEvent(ms, ev[EV_START], 0));
-  // compute: route both microbatches.
-  good = good && ok(moe::launch_route(c0, t0.x, t0.w_router, t0.bias, t0.topk_ids,
-                                      t0.topk_weights, nullptr, s0.route_ws, cs)) &&
-         ok(hipEventRecord(ev[EV_R0], cs)) &&
-         ok(moe::launch_route(c1, t1.x, t1.w_router, t1.bias, t1.topk_ids, t1.topk_weights,
-                              nullptr, s1.route_ws, cs)) &&
-         ok(hipEventRecord(ev[EV_R1], cs));
-  // comm: dispatch both as their routes finish.
-  good = good && ok(hipStreamWaitEvent(ms, ev[EV_R0], 0)) &&
-         ok(moe::launch_dispatch(c0, t0.x, t0.topk_ids, s0.counts, s0.offsets, s0.x_sorted,
-                                 s0.src_index, s0.row_of, s0.dispatch_ws, ms)) &&
-         ok(hipEventRecord(ev[EV_D0], ms)) && ok(hipStreamWaitEvent(ms, ev[EV_R1], 0)) &&
-         ok(moe::launch_dispatch(c1, t1.x, t1.topk_ids, s1.counts, s1.offsets, s1.x_sorted,
-                                 s1.src_index, s1.row_of, s1.dispatch_ws, ms)) &&
-         ok(hipEventRecord(ev[EV_D1], ms));
-  // compute: experts of microbatch 0 (overlapping dispatch 1), then of microbatch 1.
-  good = good && ok(hipStreamWaitEvent(cs, ev[EV_D0], 0)) &&
-         ok(moe::launch_expert_mlp(c0, s0.x_sorted, s0.offsets, t0.w_gate, t0.w_up, t0.w_down,
-                                   s0.y_sorted, t0.x, t0.ws_gate, t0.ws_up, t0.ws_down,
-                                   s0.y_shared, s0.mlp_ws, cs)) &&
-         ok(hipEventRecord(ev[EV_M0], cs)) && ok(hipStreamWaitEvent(cs, ev[EV_D1], 0)) &&
-         ok(moe::launch_expert_mlp(c1, s1.x_sorted, s1.offsets, t1.w_gate, t1.w_up, t1.w_down,
-                                   s1.y_sorted, t1.x, t1.ws_gate, t1.ws_up, t1.ws_down,
-                                   s1.y_shared, s1.mlp_ws, cs)) &&
-         ok(hipEventRecord(ev[EV_M1], cs));
-  // comm: combine 0 (overlapping experts of microbatch 1), then combine 1.
-  good = good && ok(hipStreamWaitEvent(ms, ev[EV_M0], 0)) &&
-         ok(moe::launch_combine(c0, s0.y_sorted, s0.row_of, t0.topk_weights, s0.y_shared, t0.out,
-                                ms)) &&
-         ok(hipStreamWaitEvent(ms, ev[EV_M1], 0)) &&
-         ok(moe::launch_combine(c1, s1.y_sorted, s1.row_of, t1.topk_weights, s1.y_shared, t1.out,
-                                ms)) &&
-         ok(hipEventRecord(ev[EV_DONE], ms)) && ok(hipStreamWaitEvent(cs, ev[EV_DONE], 0));
-  (void)good;
-  for (int i = 0; i < EV_N; ++i) hipEventDestroy(ev[i]);
-  return result;
+  return (cut > 0 && cut < num_tokens) ? cut : 0;
 }
 
 }  // extern "C"

@@ -88,11 +88,15 @@ class MoELayer:
         B.moe_forward(self.cs, self.tensors(out), self._ws_forward, stream)
 
     def forward_dbo(self, compute=None, comm=None, min_tokens_to_split: int = 0,
-                    out: Optional[torch.Tensor] = None):
+                    out: Optional[torch.Tensor] = None, split: Optional[int] = None):
+        """moe_forward_dbo (midpoint cut), or moe_forward_dbo_at with split given."""
         if self._ws_dbo is None:
             self._ws_dbo = B.alloc_workspace(self.cs, B.MOE_WS_FORWARD_DBO, self.device)
-        B.moe_forward_dbo(self.cs, self.tensors(out), self._ws_dbo, min_tokens_to_split,
-                          compute, comm)
+        if split is None:
+            B.moe_forward_dbo(self.cs, self.tensors(out), self._ws_dbo, min_tokens_to_split,
+                              compute, comm)
+        else:
+            B.moe_forward_dbo_at(self.cs, self.tensors(out), self._ws_dbo, split, compute, comm)
 
     def capture_forward(self, out: Optional[torch.Tensor] = None, dbo: bool = False,
                         min_tokens_to_split: int = 0) -> B.Graph:

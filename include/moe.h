@@ -10,7 +10,8 @@
  *   [DBO]  "Dual Batch Overlap" (vLLM design doc): Introduction (overlap
  *          schedule), UBatchRunner (midpoint split), Interfaces (compute and
  *          communication streams), Limitations and UBatchWrapper (the
- *          overlapped forward is captured whole as a graph and replayed).
+ *          overlapped forward is captured whole as a graph and replayed),
+ *          Running with DBO (token thresholds).
  *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer (HBM of the current HIP
@@ -251,6 +252,33 @@ moe_status_t moe_forward_dbo(const moe_config_t* cfg, const moe_layer_tensors_t*
                              void* workspace, size_t workspace_bytes,
                              int32_t min_tokens_to_split, moe_stream_t compute,
                              moe_stream_t comm);
+
+/*
+ * moe_forward_dbo_at -- moe_forward_dbo with the cut given: microbatch 0 =
+ * tokens [0, split), microbatch 1 = [split, T); split <= 0 or >= T runs the
+ * unsplit forward on `compute`.  Same schedule, streams and result (bitwise
+ * equal to moe_forward's for every split).  workspace >=
+ * moe_workspace_bytes(cfg, MOE_WS_FORWARD_DBO) bytes, which covers every cut.
+ */
+moe_status_t moe_forward_dbo_at(const moe_config_t* cfg, const moe_layer_tensors_t* tensors,
+                                void* workspace, size_t workspace_bytes, int32_t split,
+                                moe_stream_t compute, moe_stream_t comm);
+
+/*
+ * moe_dbo_plan_split -- whether and where to cut a batch of num_tokens tokens
+ * (pure host function).  [DBO] Running with DBO: a batch is split only when it
+ * has at least `decode_threshold` tokens (a batch of decodes only) or
+ * `prefill_threshold` tokens (a batch with at least one prefill; has_prefill
+ * != 0).  [DBO] UBatchRunner: the cut is moe_dbo_split_point's midpoint of the
+ * padded count, except that a uniform batch of multi-token queries (no
+ * prefill, uniform_query_len = q > 1 tokens per request, num_tokens a
+ * multiple of q) is cut on the request boundary nearest that midpoint (the
+ * lower of two equally near ones), so both halves stay uniform.  Returns the
+ * first token of microbatch 1, or 0 for "do not split" (below the threshold,
+ * or microbatch 1 would be empty); pass the result to moe_forward_dbo_at.
+ */
+int32_t moe_dbo_plan_split(int32_t num_tokens, int32_t has_prefill, int32_t decode_threshold,
+                           int32_t prefill_threshold, int32_t uniform_query_len);
 
 /*
  * Graph capture of a whole-layer call.  [DBO] Limitations and UBatchWrapper:

@@ -49,6 +49,8 @@ def lib():
             "oracle_forward": (_I, [_I] * 11 + [_P] * 13),
             "oracle_split_point": (_I, [_I, _I]),
             "oracle_forward_split": (None, [_I] * 11 + [_P] * 9 + [_I, _P]),
+            "oracle_forward_split_at": (None, [_I] * 11 + [_P] * 9 + [_I, _P]),
+            "oracle_dbo_split": (_I, [_I] * 6),
             "oracle_round_bf16": (None, [_LL, _P, _P]),
         }
         for name, (res, args) in sig.items():
@@ -185,6 +187,26 @@ def forward(cfg, inp: dict, x=None):
 
 def split_point(T: int, pad: int = 256) -> int:
     return int(lib().oracle_split_point(T, pad))
+
+
+def dbo_split(T: int, has_prefill: bool, decode_threshold: int, prefill_threshold: int,
+              query_len: int = 1, pad: int = 256) -> int:
+    return int(lib().oracle_dbo_split(T, int(has_prefill), decode_threshold, prefill_threshold,
+                                      query_len, pad))
+
+
+def forward_split_at(cfg, inp: dict, split: int) -> torch.Tensor:
+    x = inp["x"]
+    T, d = x.shape
+    out = torch.empty(T, d, dtype=torch.float64)
+    lib().oracle_forward_split_at(T, d, cfg.num_experts, cfg.top_k, cfg.intermediate,
+                                  cfg.expert_begin, cfg.expert_end, cfg.num_shared,
+                                  SCORE[cfg.score], int(cfg.renormalize), _dt(x), _ptr(x),
+                                  _ptr(inp["w_router"]), _ptr(inp["bias"]), _ptr(inp["w_gate"]),
+                                  _ptr(inp["w_up"]), _ptr(inp["w_down"]),
+                                  _ptr(inp.get("ws_gate")), _ptr(inp.get("ws_up")),
+                                  _ptr(inp.get("ws_down")), int(split), _ptr(out))
+    return out
 
 
 def forward_split(cfg, inp: dict, pad: int = 256) -> torch.Tensor:

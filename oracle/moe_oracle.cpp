@@ -20,8 +20,10 @@
 //   * combine: the weighted sum of the selected experts' outputs, written to a
 //     caller-owned tensor (same page, Introduction and Combine section);
 //   * the dual-microbatch split: the token range cut at the midpoint of the
-//     padded token count ("Dual Batch Overlap", UBatchRunner), each half run on
-//     its own and the results concatenated.
+//     padded token count, or on a request boundary for a uniform batch of
+//     multi-token queries, only above a token threshold ("Dual Batch
+//     Overlap", UBatchRunner and Running with DBO), each part run on its own
+//     and the results concatenated.
 //
 // Arithmetic: every value is read exactly (bf16 and fp32 inputs are exact in
 // fp64), every sum is accumulated in fp64 in ascending index order, compiled
@@ -323,25 +325,58 @@ int oracle_split_point(int T, int pad) {
   return t_pad / 2;
 }
 
-// Dual-microbatch forward: the layer run separately on the two token ranges,
-// outputs concatenated in token order.
+// Whether and where a batch of T tokens is split into two microbatches
+// ("Dual Batch Overlap": Running with DBO -- one token threshold for batches
+// of decodes only, another for batches that contain a prefill; UBatchRunner --
+// the cut is at the midpoint of the padded token count, except that a uniform
+// batch of multi-token queries is cut on a request boundary so that both
+// halves stay uniform).  q = tokens per query of a uniform decode batch (T a
+// multiple of q), or 1.  The request boundary taken is the one nearest the
+// midpoint, the lower one when two are equally near.  Returns the first token
+// of microbatch 1, or 0 when the batch is not split (below its threshold, or
+// microbatch 1 would be empty).
+int oracle_dbo_split(int T, int has_prefill, int decode_threshold, int prefill_threshold, int q,
+                     int pad) {
+  const int threshold = has_prefill ? prefill_threshold : decode_threshold;
+  if (T < threshold) return 0;
+  int split = oracle_split_point(T, pad);
+  if (!has_prefill && q > 1 && T % q == 0) {
+    const int below = split / q * q;
+    const int above = below + q;
+    split = (split - below <= above - split) ? below : above;
+  }
+  if (split <= 0 || split >= T) return 0;
+  return split;
+}
+
+// Dual-microbatch forward: the layer run separately on the token ranges
+// [0, split) and [split, T), outputs concatenated in token order (split <= 0
+// or >= T: one range).
+void oracle_forward_split_at(int T, int d, int E, int K, int I, int e_begin, int e_end,
+                             int n_shared, int score, int renorm, int dt, const void* x,
+                             const void* w_router, const float* bias, const void* w_gate,
+                             const void* w_up, const void* w_down, const void* ws_gate,
+                             const void* ws_up, const void* ws_down, int split, double* out) {
+  const int t0 = (split <= 0 || split >= T) ? T : split;
+  const size_t rb = (size_t)d * dtype_bytes(dt);
+  oracle_forward(t0, d, E, K, I, e_begin, e_end, n_shared, score, renorm, dt, x, w_router, bias,
+                 w_gate, w_up, w_down, ws_gate, ws_up, ws_down, out, nullptr, nullptr, nullptr);
+  if (t0 < T)
+    oracle_forward(T - t0, d, E, K, I, e_begin, e_end, n_shared, score, renorm, dt,
+                   static_cast<const char*>(x) + (size_t)t0 * rb, w_router, bias, w_gate, w_up,
+                   w_down, ws_gate, ws_up, ws_down, out + (size_t)t0 * d, nullptr, nullptr,
+                   nullptr);
+}
+
+// The midpoint split (an empty microbatch 1 runs nothing).
 void oracle_forward_split(int T, int d, int E, int K, int I, int e_begin, int e_end,
                           int n_shared, int score, int renorm, int dt, const void* x,
                           const void* w_router, const float* bias, const void* w_gate,
                           const void* w_up, const void* w_down, const void* ws_gate,
                           const void* ws_up, const void* ws_down, int pad, double* out) {
-  const int mid = oracle_split_point(T, pad);
-  const int t0 = std::min(mid, T);
-  const size_t rb = (size_t)d * dtype_bytes(dt);
-  if (t0 > 0)
-    oracle_forward(t0, d, E, K, I, e_begin, e_end, n_shared, score, renorm, dt, x, w_router,
-                   bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, out, nullptr, nullptr,
-                   nullptr);
-  if (T > mid)
-    oracle_forward(T - mid, d, E, K, I, e_begin, e_end, n_shared, score, renorm, dt,
-                   static_cast<const char*>(x) + (size_t)mid * rb, w_router, bias, w_gate,
-                   w_up, w_down, ws_gate, ws_up, ws_down, out + (size_t)mid * d, nullptr,
-                   nullptr, nullptr);
+  oracle_forward_split_at(T, d, E, K, I, e_begin, e_end, n_shared, score, renorm, dt, x,
+                          w_router, bias, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+                          oracle_split_point(T, pad), out);
 }
 
 // Round fp64 values to bf16 bit patterns, to nearest, ties to even, directly

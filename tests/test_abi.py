@@ -120,3 +120,24 @@ def test_graph_entry_points_reject_bad_arguments_on_host(lib):
                                          ctypes.byref(h)) == B.MOE_ERR_INVALID_ARGUMENT
     assert h.value is None  # nothing written on failure
 
+
+def test_dbo_plan_split_matches_the_oracle_rule(lib):
+    import oracle
+    for T in list(range(1, 300, 7)) + [511, 512, 600, 768, 1000, 4096, 8192, 8200]:
+        for prefill in (False, True):
+            for q in (1, 2, 3, 5, 8, 10, 64, 256):
+                for thr in (0, 300, 4096):
+                    got = B.dbo_plan_split(T, prefill, thr, thr + 7, q)
+                    assert got == oracle.dbo_split(T, prefill, thr, thr + 7, q), (T, prefill, q, thr)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "dsv2lite_decode", "dsv3_prefill_ep"])
+def test_dbo_workspace_covers_every_cut(lib, name):
+    cfg = W.CONFIGS[name]
+    for T in (2, 3, 97, 256, 700):
+        c = cfg.with_tokens(T)
+        bound = B.workspace_bytes(c, B.MOE_WS_FORWARD_DBO)
+        one = [0] + [B.workspace_bytes(cfg.with_tokens(n), B.MOE_WS_FORWARD) for n in range(1, T)]
+        need = max(one[s] + one[T - s] for s in range(1, T))
+        assert bound >= need and bound >= B.workspace_bytes(c, B.MOE_WS_FORWARD), (T, bound, need)
+

@@ -220,6 +220,26 @@ def test_dual_microbatch_equals_unsplit(name):
     assert_close(cfg, ref.cpu(), oracle.forward_split(cfg, inp), "dbo vs oracle split")
 
 
+def test_dual_microbatch_at_planned_and_lopsided_cuts():
+    # [DBO] UBatchRunner: a uniform batch of multi-token queries is cut on a
+    # request boundary; any cut gives the unsplit result bit for bit.
+    cfg, inp = inputs_for("dsv3_dbo_small")
+    T = cfg.num_tokens
+    cut = B.dbo_plan_split(T, False, 0, 0, 5)  # 120 requests of 5 tokens
+    assert cut == 385
+    L = MoELayer(cfg, inp)
+    ref = torch.empty_like(L.out)
+    L.forward(out=ref)
+    torch.cuda.synchronize()
+    comm = torch.cuda.Stream()
+    for split in (cut, 37, T - 1):
+        got = torch.empty_like(ref)
+        L.forward_dbo(comm=comm, out=got, split=split)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(got), bits(ref)), f"cut at {split}"
+    assert_close(cfg, got.cpu(), oracle.forward_split_at(cfg, inp, T - 1), "dbo cut vs oracle")
+
+
 # ------------------------------------------------------------------ graph capture
 
 @pytest.mark.parametrize("name", ["tiny_f32", "dsv2lite_small", "dsv3_small"])

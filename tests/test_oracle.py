@@ -466,3 +466,35 @@ def test_threads_do_not_change_results():
     finally:
         oracle.set_threads(n0)
     assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- dual-microbatch policy
+
+@pytest.mark.parametrize("T,prefill,dthr,pthr,q,want", [
+    (600, False, 0, 0, 1, 384),      # pad 600 -> 768, midpoint 384
+    (200, False, 0, 0, 1, 128),      # pad -> 256, midpoint 128
+    (100, False, 0, 0, 1, 0),        # midpoint 128 >= T: microbatch 1 empty, no split
+    (600, False, 601, 0, 1, 0),      # decode-only batch below its threshold
+    (600, False, 600, 10**6, 1, 384),  # exactly at the decode threshold
+    (600, True, 0, 601, 1, 0),       # a prefill batch uses the prefill threshold
+    (600, True, 10**6, 600, 1, 384),
+    (600, False, 0, 0, 5, 385),      # 120 requests of 5: boundaries 380, 385; 385 nearer
+    (600, False, 0, 0, 8, 384),      # 384 is itself a boundary
+    (600, False, 0, 0, 10, 380),     # boundaries 380 (4 away) and 390 (6 away)
+    (768, False, 0, 0, 256, 256),    # boundaries 256 and 512 equally near 384: the lower
+    (200, False, 0, 0, 40, 120),     # midpoint 128: boundaries 120 and 160
+    (130, False, 0, 0, 65, 0),       # nearest boundary 130 = T: microbatch 1 empty
+    (600, False, 0, 0, 7, 384),      # 600 is no multiple of 7: not a uniform batch
+    (600, True, 0, 0, 5, 384),       # a batch with a prefill is cut at the midpoint
+])
+def test_dbo_split_policy_worked_cases(T, prefill, dthr, pthr, q, want):
+    assert oracle.dbo_split(T, prefill, dthr, pthr, q) == want
+
+
+def test_forward_split_at_any_cut_equals_unsplit():
+    cfg = W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=37, hidden=64, intermediate=64)
+    inp = W.make_inputs(cfg, seed=12)
+    ref, _, _, _ = oracle.forward(cfg, inp)
+    for cut in (1, 5, 18, 36, 0, 37):
+        assert torch.equal(oracle.forward_split_at(cfg, inp, cut), ref), cut
+
