@@ -71,7 +71,8 @@ __device__ __forceinline__ void group_row_tiles(int rows, int BM, int& full, int
   q = qq == 4 ? 0 : qq;
 }
 
-constexpr int kMaxGroupChunks = MOE_MAX_EXPERTS / 64;  // groups per lane, at most
+// Groups per lane, at most (the local experts and the shared experts).
+constexpr int kMaxGroupChunks = (MOE_MAX_EXPERTS + MOE_MAX_SHARED + 63) / 64;
 
 constexpr int kBandRows = 16;  // row tiles per band
 
@@ -87,8 +88,10 @@ __host__ __device__ inline int tiles_per_xcd_bound(int row_tiles, int nN) {
 }
 
 // Maps this workgroup onto (group, row tile, column tile).  Groups are the
-// local experts (from the device offsets) or, with offsets == nullptr, a single
-// group of fixed_rows rows.  The row tiles form one list -- every group's
+// local experts (from the device offsets) followed by n_extra groups of
+// extra_rows rows each (the shared experts, numbered from n_groups on; their
+// rows count on from the last routed row), or, with offsets == nullptr, a
+// single group of fixed_rows rows.  The row tiles form one list -- every group's
 // full-height tiles in group order, then the short last tiles of 3, 2 and 1
 // quarters, each kind in group order -- cut into bands of kBandRows row tiles.  The 8 XCDs (workgroup ids go round-robin
 // over them, XCD x running ids x, x+8, ...) all work on the same band at a
@@ -102,24 +105,30 @@ __host__ __device__ inline int tiles_per_xcd_bound(int row_tiles, int nN) {
 // partly filled.
 // Returns false for surplus workgroups.
 __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, int n_groups,
-                                          int fixed_rows, int BM, int nN, Tile& out) {
+                                          int n_extra, int extra_rows, int fixed_rows, int BM,
+                                          int nN, Tile& out) {
   const int lane = threadIdx.x & 63;
+  const int n_all = n_groups + n_extra;
   // The offsets are read once, all at once: lane l holds group c*64 + l.
   int g0[kMaxGroupChunks], g1[kMaxGroupChunks];
   int n_full = 0, n_part[3] = {0, 0, 0};  // short last tiles of 3, 2, 1 quarters
   if (offsets != nullptr) {
+    const int extra0 = n_extra > 0 ? offsets[n_groups] : 0;
 #pragma unroll
     for (int c = 0; c < kMaxGroupChunks; ++c) {
       const int j = c * 64 + lane;
       g0[c] = g1[c] = 0;
-      if (c * 64 < n_groups && j < n_groups) {
+      if (c * 64 < n_all && j < n_groups) {
         g0[c] = offsets[j];
         g1[c] = offsets[j + 1];
+      } else if (c * 64 < n_all && j < n_all) {
+        g0[c] = extra0 + (j - n_groups) * extra_rows;
+        g1[c] = g0[c] + extra_rows;
       }
     }
 #pragma unroll
     for (int c = 0; c < kMaxGroupChunks; ++c) {
-      if (c * 64 >= n_groups) break;
+      if (c * 64 >= n_all) break;
       int f, q;
       group_row_tiles(g1[c] - g0[c], BM, f, q);
       n_full += __shfl(wave_inclusive_sum(f), 63, 64);
@@ -170,7 +179,7 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
     bool found = false;
 #pragma unroll
     for (int c = 0; c < kMaxGroupChunks; ++c) {
-      if (found || c * 64 >= n_groups) break;
+      if (found || c * 64 >= n_all) break;
       int f, q;
       group_row_tiles(g1[c] - g0[c], BM, f, q);
       const int cnt = is_short ? (q == want ? 1 : 0) : f;
@@ -506,24 +515,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     const uint16_t* __restrict__ B0,
     const uint16_t* __restrict__ B1, long long strideB_group, long long strideB_batch,
     uint16_t* __restrict__ C, int ldc, long long strideC_batch,
-    const int32_t* __restrict__ offsets, int n_groups, int fixed_rows, int N, int Kdim) {
+    const int32_t* __restrict__ offsets, int n_groups, int fixed_rows, int N, int Kdim,
+    const uint16_t* __restrict__ A2, long long strideA2, const uint16_t* __restrict__ B2_0,
+    const uint16_t* __restrict__ B2_1, long long strideB2, uint16_t* __restrict__ C2,
+    long long strideC2, int n_extra, int extra_rows) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[(kAStages + kBStages) * kSlotBytes];
 
   // Output columns per tile: EPI_STORE 256, EPI_SILU_GLU 128 (gate and up 128 each).
   constexpr int kNOut = EPI == EPI_SILU_GLU ? kBN / 2 : kBN;
   const int nN = (N + kNOut - 1) / kNOut;
   Tile tl;
-  if (!find_tile(offsets, n_groups, fixed_rows, kBM, nN, tl)) return;
+  if (!find_tile(offsets, n_groups, n_extra, extra_rows, fixed_rows, kBM, nN, tl)) return;
 
-  const long long zb = (long long)blockIdx.z * strideB_batch;
   TileArgs ta;
-  ta.A = A + (long long)blockIdx.z * strideA_batch;
   ta.lda = lda;
-  ta.bg = B0 + zb + (long long)tl.group * strideB_group;
-  ta.bu = EPI == EPI_SILU_GLU ? B1 + zb + (long long)tl.group * strideB_group : ta.bg;
-  ta.C = C + (long long)blockIdx.z * strideC_batch;
   ta.ldc = ldc;
-  ta.row0 = tl.row0;
+  if (tl.group < n_groups || offsets == nullptr) {
+    const long long zb = (long long)blockIdx.z * strideB_batch;
+    ta.A = A + (long long)blockIdx.z * strideA_batch;
+    ta.bg = B0 + zb + (long long)tl.group * strideB_group;
+    ta.bu = EPI == EPI_SILU_GLU ? B1 + zb + (long long)tl.group * strideB_group : ta.bg;
+    ta.C = C + (long long)blockIdx.z * strideC_batch;
+    ta.row0 = tl.row0;
+  } else {  // an extra group: its own operands, rows from 0
+    const int e = tl.group - n_groups;
+    ta.A = A2 + (long long)e * strideA2;
+    ta.bg = B2_0 + (long long)e * strideB2;
+    ta.bu = EPI == EPI_SILU_GLU ? B2_1 + (long long)e * strideB2 : ta.bg;
+    ta.C = C2 + (long long)e * strideC2;
+    ta.row0 = 0;
+  }
   ta.rows = tl.rows;
   ta.m0 = tl.m_tile * kBM;
   ta.n0 = tl.n_tile * kNOut;
@@ -555,22 +576,37 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
     const float* __restrict__ A, int lda, long long strideA_batch, const float* __restrict__ B0,
     const float* __restrict__ B1, long long strideB_group, long long strideB_batch,
     float* __restrict__ C, int ldc, long long strideC_batch, const int32_t* __restrict__ offsets,
-    int n_groups, int fixed_rows, int N, int Kdim) {
+    int n_groups, int fixed_rows, int N, int Kdim, const float* __restrict__ A2,
+    long long strideA2, const float* __restrict__ B2_0, const float* __restrict__ B2_1,
+    long long strideB2, float* __restrict__ C2, long long strideC2, int n_extra,
+    int extra_rows) {
   constexpr bool kGlu = EPI == EPI_SILU_GLU;
   __shared__ __attribute__((aligned(16))) float sa[2][kFK][kFM + 4];
   __shared__ __attribute__((aligned(16))) float sg[2][kFK][kFN + 4];
   __shared__ __attribute__((aligned(16))) float su[kGlu ? 2 : 1][kFK][kFN + 4];
   const int nN = (N + kFN - 1) / kFN;
   Tile tl;
-  if (!find_tile(offsets, n_groups, fixed_rows, kFM, nN, tl)) return;
+  if (!find_tile(offsets, n_groups, n_extra, extra_rows, fixed_rows, kFM, nN, tl)) return;
   const int tid = threadIdx.x;
   const int tx = tid & 15, ty = tid >> 4;
   const int m0 = tl.m_tile * kFM, n0 = tl.n_tile * kFN;
-  const long long zb = (long long)blockIdx.z * strideB_batch;
-  A += (long long)blockIdx.z * strideA_batch;
-  const float* bg = B0 + zb + (long long)tl.group * strideB_group;
-  const float* bu = kGlu ? B1 + zb + (long long)tl.group * strideB_group : bg;
-  float* Cz = C + (long long)blockIdx.z * strideC_batch;
+  const float* bg;
+  const float* bu;
+  float* Cz;
+  if (tl.group < n_groups || offsets == nullptr) {
+    const long long zb = (long long)blockIdx.z * strideB_batch;
+    A += (long long)blockIdx.z * strideA_batch;
+    bg = B0 + zb + (long long)tl.group * strideB_group;
+    bu = kGlu ? B1 + zb + (long long)tl.group * strideB_group : bg;
+    Cz = C + (long long)blockIdx.z * strideC_batch;
+  } else {  // an extra group: its own operands, rows from 0
+    const int e = tl.group - n_groups;
+    A = A2 + (long long)e * strideA2;
+    bg = B2_0 + (long long)e * strideB2;
+    bu = kGlu ? B2_1 + (long long)e * strideB2 : bg;
+    Cz = C2 + (long long)e * strideC2;
+    tl.row0 = 0;
+  }
 
   // Staging: thread t loads 4 consecutive k (k4 = 4 (t % 8)) of rows t/8 and
   // t/8 + 32 of each operand; rows past the tile's last one repeat it, k past
@@ -657,6 +693,10 @@ struct GemmArgs {
   void* C; int ldc; long long strideC_batch;
   const int32_t* offsets; int n_groups; int fixed_rows; int max_row_tiles_bound;
   int N; int Kdim; int batch;
+  // Extra groups after the offset groups (the shared experts): operand bases
+  // and strides per group, and their common row count.
+  const void* A2; long long strideA2; const void* B2_0; const void* B2_1; long long strideB2;
+  void* C2; long long strideC2; int n_extra; int extra_rows;
 };
 
 // Workgroups for an upper bound of row tiles: 8 XCDs x the most tiles one
@@ -675,7 +715,11 @@ hipError_t run_gemm(int dtype, const GemmArgs& g, hipStream_t s) {
                        static_cast<const uint16_t*>(g.A), g.lda, g.strideA_batch,
                        static_cast<const uint16_t*>(g.B0), static_cast<const uint16_t*>(g.B1),
                        g.strideB_group, g.strideB_batch, static_cast<uint16_t*>(g.C), g.ldc,
-                       g.strideC_batch, g.offsets, g.n_groups, g.fixed_rows, g.N, g.Kdim);
+                       g.strideC_batch, g.offsets, g.n_groups, g.fixed_rows, g.N, g.Kdim,
+                       static_cast<const uint16_t*>(g.A2), g.strideA2,
+                       static_cast<const uint16_t*>(g.B2_0), static_cast<const uint16_t*>(g.B2_1),
+                       g.strideB2, static_cast<uint16_t*>(g.C2), g.strideC2, g.n_extra,
+                       g.extra_rows);
   } else {
     const int rt = g.offsets ? g.max_row_tiles_bound : ceil_div(g.fixed_rows, kFM);
     const dim3 grid(grid_for(rt, ceil_div(g.N, kFN)), 1, g.batch);
@@ -684,7 +728,9 @@ hipError_t run_gemm(int dtype, const GemmArgs& g, hipStream_t s) {
                        static_cast<const float*>(g.B0),
                        static_cast<const float*>(g.B1), g.strideB_group, g.strideB_batch,
                        static_cast<float*>(g.C), g.ldc, g.strideC_batch, g.offsets, g.n_groups,
-                       g.fixed_rows, g.N, g.Kdim);
+                       g.fixed_rows, g.N, g.Kdim, static_cast<const float*>(g.A2), g.strideA2,
+                       static_cast<const float*>(g.B2_0), static_cast<const float*>(g.B2_1),
+                       g.strideB2, static_cast<float*>(g.C2), g.strideC2, g.n_extra, g.extra_rows);
   }
   return hipGetLastError();
 }
@@ -711,24 +757,21 @@ hipError_t launch_expert_mlp(const moe_config_t& c, const void* x_sorted, const 
   void* h = ws;
   void* h_sh = ws + align_up((size_t)T * K * I * elem, 256);
   const int bm = c.dtype == MOE_BF16 ? kBM : kFM;
-  const int row_bound = ceil_div(T * K, bm) + n_loc;
+  const int S = c.num_shared;
+  // The shared experts run in the same launches as the routed ones, as extra
+  // groups of T rows, so their tiles fill the routed launches' last rounds.
+  const int row_bound = ceil_div(T * K, bm) + n_loc + S * ceil_div(T, bm);
 
   GemmArgs up{x_sorted, d, 0, w_gate, w_up, (long long)I * d, 0, h, I, 0,
-              offsets, n_loc, 0, row_bound, I, d, 1};
+              offsets, n_loc, 0, row_bound, I, d, 1,
+              x, 0, ws_gate, ws_up, (long long)I * d, h_sh, (long long)T * I, S, T};
   hipError_t err = run_gemm<EPI_SILU_GLU>(c.dtype, up, s);
   if (err != hipSuccess) return err;
   GemmArgs down{h, I, 0, w_down, nullptr, (long long)d * I, 0, y_sorted, d, 0,
-                offsets, n_loc, 0, row_bound, d, I, 1};
-  err = run_gemm<EPI_STORE>(c.dtype, down, s);
-  if (err != hipSuccess || c.num_shared == 0) return err;
-
-  GemmArgs sup{x, d, 0, ws_gate, ws_up, 0, (long long)I * d, h_sh, I, (long long)T * I,
-               nullptr, 1, T, 0, I, d, c.num_shared};
-  err = run_gemm<EPI_SILU_GLU>(c.dtype, sup, s);
-  if (err != hipSuccess) return err;
-  GemmArgs sdown{h_sh, I, (long long)T * I, ws_down, nullptr, 0, (long long)d * I, y_shared, d, (long long)T * d,
-                 nullptr, 1, T, 0, d, I, c.num_shared};
-  return run_gemm<EPI_STORE>(c.dtype, sdown, s);
+                offsets, n_loc, 0, row_bound, d, I, 1,
+                h_sh, (long long)T * I, ws_down, nullptr, (long long)d * I, y_shared,
+                (long long)T * d, S, T};
+  return run_gemm<EPI_STORE>(c.dtype, down, s);
 }
 
 }  // namespace moe
