@@ -565,12 +565,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
 
 // ------------------------------------------------------------------ fp32 VALU GEMM
 
-constexpr int kFM = 64, kFN = 64, kFK = 32;
+constexpr int kFM = 64, kFN = 64, kFK = 64;
+constexpr int kFKT = kFK / 4;            // staging threads along k per row (4 k each)
+constexpr int kFRowsPass = 256 / kFKT;   // rows staged per pass
+constexpr int kFPass = kFM / kFRowsPass; // passes per operand tile
+static_assert(kFM == kFN && kFPass * kFRowsPass == kFM, "fp32 staging shape");
 
 // fp32 layers: 64 x 64 output tiles, 256 threads with 4 x 4 outputs each (and
-// the matching up outputs in the gate/up pass), 32-deep k-steps through two
+// the matching up outputs in the gate/up pass), 64-deep k-steps through two
 // LDS buffers: the next step's operands are loaded (16-byte loads) while the
-// current one is multiplied.  k runs in ascending order for every output.
+// current one is multiplied (small layers are bound by the round trip of
+// each step's loads, so the steps are deep).  k runs in ascending order for
+// every output.
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(
     const float* __restrict__ A, int lda, long long strideA_batch, const float* __restrict__ B0,
@@ -608,28 +614,28 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
     tl.row0 = 0;
   }
 
-  // Staging: thread t loads 4 consecutive k (k4 = 4 (t % 8)) of rows t/8 and
-  // t/8 + 32 of each operand; rows past the tile's last one repeat it, k past
-  // Kdim reads as zero (Kdim is a multiple of 16, so a group of 4 is wholly
-  // inside or wholly past).
-  const int k4 = (tid & 7) * 4;
-  const float* pa[2];
-  const float* pg[2];
-  const float* pu[2];
-  int rr[2];
+  // Staging: thread t loads 4 consecutive k (k4 = 4 (t % kFKT)) of rows
+  // t/kFKT + kFRowsPass*j of each operand; rows past the tile's last one repeat
+  // it, k past Kdim reads as zero (Kdim is a multiple of 16, so a group of 4 is
+  // wholly inside or wholly past).
+  const int k4 = (tid % kFKT) * 4;
+  const float* pa[kFPass];
+  const float* pg[kFPass];
+  const float* pu[kFPass];
+  int rr[kFPass];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    rr[j] = (tid >> 3) + 32 * j;
+  for (int j = 0; j < kFPass; ++j) {
+    rr[j] = tid / kFKT + kFRowsPass * j;
     pa[j] = A + (long long)(tl.row0 + min(m0 + rr[j], tl.rows - 1)) * lda + k4;
     const int bn = min(n0 + rr[j], N - 1);
     pg[j] = bg + (long long)bn * Kdim + k4;
     pu[j] = bu + (long long)bn * Kdim + k4;
   }
-  f32x4 ra[2], rg[2], ru[2];
+  f32x4 ra[kFPass], rg[kFPass], ru[kFPass];
   auto load = [&](int k0) {
     const bool in = k0 + k4 < Kdim;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < kFPass; ++j) {
       ra[j] = in ? *reinterpret_cast<const f32x4*>(pa[j] + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
       rg[j] = in ? *reinterpret_cast<const f32x4*>(pg[j] + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
       if (kGlu) ru[j] = in ? *reinterpret_cast<const f32x4*>(pu[j] + k0) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -637,7 +643,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < kFPass; ++j)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         sa[buf][k4 + c][rr[j]] = ra[j][c];

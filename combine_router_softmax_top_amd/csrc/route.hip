@@ -11,7 +11,7 @@
 // 64 tokens x up to 256 experts x one slice of the reduction dimension, its
 // operands streamed into LDS four chunks ahead, then a selection kernel that
 // adds the slices in a fixed order (deterministic).
-// fp32: each wave takes 4 tokens and reduces every dot product across its 64
+// fp32: each wave takes one token and reduces every dot product across its 64
 // lanes with a butterfly.
 // Selection: one wave per token, E/64 candidates per lane in registers, K
 // rounds of a butterfly arg-max ordered by (logit desc, expert id asc).
@@ -22,7 +22,7 @@
 namespace moe {
 namespace {
 
-constexpr int kTokTile = 16;
+constexpr int kTokTile = 4;  // fp32 router: tokens per workgroup, one per wave
 
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -361,9 +361,9 @@ __global__ __launch_bounds__(256) void route_f32_kernel(
     float* __restrict__ weights, float* __restrict__ logits) {
   constexpr int kGrp = 8;  // experts reduced together (independent butterflies)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int tt = wave * 4; tt < wave * 4 + 4; ++tt) {
-    const int t = blockIdx.x * kTokTile + tt;
-    if (t >= T) break;
+  {
+    const int t = blockIdx.x * kTokTile + wave;
+    if (t >= T) return;
     float v[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i] = -INFINITY;
