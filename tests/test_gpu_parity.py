@@ -308,6 +308,8 @@ EDGE = [
                                                               expert_end=400)),
     ("fp32_ragged", W.CONFIGS["tiny_f32"].replace(num_tokens=77, hidden=96, intermediate=80,
                                                   num_experts=5, top_k=3, expert_end=5)),
+    # fp32 with shared experts: extra groups in the fp32 expert launches
+    ("fp32_shared", W.CONFIGS["tiny_f32"].replace(num_tokens=70, num_shared=2, renormalize=False)),
     ("bf16_unaligned_tiles", W.CONFIGS["mixtral_bf16"].replace(num_tokens=515, hidden=320,
                                                                intermediate=448)),
     # the Zipf bias keeps every token off the least popular experts: no local
