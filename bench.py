@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true",
                    help="skip the graph-replay timing of the whole layer")
+    p.add_argument("--no-cold", action="store_true",
+                   help="skip the cold-cache dispatch/combine timing")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -324,9 +326,39 @@ def main():
     }
     if not args.no_graph:
         result["graph_replay"] = graph_replay(args, layer, stream, torch)
+    if not args.no_cold:
+        result["dispatch_combine_cold"] = cold_dispatch_combine(layer, stream, torch, alg)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def cold_dispatch_combine(layer, stream, torch, alg, iters: int = 10) -> dict:
+    """Dispatch and combine with cold caches: 1 GiB is written right before each
+    of them, which evicts L2 and the 256 MB Infinity Cache, so their reads come
+    from HBM (the layer's own sequence leaves part of y_sorted in the cache)."""
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters)]
+    with torch.cuda.stream(stream):
+        for i in range(iters):
+            flush.fill_(i & 255)
+            ev[i][0].record(stream)
+            layer.dispatch(stream)
+            ev[i][1].record(stream)
+            layer.expert_mlp(stream)
+            flush.fill_((i + 1) & 255)
+            ev[i][2].record(stream)
+            layer.combine(stream)
+            ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    d = sum(e[0].elapsed_time(e[1]) for e in ev) / iters
+    c = sum(e[2].elapsed_time(e[3]) for e in ev) / iters
+    nbytes = alg["dispatch"] + alg["combine"]
+    gbs = nbytes / ((d + c) * 1e-3) / 1e9
+    del flush
+    return {"dispatch_us": d * 1e3, "combine_us": c * 1e3, "GB_per_s": gbs,
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+            "how": "1 GiB written before each stage (L2 and Infinity Cache evicted), HIP events"}
 
 
 def graph_replay(args, layer, stream, torch) -> dict:
