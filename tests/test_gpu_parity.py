@@ -240,6 +240,35 @@ def test_dual_microbatch_at_planned_and_lopsided_cuts():
     assert_close(cfg, got.cpu(), oracle.forward_split_at(cfg, inp, T - 1), "dbo cut vs oracle")
 
 
+def _random_layer(seed: int):
+    """A small seeded random layer: every routing option and ragged sizes."""
+    g = torch.Generator().manual_seed(10_000 + seed)
+    ri = lambda lo, hi: int(torch.randint(lo, hi + 1, (1,), generator=g))
+    bf16 = seed % 3 != 0
+    q = 64 if bf16 else 16
+    E = ri(1, 40)
+    K = ri(1, min(E, 8))
+    eb = ri(0, E - 1)
+    ee = ri(eb + 1, E)
+    sig = seed % 4 == 1
+    return W.CONFIGS["mixtral_bf16" if bf16 else "tiny_f32"].replace(
+        num_tokens=ri(1, 150), hidden=q * ri(1, 4), intermediate=q * ri(1, 4), num_experts=E,
+        top_k=K, expert_begin=eb, expert_end=ee, num_shared=ri(0, 2) if seed % 2 else 0,
+        score="sigmoid" if sig else "softmax", renormalize=bool(seed % 5 != 2),
+        zipf_s=1.1 if sig else None, router_init="normal")
+
+
+@pytest.mark.parametrize("seed", range(14))
+def test_random_small_layers(seed):
+    cfg = _random_layer(seed)
+    inp = W.make_inputs(cfg, seed=seed)
+    L = run_stages(cfg, inp)
+    check_route(cfg, inp, L)
+    check_dispatch(cfg, inp, L)
+    check_mlp(cfg, inp, L)
+    check_combine(cfg, L)
+
+
 # ------------------------------------------------------------------ graph capture
 
 @pytest.mark.parametrize("name", ["tiny_f32", "dsv2lite_small", "dsv3_small"])
