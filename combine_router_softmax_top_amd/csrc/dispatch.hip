@@ -8,7 +8,8 @@
 // pages' receive side fills slots in arbitrary order; here the order is fixed
 // (expert ascending, then token ascending), so the layout has one answer.
 //
-// Three kernels, no host synchronisation and no memset:
+// Two kernels (three for very large histograms), no host synchronisation and
+// no memset:
 //  1. count: one workgroup per chunk of 1024 assignments (t*K + k in
 //     ascending order, one per thread).  Each local expert gets a 1024-bit
 //     mask over the chunk's assignment slots in LDS (64-bit LDS atomic OR);
@@ -17,13 +18,16 @@
 //     ranks in (t, k) order, like any other pair of assignments.  Every
 //     expert's chunk count goes to a histogram row (LDS atomic add); invalid
 //     ids are tallied into an extra column.
-//  2. scan: one workgroup turns the chunk histograms into global counts,
-//     exclusive offsets over the local experts and per-(chunk, expert) row
-//     bases.
-//  3. scatter: one wave per token; the token row is read once (16-byte
-//     loads, held in registers) and written to each of its local rows; the
-//     row maps are written alongside.  Tokens with no local expert are not
-//     read at all.
+//  2. scatter: one wave per token, four per workgroup.  Each workgroup first
+//     turns the local columns of the chunk histograms into expert offsets and
+//     the row bases of its own chunks (inline_scan; the lowest workgroups
+//     also write the global counts, the offsets and n_invalid); the token
+//     row's loads are already in flight meanwhile.  The row (16-byte loads,
+//     held in registers) is then written to each of its local rows, with the
+//     row maps.  Tokens with no local expert are not read at all.
+//  When the local chunk counts do not fit a scatter workgroup's LDS, a
+//  one-workgroup scan kernel computes the offsets and per-(chunk, expert)
+//  row bases first, and the scatter reads them.
 #include <type_traits>
 
 #include "moe_internal.h"

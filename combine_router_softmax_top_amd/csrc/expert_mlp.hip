@@ -23,17 +23,19 @@
 //     conflicts;
 //   * ragged groups: the tile list (expert, row tile, column tile) is derived
 //     on the device from the expert offsets; the grid is the host's upper
-//     bound and surplus workgroups exit at once (no host synchronisation);
+//     bound and surplus workgroups exit at once (no host synchronisation); the
+//     shared experts join the same two launches as extra groups of T rows;
 //   * the row tiles of all experts (full-height first, then the shorter last
-//     tiles, tallest first) form bands of 16; the 8 XCDs work on the same band at
-//     once as a 2 x 4 grid (8 rows x a quarter of the columns each), so a
+//     tiles, tallest first) form bands of 16; the 8 XCDs work on the same band
+//     at once as a 2 x 4 grid (8 rows x a quarter of the columns each), so a
 //     weight tile streams from memory at most twice per band and an
 //     activation tile is shared by 4 XCDs, the repeats served by the
 //     Infinity Cache;
 //   * the k order of every output is fixed (64-wide tiles ascending, MFMA
 //     k-blocks of 16 ascending) and independent of the row tiling, so a row's
 //     result does not depend on which other rows share its call.
-// fp32 path: a plain LDS-tiled VALU kernel (64x64 tiles, 4x4 per thread).
+// fp32 path: a plain LDS-tiled VALU kernel (64x64 tiles, 4x4 per thread,
+// 64-deep k-steps), on the same tile list.
 #include <math.h>
 
 #include "moe_internal.h"
