@@ -101,11 +101,15 @@ def bench_dbo(args, cfg, layer, torch) -> dict:
 
 
 def source_digest() -> str:
-    h = hashlib.sha256()
+    """Digest of the expert-MLP kernel source's code: // comments and blank
+    lines are left out, so a change to the comments alone keeps a traffic
+    record valid and any change to the code voids it."""
+    import re
     src = os.path.join(_ROOT, "combine_router_softmax_top_amd", "csrc", "expert_mlp.hip")
-    with open(src, "rb") as f:
-        h.update(f.read())
-    return h.hexdigest()[:16]
+    with open(src) as f:
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in f.read().splitlines()]
+    code = "\n".join(ln for ln in lines if ln.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def algorithmic(cfg, n_loc: int, t_touch: int) -> dict:
