@@ -52,6 +52,10 @@ def lib():
             "oracle_forward_split_at": (None, [_I] * 11 + [_P] * 9 + [_I, _P]),
             "oracle_dbo_split": (_I, [_I] * 6),
             "oracle_round_bf16": (None, [_LL, _P, _P]),
+            "oracle_e4m3_encode": (ctypes.c_uint8, [ctypes.c_double]),
+            "oracle_e4m3_decode": (ctypes.c_double, [ctypes.c_uint8]),
+            "oracle_mxfp8_quantize": (None, [_I, _I, _I, _P, _LL, _P, _P]),
+            "oracle_mxfp8_dequantize": (None, [_I, _I, _P, _P, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -219,6 +223,34 @@ def forward_split(cfg, inp: dict, pad: int = 256) -> torch.Tensor:
                                _ptr(inp["w_router"]), _ptr(inp["bias"]), _ptr(inp["w_gate"]),
                                _ptr(inp["w_up"]), _ptr(inp["w_down"]), _ptr(inp.get("ws_gate")),
                                _ptr(inp.get("ws_up")), _ptr(inp.get("ws_down")), pad, _ptr(out))
+    return out
+
+
+def e4m3_encode(v: float) -> int:
+    return int(lib().oracle_e4m3_encode(float(v)))
+
+
+def e4m3_decode(code: int) -> float:
+    return float(lib().oracle_e4m3_decode(int(code)))
+
+
+def mxfp8_quantize(x: torch.Tensor):
+    """Rows of x (bf16 / fp32 / fp64) -> (E4M3 codes [rows, cols] uint8,
+    scale bytes [rows, cols/32] uint8)."""
+    x = x.contiguous()
+    rows, cols = x.shape
+    assert cols % 32 == 0
+    codes = torch.empty(rows, cols, dtype=torch.uint8)
+    scales = torch.empty(rows, cols // 32, dtype=torch.uint8)
+    lib().oracle_mxfp8_quantize(rows, cols, _dt(x), _ptr(x), cols, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def mxfp8_dequantize(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    codes, scales = codes.contiguous(), scales.contiguous()
+    rows, cols = codes.shape
+    out = torch.empty(rows, cols, dtype=torch.float64)
+    lib().oracle_mxfp8_dequantize(rows, cols, _ptr(codes), _ptr(scales), _ptr(out))
     return out
 
 

@@ -379,6 +379,81 @@ void oracle_forward_split(int T, int d, int E, int K, int I, int e_begin, int e_
                           oracle_split_point(T, pad), out);
 }
 
+// ---------------------------------------------------------------- MX-FP8 blocks
+// Block-scaled 8-bit payload ("Efficient and portable mixture-of-experts
+// communication", Dispatch: tokens travel with block scaling factors; the
+// pages fix no format).  Reading: OCP MX-FP8 -- every 32 consecutive elements
+// along a row share one power-of-two scale 2^s stored as the biased byte
+// s + 127 (E8M0), and each element is an E4M3 code (1 sign, 4 exponent bits
+// with bias 7, 3 mantissa bits; largest magnitude 448, subnormals down to
+// 2^-9, no infinities).  s = floor(log2(max |x|)) - 8, kept within
+// [-127, 127] (an all-zero block takes -127), so that the block's largest
+// element lands in [256, 512); elements are x / 2^s clamped to +-448 and
+// rounded to the nearest E4M3 value, ties to even.
+
+// E4M3 code of a value already clamped to [-448, 448].
+uint8_t oracle_e4m3_encode(double v) {
+  const int sign = std::signbit(v) ? 0x80 : 0;
+  const double a = std::fabs(v);
+  if (a == 0.0) return (uint8_t)sign;
+  // Spacing of E4M3 values around a: 2^-9 below 2^-6 (subnormals), else
+  // 2^(e-3) in the binade [2^e, 2^(e+1)).
+  int e;
+  std::frexp(a, &e);  // a = f * 2^e, f in [0.5, 1): the binade starts at 2^(e-1)
+  const int binade = e - 1;
+  const double q = binade < -6 ? std::ldexp(1.0, -9) : std::ldexp(1.0, binade - 3);
+  const double r = std::nearbyint(a / q) * q;  // round to nearest, ties to even
+  if (r == 0.0) return (uint8_t)sign;
+  if (r < std::ldexp(1.0, -6)) return (uint8_t)(sign | (int)(r / std::ldexp(1.0, -9)));
+  int re;
+  const double rf = std::frexp(r, &re);  // r = rf * 2^re, rf in [0.5, 1)
+  const int exp_field = re - 1 + 7;
+  const int mant = (int)((rf * 2.0 - 1.0) * 8.0);
+  return (uint8_t)(sign | (exp_field << 3) | mant);
+}
+
+double oracle_e4m3_decode(uint8_t c) {
+  const double sign = (c & 0x80) ? -1.0 : 1.0;
+  const int ef = (c >> 3) & 0xf, m = c & 7;
+  if (ef == 0) return sign * std::ldexp((double)m, -9);
+  return sign * std::ldexp(1.0 + m / 8.0, ef - 7);
+}
+
+// rows x cols values (dtype dt, row pitch ld elements; cols a multiple of 32)
+// -> codes [rows, cols] and scale bytes [rows, cols/32].
+void oracle_mxfp8_quantize(int rows, int cols, int dt, const void* in, long long ld,
+                           uint8_t* codes, uint8_t* scales) {
+  const int nb = cols / 32;
+  for (int r = 0; r < rows; ++r) {
+    for (int b = 0; b < nb; ++b) {
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i)
+        amax = std::max(amax, std::fabs(value_at(in, (size_t)r * ld + b * 32 + i, dt)));
+      int s = -127;
+      if (amax > 0.0) {
+        int e;
+        std::frexp(amax, &e);  // floor(log2(amax)) = e - 1
+        s = std::min(127, std::max(-127, e - 1 - 8));
+      }
+      scales[(size_t)r * nb + b] = (uint8_t)(s + 127);
+      for (int i = 0; i < 32; ++i) {
+        const double v = value_at(in, (size_t)r * ld + b * 32 + i, dt) / std::ldexp(1.0, s);
+        codes[(size_t)r * cols + b * 32 + i] = oracle_e4m3_encode(std::min(448.0, std::max(-448.0, v)));
+      }
+    }
+  }
+}
+
+// The values an MX-FP8 block encodes: code value * 2^(scale - 127), in fp64.
+void oracle_mxfp8_dequantize(int rows, int cols, const uint8_t* codes, const uint8_t* scales,
+                             double* out) {
+  const int nb = cols / 32;
+  for (int r = 0; r < rows; ++r)
+    for (int c = 0; c < cols; ++c)
+      out[(size_t)r * cols + c] = oracle_e4m3_decode(codes[(size_t)r * cols + c]) *
+                                  std::ldexp(1.0, (int)scales[(size_t)r * nb + c / 32] - 127);
+}
+
 // Round fp64 values to bf16 bit patterns, to nearest, ties to even, directly
 // from fp64 (no intermediate fp32 rounding).  Finite inputs within the bf16
 // range only.

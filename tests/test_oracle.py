@@ -498,3 +498,58 @@ def test_forward_split_at_any_cut_equals_unsplit():
     for cut in (1, 5, 18, 36, 0, 37):
         assert torch.equal(oracle.forward_split_at(cfg, inp, cut), ref), cut
 
+
+
+# ---------------------------------------------------------------- MX-FP8 blocks
+
+def test_e4m3_encode_matches_torch_on_every_bf16_value_in_range():
+    v = (torch.arange(65536, dtype=torch.int32) << 16).view(torch.float32)
+    v = v[torch.isfinite(v) & (v.abs() <= 464)]
+    ref = v.to(torch.float8_e4m3fn).view(torch.uint8)
+    got = torch.tensor([oracle.e4m3_encode(float(x)) for x in v.tolist()], dtype=torch.uint8)
+    assert torch.equal(got, ref)
+
+
+def test_e4m3_codes_round_trip():
+    for c in range(256):
+        if c & 0x7F == 0x7F:  # NaN codes
+            continue
+        assert oracle.e4m3_encode(oracle.e4m3_decode(c)) == c
+    assert oracle.e4m3_decode(0x7E) == 448.0 and oracle.e4m3_decode(0x01) == 2.0 ** -9
+
+
+def test_mxfp8_scale_rule_worked_cases():
+    def q(vals):
+        x = torch.tensor([vals + [0.0] * (32 - len(vals))], dtype=torch.float64)
+        codes, scales = oracle.mxfp8_quantize(x)
+        return codes[0].tolist(), int(scales[0, 0])
+    codes, sc = q([1.0, -0.5])
+    assert sc == 127 - 8 and codes[:2] == [0x78, 0xF0]     # 1 -> 2^8, -0.5 -> -2^7
+    codes, sc = q([448.0, 3.0])
+    assert sc == 127 and codes[:2] == [0x7E, 0x44]         # 3 = 1.5 * 2^1: exponent field 8, mantissa 4
+    codes, sc = q([500.0, -500.0])
+    assert sc == 127 and codes[:2] == [0x7E, 0xFE]         # clamped to +-448
+    codes, sc = q([0.0])
+    assert sc == 0 and codes == [0] * 32                   # all-zero block
+    codes, sc = q([2.0 ** -130])
+    assert sc == 0 and codes[0] == 0x20                    # s clamped to -127: 2^-3
+
+
+def test_mxfp8_dequantized_error_bound():
+    g = torch.Generator().manual_seed(3)
+    x = (torch.randn(16, 256, generator=g) * torch.exp(torch.randn(16, 1, generator=g) * 3))
+    x = x.to(torch.bfloat16)
+    codes, scales = oracle.mxfp8_quantize(x)
+    deq = oracle.mxfp8_dequantize(codes, scales)
+    xd = x.double()
+    s = torch.pow(2.0, scales.double() - 127).repeat_interleave(32, 1)
+    y = (xd / s).abs()
+    # E4M3 spacing at |y|: 2^-9 below 2^-6, else 2^(floor(log2 y) - 3)
+    spacing = torch.where(y < 2.0 ** -6, torch.full_like(y, 2.0 ** -9),
+                          torch.pow(2.0, torch.floor(torch.log2(y.clamp_min(1e-300))) - 3))
+    inside = y <= 448
+    assert bool(((deq - xd).abs()[inside] <= (spacing * s / 2)[inside]).all())
+    assert bool((deq[~inside].abs() == (448 * s)[~inside]).all())
+    # the largest element of every block lands in [256, 512) before clamping
+    ymax = y.view(16, -1, 32).amax(-1)
+    assert bool(((ymax >= 256) & (ymax < 512)).all())
