@@ -27,7 +27,7 @@ EXPORTED = ["moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_f
             "moe_forward_dbo", "moe_forward_dbo_at", "moe_graph_capture_forward",
             "moe_graph_capture_forward_dbo", "moe_graph_launch", "moe_graph_destroy",
             "moe_workspace_bytes", "moe_dbo_split_point", "moe_dbo_plan_split",
-            "moe_status_string"]
+            "moe_quantize_mxfp8", "moe_status_string"]
 
 
 class MoEError(RuntimeError):
@@ -75,6 +75,7 @@ def lib() -> ctypes.CDLL:
             "moe_graph_capture_forward_dbo": [C, LT, P, SZ, I32, ctypes.POINTER(P)],
             "moe_graph_launch": [P, P],
             "moe_graph_destroy": [P],
+            "moe_quantize_mxfp8": [I32, I32, I32, P, ctypes.c_int64, P, P, P],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -311,6 +312,24 @@ def dbo_plan_split(num_tokens: int, has_prefill: bool, decode_threshold: int,
                    prefill_threshold: int, uniform_query_len: int = 1) -> int:
     return int(lib().moe_dbo_plan_split(int(num_tokens), int(has_prefill), int(decode_threshold),
                                         int(prefill_threshold), int(uniform_query_len)))
+
+
+def moe_quantize_mxfp8(x, codes, scales, stream=None):
+    """MX-FP8 encoding of the rows of x ([rows, cols] bf16 or fp32, unit column
+    stride; the row stride may be larger) into codes ([rows, cols] uint8, E4M3)
+    and scales ([rows, cols // 32] uint8, E8M0)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.device.type != "cuda":
+        raise ValueError("x: expected a 2-D device tensor")
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"x: dtype {x.dtype}, expected bfloat16 or float32")
+    if x.shape[0] > 1 and x.stride(1) != 1:
+        raise ValueError("x: columns must be contiguous")
+    rows, cols = x.shape
+    ld = x.stride(0) if rows > 1 else cols
+    _check("moe_quantize_mxfp8", lib().moe_quantize_mxfp8(
+        rows, cols, MOE_BF16 if x.dtype == torch.bfloat16 else MOE_F32, x.data_ptr(), ld,
+        _p(codes, "codes", (rows, cols), torch.uint8),
+        _p(scales, "scales", (rows, cols // 32), torch.uint8), _stream(stream)))
 
 
 def alloc_workspace(cfg, kind: int, device="cuda") -> Optional[torch.Tensor]:

@@ -338,6 +338,22 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y_sorted, const in
                                         static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t dtype, const void* in,
+                                int64_t ld, uint8_t* codes, uint8_t* scales,
+                                moe_stream_t stream) {
+  if (rows < 0 || cols <= 0 || cols % 32 != 0 || ld < cols) return MOE_ERR_INVALID_ARGUMENT;
+  if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ERR_INVALID_ARGUMENT;
+  if (rows == 0) return MOE_OK;
+  if (!in || !codes || !scales) return MOE_ERR_INVALID_ARGUMENT;
+  const int elem = dtype == MOE_BF16 ? 2 : 4;
+  if (!aligned(in, 16) || (ld * elem) % 16 != 0 || !aligned(codes, 8))
+    return MOE_ERR_INVALID_ARGUMENT;
+  // One lane per 8 elements, 256 lanes per workgroup: the grid must fit.
+  if ((int64_t)rows * (cols / 8) > (int64_t)0x7fffffff * 256) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_mxfp8_quantize(rows, cols, dtype, in, ld, codes, scales,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 moe_status_t moe_forward(const moe_config_t* cfg, const moe_layer_tensors_t* tensors,
                          void* workspace, size_t workspace_bytes, moe_stream_t stream) {
   moe_status_t st = check_config(cfg);

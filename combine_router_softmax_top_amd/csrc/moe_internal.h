@@ -50,6 +50,9 @@ hipError_t launch_expert_mlp(const moe_config_t& c, const void* x_sorted, const 
                              const void* ws_up, const void* ws_down, void* y_shared,
                              void* workspace, hipStream_t s);
 
+hipError_t launch_mxfp8_quantize(int rows, int cols, int dtype, const void* in, long long ld,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t s);
+
 hipError_t launch_combine(const moe_config_t& c, const void* y_sorted, const int32_t* row_of,
                           const float* weights, const void* y_shared, void* out, hipStream_t s);
 

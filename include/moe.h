@@ -206,6 +206,31 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y_sorted, const in
                          const float* topk_weights, const void* y_shared, void* out,
                          moe_stream_t stream);
 
+/*
+ * moe_quantize_mxfp8 -- block-scaled 8-bit encoding of the rows of a matrix,
+ * the form in which [PPLX] Dispatch sends token payloads (activations with
+ * per-block scaling factors; the page fixes no format).  Format: OCP MX-FP8,
+ * the operand format of gfx950's scaled MFMA.  Each run of 32 consecutive
+ * elements of a row shares one scale 2^s with s = floor(log2 max|x|) - 8,
+ * kept within [-127, 127] (s = -127 for an all-zero block), stored as the
+ * E8M0 byte s + 127; each element becomes x / 2^s, clamped to +-448 and
+ * rounded to the nearest E4M3 (fn) value, ties to even.  A decoded element is
+ * e4m3(code) * 2^(scale - 127).  Inputs must be finite.
+ * Arguments:
+ *   rows, cols  rows >= 0; cols > 0, a multiple of 32
+ *   dtype       MOE_BF16 or MOE_F32
+ *   in          [rows, ld] dtype: the first cols elements of each row are
+ *               encoded; 16-byte aligned, ld >= cols, ld * element size a
+ *               multiple of 16 bytes
+ *   codes       [rows, cols] uint8 E4M3 (out), 8-byte aligned
+ *   scales      [rows, cols / 32] uint8 E8M0 (out)
+ * The result is bit-exact and independent of the launch.  rows == 0 enqueues
+ * nothing and reads no pointer.
+ */
+moe_status_t moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t dtype, const void* in,
+                                int64_t ld, uint8_t* codes, uint8_t* scales,
+                                moe_stream_t stream);
+
 /* Tensors of a whole-layer call (moe_forward, moe_forward_dbo). */
 typedef struct moe_layer_tensors {
   const void* x;             /* [T, d] dtype                                     */

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 
 def _declared():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"^\S.*?\b(moe_[a-z_]+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\S.*?\b(moe_[a-z0-9_]+)\s*\(", src, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -141,3 +141,23 @@ def test_dbo_workspace_covers_every_cut(lib, name):
         need = max(one[s] + one[T - s] for s in range(1, T))
         assert bound >= need and bound >= B.workspace_bytes(c, B.MOE_WS_FORWARD), (T, bound, need)
 
+
+
+def test_quantize_mxfp8_rejects_bad_arguments_on_host(lib):
+    P = 0x10000  # never dereferenced: every case below fails before any HIP call
+    BF, F32, BAD = B.MOE_BF16, B.MOE_F32, 7
+    inv = B.MOE_ERR_INVALID_ARGUMENT
+    q = lib.moe_quantize_mxfp8
+    assert q(4, 48, BF, P, 48, P, P, None) == inv          # cols not a multiple of 32
+    assert q(4, 0, BF, P, 0, P, P, None) == inv            # no columns
+    assert q(-1, 64, BF, P, 64, P, P, None) == inv         # negative rows
+    assert q(4, 64, BF, P, 32, P, P, None) == inv          # pitch below cols
+    assert q(4, 64, BAD, P, 64, P, P, None) == inv         # unknown element type
+    assert q(4, 64, BF, None, 64, P, P, None) == inv       # NULL input
+    assert q(4, 64, BF, P, 64, None, P, None) == inv       # NULL codes
+    assert q(4, 64, BF, P, 64, P, None, None) == inv       # NULL scales
+    assert q(4, 64, BF, P + 8, 64, P, P, None) == inv      # input not 16-byte aligned
+    assert q(4, 64, BF, P, 68, P, P, None) == inv          # bf16 pitch not 16-byte aligned
+    assert q(4, 64, F32, P, 66, P, P, None) == inv         # fp32 pitch not 16-byte aligned
+    assert q(4, 64, BF, P, 64, P + 4, P, None) == inv      # codes not 8-byte aligned
+    assert q(0, 64, BF, None, 64, None, None, None) == B.MOE_OK  # nothing to do
