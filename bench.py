@@ -101,15 +101,18 @@ def bench_dbo(args, cfg, layer, torch) -> dict:
 
 
 def source_digest() -> str:
-    """Digest of the expert-MLP kernel source's code: // comments and blank
-    lines are left out, so a change to the comments alone keeps a traffic
-    record valid and any change to the code voids it."""
+    """Digest of the bf16 expert-MLP kernel's source code (its file and the
+    shared grouped-GEMM header): // comments and blank lines are left out, so
+    a change to the comments alone keeps a traffic record valid and any change
+    to the code voids it."""
     import re
-    src = os.path.join(_ROOT, "combine_router_softmax_top_amd", "csrc", "expert_mlp.hip")
-    with open(src) as f:
-        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in f.read().splitlines()]
-    code = "\n".join(ln for ln in lines if ln.strip())
-    return hashlib.sha256(code.encode()).hexdigest()[:16]
+    csrc = os.path.join(_ROOT, "combine_router_softmax_top_amd", "csrc")
+    code = []
+    for name in ("expert_mlp.hip", "grouped_gemm.h"):
+        with open(os.path.join(csrc, name)) as f:
+            lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in f.read().splitlines()]
+        code.append("\n".join(ln for ln in lines if ln.strip()))
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def algorithmic(cfg, n_loc: int, t_touch: int) -> dict:
