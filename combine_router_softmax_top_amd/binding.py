@@ -20,6 +20,7 @@ _LIB = None
 
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
+MOE_MX_ROWS, MOE_MX_MFMA = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_EXPERT_MLP, MOE_WS_FORWARD, MOE_WS_FORWARD_DBO = range(5)
 
@@ -27,7 +28,7 @@ EXPORTED = ["moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_f
             "moe_forward_dbo", "moe_forward_dbo_at", "moe_graph_capture_forward",
             "moe_graph_capture_forward_dbo", "moe_graph_launch", "moe_graph_destroy",
             "moe_workspace_bytes", "moe_dbo_split_point", "moe_dbo_plan_split",
-            "moe_quantize_mxfp8", "moe_status_string"]
+            "moe_quantize_mxfp8", "moe_expert_mlp_mxfp8", "moe_status_string"]
 
 
 class MoEError(RuntimeError):
@@ -75,7 +76,8 @@ def lib() -> ctypes.CDLL:
             "moe_graph_capture_forward_dbo": [C, LT, P, SZ, I32, ctypes.POINTER(P)],
             "moe_graph_launch": [P, P],
             "moe_graph_destroy": [P],
-            "moe_quantize_mxfp8": [I32, I32, I32, P, ctypes.c_int64, P, P, P],
+            "moe_quantize_mxfp8": [I32, I32, I32, P, ctypes.c_int64, I32, P, P, P],
+            "moe_expert_mlp_mxfp8": [C, P, P, P, P, P, P, P, P, P, P, SZ, P],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -314,22 +316,44 @@ def dbo_plan_split(num_tokens: int, has_prefill: bool, decode_threshold: int,
                                         int(prefill_threshold), int(uniform_query_len)))
 
 
-def moe_quantize_mxfp8(x, codes, scales, stream=None):
+def moe_quantize_mxfp8(x, codes, scales, scale_layout: int = 0, stream=None):
     """MX-FP8 encoding of the rows of x ([rows, cols] bf16 or fp32, unit column
     stride; the row stride may be larger) into codes ([rows, cols] uint8, E4M3)
-    and scales ([rows, cols // 32] uint8, E8M0)."""
+    and scales (rows * cols // 32 uint8 E8M0 bytes, in MOE_MX_ROWS or
+    MOE_MX_MFMA order)."""
     if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.device.type != "cuda":
         raise ValueError("x: expected a 2-D device tensor")
     if x.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError(f"x: dtype {x.dtype}, expected bfloat16 or float32")
-    if x.shape[0] > 1 and x.stride(1) != 1:
+    if x.shape[1] > 1 and x.stride(1) != 1:
         raise ValueError("x: columns must be contiguous")
     rows, cols = x.shape
     ld = x.stride(0) if rows > 1 else cols
     _check("moe_quantize_mxfp8", lib().moe_quantize_mxfp8(
         rows, cols, MOE_BF16 if x.dtype == torch.bfloat16 else MOE_F32, x.data_ptr(), ld,
-        _p(codes, "codes", (rows, cols), torch.uint8),
-        _p(scales, "scales", (rows, cols // 32), torch.uint8), _stream(stream)))
+        int(scale_layout), _p(codes, "codes", (rows, cols), torch.uint8),
+        _p(scales, "scales", (rows * cols // 32,), torch.uint8), _stream(stream)))
+
+
+def moe_expert_mlp_mxfp8(cfg, xq_sorted, xq_scales, expert_offsets, wq_gate, wq_gate_scales,
+                         wq_up, wq_up_scales, w_down, y_sorted, workspace, stream=None):
+    c = _cs(cfg)
+    T, d, K, I = c.num_tokens, c.hidden, c.top_k, c.intermediate
+    n_loc = c.expert_end - c.expert_begin
+    u8 = torch.uint8
+    st = lib().moe_expert_mlp_mxfp8(
+        ctypes.byref(c), _p(xq_sorted, "xq_sorted", (T * K, d), u8),
+        _p(xq_scales, "xq_scales", (T * K * d // 32,), u8),
+        _p(expert_offsets, "expert_offsets", (n_loc + 1,), torch.int32),
+        _p(wq_gate, "wq_gate", (n_loc, I, d), u8),
+        _p(wq_gate_scales, "wq_gate_scales", (n_loc * I * d // 32,), u8),
+        _p(wq_up, "wq_up", (n_loc, I, d), u8),
+        _p(wq_up_scales, "wq_up_scales", (n_loc * I * d // 32,), u8),
+        _p(w_down, "w_down", (n_loc, d, I), torch.bfloat16),
+        _p(y_sorted, "y_sorted", (T * K, d), torch.bfloat16), _p(workspace, "workspace"),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check("moe_expert_mlp_mxfp8", st)
 
 
 def alloc_workspace(cfg, kind: int, device="cuda") -> Optional[torch.Tensor]:

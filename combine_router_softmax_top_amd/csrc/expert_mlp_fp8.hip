@@ -1,0 +1,392 @@
+// Grouped SiLU-gated expert MLP with a block-scaled 8-bit gate/up projection.
+//
+// Operation ("Efficient and portable mixture-of-experts communication",
+// Dispatch: token payloads travel with block scaling factors into the grouped
+// GEMM; Combine: expert outputs travel back unquantized, in 16 bits):
+//     h = SiLU(Xq Gq^T) * (Xq Uq^T),   y = h W_down^T
+// with Xq, Gq, Uq MX-FP8 matrices (E4M3 elements, one power-of-two scale per
+// 32 consecutive k) and h, W_down, y in bf16.  Every product of two E4M3
+// values and their two scales is exact in fp32, so the gate/up sums differ
+// from those of the dequantized operands only by fp32 accumulation.
+//
+// Gate/up kernel (gfx950 v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 x E4M3 with
+// E8M0 scales, fp32 accumulation):
+//   * one 256-thread workgroup per 256 x 256 tile (256 rows x 128 gate + 128
+//     up columns, multiplied in the epilogue so h is written once); four
+//     waves, one per SIMD, in a 2 x 2 grid, each 128 rows x (64 gate + 64 up)
+//     as 4 x 4 MFMA blocks of 32 x 32, so each fragment read from LDS feeds
+//     four MFMAs (the 32-byte fp8 fragments would not fit two waves per SIMD
+//     in the register file); an expert's last row tile of at most 192 rows
+//     runs at its rows rounded up to 64, as in the bf16 kernel;
+//   * k-tiles of 128 (128-byte rows, the same bytes as the bf16 kernel's
+//     64-deep tiles) go straight from global memory into the shared swizzled
+//     LDS rings (activations two slots, weights three); a lane's operand for
+//     64-deep k-step s is two 16-byte chunks of its row, 4s + h and 4s + 2 + h
+//     (h = lane / 32);
+//   * the scales bypass LDS: they are stored pre-arranged for the MFMA (the
+//     MFMA scale layout of moe_quantize_mxfp8) so that one 8-byte load per
+//     lane and fragment brings every scale that lane needs for four k-tiles;
+//     the loads for the next four k-tiles are issued with the activation loads
+//     and complete by the same barrier;
+//   * tile list, XCD band order and a fixed k order as in the bf16 kernel.
+// The down projection runs on h with the bf16 grouped GEMM.
+#include <type_traits>
+
+#include "grouped_gemm.h"
+
+namespace moe {
+
+hipError_t launch_grouped_down_bf16(const moe_config_t& c, const void* h, const int32_t* offsets,
+                                    const void* w_down, void* y_sorted, hipStream_t s);
+
+namespace {
+
+constexpr int kQWaves = 4;                            // 2 x 2, one wave per SIMD
+constexpr int kQThreads = 64 * kQWaves;
+constexpr int kQK = kRowBytes;                        // k per k-tile (one byte each)
+constexpr int kQGroupTiles = 4;                       // k-tiles per scale load (512 k)
+constexpr int kQBF = 4;                               // B fragments per wave: 2 gate + 2 up
+constexpr int kQDmaB = kSlotBytes / 1024 / kQWaves;   // 1-KB loads per wave for a B k-tile
+constexpr int kQNOut = kBN / 2;                       // h columns per tile
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+struct QFrags {
+  i32x8 a[4], b[kQBF];
+};
+
+// A lane's 32-byte operand for k-step s: with base = row * 128 | (h ^
+// swz(row)) * 16, logical chunk 4s + h (4s + 2 + h) sits at byte base ^ 64s
+// (base ^ (64s + 32)) of the slot.
+template <int S>
+__device__ __forceinline__ i32x8 read_operand(const uint8_t* slot, uint32_t base) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(slot + (base ^ (64u * S)));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(slot + (base ^ (64u * S + 32u)));
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
+// Fragments of k-step S (64 deep) of a staged k-tile.  The per-fragment bases
+// are passed through an empty asm first, so the compiler re-derives the four
+// addresses of a fragment next to the reads (one xor each) instead of
+// keeping every combination live in registers across the loop.
+template <int NFA, int S>
+__device__ __forceinline__ void load_qfrags(const uint8_t* sa, const uint8_t* sb,
+                                            const uint32_t (&abase)[4],
+                                            const uint32_t (&bbase)[kQBF], QFrags& f) {
+#pragma unroll
+  for (int i = 0; i < NFA; ++i) {
+    uint32_t b = abase[i];
+    asm volatile("" : "+v"(b));
+    f.a[i] = read_operand<S>(sa, b);
+  }
+#pragma unroll
+  for (int j = 0; j < kQBF; ++j) {
+    uint32_t b = bbase[j];
+    asm volatile("" : "+v"(b));
+    f.b[j] = read_operand<S>(sb, b);
+  }
+}
+
+// One 64-deep k-step: the weights are the MFMA's first operand (as in the
+// bf16 kernel, so a lane keeps one output row), each operand with the scale
+// register of its fragment; OPSEL picks the byte of that register that holds
+// this lane's scale for this k-step.
+template <int NFA, int OPSEL>
+__device__ __forceinline__ void qmma_step(const QFrags& f, const uint32_t (&sca)[4],
+                                          const uint32_t (&scb)[kQBF],
+                                          f32x16 (&acc)[4][kQBF]) {
+#pragma unroll
+  for (int i = 0; i < NFA; ++i)
+#pragma unroll
+    for (int j = 0; j < kQBF; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          f.b[j], f.a[i], acc[i][j], 0, 0, OPSEL, (int)scb[j], OPSEL, (int)sca[i]);
+}
+
+// Staging with four waves: instruction j of wave w fills rows (4j + w) * 8 ..
+// +8 of the slot; the per-lane source offsets come from `off`.
+template <int N>
+__device__ __forceinline__ void qstage(uint8_t* slot, const uint8_t* lo, const uint8_t* hi,
+                                       int n_lo, const uint32_t* off, int wave, int kbytes) {
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>((j < n_lo ? lo : hi) + kbytes + off[j]),
+                                     (lds_ptr_t)(slot + (j * kQWaves + wave) * 1024), 16, 0, 0);
+}
+
+struct QTileArgs {
+  const uint8_t* A;    // codes of the rows, pitch lda bytes
+  const uint8_t* As;   // scales of A, MFMA layout over rows_as rows
+  const uint8_t* Bg;   // gate / up codes of the group, [N, Kdim]
+  const uint8_t* Bu;
+  const uint8_t* Bgs;  // gate / up scales, MFMA layout over rows_bs rows
+  const uint8_t* Bus;
+  uint16_t* C;
+  long long rows_as, rows_bs;
+  int lda, ldc, brow0;  // brow0: the group's first row in the weight stack
+  int row0, rows, m0, n0, N, Kdim;
+};
+
+// LDS: activation and weight k-tiles in rings of two slots each, and two scale
+// regions of 4 KB (region d holds dword d of the current group's scales: 256
+// activation rows x 2 halves, then 256 weight rows x 2 halves).
+constexpr int kQStages = 2;
+constexpr int kQScaleRegion = 4096;
+constexpr int kQLds = 2 * kQStages * kSlotBytes + 2 * kQScaleRegion;
+static_assert(kQLds <= 160 * 1024, "LDS budget");
+
+template <int NFA>
+__device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  constexpr int kWaveRows = NFA * 32;
+  constexpr int NA = 2 * NFA;  // A loads per wave: NFA * 64 rows across the 4 waves
+  const int m0 = ta.m0, n0 = ta.n0, N = ta.N, Kdim = ta.Kdim;
+
+  const uint8_t* a_tile = ta.A + (long long)(ta.row0 + m0) * ta.lda;
+  const uint8_t* b_lo = ta.Bg + (long long)n0 * Kdim;
+  const uint8_t* b_hi = ta.Bu + (long long)n0 * Kdim;
+  const int a_last = ta.rows - 1 - m0;
+  const int b_last = N - 1 - n0;
+  // Per-lane source offsets; B instructions 4..7 fill tile rows 128..255, the
+  // up rows 0..127.
+  uint32_t offa[NA], offb[kQDmaB];
+#pragma unroll
+  for (int j = 0; j < kQDmaB; ++j) {
+    const int r = (j * kQWaves + wave) * (1024 / kRowBytes) + lane / 8;
+    const int lchunk = (lane & 7) ^ swz(r);
+    if (j < NA) offa[j] = (uint32_t)(min(r, a_last) * ta.lda + lchunk * 16);
+    const int br = j < kQDmaB / 2 ? r : r - kQNOut;
+    offb[j] = (uint32_t)(min(br, b_last) * Kdim + lchunk * 16);
+  }
+
+  // Fragment rows: A rows wm * kWaveRows + 32i + lane % 32; B rows: the wave's
+  // 64 gate rows, then the matching 64 up rows (tile rows 128..).
+  const int a_row0 = wm * kWaveRows + (lane & 31);
+  uint32_t abase[4], bbase[kQBF];
+#pragma unroll
+  for (int j = 0; j < kQBF; ++j) {
+    const int br = (j >> 1) * kQNOut + wn * 64 + (j & 1) * 32 + (lane & 31);
+    bbase[j] = (uint32_t)(br * kRowBytes) | ((uint32_t)(h ^ swz(br)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int ar = a_row0 + i * 32;
+    abase[i] = (uint32_t)(ar * kRowBytes) | ((uint32_t)(h ^ swz(ar)) << 4);
+  }
+
+  // Scales, MFMA layout: dword d of group g for row r, half h at dword
+  // ((2g + d) R + r) 2 + h; byte 2(J % 2) + s of dword d = J / 2 serves k-step
+  // s of k-tile J of the group.  A region load is four 64-lane dword DMAs per
+  // wave: instruction q = wave + 4t (t = 0..3) fills dwords 64q .. 64q + 63 of
+  // the region, activation rows 32q .. for q < 8, weight tile rows 32(q-8) ..
+  // (gate rows, then up rows) after; rows past the group repeat its last row.
+  // The host keeps every scale array below 2^31 dwords.
+  const uint32_t* as32 = reinterpret_cast<const uint32_t*>(ta.As);
+  const uint32_t* bgs32 = reinterpret_cast<const uint32_t*>(ta.Bgs);
+  const uint32_t* bus32 = reinterpret_cast<const uint32_t*>(ta.Bus);
+  uint32_t soff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int q = wave + 4 * t;
+    const int r = (q & 7) * 32 + lane / 2;  // row of the A part or B tile row
+    if (q < 8) {
+      soff[t] = (uint32_t)(ta.row0 + min(m0 + r, ta.rows - 1)) * 2 + (lane & 1);
+    } else {
+      const int n = r < kQNOut ? r : r - kQNOut;
+      soff[t] = (uint32_t)(ta.brow0 + min(n0 + n, N - 1)) * 2 + (lane & 1);
+    }
+  }
+  const uint32_t a_gs = (uint32_t)ta.rows_as * 2, b_gs = (uint32_t)ta.rows_bs * 2;
+  uint8_t* regions = lds + 2 * kQStages * kSlotBytes;
+  // Dword d of group g into region d (t = 0, 1: activations; 2, 3: weights;
+  // wave 0..3 fill weight rows 0..127 (gate) for t = 2, 128..255 (up) for t = 3).
+  auto stage_scales = [&](int g, int d) {
+    uint8_t* region = regions + d * kQScaleRegion;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t* src = t < 2 ? as32 + (uint32_t)(2 * g + d) * a_gs
+                                  : (t == 2 ? bgs32 : bus32) + (uint32_t)(2 * g + d) * b_gs;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + soff[t]),
+                                       (lds_ptr_t)(region + (wave + 4 * t) * 256), 4, 0, 0);
+    }
+  };
+  // This lane's scale dwords of one region: A fragment i at row a_row0 + 32i,
+  // B fragment j at weight tile row (j / 2) * 128 + wn * 64 + (j % 2) * 32 + lane % 32.
+  const uint32_t* rs_a = reinterpret_cast<const uint32_t*>(regions) + a_row0 * 2 + h;
+  const uint32_t* rs_b =
+      reinterpret_cast<const uint32_t*>(regions) + 512 + (wn * 64 + (lane & 31)) * 2 + h;
+  auto read_scales = [&](int d, uint32_t (&ra)[4], uint32_t (&rb)[kQBF]) {
+#pragma unroll
+    for (int i = 0; i < NFA; ++i) ra[i] = rs_a[d * (kQScaleRegion / 4) + i * 64];
+#pragma unroll
+    for (int j = 0; j < kQBF; ++j)
+      rb[j] = rs_b[d * (kQScaleRegion / 4) + (j >> 1) * 256 + (j & 1) * 64];
+  };
+
+  f32x16 acc[4][kQBF];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < kQBF; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Pipeline: both operands in rings of two; A(kt+2) and B(kt+2) are issued
+  // after barrier kt into tile kt's slots and must land by barrier kt+1, one
+  // k-tile later, where the wait covers every load (nothing is issued before a
+  // barrier within an iteration).  Fragments are double-buffered across the
+  // two k-steps; the barrier comes before the second k-step's MFMAs.  Scales:
+  // region 1 (k-tiles 2, 3 of group g) is refilled after barrier 0 of the
+  // group and read into registers after barrier 1; region 0 (k-tiles 0, 1 of
+  // group g+1) is refilled after barrier 2 and read after barrier 3.  Every
+  // refill lands by the next barrier and the reads of the old contents precede
+  // the barrier before the refill.
+  constexpr int kMfma = NFA * kQBF, kReads = 2 * (NFA + kQBF);
+  constexpr int kVmPrologue = NA + kQDmaB;  // tile 1 still in flight
+  uint8_t* a_slots = lds;
+  uint8_t* b_slots = lds + kQStages * kSlotBytes;
+  const int nk = Kdim / kQK;  // a multiple of kQGroupTiles
+  const int ng = nk / kQGroupTiles;
+  const int last = (nk - 1) * kRowBytes;
+  stage_scales(0, 0);
+#pragma unroll
+  for (int t = 0; t < kQStages; ++t) {
+    qstage<NA>(a_slots + t * kSlotBytes, a_tile, a_tile, NA, offa, wave, min(t * kRowBytes, last));
+    qstage<kQDmaB>(b_slots + t * kSlotBytes, b_lo, b_hi, kQDmaB / 2, offb, wave,
+                   min(t * kRowBytes, last));
+  }
+  wait_loads_and_barrier<kVmPrologue>();  // tile 0 and region 0 landed
+  QFrags f0, f1;
+  uint32_t sca[4], scb[kQBF];  // the current k-tile pair's scale dwords
+#pragma unroll
+  for (int i = NFA; i < 4; ++i) sca[i] = 0u;
+  read_scales(0, sca, scb);
+  load_qfrags<NFA, 0>(a_slots, b_slots, abase, bbase, f0);
+
+  for (int g = 0; g < ng; ++g) {
+    auto ktile = [&](auto Jc) {
+      constexpr int J = decltype(Jc)::value;
+      const int kt = g * kQGroupTiles + J;
+      uint8_t* sa = a_slots + (kt & 1) * kSlotBytes;
+      uint8_t* sb = b_slots + (kt & 1) * kSlotBytes;
+      const uint8_t* na = a_slots + ((kt + 1) & 1) * kSlotBytes;
+      const uint8_t* nb = b_slots + ((kt + 1) & 1) * kSlotBytes;
+      load_qfrags<NFA, 1>(sa, sb, abase, bbase, f1);
+      qmma_step<NFA, 2 * (J % 2)>(f0, sca, scb, acc);
+      pin_kstep_schedule<kMfma, kReads, 0>();
+      wait_loads_and_barrier<0>();  // tile kt+1 (and any refilled region) landed
+      load_qfrags<NFA, 0>(na, nb, abase, bbase, f0);
+      const int kb = min((kt + kQStages) * kRowBytes, last);
+      qstage<NA>(sa, a_tile, a_tile, NA, offa, wave, kb);
+      qstage<kQDmaB>(sb, b_lo, b_hi, kQDmaB / 2, offb, wave, kb);
+      if constexpr (J == 0) stage_scales(g, 1);
+      if constexpr (J == 2) stage_scales(min(g + 1, ng - 1), 0);
+      qmma_step<NFA, 2 * (J % 2) + 1>(f1, sca, scb, acc);
+      // After the last MFMA of the pair that uses them, the scale registers
+      // take the next pair's dwords.
+      if constexpr (J == 1) read_scales(1, sca, scb);
+      if constexpr (J == 3) read_scales(0, sca, scb);
+      constexpr int kScaleReads = (J == 1 || J == 3) ? NFA + kQBF : 0;
+      pin_kstep_schedule<kMfma, kReads + kScaleReads,
+                         NA + kQDmaB + ((J == 0 || J == 2) ? 4 : 0)>();
+    };
+    ktile(std::integral_constant<int, 0>{});
+    ktile(std::integral_constant<int, 1>{});
+    ktile(std::integral_constant<int, 2>{});
+    ktile(std::integral_constant<int, 3>{});
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // Epilogue: element r of lane l in a 32 x 32 block is output row l % 32 and
+  // column (r / 4) * 8 + (l / 32) * 4 + r % 4; gate block j pairs with up
+  // block j + 2.  N is a multiple of 64, so a run of four columns is wholly
+  // inside or wholly past N.
+  const int row_l = lane & 31;
+  const int col_l = h * 4;
+#pragma unroll
+  for (int i = 0; i < NFA; ++i) {
+    const int m = m0 + wm * kWaveRows + i * 32 + row_l;
+    if (m >= ta.rows) continue;
+    uint16_t* crow = ta.C + (long long)(ta.row0 + m) * ta.ldc;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + wn * 64 + j * 32 + gq * 8 + col_l;
+        if (n < N) {
+          float v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            v[q] = silu_f(acc[i][j][4 * gq + q]) * acc[i][j + 2][4 * gq + q];
+          store_bf16x4(crow + n, v);
+        }
+      }
+  }
+}
+
+__global__ __launch_bounds__(kQThreads, 1) void gemm_mxfp8_glu_kernel(
+    const uint8_t* __restrict__ A, int lda, const uint8_t* __restrict__ As, long long rows_as,
+    const uint8_t* __restrict__ Bg, const uint8_t* __restrict__ Bu, long long strideB_group,
+    const uint8_t* __restrict__ Bgs, const uint8_t* __restrict__ Bus, long long rows_bs,
+    uint16_t* __restrict__ C, int ldc, const int32_t* __restrict__ offsets, int n_groups, int N,
+    int Kdim) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kQLds];
+  const int nN = (N + kQNOut - 1) / kQNOut;
+  Tile tl;
+  if (!find_tile(offsets, n_groups, 0, 0, 0, kBM, nN, tl)) return;
+  QTileArgs ta;
+  ta.A = A;
+  ta.As = As;
+  ta.Bg = Bg + (long long)tl.group * strideB_group;
+  ta.Bu = Bu + (long long)tl.group * strideB_group;
+  ta.Bgs = Bgs;
+  ta.Bus = Bus;
+  ta.C = C;
+  ta.rows_as = rows_as;
+  ta.rows_bs = rows_bs;
+  ta.lda = lda;
+  ta.ldc = ldc;
+  ta.brow0 = tl.group * N;
+  ta.row0 = tl.row0;
+  ta.rows = tl.rows;
+  ta.m0 = tl.m_tile * kBM;
+  ta.n0 = tl.n_tile * kQNOut;
+  ta.N = N;
+  ta.Kdim = Kdim;
+  const int left = tl.rows - ta.m0;
+  if (left > 3 * kBM / 4)
+    qgemm_tile<4>(ta, lds);
+  else if (left > kBM / 2)
+    qgemm_tile<3>(ta, lds);
+  else if (left > kBM / 4)
+    qgemm_tile<2>(ta, lds);
+  else
+    qgemm_tile<1>(ta, lds);
+}
+
+}  // namespace
+
+hipError_t launch_expert_mlp_mxfp8(const moe_config_t& c, const uint8_t* xq, const uint8_t* xq_scales,
+                                   const int32_t* offsets, const uint8_t* wq_gate,
+                                   const uint8_t* wq_gate_scales, const uint8_t* wq_up,
+                                   const uint8_t* wq_up_scales, const void* w_down,
+                                   void* y_sorted, void* workspace, hipStream_t s) {
+  const int T = c.num_tokens, K = c.top_k, d = c.hidden, I = c.intermediate;
+  const int n_loc = c.expert_end - c.expert_begin;
+  const int row_bound = ceil_div(T * K, kBM) + n_loc;
+  const dim3 grid(grid_for(row_bound, ceil_div(I, kQNOut)));
+  uint16_t* h = static_cast<uint16_t*>(workspace);
+  hipLaunchKernelGGL(gemm_mxfp8_glu_kernel, grid, dim3(kQThreads), 0, s, xq, d, xq_scales,
+                     (long long)T * K, wq_gate, wq_up, (long long)I * d, wq_gate_scales,
+                     wq_up_scales, (long long)n_loc * I, h, I, offsets, n_loc, I, d);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_grouped_down_bf16(c, h, offsets, w_down, y_sorted, s);
+}
+
+}  // namespace moe

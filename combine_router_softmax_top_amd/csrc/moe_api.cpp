@@ -339,19 +339,53 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y_sorted, const in
 }
 
 moe_status_t moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t dtype, const void* in,
-                                int64_t ld, uint8_t* codes, uint8_t* scales,
-                                moe_stream_t stream) {
+                                int64_t ld, int32_t scale_layout, uint8_t* codes,
+                                uint8_t* scales, moe_stream_t stream) {
   if (rows < 0 || cols <= 0 || cols % 32 != 0 || ld < cols) return MOE_ERR_INVALID_ARGUMENT;
   if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_ERR_INVALID_ARGUMENT;
+  if (scale_layout != MOE_MX_ROWS && scale_layout != MOE_MX_MFMA) return MOE_ERR_INVALID_ARGUMENT;
+  if (scale_layout == MOE_MX_MFMA && cols % 512 != 0) return MOE_ERR_INVALID_ARGUMENT;
   if (rows == 0) return MOE_OK;
   if (!in || !codes || !scales) return MOE_ERR_INVALID_ARGUMENT;
   const int elem = dtype == MOE_BF16 ? 2 : 4;
-  if (!aligned(in, 16) || (ld * elem) % 16 != 0 || !aligned(codes, 8))
+  if (!aligned(in, 16) || (ld * elem) % 16 != 0 || !aligned(codes, 8) || !aligned(scales, 4))
     return MOE_ERR_INVALID_ARGUMENT;
   // One lane per 8 elements, 256 lanes per workgroup: the grid must fit.
   if ((int64_t)rows * (cols / 8) > (int64_t)0x7fffffff * 256) return MOE_ERR_UNSUPPORTED;
-  return hip_status(moe::launch_mxfp8_quantize(rows, cols, dtype, in, ld, codes, scales,
-                                               static_cast<hipStream_t>(stream)));
+  return hip_status(moe::launch_mxfp8_quantize(rows, cols, dtype, in, ld, scale_layout, codes,
+                                               scales, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expert_mlp_mxfp8(const moe_config_t* cfg, const uint8_t* xq_sorted,
+                                  const uint8_t* xq_scales, const int32_t* expert_offsets,
+                                  const uint8_t* wq_gate, const uint8_t* wq_gate_scales,
+                                  const uint8_t* wq_up, const uint8_t* wq_up_scales,
+                                  const void* w_down, void* y_sorted, void* workspace,
+                                  size_t workspace_bytes, moe_stream_t stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16 || cfg->num_shared != 0 || cfg->hidden % 512 != 0)
+    return MOE_ERR_UNSUPPORTED;
+  if (!xq_sorted || !xq_scales || !expert_offsets || !wq_gate || !wq_gate_scales || !wq_up ||
+      !wq_up_scales || !w_down || !y_sorted || !workspace)
+    return MOE_ERR_INVALID_ARGUMENT;
+  for (const void* p : {(const void*)xq_sorted, (const void*)wq_gate, (const void*)wq_up, w_down,
+                        (const void*)y_sorted})
+    if (!aligned(p, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  for (const void* p : {(const void*)xq_scales, (const void*)wq_gate_scales,
+                        (const void*)wq_up_scales})
+    if (!aligned(p, 4)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < moe::mlp_workspace_bytes(*cfg)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  // The kernel indexes each scale array in 32-bit dwords.
+  const int64_t n_loc = cfg->expert_end - cfg->expert_begin;
+  const int64_t kdw = cfg->hidden / 128;  // scale dwords per row
+  if ((int64_t)cfg->num_tokens * cfg->top_k * kdw >= (int64_t(1) << 31) ||
+      n_loc * cfg->intermediate * kdw >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_expert_mlp_mxfp8(
+      *cfg, xq_sorted, xq_scales, expert_offsets, wq_gate, wq_gate_scales, wq_up, wq_up_scales,
+      w_down, y_sorted, workspace, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_forward(const moe_config_t* cfg, const moe_layer_tensors_t* tensors,

@@ -51,7 +51,14 @@ hipError_t launch_expert_mlp(const moe_config_t& c, const void* x_sorted, const 
                              void* workspace, hipStream_t s);
 
 hipError_t launch_mxfp8_quantize(int rows, int cols, int dtype, const void* in, long long ld,
-                                 uint8_t* codes, uint8_t* scales, hipStream_t s);
+                                 int layout, uint8_t* codes, uint8_t* scales, hipStream_t s);
+
+hipError_t launch_expert_mlp_mxfp8(const moe_config_t& c, const uint8_t* xq,
+                                   const uint8_t* xq_scales, const int32_t* offsets,
+                                   const uint8_t* wq_gate, const uint8_t* wq_gate_scales,
+                                   const uint8_t* wq_up, const uint8_t* wq_up_scales,
+                                   const void* w_down, void* y_sorted, void* workspace,
+                                   hipStream_t s);
 
 hipError_t launch_combine(const moe_config_t& c, const void* y_sorted, const int32_t* row_of,
                           const float* weights, const void* y_shared, void* out, hipStream_t s);

@@ -9,6 +9,11 @@
 // element is x / 2^s clamped to +-448 and rounded to the nearest E4M3 value,
 // ties to even.
 //
+// Scale layouts: MOE_MX_ROWS keeps row r's scales at r * cols/32 + block;
+// MOE_MX_MFMA arranges them for the scaled-MFMA grouped GEMM, which reads, per
+// lane, one dword for two 128-deep k-tiles: block 16g + m of row r (m = 8d +
+// 4j + 2s + h) is byte 2j + s of dword ((2g + d) R + r) 2 + h, R = rows.
+//
 // One lane per 8 consecutive elements, four lanes per block: the block maximum
 // is shared with two xor shuffles; floor(log2 max) is the maximum's exponent
 // field (a zero or subnormal maximum gives the clamped -127); x * 2^-s is exact
@@ -43,6 +48,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 template <typename T>
 __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const T* __restrict__ in,
                                                              long long ld, int rows, int cols,
+                                                             int layout,
                                                              uint8_t* __restrict__ codes,
                                                              uint8_t* __restrict__ scales) {
   const int per_row = cols / 8;  // pieces of 8 elements
@@ -73,21 +79,32 @@ __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const T* __restrict
   if (!live) return;
   *reinterpret_cast<u32x2*>(codes + (long long)r * cols + (long long)c8 * 8) =
       u32x2{(uint32_t)lo, (uint32_t)hi};
-  if ((c8 & 3) == 0) scales[(long long)r * (cols / 32) + c8 / 4] = (uint8_t)(s + 127);
+  if ((c8 & 3) == 0) {
+    const int q = c8 / 4;
+    long long at;
+    if (layout == MOE_MX_ROWS) {
+      at = (long long)r * (cols / 32) + q;
+    } else {
+      const int g = q >> 4, m = q & 15;
+      const int d = m >> 3, b = ((m >> 2) & 1) * 2 + ((m >> 1) & 1), hh = m & 1;
+      at = (((long long)(2 * g + d) * rows + r) * 2 + hh) * 4 + b;
+    }
+    scales[at] = (uint8_t)(s + 127);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_mxfp8_quantize(int rows, int cols, int dtype, const void* in, long long ld,
-                                 uint8_t* codes, uint8_t* scales, hipStream_t s) {
+                                 int layout, uint8_t* codes, uint8_t* scales, hipStream_t s) {
   const long long pieces = (long long)rows * (cols / 8);
   const dim3 grid((unsigned)((pieces + 255) / 256));
   if (dtype == MOE_BF16)
     hipLaunchKernelGGL(mxfp8_quantize_kernel<uint16_t>, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(in), ld, rows, cols, codes, scales);
+                       static_cast<const uint16_t*>(in), ld, rows, cols, layout, codes, scales);
   else
     hipLaunchKernelGGL(mxfp8_quantize_kernel<float>, grid, dim3(256), 0, s,
-                       static_cast<const float*>(in), ld, rows, cols, codes, scales);
+                       static_cast<const float*>(in), ld, rows, cols, layout, codes, scales);
   return hipGetLastError();
 }
 

@@ -206,6 +206,9 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y_sorted, const in
                          const float* topk_weights, const void* y_shared, void* out,
                          moe_stream_t stream);
 
+/* Scale layouts of moe_quantize_mxfp8. */
+enum { MOE_MX_ROWS = 0, MOE_MX_MFMA = 1 };
+
 /*
  * moe_quantize_mxfp8 -- block-scaled 8-bit encoding of the rows of a matrix,
  * the form in which [PPLX] Dispatch sends token payloads (activations with
@@ -217,19 +220,62 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y_sorted, const in
  * rounded to the nearest E4M3 (fn) value, ties to even.  A decoded element is
  * e4m3(code) * 2^(scale - 127).  Inputs must be finite.
  * Arguments:
- *   rows, cols  rows >= 0; cols > 0, a multiple of 32
- *   dtype       MOE_BF16 or MOE_F32
- *   in          [rows, ld] dtype: the first cols elements of each row are
- *               encoded; 16-byte aligned, ld >= cols, ld * element size a
- *               multiple of 16 bytes
- *   codes       [rows, cols] uint8 E4M3 (out), 8-byte aligned
- *   scales      [rows, cols / 32] uint8 E8M0 (out)
+ *   rows, cols    rows >= 0; cols > 0, a multiple of 32 (of 512 for
+ *                 MOE_MX_MFMA)
+ *   dtype         MOE_BF16 or MOE_F32
+ *   in            [rows, ld] dtype: the first cols elements of each row are
+ *                 encoded; 16-byte aligned, ld >= cols, ld * element size a
+ *                 multiple of 16 bytes
+ *   scale_layout  where the scale of block q (elements 32q .. 32q + 31) of
+ *                 row r goes in `scales` (rows * cols / 32 bytes either way):
+ *                 MOE_MX_ROWS: byte r * cols/32 + q;
+ *                 MOE_MX_MFMA: with q = 16g + m, m = 8d + 4j + 2s + h (each of
+ *                 d, j, s, h 0 or 1), byte 2j + s of 32-bit word
+ *                 ((2g + d) * rows + r) * 2 + h -- the layout that
+ *                 moe_expert_mlp_mxfp8 reads
+ *   codes         [rows, cols] uint8 E4M3 (out), 8-byte aligned
+ *   scales        uint8 E8M0 (out), 4-byte aligned
  * The result is bit-exact and independent of the launch.  rows == 0 enqueues
  * nothing and reads no pointer.
  */
 moe_status_t moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t dtype, const void* in,
-                                int64_t ld, uint8_t* codes, uint8_t* scales,
-                                moe_stream_t stream);
+                                int64_t ld, int32_t scale_layout, uint8_t* codes,
+                                uint8_t* scales, moe_stream_t stream);
+
+/*
+ * moe_expert_mlp_mxfp8 -- moe_expert_mlp with the gate/up projection on
+ * MX-FP8 operands: the dispatched payload reaches the grouped GEMM with block
+ * scaling factors ([PPLX] Dispatch) and the expert outputs return in 16 bits
+ * ([PPLX] Combine).  For each local expert e and each of its rows,
+ *   h = SiLU(D(xq) D(gq_e)^T) * (D(xq) D(uq_e)^T)   accumulated in fp32,
+ *                                                   rounded to bf16,
+ *   y = h W_down[e]^T                               bf16 operands, fp32
+ *                                                   accumulation, rounded,
+ * with D() the decoding of moe_quantize_mxfp8 (every product of two decoded
+ * elements is exact in fp32).  Requires cfg->dtype == MOE_BF16,
+ * cfg->num_shared == 0 and cfg->hidden a multiple of 512
+ * (MOE_ERR_UNSUPPORTED otherwise).
+ * Arguments (T = num_tokens, K = top_k, d = hidden, I = intermediate,
+ * E_loc = expert_end - expert_begin):
+ *   xq_sorted       [T*K, d] E4M3 codes of the dispatched rows
+ *   xq_scales       their scales, MOE_MX_MFMA layout with rows = T*K
+ *   expert_offsets  [E_loc + 1] int32 (from moe_dispatch)
+ *   wq_gate, wq_up  [E_loc, I, d] E4M3 codes
+ *   wq_gate_scales, wq_up_scales
+ *                   scales of the [E_loc * I, d] stacks, MOE_MX_MFMA layout
+ *                   with rows = E_loc * I
+ *   w_down          [E_loc, d, I] bf16
+ *   y_sorted        [T*K, d] bf16 (out); rows past the local count untouched
+ *   workspace       >= moe_workspace_bytes(cfg, MOE_WS_EXPERT_MLP) bytes,
+ *                   256-byte aligned
+ * Code arrays and bf16 arrays 16-byte aligned, scale arrays 4-byte aligned.
+ */
+moe_status_t moe_expert_mlp_mxfp8(const moe_config_t* cfg, const uint8_t* xq_sorted,
+                                  const uint8_t* xq_scales, const int32_t* expert_offsets,
+                                  const uint8_t* wq_gate, const uint8_t* wq_gate_scales,
+                                  const uint8_t* wq_up, const uint8_t* wq_up_scales,
+                                  const void* w_down, void* y_sorted, void* workspace,
+                                  size_t workspace_bytes, moe_stream_t stream);
 
 /* Tensors of a whole-layer call (moe_forward, moe_forward_dbo). */
 typedef struct moe_layer_tensors {

@@ -146,18 +146,48 @@ def test_dbo_workspace_covers_every_cut(lib, name):
 def test_quantize_mxfp8_rejects_bad_arguments_on_host(lib):
     P = 0x10000  # never dereferenced: every case below fails before any HIP call
     BF, F32, BAD = B.MOE_BF16, B.MOE_F32, 7
+    R, M = B.MOE_MX_ROWS, B.MOE_MX_MFMA
     inv = B.MOE_ERR_INVALID_ARGUMENT
     q = lib.moe_quantize_mxfp8
-    assert q(4, 48, BF, P, 48, P, P, None) == inv          # cols not a multiple of 32
-    assert q(4, 0, BF, P, 0, P, P, None) == inv            # no columns
-    assert q(-1, 64, BF, P, 64, P, P, None) == inv         # negative rows
-    assert q(4, 64, BF, P, 32, P, P, None) == inv          # pitch below cols
-    assert q(4, 64, BAD, P, 64, P, P, None) == inv         # unknown element type
-    assert q(4, 64, BF, None, 64, P, P, None) == inv       # NULL input
-    assert q(4, 64, BF, P, 64, None, P, None) == inv       # NULL codes
-    assert q(4, 64, BF, P, 64, P, None, None) == inv       # NULL scales
-    assert q(4, 64, BF, P + 8, 64, P, P, None) == inv      # input not 16-byte aligned
-    assert q(4, 64, BF, P, 68, P, P, None) == inv          # bf16 pitch not 16-byte aligned
-    assert q(4, 64, F32, P, 66, P, P, None) == inv         # fp32 pitch not 16-byte aligned
-    assert q(4, 64, BF, P, 64, P + 4, P, None) == inv      # codes not 8-byte aligned
-    assert q(0, 64, BF, None, 64, None, None, None) == B.MOE_OK  # nothing to do
+    assert q(4, 48, BF, P, 48, R, P, P, None) == inv          # cols not a multiple of 32
+    assert q(4, 0, BF, P, 0, R, P, P, None) == inv            # no columns
+    assert q(-1, 64, BF, P, 64, R, P, P, None) == inv         # negative rows
+    assert q(4, 64, BF, P, 32, R, P, P, None) == inv          # pitch below cols
+    assert q(4, 64, BAD, P, 64, R, P, P, None) == inv         # unknown element type
+    assert q(4, 64, BF, P, 64, 2, P, P, None) == inv          # unknown scale layout
+    assert q(4, 992, BF, P, 992, M, P, P, None) == inv        # MFMA layout: cols % 512 != 0
+    assert q(4, 64, BF, None, 64, R, P, P, None) == inv       # NULL input
+    assert q(4, 64, BF, P, 64, R, None, P, None) == inv       # NULL codes
+    assert q(4, 64, BF, P, 64, R, P, None, None) == inv       # NULL scales
+    assert q(4, 64, BF, P + 8, 64, R, P, P, None) == inv      # input not 16-byte aligned
+    assert q(4, 64, BF, P, 68, R, P, P, None) == inv          # bf16 pitch not 16-byte aligned
+    assert q(4, 64, F32, P, 66, R, P, P, None) == inv         # fp32 pitch not 16-byte aligned
+    assert q(4, 64, BF, P, 64, R, P + 4, P, None) == inv      # codes not 8-byte aligned
+    assert q(4, 64, BF, P, 64, R, P, P + 2, None) == inv      # scales not 4-byte aligned
+    assert q(0, 64, BF, None, 64, R, None, None, None) == B.MOE_OK  # nothing to do
+
+
+def test_expert_mlp_mxfp8_rejects_bad_arguments_on_host(lib):
+    P = 0x10000
+    f = lib.moe_expert_mlp_mxfp8
+    cfg = W.CONFIGS["dsv3_prefill_ep"]
+    big = 1 << 30
+
+    def call(c, ptrs=None, ws=big):
+        p = ptrs or [P] * 10
+        return f(ctypes.byref(B.config_struct(c)), *p, ws, None)
+
+    assert call(cfg.replace(dtype="f32")) == B.MOE_ERR_UNSUPPORTED
+    assert call(cfg.replace(num_shared=1)) == B.MOE_ERR_UNSUPPORTED
+    assert call(cfg.replace(hidden=7168 - 256)) == B.MOE_ERR_UNSUPPORTED  # d % 512 != 0
+    for k in range(10):  # every pointer is required
+        p = [P] * 10
+        p[k] = None
+        assert call(cfg, p) == B.MOE_ERR_INVALID_ARGUMENT, k
+    p = [P] * 10
+    p[1] = P + 2  # scales must be 4-byte aligned
+    assert call(cfg, p) == B.MOE_ERR_INVALID_ARGUMENT
+    p = [P] * 10
+    p[0] = P + 4  # codes must be 16-byte aligned
+    assert call(cfg, p) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(cfg, ws=1) == B.MOE_ERR_WORKSPACE_TOO_SMALL

@@ -5,7 +5,12 @@ against the oracle on seeded rows, on hand-built edge blocks (all-zero and
 negative-zero blocks, subnormal inputs, ties at every level of E4M3, values that
 scale past 448 and into the non-saturating range of the hardware conversion,
 values near the top of the input type) and on ragged, strided and full-width
-shapes.
+shapes; in the MFMA scale order, the same bytes permuted as the header states.
+
+Block-scaled expert MLP (moe_expert_mlp_mxfp8): against the oracle's fp64 MLP
+on the decoded operands (the oracle's own quantization, bit-equal to the GPU's),
+rel-L2 <= 1e-2 per output tensor like every bf16 output; the GPU's error comes
+only from fp32 accumulation and the bf16 roundings of h and y.
 """
 import sys
 
@@ -14,6 +19,7 @@ import torch
 
 import oracle
 from combine_router_softmax_top_amd import binding as B
+from combine_router_softmax_top_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
@@ -56,13 +62,27 @@ def _edge_rows(dtype) -> torch.Tensor:
     return torch.tensor(cases, dtype=torch.float64).to(dtype)
 
 
-def _gpu_quantize(x: torch.Tensor):
+def _gpu_quantize(x: torch.Tensor, layout: int = B.MOE_MX_ROWS):
     rows, cols = x.shape
     codes = torch.full((rows, cols), 0xAB, dtype=torch.uint8, device="cuda")
     scales = torch.full((rows, cols // 32), 0xAB, dtype=torch.uint8, device="cuda")
-    B.moe_quantize_mxfp8(x, codes, scales)
+    B.moe_quantize_mxfp8(x, codes, scales, layout)
     torch.cuda.synchronize()
     return codes.cpu(), scales.cpu()
+
+
+def _to_mfma_order(nat: torch.Tensor) -> torch.Tensor:
+    """Scale bytes in row order [rows, cols/32] -> the MFMA order: block
+    q = 16g + m of row r, m = 8d + 4j + 2s + h, to byte 2j + s of 32-bit word
+    ((2g + d) rows + r) 2 + h."""
+    rows, nb = nat.shape
+    out = torch.empty(rows * nb, dtype=torch.uint8)
+    r = torch.arange(rows)
+    for q in range(nb):
+        g, m = divmod(q, 16)
+        d, j, s_, h = m >> 3, (m >> 2) & 1, (m >> 1) & 1, m & 1
+        out[(((2 * g + d) * rows + r) * 2 + h) * 4 + 2 * j + s_] = nat[:, q]
+    return out.view(rows, nb)
 
 
 def _check(x_cpu: torch.Tensor, x_dev: torch.Tensor):
@@ -108,9 +128,141 @@ def test_mxfp8_quantize_full_width_dispatch_payload():
     _check(x, x.cuda())
 
 
+@pytest.mark.parametrize("rows,cols", [(3, 512), (37, 1024), (130, 7168)])
+def test_mxfp8_quantize_mfma_scale_order(rows, cols):
+    x = _seeded_rows(rows, cols, 7 + rows, torch.bfloat16)
+    want_c, want_s = oracle.mxfp8_quantize(x)
+    got_c, got_s = _gpu_quantize(x.cuda(), B.MOE_MX_MFMA)
+    assert torch.equal(got_c, want_c)
+    assert torch.equal(got_s, _to_mfma_order(want_s))
+
+
 def test_mxfp8_quantize_zero_rows_is_a_no_op():
     x = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
     codes = torch.empty(0, 64, dtype=torch.uint8, device="cuda")
     scales = torch.empty(0, 2, dtype=torch.uint8, device="cuda")
     B.moe_quantize_mxfp8(x, codes, scales)
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------- expert MLP
+
+def _mlp_case(n_loc, counts, d, I, seed):
+    """Seeded operands of one block-scaled expert-MLP call: x_sorted rows with
+    per-block magnitudes 2^[-6, 6], weights N(0, 0.02^2) with per-block
+    magnitudes 2^[-3, 3], and expert row counts `counts` (padded with empty
+    experts) in a buffer of T*K rows."""
+    g = torch.Generator().manual_seed(seed)
+    total = int(sum(counts))
+    cap = total + 37  # rows past the local count are never read
+    def blocky(rows, cols, lo, hi, std):
+        v = torch.randn(rows, cols, generator=g, dtype=torch.float64) * std
+        mag = torch.randint(lo, hi + 1, (rows, cols // 32), generator=g).to(torch.float64)
+        return (v * torch.exp2(mag).repeat_interleave(32, dim=1)).to(torch.bfloat16)
+    x = blocky(cap, d, -6, 6, 1.0)
+    wg = blocky(n_loc * I, d, -3, 3, 0.02).view(n_loc, I, d)
+    wu = blocky(n_loc * I, d, -3, 3, 0.02).view(n_loc, I, d)
+    wd = (torch.randn(n_loc, d, I, generator=g) * 0.02).to(torch.bfloat16)
+    offsets = torch.zeros(n_loc + 1, dtype=torch.int32)
+    offsets[1:len(counts) + 1] = torch.tensor(counts, dtype=torch.int32).cumsum(0)
+    offsets[len(counts) + 1:] = total
+    return x, wg, wu, wd, offsets, cap
+
+
+def _run_mlp_mxfp8(cfg, x, wg, wu, wd, offsets):
+    n_loc, I, d = wg.shape
+    rows = x.shape[0]
+    dev = lambda t: t.cuda()
+    xq = torch.empty(rows, d, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(rows * d // 32, dtype=torch.uint8, device="cuda")
+    B.moe_quantize_mxfp8(dev(x), xq, xs.view(rows, d // 32), B.MOE_MX_MFMA)
+    wq, ws = [], []
+    for w in (wg, wu):
+        q = torch.empty(n_loc * I, d, dtype=torch.uint8, device="cuda")
+        s_ = torch.empty(n_loc * I * d // 32, dtype=torch.uint8, device="cuda")
+        B.moe_quantize_mxfp8(dev(w.reshape(n_loc * I, d)), q, s_.view(n_loc * I, d // 32),
+                             B.MOE_MX_MFMA)
+        wq.append(q)
+        ws.append(s_)
+    y = torch.full((rows, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    work = B.alloc_workspace(cfg, B.MOE_WS_EXPERT_MLP)
+    B.moe_expert_mlp_mxfp8(cfg, xq, xs, dev(offsets), wq[0], ws[0], wq[1], ws[1], dev(wd), y, work)
+    torch.cuda.synchronize()
+    return y.cpu()
+
+
+def _oracle_rows(rows, row_expert, x, wg, wu, wd):
+    """fp64 MLP of the given x_sorted rows on the oracle-decoded operands."""
+    n_loc, I, d = wg.shape
+    used = sorted(set(row_expert.tolist()))
+    remap = {e: k for k, e in enumerate(used)}
+    deq = lambda t: oracle.mxfp8_dequantize(*oracle.mxfp8_quantize(t))
+    xd = deq(x[rows])
+    gd = torch.stack([deq(wg[e]) for e in used])
+    ud = torch.stack([deq(wu[e]) for e in used])
+    dd = torch.stack([wd[e].double() for e in used])
+    re = torch.tensor([remap[int(e)] for e in row_expert], dtype=torch.int32)
+    return oracle.expert_mlp(xd, re, gd, ud, dd)
+
+
+def _rel_l2(got, want):
+    return float((got.double() - want).norm() / want.norm())
+
+
+MLP_CASES = {
+    # name: (n_loc, counts, d, I): ragged groups, empty experts, every short-tile
+    # height, several row and column tiles, a partial column tile (I % 128 = 64)
+    "ragged_small": (6, [300, 0, 77, 193, 64, 1], 512, 320),
+    "deep_k": (3, [257, 130, 511], 2048, 256),
+    "one_expert": (1, [700], 1024, 192),
+}
+
+
+@pytest.mark.parametrize("name", list(MLP_CASES))
+def test_expert_mlp_mxfp8_matches_oracle(name):
+    n_loc, counts, d, I = MLP_CASES[name]
+    x, wg, wu, wd, offsets, cap = _mlp_case(n_loc, counts, d, I, seed=len(name))
+    K = 1
+    cfg = W.MoEConfig(name, cap, d, max(n_loc, 1), K, I, 0, n_loc, 0, "softmax", True, "bf16",
+                      "normal")
+    y = _run_mlp_mxfp8(cfg, x, wg, wu, wd, offsets)
+    total = int(offsets[-1])
+    row_expert = torch.repeat_interleave(torch.arange(n_loc), (offsets[1:] - offsets[:-1]).long())
+    want = _oracle_rows(torch.arange(total), row_expert, x, wg, wu, wd)
+    err = _rel_l2(y[:total], want)
+    print(f"{name}: rel-L2 {err:.2e}", file=sys.stderr)
+    assert torch.isfinite(y[:total].float()).all()
+    assert err <= 1e-2
+    assert torch.isnan(y[total:].float()).all()  # rows past the local count untouched
+
+
+def test_expert_mlp_mxfp8_full_size_sampled_rows():
+    """The DeepSeek-V3 expert share at full size (T=4096, d=7168, 32 local
+    experts, I=2048) with the routing of its seeded workload: sampled rows of
+    every fourth expert against the oracle."""
+    cfg = W.CONFIGS["dsv3_prefill_ep"]
+    T, K, d, I, n_loc = cfg.num_tokens, cfg.top_k, cfg.hidden, cfg.intermediate, cfg.num_local
+    inp = W.make_inputs(cfg, 0, with_experts=False)
+    ids, _, _ = oracle.route(inp["x"], inp["w_router"], inp["bias"], K, cfg.score,
+                            cfg.renormalize)
+    counts = torch.bincount(ids.flatten().long(), minlength=cfg.num_experts)[:n_loc]
+    g = torch.Generator().manual_seed(5)
+    x = (torch.randn(T * K, d, generator=g) * 0.5).to(torch.bfloat16)
+    wg = (torch.randn(n_loc, I, d, generator=g) * 0.02).to(torch.bfloat16)
+    wu = (torch.randn(n_loc, I, d, generator=g) * 0.02).to(torch.bfloat16)
+    wd = (torch.randn(n_loc, d, I, generator=g) * 0.02).to(torch.bfloat16)
+    offsets = torch.zeros(n_loc + 1, dtype=torch.int32)
+    offsets[1:] = counts.cumsum(0).to(torch.int32)
+    y = _run_mlp_mxfp8(cfg, x, wg, wu, wd, offsets)
+    rows, row_expert = [], []
+    for e in range(0, n_loc, 4):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            pick = torch.unique(torch.tensor([lo, hi - 1, (lo + hi) // 2, lo + (hi - lo) // 3]))
+            rows += pick.tolist()
+            row_expert += [e] * len(pick)
+    rows_t = torch.tensor(rows)
+    want = _oracle_rows(rows_t, torch.tensor(row_expert), x, wg, wu, wd)
+    err = _rel_l2(y[rows_t], want)
+    print(f"dsv3 full size, {len(rows)} sampled rows: rel-L2 {err:.2e}", file=sys.stderr)
+    assert err <= 1e-2
