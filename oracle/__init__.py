@@ -56,6 +56,7 @@ def lib():
             "oracle_e4m3_decode": (ctypes.c_double, [ctypes.c_uint8]),
             "oracle_mxfp8_quantize": (None, [_I, _I, _I, _P, _LL, _P, _P]),
             "oracle_mxfp8_dequantize": (None, [_I, _I, _P, _P, _P]),
+            "oracle_forward_mxfp8": (_I, [_I] * 10 + [_P] * 10),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -186,6 +187,25 @@ def forward(cfg, inp: dict, x=None):
                          _ptr(inp["w_up"]), _ptr(inp["w_down"]), _ptr(inp.get("ws_gate")),
                          _ptr(inp.get("ws_up")), _ptr(inp.get("ws_down")), _ptr(out), _ptr(ids),
                          _ptr(w), _ptr(counts))
+    return out, ids, w, counts
+
+
+def forward_mxfp8(cfg, inp: dict):
+    """Whole layer with the MX-FP8 payload: the dispatched rows and the gate /
+    up weights decoded from their MX-FP8 encodings; returns like forward."""
+    x = inp["x"]
+    T, d = x.shape
+    K, E = cfg.top_k, cfg.num_experts
+    assert cfg.num_shared == 0 and d % 32 == 0
+    out = torch.empty(T, d, dtype=torch.float64)
+    ids = torch.empty(T, K, dtype=torch.int32)
+    w = torch.empty(T, K, dtype=torch.float64)
+    counts = torch.empty(E, dtype=torch.int32)
+    lib().oracle_forward_mxfp8(T, d, E, K, cfg.intermediate, cfg.expert_begin, cfg.expert_end,
+                               SCORE[cfg.score], int(cfg.renormalize), _dt(x), _ptr(x),
+                               _ptr(inp["w_router"]), _ptr(inp["bias"]), _ptr(inp["w_gate"]),
+                               _ptr(inp["w_up"]), _ptr(inp["w_down"]), _ptr(out), _ptr(ids),
+                               _ptr(w), _ptr(counts))
     return out, ids, w, counts
 
 

@@ -19,6 +19,11 @@
 //     experts are small MLPs evaluated by a grouped GEMM, Dispatch section);
 //   * combine: the weighted sum of the selected experts' outputs, written to a
 //     caller-owned tensor (same page, Introduction and Combine section);
+//   * the block-scaled payload: MX-FP8 encoding of rows (E4M3 elements, one
+//     power-of-two scale per 32) and the layer with the dispatched rows and
+//     the gate / up weights replaced by their decodings (same page, Dispatch:
+//     block scaling factors travel with the tokens; Combine: results return
+//     unquantized);
 //   * the dual-microbatch split: the token range cut at the midpoint of the
 //     padded token count, or on a request boundary for a uniform batch of
 //     multi-token queries, only above a token threshold ("Dual Batch
@@ -311,6 +316,63 @@ int oracle_forward(int T, int d, int E, int K, int I, int e_begin, int e_end, in
   }
   oracle_combine(T, d, K, ODT_F64, y.data(), row_of.data(), ODT_F64, w.data(), n_shared,
                  n_shared > 0 ? ysh.data() : nullptr, out);
+  if (ids_out) std::memcpy(ids_out, ids.data(), sizeof(int32_t) * ids.size());
+  if (weights_out) std::memcpy(weights_out, w.data(), sizeof(double) * w.size());
+  if (counts_out) std::memcpy(counts_out, counts.data(), sizeof(int32_t) * counts.size());
+  return n_rows;
+}
+
+void oracle_mxfp8_quantize(int rows, int cols, int dt, const void* in, long long ld,
+                           uint8_t* codes, uint8_t* scales);
+void oracle_mxfp8_dequantize(int rows, int cols, const uint8_t* codes, const uint8_t* scales,
+                             double* out);
+
+// Whole layer with a block-scaled 8-bit payload ("Efficient and portable
+// mixture-of-experts communication", Dispatch: tokens travel to the experts
+// with block scaling factors; Combine: the expert outputs travel back
+// unquantized): as oracle_forward, except that every dispatched row and every
+// row of the gate and up weight stacks is replaced by its MX-FP8 decoding
+// (oracle_mxfp8_quantize, then oracle_mxfp8_dequantize) before the expert
+// MLP.  The router sees the original tokens; the down weights and the combine
+// stay in dtype dt.  No shared experts.  Same outputs as oracle_forward.
+int oracle_forward_mxfp8(int T, int d, int E, int K, int I, int e_begin, int e_end, int score,
+                         int renorm, int dt, const void* x, const void* w_router,
+                         const float* bias, const void* w_gate, const void* w_up,
+                         const void* w_down, double* out, int32_t* ids_out,
+                         double* weights_out, int32_t* counts_out) {
+  const int n_loc = e_end - e_begin;
+  std::vector<int32_t> ids((size_t)T * K), counts(E), offsets(n_loc + 1),
+      src((size_t)T * K), row_of((size_t)T * K);
+  std::vector<double> w((size_t)T * K);
+  oracle_route(T, d, E, K, dt, x, w_router, bias, score, renorm, ids.data(), w.data(), nullptr);
+  int32_t bad = 0;
+  const size_t rb = (size_t)d * dtype_bytes(dt);
+  std::vector<char> xs((size_t)T * K * rb);
+  const int n_rows = oracle_dispatch(T, E, K, e_begin, e_end, ids.data(), counts.data(),
+                                     offsets.data(), src.data(), row_of.data(), &bad, x,
+                                     xs.data(), (long long)rb);
+  std::vector<int32_t> row_expert(std::max(n_rows, 1));
+  for (int j = 0; j < n_loc; ++j)
+    for (int r = offsets[j]; r < offsets[j + 1]; ++r) row_expert[r] = j;
+  // The MX-FP8 decodings of the dispatched rows and of the gate / up stacks.
+  auto decoded = [&](int rows, const void* m) {
+    std::vector<uint8_t> codes((size_t)rows * d), scales((size_t)rows * (d / 32));
+    std::vector<double> v((size_t)rows * d);
+    oracle_mxfp8_quantize(rows, d, dt, m, d, codes.data(), scales.data());
+    oracle_mxfp8_dequantize(rows, d, codes.data(), scales.data(), v.data());
+    return v;
+  };
+  std::vector<double> y((size_t)std::max(n_rows, 1) * d);
+  if (n_rows > 0) {
+    const std::vector<double> xq = decoded(n_rows, xs.data());
+    const std::vector<double> gq = decoded(n_loc * I, w_gate);
+    const std::vector<double> uq = decoded(n_loc * I, w_up);
+    std::vector<double> wd((size_t)n_loc * d * I);
+    for (size_t i = 0; i < wd.size(); ++i) wd[i] = value_at(w_down, i, dt);
+    oracle_expert_mlp(n_rows, d, I, ODT_F64, xq.data(), row_expert.data(), ODT_F64, gq.data(),
+                      uq.data(), wd.data(), y.data());
+  }
+  oracle_combine(T, d, K, ODT_F64, y.data(), row_of.data(), ODT_F64, w.data(), 0, nullptr, out);
   if (ids_out) std::memcpy(ids_out, ids.data(), sizeof(int32_t) * ids.size());
   if (weights_out) std::memcpy(weights_out, w.data(), sizeof(double) * w.size());
   if (counts_out) std::memcpy(counts_out, counts.data(), sizeof(int32_t) * counts.size());

@@ -553,3 +553,61 @@ def test_mxfp8_dequantized_error_bound():
     # the largest element of every block lands in [256, 512) before clamping
     ymax = y.view(16, -1, 32).amax(-1)
     assert bool(((ymax >= 256) & (ymax < 512)).all())
+
+
+def _mx_lossless(shape, gen, lo, hi):
+    """Values (1 + m/8) * 2^e with m in 0..6 and e in [lo, hi], random signs;
+    with every 32-block spanning at most 14 binades below its largest, MX-FP8
+    encodes them exactly (and so does bf16).  m = 7 is left out: a block whose
+    largest value is 1.875 * 2^e scales it to 480 and clamps it to 448."""
+    m = torch.randint(0, 7, shape, generator=gen).double()
+    e = torch.randint(lo, hi + 1, shape, generator=gen).double()
+    sgn = torch.where(torch.rand(shape, generator=gen) < 0.5, -1.0, 1.0).double()
+    return (sgn * (1 + m / 8) * torch.exp2(e)).to(torch.bfloat16)
+
+
+def _mx_layer(seed, lossless):
+    cfg = W.MoEConfig("mx", 40, 96, 8, 2, 64, 1, 6, 0, "softmax", True, "bf16", "normal")
+    inp = W.make_inputs(cfg, seed)
+    if lossless:
+        g = torch.Generator().manual_seed(100 + seed)
+        inp["x"] = _mx_lossless((40, 96), g, -4, 0)
+        inp["w_gate"] = _mx_lossless(inp["w_gate"].shape, g, -9, -5)
+        inp["w_up"] = _mx_lossless(inp["w_up"].shape, g, -9, -5)
+    return cfg, inp
+
+
+def test_mxfp8_forward_equals_forward_on_exactly_encodable_inputs():
+    """When every token and gate / up weight is an MX-FP8 value, the block-scaled
+    layer is the plain layer, bit for bit (same routing, same fp64 sums)."""
+    cfg, inp = _mx_layer(1, lossless=True)
+    codes, scales = oracle.mxfp8_quantize(inp["x"])
+    assert torch.equal(oracle.mxfp8_dequantize(codes, scales), inp["x"].double())
+    out8, ids8, w8, c8 = oracle.forward_mxfp8(cfg, inp)
+    out, ids, w, c = oracle.forward(cfg, inp)
+    assert torch.equal(ids8, ids) and torch.equal(w8, w) and torch.equal(c8, c)
+    assert torch.equal(out8, out)
+
+
+def test_mxfp8_forward_quantizes_payload_and_gate_up_only():
+    """On general inputs the routing is unchanged and the output moves by about
+    the E4M3 rounding (relative 2^-4 per element at most); it equals the plain
+    layer evaluated on the decoded payload and gate / up weights, assembled here
+    from the oracle's own dispatch, expert MLP and combine."""
+    cfg, inp = _mx_layer(2, lossless=False)
+    out8, ids8, w8, _ = oracle.forward_mxfp8(cfg, inp)
+    out, ids, w, _ = oracle.forward(cfg, inp)
+    assert torch.equal(ids8, ids) and torch.equal(w8, w)
+    rel = float((out8 - out).norm() / out.norm())
+    assert 1e-4 < rel < 0.1
+    dq = lambda t: oracle.mxfp8_dequantize(*oracle.mxfp8_quantize(t))
+    n_loc, I, d = inp["w_gate"].shape
+    disp = oracle.dispatch(ids, cfg.num_experts, cfg.expert_begin, cfg.expert_end, inp["x"])
+    offs = disp["offsets"]
+    row_expert = torch.repeat_interleave(torch.arange(n_loc), (offs[1:] - offs[:-1]).long())
+    y = oracle.expert_mlp(dq(disp["x_sorted"]), row_expert,
+                          dq(inp["w_gate"].reshape(-1, d)).view(n_loc, I, d),
+                          dq(inp["w_up"].reshape(-1, d)).view(n_loc, I, d),
+                          inp["w_down"].double())
+    want = oracle.combine(y, disp["row_of"], w, cfg.num_tokens, cfg.top_k)
+    assert torch.equal(out8, want)

@@ -43,6 +43,15 @@ MUTANTS = [
     ("split_without_padding", "  const int t_pad = (T + pad - 1) / pad * pad;", "  const int t_pad = T;"),
     ("bf16_round_truncates", "      r = std::ldexp(std::nearbyint(std::ldexp(v, -q)), q);",
      "      r = std::ldexp(std::trunc(std::ldexp(v, -q)), q);"),
+    ("e4m3_ties_away", "  const double r = std::nearbyint(a / q) * q;  // round to nearest, ties to even",
+     "  const double r = std::round(a / q) * q;"),
+    ("mx_scale_one_binade_low", "        s = std::min(127, std::max(-127, e - 1 - 8));",
+     "        s = std::min(127, std::max(-127, e - 8));"),
+    ("mx_no_clamp", "        codes[(size_t)r * cols + b * 32 + i] = oracle_e4m3_encode(std::min(448.0, std::max(-448.0, v)));",
+     "        codes[(size_t)r * cols + b * 32 + i] = oracle_e4m3_encode(v);"),
+    ("mx_forward_payload_not_encoded",
+     "    oracle_mxfp8_dequantize(rows, d, codes.data(), scales.data(), v.data());",
+     "    for (size_t i = 0; i < v.size(); ++i) v[i] = value_at(m, i, dt);"),
 ]
 
 
