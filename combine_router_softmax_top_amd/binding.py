@@ -28,7 +28,8 @@ EXPORTED = ["moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_f
             "moe_forward_dbo", "moe_forward_dbo_at", "moe_graph_capture_forward",
             "moe_graph_capture_forward_dbo", "moe_graph_launch", "moe_graph_destroy",
             "moe_workspace_bytes", "moe_dbo_split_point", "moe_dbo_plan_split",
-            "moe_quantize_mxfp8", "moe_expert_mlp_mxfp8", "moe_status_string"]
+            "moe_quantize_mxfp8", "moe_expert_mlp_mxfp8", "moe_dispatch_mxfp8",
+            "moe_forward_mxfp8", "moe_status_string"]
 
 
 class MoEError(RuntimeError):
@@ -41,6 +42,12 @@ class ConfigStruct(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_tokens", "hidden", "num_experts", "top_k", "intermediate", "expert_begin",
         "expert_end", "num_shared", "score", "renormalize", "dtype")]
+
+
+class LayerTensorsMxfp8Struct(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "x", "w_router", "bias", "wq_gate", "wq_gate_scales", "wq_up", "wq_up_scales", "w_down",
+        "out", "topk_ids", "topk_weights")]
 
 
 class LayerTensorsStruct(ctypes.Structure):
@@ -78,6 +85,8 @@ def lib() -> ctypes.CDLL:
             "moe_graph_destroy": [P],
             "moe_quantize_mxfp8": [I32, I32, I32, P, ctypes.c_int64, I32, P, P, P],
             "moe_expert_mlp_mxfp8": [C, P, P, P, P, P, P, P, P, P, P, SZ, P],
+            "moe_dispatch_mxfp8": [C, P, P, P, P, P, P, P, P, P, SZ, P],
+            "moe_forward_mxfp8": [C, ctypes.POINTER(LayerTensorsMxfp8Struct), P, SZ, P],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -354,6 +363,49 @@ def moe_expert_mlp_mxfp8(cfg, xq_sorted, xq_scales, expert_offsets, wq_gate, wq_
         0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(stream))
     _check("moe_expert_mlp_mxfp8", st)
+
+
+def moe_dispatch_mxfp8(cfg, x, topk_ids, expert_counts, expert_offsets, xq_sorted, xq_scales,
+                       src_index, row_of, workspace, stream=None):
+    c = _cs(cfg)
+    T, d, E, K = c.num_tokens, c.hidden, c.num_experts, c.top_k
+    n_loc = c.expert_end - c.expert_begin
+    st = lib().moe_dispatch_mxfp8(
+        ctypes.byref(c), _p(x, "x", (T, d), torch.bfloat16),
+        _p(topk_ids, "topk_ids", (T, K), torch.int32),
+        _p(expert_counts, "expert_counts", (E,), torch.int32),
+        _p(expert_offsets, "expert_offsets", (n_loc + 1,), torch.int32),
+        _p(xq_sorted, "xq_sorted", (T * K, d), torch.uint8),
+        _p(xq_scales, "xq_scales", (T * K * d // 32,), torch.uint8),
+        _p(src_index, "src_index", (T * K,), torch.int32),
+        _p(row_of, "row_of", (T * K,), torch.int32), _p(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("moe_dispatch_mxfp8", st)
+
+
+def layer_tensors_mxfp8(cfg, t: dict) -> LayerTensorsMxfp8Struct:
+    c = _cs(cfg)
+    T, d, E, K, I = c.num_tokens, c.hidden, c.num_experts, c.top_k, c.intermediate
+    n_loc = c.expert_end - c.expert_begin
+    u8, bf = torch.uint8, torch.bfloat16
+    return LayerTensorsMxfp8Struct(
+        _p(t["x"], "x", (T, d), bf), _p(t["w_router"], "w_router", (E, d), bf),
+        _p(t.get("bias"), "bias", (E,), torch.float32),
+        _p(t["wq_gate"], "wq_gate", (n_loc, I, d), u8),
+        _p(t["wq_gate_scales"], "wq_gate_scales", (n_loc * I * d // 32,), u8),
+        _p(t["wq_up"], "wq_up", (n_loc, I, d), u8),
+        _p(t["wq_up_scales"], "wq_up_scales", (n_loc * I * d // 32,), u8),
+        _p(t["w_down"], "w_down", (n_loc, d, I), bf), _p(t["out"], "out", (T, d), bf),
+        _p(t["topk_ids"], "topk_ids", (T, K), torch.int32),
+        _p(t["topk_weights"], "topk_weights", (T, K), torch.float32))
+
+
+def moe_forward_mxfp8(cfg, tensors: dict, workspace, stream=None):
+    c = _cs(cfg)
+    lt = layer_tensors_mxfp8(c, tensors)
+    st = lib().moe_forward_mxfp8(ctypes.byref(c), ctypes.byref(lt), _p(workspace, "workspace"),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("moe_forward_mxfp8", st)
 
 
 def alloc_workspace(cfg, kind: int, device="cuda") -> Optional[torch.Tensor]:

@@ -28,6 +28,11 @@
 //  When the local chunk counts do not fit a scatter workgroup's LDS, a
 //  one-workgroup scan kernel computes the offsets and per-(chunk, expert)
 //  row bases first, and the scatter reads them.
+// Block-scaled payload ([PPLX] Dispatch sends tokens with block scaling
+// factors): the scatter can instead encode each bf16 token row once, while it
+// holds it, as MX-FP8 (E4M3 codes, one E8M0 scale per 32 elements, the rule of
+// moe_quantize_mxfp8) and write the codes and the scale words in the MFMA
+// scale layout to every local row of the token: half the row bytes.
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -187,14 +192,16 @@ __device__ void inline_scan(InlineScan& L, const int32_t* __restrict__ hist, int
 
 // NV = 16-byte pieces of the row each lane holds at once.  INLINE: row
 // numbers from inline_scan (hist), else from the scan kernel (base).
-template <int NV, bool INLINE>
+// Q: encode the (bf16) row as MX-FP8 into codes xq [T*K, d] and scale words
+// xs (MFMA layout over T*K rows) instead of copying it to x_sorted.
+template <int NV, bool INLINE, bool Q>
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ base,
     const int32_t* __restrict__ hist, int n_chunks, int E, int T, int K, int eb, int n_loc,
     int row_vecs, u32x4* __restrict__ x_sorted, int32_t* __restrict__ src_index,
     int32_t* __restrict__ row_of, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ n_invalid) {
+    int32_t* __restrict__ n_invalid, uint8_t* __restrict__ xq, uint32_t* __restrict__ xs) {
   __shared__ typename std::conditional<INLINE, InlineScan, int>::type lds;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -234,14 +241,70 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   if (!any) return;
   for (int v0 = 0; v0 < row_vecs; v0 += kWave * NV) {
     if (v0 > 0) load_piece(v0);
-    for (int k = 0; k < K; ++k) {
-      const int rk = __builtin_amdgcn_readlane(myrow, k);
-      if (rk < 0) continue;
-      u32x4* dst = x_sorted + (size_t)rk * row_vecs;
+    if constexpr (Q) {
+      // Piece v (8 elements) sits in lane v % 64 of step u, so a step holds
+      // 16 whole blocks (block q = v / 4, its 4 pieces in lanes 4q'..4q'+3,
+      // q' = q % 16): one scale group g = v0 / 64 + u of the MFMA layout.
+      // row_vecs is a multiple of 64, so a step is wholly in or out.
+      uint32_t code_lo[NV], code_hi[NV], word[NV];
 #pragma unroll
       for (int u = 0; u < NV; ++u) {
-        const int v = v0 + u * kWave + lane;
-        if (v < row_vecs) dst[v] = buf[u];
+        if (v0 + u * kWave >= row_vecs) break;
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[2 * i] = __uint_as_float(buf[u][i] << 16);
+          f[2 * i + 1] = __uint_as_float(buf[u][i] & 0xffff0000u);
+        }
+        float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
+        m = fmaxf(m, __shfl_xor(m, 1));
+        m = fmaxf(m, __shfl_xor(m, 2));
+        const int ef = (int)((__float_as_uint(m) >> 23) & 0xff);
+        const int sc = min(127, max(-127, ef - 127 - 8));
+        const float inv = __uint_as_float((uint32_t)(127 - sc) << 23);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = fminf(448.f, fmaxf(-448.f, f[i] * inv));
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+        code_lo[u] = (uint32_t)lo;
+        code_hi[u] = (uint32_t)hi;
+        // Scale word (d, h) of the group: bytes b = 0..3 are blocks
+        // m = 8d + 2b + h, i.e. lanes 32d + 4h + 8b; lanes 0, 4, 32, 36 write.
+        const int sb = sc + 127;
+        word[u] = (uint32_t)__shfl(sb, lane) | ((uint32_t)__shfl(sb, lane + 8) << 8) |
+                  ((uint32_t)__shfl(sb, lane + 16) << 16) | ((uint32_t)__shfl(sb, lane + 24) << 24);
+      }
+      const bool writer = (lane & ~36) == 0;  // lanes 0, 4, 32, 36
+      const int wd = lane >> 5, wh = (lane >> 2) & 1;
+      for (int k = 0; k < K; ++k) {
+        const int rk = __builtin_amdgcn_readlane(myrow, k);
+        if (rk < 0) continue;
+        uint8_t* dst = xq + (size_t)rk * row_vecs * 8;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          if (v0 + u * kWave >= row_vecs) break;
+          const int v = v0 + u * kWave + lane;
+          *reinterpret_cast<u32x2*>(dst + (size_t)v * 8) = u32x2{code_lo[u], code_hi[u]};
+          if (writer) {
+            const size_t g = (size_t)(v0 / kWave + u);
+            xs[((2 * g + wd) * (size_t)T * K + rk) * 2 + wh] = word[u];
+          }
+        }
+      }
+    } else {
+      for (int k = 0; k < K; ++k) {
+        const int rk = __builtin_amdgcn_readlane(myrow, k);
+        if (rk < 0) continue;
+        u32x4* dst = x_sorted + (size_t)rk * row_vecs;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+          const int v = v0 + u * kWave + lane;
+          if (v < row_vecs) dst[v] = buf[u];
+        }
       }
     }
   }
@@ -252,12 +315,15 @@ void launch_scatter(bool inl, dim3 grid, hipStream_t s, const void* x, const int
                     const int32_t* rank, const int32_t* base, const int32_t* hist, int n_chunks,
                     int E, int T, int K, int eb, int n_loc, int row_vecs, void* x_sorted,
                     int32_t* src_index, int32_t* row_of, int32_t* counts, int32_t* offsets,
-                    int32_t* n_invalid) {
-  auto kern = inl ? dispatch_scatter_kernel<NV, true> : dispatch_scatter_kernel<NV, false>;
+                    int32_t* n_invalid, uint8_t* xq, uint32_t* xs) {
+  auto kern = xq ? (inl ? dispatch_scatter_kernel<NV, true, true>
+                        : dispatch_scatter_kernel<NV, false, true>)
+                 : (inl ? dispatch_scatter_kernel<NV, true, false>
+                        : dispatch_scatter_kernel<NV, false, false>);
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, static_cast<const u32x4*>(x), ids, rank, base,
                      hist, n_chunks, E, T, K, eb, n_loc, row_vecs,
                      static_cast<u32x4*>(x_sorted), src_index, row_of, counts, offsets,
-                     n_invalid);
+                     n_invalid, xq, xs);
 }
 
 }  // namespace
@@ -275,7 +341,8 @@ size_t dispatch_workspace_bytes(const moe_config_t& c) {
 
 hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* ids,
                            int32_t* counts, int32_t* offsets, void* x_sorted, int32_t* src_index,
-                           int32_t* row_of, void* workspace, hipStream_t s) {
+                           int32_t* row_of, void* workspace, hipStream_t s, uint8_t* xq,
+                           uint32_t* xs) {
   const int T = c.num_tokens, K = c.top_k, E = c.num_experts;
   const int eb = c.expert_begin, ee = c.expert_end, n_loc = ee - eb;
   const int n_assign = T * K;
@@ -307,13 +374,13 @@ hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* 
   const dim3 grid(ceil_div(T, 4));
   if (per_lane <= 4)
     launch_scatter<4>(inl, grid, s, x, ids, rank, base, hist, n_chunks, E, T, K, eb, n_loc,
-                      row_vecs, x_sorted, src_index, row_of, counts, offsets, n_invalid);
+                      row_vecs, x_sorted, src_index, row_of, counts, offsets, n_invalid, xq, xs);
   else if (per_lane <= 8)
     launch_scatter<8>(inl, grid, s, x, ids, rank, base, hist, n_chunks, E, T, K, eb, n_loc,
-                      row_vecs, x_sorted, src_index, row_of, counts, offsets, n_invalid);
+                      row_vecs, x_sorted, src_index, row_of, counts, offsets, n_invalid, xq, xs);
   else
     launch_scatter<16>(inl, grid, s, x, ids, rank, base, hist, n_chunks, E, T, K, eb, n_loc,
-                       row_vecs, x_sorted, src_index, row_of, counts, offsets, n_invalid);
+                       row_vecs, x_sorted, src_index, row_of, counts, offsets, n_invalid, xq, xs);
   return hipGetLastError();
 }
 

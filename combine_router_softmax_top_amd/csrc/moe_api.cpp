@@ -299,6 +299,27 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const void* x, const int32_t*
                                          static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_dispatch_mxfp8(const moe_config_t* cfg, const void* x, const int32_t* topk_ids,
+                                int32_t* expert_counts, int32_t* expert_offsets,
+                                uint8_t* xq_sorted, uint8_t* xq_scales, int32_t* src_index,
+                                int32_t* row_of, void* workspace, size_t workspace_bytes,
+                                moe_stream_t stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16 || cfg->hidden % 512 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!x || !topk_ids || !expert_counts || !expert_offsets || !xq_sorted || !xq_scales ||
+      !src_index || !row_of || !workspace)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(xq_sorted, 16) || !aligned(xq_scales, 4) ||
+      !aligned(workspace, 256))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < moe::dispatch_workspace_bytes(*cfg)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return hip_status(moe::launch_dispatch(*cfg, x, topk_ids, expert_counts, expert_offsets,
+                                         nullptr, src_index, row_of, workspace,
+                                         static_cast<hipStream_t>(stream), xq_sorted,
+                                         reinterpret_cast<uint32_t*>(xq_scales)));
+}
+
 moe_status_t moe_expert_mlp(const moe_config_t* cfg, const void* x_sorted,
                             const int32_t* expert_offsets, const void* w_gate, const void* w_up,
                             const void* w_down, void* y_sorted, const void* x,
@@ -397,6 +418,51 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_layer_tensors_t* ten
   if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < layer_scratch(*cfg, nullptr, nullptr)) return MOE_ERR_WORKSPACE_TOO_SMALL;
   return enqueue_layer(*cfg, *tensors, workspace, static_cast<hipStream_t>(stream));
+}
+
+moe_status_t moe_forward_mxfp8(const moe_config_t* cfg,
+                               const moe_layer_tensors_mxfp8_t* tensors, void* workspace,
+                               size_t workspace_bytes, moe_stream_t stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->dtype != MOE_BF16 || cfg->num_shared != 0 || cfg->hidden % 512 != 0)
+    return MOE_ERR_UNSUPPORTED;
+  const moe_layer_tensors_mxfp8_t* t = tensors;
+  if (!t || !t->x || !t->w_router || !t->wq_gate || !t->wq_gate_scales || !t->wq_up ||
+      !t->wq_up_scales || !t->w_down || !t->out || !t->topk_ids || !t->topk_weights)
+    return MOE_ERR_INVALID_ARGUMENT;
+  for (const void* p : {t->x, t->w_router, (const void*)t->wq_gate, (const void*)t->wq_up,
+                        t->w_down, (const void*)t->out})
+    if (!aligned(p, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(t->wq_gate_scales, 4) || !aligned(t->wq_up_scales, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < layer_scratch(*cfg, nullptr, nullptr)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  const int64_t n_loc = cfg->expert_end - cfg->expert_begin;
+  const int64_t kdw = cfg->hidden / 128;
+  if ((int64_t)cfg->num_tokens * cfg->top_k * kdw >= (int64_t(1) << 31) ||
+      n_loc * cfg->intermediate * kdw >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
+  // The bf16 x_sorted region of the layer scratch (T*K*d*2 bytes) holds the
+  // codes (T*K*d bytes) and, after them, the scales (T*K*d/32 bytes).
+  LayerScratch sc;
+  layer_scratch(*cfg, workspace, &sc);
+  const size_t n_codes = (size_t)cfg->num_tokens * cfg->top_k * cfg->hidden;
+  uint8_t* xq = static_cast<uint8_t*>(sc.x_sorted);
+  uint8_t* xs = xq + align_up(n_codes, 256);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = moe::launch_route(*cfg, t->x, t->w_router, t->bias, t->topk_ids,
+                                   t->topk_weights, nullptr, sc.route_ws, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_dispatch(*cfg, t->x, t->topk_ids, sc.counts, sc.offsets, nullptr, sc.src_index,
+                           sc.row_of, sc.dispatch_ws, s, xq, reinterpret_cast<uint32_t*>(xs));
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_expert_mlp_mxfp8(*cfg, xq, xs, sc.offsets, t->wq_gate, t->wq_gate_scales,
+                                   t->wq_up, t->wq_up_scales, t->w_down, sc.y_sorted, sc.mlp_ws,
+                                   s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(
+      moe::launch_combine(*cfg, sc.y_sorted, sc.row_of, t->topk_weights, nullptr, t->out, s));
 }
 
 moe_status_t moe_forward_dbo(const moe_config_t* cfg, const moe_layer_tensors_t* tensors,

@@ -17,6 +17,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -39,9 +40,12 @@ hipError_t launch_route(const moe_config_t& c, const void* x, const void* w_rout
                         void* workspace, hipStream_t s);
 
 size_t dispatch_workspace_bytes(const moe_config_t& c);
+// xq != nullptr: the bf16 rows are encoded as MX-FP8 into codes xq [T*K, d]
+// and scale words xs (MFMA layout, T*K rows); x_sorted is not written.
 hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* ids,
                            int32_t* counts, int32_t* offsets, void* x_sorted, int32_t* src_index,
-                           int32_t* row_of, void* workspace, hipStream_t s);
+                           int32_t* row_of, void* workspace, hipStream_t s,
+                           uint8_t* xq = nullptr, uint32_t* xs = nullptr);
 
 size_t mlp_workspace_bytes(const moe_config_t& c);
 hipError_t launch_expert_mlp(const moe_config_t& c, const void* x_sorted, const int32_t* offsets,

@@ -43,7 +43,6 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
   v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
 }
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 template <typename T>
 __global__ __launch_bounds__(256) void mxfp8_quantize_kernel(const T* __restrict__ in,

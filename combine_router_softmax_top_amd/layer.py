@@ -51,6 +51,35 @@ class MoELayer:
         self.ws_mlp = B.alloc_workspace(self.cs, B.MOE_WS_EXPERT_MLP, dev)
         self._ws_forward: Optional[torch.Tensor] = None
         self._ws_dbo: Optional[torch.Tensor] = None
+        self.mx: Optional[dict] = None  # MX-FP8 gate / up weights (quantize_weights)
+
+    # ---- block-scaled (MX-FP8) path ------------------------------------------
+    def quantize_weights(self) -> dict:
+        """MX-FP8 encodings of the gate and up stacks in the MFMA scale layout
+        (done once, like an offline weight conversion)."""
+        c = self.cfg
+        n_loc, I, d = c.num_local, c.intermediate, c.hidden
+        mx = {}
+        for name, w in (("gate", self.w_gate), ("up", self.w_up)):
+            codes = torch.empty(n_loc, I, d, dtype=torch.uint8, device=self.device)
+            scales = torch.empty(n_loc * I * d // 32, dtype=torch.uint8, device=self.device)
+            B.moe_quantize_mxfp8(w.view(n_loc * I, d), codes.view(n_loc * I, d), scales,
+                                 B.MOE_MX_MFMA)
+            mx["wq_" + name], mx["wq_" + name + "_scales"] = codes, scales
+        self.mx = mx
+        return mx
+
+    def tensors_mxfp8(self, out: Optional[torch.Tensor] = None) -> dict:
+        if self.mx is None:
+            self.quantize_weights()
+        return dict(x=self.x, w_router=self.w_router, bias=self.bias, w_down=self.w_down,
+                    out=self.out if out is None else out, topk_ids=self.topk_ids,
+                    topk_weights=self.topk_weights, **self.mx)
+
+    def forward_mxfp8(self, stream=None, out: Optional[torch.Tensor] = None):
+        if self._ws_forward is None:
+            self._ws_forward = B.alloc_workspace(self.cs, B.MOE_WS_FORWARD, self.device)
+        B.moe_forward_mxfp8(self.cs, self.tensors_mxfp8(out), self._ws_forward, stream)
 
     # ---- stages -------------------------------------------------------------
     def route(self, stream=None, with_logits: bool = True):

@@ -277,6 +277,27 @@ moe_status_t moe_expert_mlp_mxfp8(const moe_config_t* cfg, const uint8_t* xq_sor
                                   const void* w_down, void* y_sorted, void* workspace,
                                   size_t workspace_bytes, moe_stream_t stream);
 
+/*
+ * moe_dispatch_mxfp8 -- moe_dispatch with the block-scaled payload of [PPLX]
+ * Dispatch: each routed token row is encoded once as MX-FP8 (the rule of
+ * moe_quantize_mxfp8) and its codes and scales are written to every local
+ * row of the token.  expert_counts, expert_offsets, src_index, row_of and
+ * n_invalid are exactly those of moe_dispatch; the codes and scales of row r
+ * are moe_quantize_mxfp8 of row r of moe_dispatch's x_sorted.  Requires
+ * cfg->dtype == MOE_BF16 and cfg->hidden a multiple of 512
+ * (MOE_ERR_UNSUPPORTED otherwise).
+ * Arguments as moe_dispatch, with x_sorted replaced by
+ *   xq_sorted  [T*K, d] uint8 E4M3 (out; rows >= N_loc untouched), 16-byte
+ *              aligned
+ *   xq_scales  T*K*d/32 bytes (out), MOE_MX_MFMA layout with rows = T*K
+ *              (entries of rows >= N_loc untouched), 4-byte aligned
+ */
+moe_status_t moe_dispatch_mxfp8(const moe_config_t* cfg, const void* x, const int32_t* topk_ids,
+                                int32_t* expert_counts, int32_t* expert_offsets,
+                                uint8_t* xq_sorted, uint8_t* xq_scales, int32_t* src_index,
+                                int32_t* row_of, void* workspace, size_t workspace_bytes,
+                                moe_stream_t stream);
+
 /* Tensors of a whole-layer call (moe_forward, moe_forward_dbo). */
 typedef struct moe_layer_tensors {
   const void* x;             /* [T, d] dtype                                     */
@@ -301,6 +322,34 @@ typedef struct moe_layer_tensors {
  */
 moe_status_t moe_forward(const moe_config_t* cfg, const moe_layer_tensors_t* tensors,
                          void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/* Tensors of a block-scaled whole-layer call (moe_forward_mxfp8). */
+typedef struct moe_layer_tensors_mxfp8 {
+  const void* x;                /* [T, d] bf16                                      */
+  const void* w_router;         /* [E, d] bf16                                      */
+  const float* bias;            /* [E] fp32 or NULL                                 */
+  const uint8_t* wq_gate;       /* [E_loc, I, d] E4M3 codes                         */
+  const uint8_t* wq_gate_scales;/* MOE_MX_MFMA scales of the [E_loc*I, d] stack     */
+  const uint8_t* wq_up;         /* [E_loc, I, d] E4M3 codes                         */
+  const uint8_t* wq_up_scales;  /* MOE_MX_MFMA scales of the [E_loc*I, d] stack     */
+  const void* w_down;           /* [E_loc, d, I] bf16                               */
+  void* out;                    /* [T, d] bf16 (out)                                */
+  int32_t* topk_ids;            /* [T, K] int32 (out)                               */
+  float* topk_weights;          /* [T, K] fp32 (out)                                */
+} moe_layer_tensors_mxfp8_t;
+
+/*
+ * moe_forward_mxfp8 -- the whole layer with the block-scaled payload on one
+ * stream: moe_route, moe_dispatch_mxfp8, moe_expert_mlp_mxfp8, moe_combine,
+ * the intermediates carved from a workspace of at least
+ * moe_workspace_bytes(cfg, MOE_WS_FORWARD) bytes (256-byte aligned).  The
+ * gate and up weights are passed encoded (moe_quantize_mxfp8 of the
+ * [E_loc*I, d] stacks, MOE_MX_MFMA layout, done once, offline).  Same
+ * requirements as moe_expert_mlp_mxfp8.
+ */
+moe_status_t moe_forward_mxfp8(const moe_config_t* cfg,
+                               const moe_layer_tensors_mxfp8_t* tensors, void* workspace,
+                               size_t workspace_bytes, moe_stream_t stream);
 
 /*
  * moe_forward_dbo -- the layer as two microbatches on two streams of one GPU.
