@@ -44,6 +44,8 @@ def parse():
                    help="skip the graph-replay timing of the whole layer")
     p.add_argument("--no-cold", action="store_true",
                    help="skip the cold-cache dispatch/combine timing")
+    p.add_argument("--no-mxfp8", action="store_true",
+                   help="skip the block-scaled (MX-FP8 payload and gate/up) layer timing")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -335,9 +337,78 @@ def main():
         result["graph_replay"] = graph_replay(args, layer, stream, torch)
     if not args.no_cold:
         result["dispatch_combine_cold"] = cold_dispatch_combine(layer, stream, torch, alg)
+    if not args.no_mxfp8 and cfg.dtype == "bf16" and cfg.num_shared == 0 and cfg.hidden % 512 == 0:
+        result["mxfp8"] = mxfp8_leg(args, layer, stream, torch, alg, n_loc, t_touch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def mxfp8_leg(args, layer, stream, torch, alg, n_loc: int, t_touch: int) -> dict:
+    """The same step with the block-scaled payload: route, moe_dispatch_mxfp8
+    (MX-FP8 rows), moe_expert_mlp_mxfp8 (fp8 gate/up, bf16 down), combine, on
+    the same tokens and the same (encoded) weights, timed the same way."""
+    from combine_router_softmax_top_amd import binding as B
+    cfg = layer.cfg
+    T, K, d, I, E = cfg.num_tokens, cfg.top_k, cfg.hidden, cfg.intermediate, cfg.num_experts
+    ref = layer.out.clone()
+    mx = layer.quantize_weights()
+    xq = torch.empty(T * K, d, dtype=torch.uint8, device=layer.device)
+    xs = torch.empty(T * K * d // 32, dtype=torch.uint8, device=layer.device)
+
+    def step(evs=None):
+        with torch.cuda.stream(stream):
+            if evs is not None:
+                evs[0].record(stream)
+            layer.route(stream, with_logits=False)
+            if evs is not None:
+                evs[1].record(stream)
+            B.moe_dispatch_mxfp8(layer.cs, layer.x, layer.topk_ids, layer.counts, layer.offsets,
+                                 xq, xs, layer.src_index, layer.row_of, layer.ws_dispatch, stream)
+            if evs is not None:
+                evs[2].record(stream)
+            B.moe_expert_mlp_mxfp8(layer.cs, xq, xs, layer.offsets, mx["wq_gate"],
+                                   mx["wq_gate_scales"], mx["wq_up"], mx["wq_up_scales"],
+                                   layer.w_down, layer.y_sorted, layer.ws_mlp, stream)
+            if evs is not None:
+                evs[3].record(stream)
+            layer.combine(stream)
+            if evs is not None:
+                evs[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["route", "dispatch", "expert_mlp", "combine"]
+    stage = {nm: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps
+             for j, nm in enumerate(names)}
+    ms = wall * 1e3 / args.steps
+    # Algorithmic bytes of the block-scaled dispatch: bf16 token rows read once,
+    # codes and scales written per local row, the maps as in the bf16 dispatch.
+    disp = t_touch * d * 2 + n_loc * (d + d // 32) + n_loc * 4 + 2 * T * K * 4 + 2 * E * 4
+    dc_ms = stage["dispatch"] + stage["combine"]
+    dc = disp + alg["combine"]
+    mlp_tf = alg["gemm_flops"] / (stage["expert_mlp"] * 1e-3) / 1e12
+    out = layer.out.float()
+    rel = float((out - ref.float()).norm() / ref.float().norm())
+    return {
+        "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms,
+        "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
+        "dispatch_GB_per_s": disp / (stage["dispatch"] * 1e-3) / 1e9,
+        "dispatch_combine": {"tokens_per_s": T / (dc_ms * 1e-3),
+                             "GB_per_s": dc / (dc_ms * 1e-3) / 1e9,
+                             "frac_hbm_peak": dc / (dc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "algorithmic_bytes": dc},
+        "expert_mlp_TFLOP_per_s": mlp_tf,
+        "expert_mlp_note": "gate/up on fp8 scaled MFMA (peak 5.0 PFLOP/s dense), down on bf16 "
+                           "MFMA (2.5); per-kernel split in the rocprofv3 summary",
+        "rel_l2_vs_bf16_layer": rel}
 
 
 def cold_dispatch_combine(layer, stream, torch, alg, iters: int = 10) -> dict:

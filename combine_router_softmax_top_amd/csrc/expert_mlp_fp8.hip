@@ -128,12 +128,13 @@ struct QTileArgs {
   int row0, rows, m0, n0, N, Kdim;
 };
 
-// LDS: activation and weight k-tiles in rings of two slots each, and two scale
-// regions of 4 KB (region d holds dword d of the current group's scales: 256
-// activation rows x 2 halves, then 256 weight rows x 2 halves).
+// LDS: activation and weight k-tiles in rings of two slots each, and the
+// scales of two groups of four k-tiles, 4 KB per group and dword (region
+// (b, d) holds dword d of the group in buffer b: 256 activation rows x 2
+// halves, then 256 weight rows x 2 halves).
 constexpr int kQStages = 2;
 constexpr int kQScaleRegion = 4096;
-constexpr int kQLds = 2 * kQStages * kSlotBytes + 2 * kQScaleRegion;
+constexpr int kQLds = 2 * kQStages * kSlotBytes + 4 * kQScaleRegion;
 static_assert(kQLds <= 160 * 1024, "LDS budget");
 
 template <int NFA>
@@ -203,10 +204,11 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
   }
   const uint32_t a_gs = (uint32_t)ta.rows_as * 2, b_gs = (uint32_t)ta.rows_bs * 2;
   uint8_t* regions = lds + 2 * kQStages * kSlotBytes;
-  // Dword d of group g into region d (t = 0, 1: activations; 2, 3: weights;
-  // wave 0..3 fill weight rows 0..127 (gate) for t = 2, 128..255 (up) for t = 3).
+  // Dword d of group g into region (g % 2, d) (t = 0, 1: activations; 2, 3:
+  // weights; waves 0..3 fill weight rows 0..127 (gate) for t = 2, 128..255
+  // (up) for t = 3).
   auto stage_scales = [&](int g, int d) {
-    uint8_t* region = regions + d * kQScaleRegion;
+    uint8_t* region = regions + ((g & 1) * 2 + d) * kQScaleRegion;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const uint32_t* src = t < 2 ? as32 + (uint32_t)(2 * g + d) * a_gs
@@ -220,12 +222,12 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
   const uint32_t* rs_a = reinterpret_cast<const uint32_t*>(regions) + a_row0 * 2 + h;
   const uint32_t* rs_b =
       reinterpret_cast<const uint32_t*>(regions) + 512 + (wn * 64 + (lane & 31)) * 2 + h;
-  auto read_scales = [&](int d, uint32_t (&ra)[4], uint32_t (&rb)[kQBF]) {
+  auto read_scales = [&](int g, int d, uint32_t (&ra)[4], uint32_t (&rb)[kQBF]) {
+    const int reg = ((g & 1) * 2 + d) * (kQScaleRegion / 4);
 #pragma unroll
-    for (int i = 0; i < NFA; ++i) ra[i] = rs_a[d * (kQScaleRegion / 4) + i * 64];
+    for (int i = 0; i < NFA; ++i) ra[i] = rs_a[reg + i * 64];
 #pragma unroll
-    for (int j = 0; j < kQBF; ++j)
-      rb[j] = rs_b[d * (kQScaleRegion / 4) + (j >> 1) * 256 + (j & 1) * 64];
+    for (int j = 0; j < kQBF; ++j) rb[j] = rs_b[reg + (j >> 1) * 256 + (j & 1) * 64];
   };
 
   f32x16 acc[4][kQBF];
@@ -238,22 +240,26 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
 
   // Pipeline: both operands in rings of two; A(kt+2) and B(kt+2) are issued
   // after barrier kt into tile kt's slots and must land by barrier kt+1, one
-  // k-tile later, where the wait covers every load (nothing is issued before a
-  // barrier within an iteration).  Fragments are double-buffered across the
-  // two k-steps; the barrier comes before the second k-step's MFMAs.  Scales:
-  // region 1 (k-tiles 2, 3 of group g) is refilled after barrier 0 of the
-  // group and read into registers after barrier 1; region 0 (k-tiles 0, 1 of
-  // group g+1) is refilled after barrier 2 and read after barrier 3.  Every
-  // refill lands by the next barrier and the reads of the old contents precede
-  // the barrier before the refill.
+  // k-tile later.  Fragments are double-buffered across the two k-steps; the
+  // barrier comes before the second k-step's MFMAs.  Scales: both dwords of
+  // group g+1 are loaded after barrier 0 of group g, after that k-tile's tile
+  // loads, into the buffer group g-1 used (its last read, dword 1, preceded
+  // barrier 2 of group g-1).  Loads complete in issue order, so barrier 1 of
+  // the group waits for everything but those 8 youngest loads, and barrier 2
+  // (which waits for barrier 1's k-tile loads) for them too: the scale loads
+  // get two k-tiles, which matters, as they miss the caches more often than
+  // the tiles.  Dword 0 of group g+1 is read into registers after barrier 3
+  // of group g, dword 1 after barrier 1 of group g+1.
   constexpr int kMfma = NFA * kQBF, kReads = 2 * (NFA + kQBF);
   constexpr int kVmPrologue = NA + kQDmaB;  // tile 1 still in flight
+  constexpr int kScaleDma = 8;               // scale loads per wave for one group
   uint8_t* a_slots = lds;
   uint8_t* b_slots = lds + kQStages * kSlotBytes;
   const int nk = Kdim / kQK;  // a multiple of kQGroupTiles
   const int ng = nk / kQGroupTiles;
   const int last = (nk - 1) * kRowBytes;
   stage_scales(0, 0);
+  stage_scales(0, 1);
 #pragma unroll
   for (int t = 0; t < kQStages; ++t) {
     qstage<NA>(a_slots + t * kSlotBytes, a_tile, a_tile, NA, offa, wave, min(t * kRowBytes, last));
@@ -265,7 +271,7 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
   uint32_t sca[4], scb[kQBF];  // the current k-tile pair's scale dwords
 #pragma unroll
   for (int i = NFA; i < 4; ++i) sca[i] = 0u;
-  read_scales(0, sca, scb);
+  read_scales(0, 0, sca, scb);
   load_qfrags<NFA, 0>(a_slots, b_slots, abase, bbase, f0);
 
   for (int g = 0; g < ng; ++g) {
@@ -279,21 +285,26 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
       load_qfrags<NFA, 1>(sa, sb, abase, bbase, f1);
       qmma_step<NFA, 2 * (J % 2)>(f0, sca, scb, acc);
       pin_kstep_schedule<kMfma, kReads, 0>();
-      wait_loads_and_barrier<0>();  // tile kt+1 (and any refilled region) landed
+      // Tile kt+1 landed (and, at J = 2, the scales of group g+1).
+      wait_loads_and_barrier<J == 1 ? kScaleDma : 0>();
       load_qfrags<NFA, 0>(na, nb, abase, bbase, f0);
       const int kb = min((kt + kQStages) * kRowBytes, last);
       qstage<NA>(sa, a_tile, a_tile, NA, offa, wave, kb);
       qstage<kQDmaB>(sb, b_lo, b_hi, kQDmaB / 2, offb, wave, kb);
-      if constexpr (J == 0) stage_scales(g, 1);
-      if constexpr (J == 2) stage_scales(min(g + 1, ng - 1), 0);
+      if constexpr (J == 0) {
+        // In the last group this reloads the group's own scales into its own
+        // buffer: the same bytes, so a read racing the load sees them either
+        // way; the load count stays the one the barrier waits assume.
+        stage_scales(min(g + 1, ng - 1), 0);
+        stage_scales(min(g + 1, ng - 1), 1);
+      }
       qmma_step<NFA, 2 * (J % 2) + 1>(f1, sca, scb, acc);
       // After the last MFMA of the pair that uses them, the scale registers
       // take the next pair's dwords.
-      if constexpr (J == 1) read_scales(1, sca, scb);
-      if constexpr (J == 3) read_scales(0, sca, scb);
+      if constexpr (J == 1) read_scales(g, 1, sca, scb);
+      if constexpr (J == 3) read_scales(g + 1, 0, sca, scb);
       constexpr int kScaleReads = (J == 1 || J == 3) ? NFA + kQBF : 0;
-      pin_kstep_schedule<kMfma, kReads + kScaleReads,
-                         NA + kQDmaB + ((J == 0 || J == 2) ? 4 : 0)>();
+      pin_kstep_schedule<kMfma, kReads + kScaleReads, NA + kQDmaB + (J == 0 ? kScaleDma : 0)>();
     };
     ktile(std::integral_constant<int, 0>{});
     ktile(std::integral_constant<int, 1>{});
