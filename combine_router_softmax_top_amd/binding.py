@@ -29,7 +29,7 @@ EXPORTED = ["moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_f
             "moe_graph_capture_forward_dbo", "moe_graph_launch", "moe_graph_destroy",
             "moe_workspace_bytes", "moe_dbo_split_point", "moe_dbo_plan_split",
             "moe_quantize_mxfp8", "moe_expert_mlp_mxfp8", "moe_dispatch_mxfp8",
-            "moe_forward_mxfp8", "moe_status_string"]
+            "moe_forward_mxfp8", "moe_graph_capture_forward_mxfp8", "moe_status_string"]
 
 
 class MoEError(RuntimeError):
@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
             "moe_expert_mlp_mxfp8": [C, P, P, P, P, P, P, P, P, P, P, SZ, P],
             "moe_dispatch_mxfp8": [C, P, P, P, P, P, P, P, P, P, SZ, P],
             "moe_forward_mxfp8": [C, ctypes.POINTER(LayerTensorsMxfp8Struct), P, SZ, P],
+            "moe_graph_capture_forward_mxfp8": [C, ctypes.POINTER(LayerTensorsMxfp8Struct), P, SZ,
+                                                ctypes.POINTER(P)],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -305,6 +307,18 @@ def moe_graph_capture_forward(cfg, tensors: dict, workspace, dbo: bool = False,
         st = lib().moe_graph_capture_forward(ctypes.byref(c), ctypes.byref(lt),
                                              _p(workspace, "workspace"), nbytes, ctypes.byref(h))
     _check("moe_graph_capture_forward" + ("_dbo" if dbo else ""), st)
+    return Graph(h.value, (tuple(v for v in tensors.values() if v is not None), workspace))
+
+
+def moe_graph_capture_forward_mxfp8(cfg, tensors: dict, workspace) -> "Graph":
+    c = _cs(cfg)
+    lt = layer_tensors_mxfp8(c, tensors)
+    h = ctypes.c_void_p()
+    st = lib().moe_graph_capture_forward_mxfp8(ctypes.byref(c), ctypes.byref(lt),
+                                               _p(workspace, "workspace"),
+                                               workspace.numel() * workspace.element_size(),
+                                               ctypes.byref(h))
+    _check("moe_graph_capture_forward_mxfp8", st)
     return Graph(h.value, (tuple(v for v in tensors.values() if v is not None), workspace))
 
 

@@ -420,14 +420,14 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_layer_tensors_t* ten
   return enqueue_layer(*cfg, *tensors, workspace, static_cast<hipStream_t>(stream));
 }
 
-moe_status_t moe_forward_mxfp8(const moe_config_t* cfg,
-                               const moe_layer_tensors_mxfp8_t* tensors, void* workspace,
-                               size_t workspace_bytes, moe_stream_t stream) {
+// Host checks of a block-scaled whole-layer call (MOE_OK when it may be
+// enqueued).
+moe_status_t check_forward_mxfp8(const moe_config_t* cfg, const moe_layer_tensors_mxfp8_t* t,
+                                 const void* workspace, size_t workspace_bytes) {
   moe_status_t st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (cfg->dtype != MOE_BF16 || cfg->num_shared != 0 || cfg->hidden % 512 != 0)
     return MOE_ERR_UNSUPPORTED;
-  const moe_layer_tensors_mxfp8_t* t = tensors;
   if (!t || !t->x || !t->w_router || !t->wq_gate || !t->wq_gate_scales || !t->wq_up ||
       !t->wq_up_scales || !t->w_down || !t->out || !t->topk_ids || !t->topk_weights)
     return MOE_ERR_INVALID_ARGUMENT;
@@ -443,26 +443,36 @@ moe_status_t moe_forward_mxfp8(const moe_config_t* cfg,
   if ((int64_t)cfg->num_tokens * cfg->top_k * kdw >= (int64_t(1) << 31) ||
       n_loc * cfg->intermediate * kdw >= (int64_t(1) << 31))
     return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status_t enqueue_forward_mxfp8(const moe_config_t& c, const moe_layer_tensors_mxfp8_t& t,
+                                   void* workspace, hipStream_t s) {
   // The bf16 x_sorted region of the layer scratch (T*K*d*2 bytes) holds the
   // codes (T*K*d bytes) and, after them, the scales (T*K*d/32 bytes).
   LayerScratch sc;
-  layer_scratch(*cfg, workspace, &sc);
-  const size_t n_codes = (size_t)cfg->num_tokens * cfg->top_k * cfg->hidden;
+  layer_scratch(c, workspace, &sc);
+  const size_t n_codes = (size_t)c.num_tokens * c.top_k * c.hidden;
   uint8_t* xq = static_cast<uint8_t*>(sc.x_sorted);
   uint8_t* xs = xq + align_up(n_codes, 256);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = moe::launch_route(*cfg, t->x, t->w_router, t->bias, t->topk_ids,
-                                   t->topk_weights, nullptr, sc.route_ws, s);
+  hipError_t e = moe::launch_route(c, t.x, t.w_router, t.bias, t.topk_ids, t.topk_weights,
+                                   nullptr, sc.route_ws, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = moe::launch_dispatch(*cfg, t->x, t->topk_ids, sc.counts, sc.offsets, nullptr, sc.src_index,
+  e = moe::launch_dispatch(c, t.x, t.topk_ids, sc.counts, sc.offsets, nullptr, sc.src_index,
                            sc.row_of, sc.dispatch_ws, s, xq, reinterpret_cast<uint32_t*>(xs));
   if (e != hipSuccess) return MOE_ERR_HIP;
-  e = moe::launch_expert_mlp_mxfp8(*cfg, xq, xs, sc.offsets, t->wq_gate, t->wq_gate_scales,
-                                   t->wq_up, t->wq_up_scales, t->w_down, sc.y_sorted, sc.mlp_ws,
-                                   s);
+  e = moe::launch_expert_mlp_mxfp8(c, xq, xs, sc.offsets, t.wq_gate, t.wq_gate_scales, t.wq_up,
+                                   t.wq_up_scales, t.w_down, sc.y_sorted, sc.mlp_ws, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(
-      moe::launch_combine(*cfg, sc.y_sorted, sc.row_of, t->topk_weights, nullptr, t->out, s));
+  return hip_status(moe::launch_combine(c, sc.y_sorted, sc.row_of, t.topk_weights, nullptr, t.out, s));
+}
+
+moe_status_t moe_forward_mxfp8(const moe_config_t* cfg,
+                               const moe_layer_tensors_mxfp8_t* tensors, void* workspace,
+                               size_t workspace_bytes, moe_stream_t stream) {
+  const moe_status_t st = check_forward_mxfp8(cfg, tensors, workspace, workspace_bytes);
+  if (st != MOE_OK) return st;
+  return enqueue_forward_mxfp8(*cfg, *tensors, workspace, static_cast<hipStream_t>(stream));
 }
 
 moe_status_t moe_forward_dbo(const moe_config_t* cfg, const moe_layer_tensors_t* tensors,
@@ -593,6 +603,20 @@ moe_status_t moe_graph_capture_forward_dbo(const moe_config_t* cfg,
       [&](hipStream_t s0, hipStream_t s1) {
         return moe_forward_dbo(cfg, tensors, workspace, workspace_bytes, min_tokens_to_split, s0,
                                s1);
+      },
+      graph);
+}
+
+moe_status_t moe_graph_capture_forward_mxfp8(const moe_config_t* cfg,
+                                             const moe_layer_tensors_mxfp8_t* tensors,
+                                             void* workspace, size_t workspace_bytes,
+                                             moe_graph_t* graph) {
+  if (!graph) return MOE_ERR_INVALID_ARGUMENT;
+  const moe_status_t st = check_forward_mxfp8(cfg, tensors, workspace, workspace_bytes);
+  if (st != MOE_OK) return st;
+  return capture(
+      [&](hipStream_t s0, hipStream_t) {
+        return enqueue_forward_mxfp8(*cfg, *tensors, workspace, s0);
       },
       graph);
 }

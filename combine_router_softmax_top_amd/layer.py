@@ -142,5 +142,12 @@ class MoELayer:
         return B.moe_graph_capture_forward(self.cs, self.tensors(out), ws, dbo=dbo,
                                            min_tokens_to_split=min_tokens_to_split)
 
+    def capture_forward_mxfp8(self, out: Optional[torch.Tensor] = None) -> B.Graph:
+        """The block-scaled layer (moe_forward_mxfp8) captured as a HIP graph."""
+        if self._ws_forward is None:
+            self._ws_forward = B.alloc_workspace(self.cs, B.MOE_WS_FORWARD, self.device)
+        return B.moe_graph_capture_forward_mxfp8(self.cs, self.tensors_mxfp8(out),
+                                                 self._ws_forward)
+
     def n_rows(self) -> int:
         return int(self.offsets[-1].item())

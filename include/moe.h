@@ -426,6 +426,11 @@ moe_status_t moe_graph_capture_forward_dbo(const moe_config_t* cfg,
                                            const moe_layer_tensors_t* tensors, void* workspace,
                                            size_t workspace_bytes, int32_t min_tokens_to_split,
                                            moe_graph_t* graph);
+/* The same for one moe_forward_mxfp8 call (block-scaled layer). */
+moe_status_t moe_graph_capture_forward_mxfp8(const moe_config_t* cfg,
+                                             const moe_layer_tensors_mxfp8_t* tensors,
+                                             void* workspace, size_t workspace_bytes,
+                                             moe_graph_t* graph);
 moe_status_t moe_graph_launch(moe_graph_t graph, moe_stream_t stream);
 moe_status_t moe_graph_destroy(moe_graph_t graph);
 

@@ -191,3 +191,26 @@ def test_expert_mlp_mxfp8_rejects_bad_arguments_on_host(lib):
     p[0] = P + 4  # codes must be 16-byte aligned
     assert call(cfg, p) == B.MOE_ERR_INVALID_ARGUMENT
     assert call(cfg, ws=1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_block_scaled_forward_and_capture_reject_bad_arguments_on_host(lib):
+    cs = B.config_struct(W.CONFIGS["dsv3_prefill_ep"])
+    h = ctypes.c_void_p()
+    lt = B.LayerTensorsMxfp8Struct()  # all NULL
+    inv, uns = B.MOE_ERR_INVALID_ARGUMENT, B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_forward_mxfp8(ctypes.byref(cs), ctypes.byref(lt), None, 0, None) == inv
+    assert lib.moe_graph_capture_forward_mxfp8(ctypes.byref(cs), ctypes.byref(lt), None, 0,
+                                               ctypes.byref(h)) == inv
+    assert lib.moe_graph_capture_forward_mxfp8(ctypes.byref(cs), ctypes.byref(lt), None, 0,
+                                               None) == inv
+    shared = B.config_struct(W.CONFIGS["dsv2lite_decode"])  # shared experts: not on this path
+    assert lib.moe_forward_mxfp8(ctypes.byref(shared), ctypes.byref(lt), None, 0, None) == uns
+    assert lib.moe_graph_capture_forward_mxfp8(ctypes.byref(shared), ctypes.byref(lt), None, 0,
+                                               ctypes.byref(h)) == uns
+    assert h.value is None
+    P = 0x10000
+    full = B.LayerTensorsMxfp8Struct(*([P] * 11))
+    assert lib.moe_forward_mxfp8(ctypes.byref(cs), ctypes.byref(full), P, 1, None) == \
+        B.MOE_ERR_WORKSPACE_TOO_SMALL
+    full.wq_gate_scales = P + 2  # scales must be 4-byte aligned
+    assert lib.moe_forward_mxfp8(ctypes.byref(cs), ctypes.byref(full), P, 1 << 40, None) == inv

@@ -376,3 +376,30 @@ def test_forward_mxfp8_matches_oracle(name):
     L.forward_mxfp8()
     torch.cuda.synchronize()
     assert torch.equal(first.view(torch.int16), L.out.view(torch.int16))
+
+
+def test_graph_replay_of_the_block_scaled_layer():
+    """The captured block-scaled layer replays bit-equal to the eager call, three
+    times with eager work between, and follows a change of the token buffer."""
+    cfg = MX_LAYERS["dsv3_mx_small"]
+    inp = W.make_inputs(cfg, 0)
+    L = MoELayer(cfg, inp)
+    L.forward_mxfp8()
+    torch.cuda.synchronize()
+    ref = L.out.clone()
+    out = torch.empty_like(L.out)
+    g = L.capture_forward_mxfp8(out=out)
+    for _ in range(3):
+        out.zero_()
+        g.launch()
+        L.forward_mxfp8(out=torch.empty_like(ref))  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    L.x.copy_(torch.flip(L.x, dims=[0]))
+    L.forward_mxfp8()
+    torch.cuda.synchronize()
+    ref2 = L.out.clone()
+    g.launch()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref2.view(torch.int16))
+    g.destroy()
