@@ -346,13 +346,15 @@ def main():
 
 def mxfp8_leg(args, layer, stream, torch, alg, n_loc: int, t_touch: int) -> dict:
     """The same step with the block-scaled payload: route, moe_dispatch_mxfp8
-    (MX-FP8 rows), moe_expert_mlp_mxfp8 (fp8 gate/up, bf16 down), combine, on
-    the same tokens and the same (encoded) weights, timed the same way."""
+    (MX-FP8 rows), moe_expert_mlp_mxfp8 (fp8 gate/up; the down projection in
+    fp8 too when I is a multiple of 512, else in bf16), combine, on the same
+    tokens and the same (encoded) weights, timed the same way."""
     from combine_router_softmax_top_amd import binding as B
     cfg = layer.cfg
     T, K, d, I, E = cfg.num_tokens, cfg.top_k, cfg.hidden, cfg.intermediate, cfg.num_experts
     ref = layer.out.clone()
-    mx = layer.quantize_weights()
+    fp8_down = I % 512 == 0
+    mx = layer.quantize_weights(down=fp8_down)
     xq = torch.empty(T * K, d, dtype=torch.uint8, device=layer.device)
     xs = torch.empty(T * K * d // 32, dtype=torch.uint8, device=layer.device)
 
@@ -369,7 +371,9 @@ def mxfp8_leg(args, layer, stream, torch, alg, n_loc: int, t_touch: int) -> dict
                 evs[2].record(stream)
             B.moe_expert_mlp_mxfp8(layer.cs, xq, xs, layer.offsets, mx["wq_gate"],
                                    mx["wq_gate_scales"], mx["wq_up"], mx["wq_up_scales"],
-                                   layer.w_down, layer.y_sorted, layer.ws_mlp, stream)
+                                   None if fp8_down else layer.w_down, layer.y_sorted,
+                                   layer.ws_mlp, stream, wq_down=mx.get("wq_down"),
+                                   wq_down_scales=mx.get("wq_down_scales"))
             if evs is not None:
                 evs[3].record(stream)
             layer.combine(stream)
@@ -406,8 +410,11 @@ def mxfp8_leg(args, layer, stream, torch, alg, n_loc: int, t_touch: int) -> dict
                              "frac_hbm_peak": dc / (dc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                              "algorithmic_bytes": dc},
         "expert_mlp_TFLOP_per_s": mlp_tf,
-        "expert_mlp_note": "gate/up on fp8 scaled MFMA (peak 5.0 PFLOP/s dense), down on bf16 "
-                           "MFMA (2.5); per-kernel split in the rocprofv3 summary",
+        "down_projection": "fp8" if fp8_down else "bf16",
+        "expert_mlp_note": "gate/up on the fp8 scaled MFMA (dense peak 5.0 PFLOP/s); down on the "
+                           + ("fp8 scaled MFMA with h encoded in the gate/up epilogue"
+                              if fp8_down else "bf16 MFMA (2.5)")
+                           + "; per-kernel split in the rocprofv3 summary",
         "rel_l2_vs_bf16_layer": rel}
 
 

@@ -47,7 +47,7 @@ class ConfigStruct(ctypes.Structure):
 class LayerTensorsMxfp8Struct(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "w_router", "bias", "wq_gate", "wq_gate_scales", "wq_up", "wq_up_scales", "w_down",
-        "out", "topk_ids", "topk_weights")]
+        "wq_down", "wq_down_scales", "out", "topk_ids", "topk_weights")]
 
 
 class LayerTensorsStruct(ctypes.Structure):
@@ -84,7 +84,7 @@ def lib() -> ctypes.CDLL:
             "moe_graph_launch": [P, P],
             "moe_graph_destroy": [P],
             "moe_quantize_mxfp8": [I32, I32, I32, P, ctypes.c_int64, I32, P, P, P],
-            "moe_expert_mlp_mxfp8": [C, P, P, P, P, P, P, P, P, P, P, SZ, P],
+            "moe_expert_mlp_mxfp8": [C, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
             "moe_dispatch_mxfp8": [C, P, P, P, P, P, P, P, P, P, SZ, P],
             "moe_forward_mxfp8": [C, ctypes.POINTER(LayerTensorsMxfp8Struct), P, SZ, P],
             "moe_graph_capture_forward_mxfp8": [C, ctypes.POINTER(LayerTensorsMxfp8Struct), P, SZ,
@@ -359,7 +359,10 @@ def moe_quantize_mxfp8(x, codes, scales, scale_layout: int = 0, stream=None):
 
 
 def moe_expert_mlp_mxfp8(cfg, xq_sorted, xq_scales, expert_offsets, wq_gate, wq_gate_scales,
-                         wq_up, wq_up_scales, w_down, y_sorted, workspace, stream=None):
+                         wq_up, wq_up_scales, w_down, y_sorted, workspace, stream=None,
+                         wq_down=None, wq_down_scales=None):
+    """Block-scaled expert MLP; the down projection in bf16 (w_down) or, with
+    w_down=None and wq_down / wq_down_scales given, in MX-FP8."""
     c = _cs(cfg)
     T, d, K, I = c.num_tokens, c.hidden, c.top_k, c.intermediate
     n_loc = c.expert_end - c.expert_begin
@@ -373,6 +376,8 @@ def moe_expert_mlp_mxfp8(cfg, xq_sorted, xq_scales, expert_offsets, wq_gate, wq_
         _p(wq_up, "wq_up", (n_loc, I, d), u8),
         _p(wq_up_scales, "wq_up_scales", (n_loc * I * d // 32,), u8),
         _p(w_down, "w_down", (n_loc, d, I), torch.bfloat16),
+        _p(wq_down, "wq_down", (n_loc, d, I), u8),
+        _p(wq_down_scales, "wq_down_scales", (n_loc * d * I // 32,), u8),
         _p(y_sorted, "y_sorted", (T * K, d), torch.bfloat16), _p(workspace, "workspace"),
         0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(stream))
@@ -409,7 +414,10 @@ def layer_tensors_mxfp8(cfg, t: dict) -> LayerTensorsMxfp8Struct:
         _p(t["wq_gate_scales"], "wq_gate_scales", (n_loc * I * d // 32,), u8),
         _p(t["wq_up"], "wq_up", (n_loc, I, d), u8),
         _p(t["wq_up_scales"], "wq_up_scales", (n_loc * I * d // 32,), u8),
-        _p(t["w_down"], "w_down", (n_loc, d, I), bf), _p(t["out"], "out", (T, d), bf),
+        _p(t.get("w_down"), "w_down", (n_loc, d, I), bf),
+        _p(t.get("wq_down"), "wq_down", (n_loc, d, I), u8),
+        _p(t.get("wq_down_scales"), "wq_down_scales", (n_loc * d * I // 32,), u8),
+        _p(t["out"], "out", (T, d), bf),
         _p(t["topk_ids"], "topk_ids", (T, K), torch.int32),
         _p(t["topk_weights"], "topk_weights", (T, K), torch.float32))
 

@@ -29,7 +29,10 @@
 //     the loads for the next four k-tiles are issued with the activation loads
 //     and complete by the same barrier;
 //   * tile list, XCD band order and a fixed k order as in the bf16 kernel.
-// The down projection runs on h with the bf16 grouped GEMM.
+// The down projection runs either on bf16 h with the bf16 grouped GEMM, or,
+// with MX-FP8 down weights, on h encoded in the gate/up epilogue (the
+// dispatch's encoding rule, per 32 columns of a row) with this kernel's plain
+// store variant (B tile = 256 rows of one weight matrix, y in bf16).
 #include <type_traits>
 
 #include "grouped_gemm.h"
@@ -118,11 +121,13 @@ __device__ __forceinline__ void qstage(uint8_t* slot, const uint8_t* lo, const u
 struct QTileArgs {
   const uint8_t* A;    // codes of the rows, pitch lda bytes
   const uint8_t* As;   // scales of A, MFMA layout over rows_as rows
-  const uint8_t* Bg;   // gate / up codes of the group, [N, Kdim]
+  const uint8_t* Bg;   // weight codes of the group, [N, Kdim] (gate; up in Bu)
   const uint8_t* Bu;
-  const uint8_t* Bgs;  // gate / up scales, MFMA layout over rows_bs rows
+  const uint8_t* Bgs;  // weight scales, MFMA layout over rows_bs rows (gate; up in Bus)
   const uint8_t* Bus;
-  uint16_t* C;
+  uint16_t* C;         // bf16 output, pitch ldc elements
+  uint8_t* Cq;         // or MX-FP8 output codes (pitch ldc bytes) ...
+  uint8_t* Cs;         // ... and scales, MFMA layout over rows_as rows
   long long rows_as, rows_bs;
   int lda, ldc, brow0;  // brow0: the group's first row in the weight stack
   int row0, rows, m0, n0, N, Kdim;
@@ -137,8 +142,12 @@ constexpr int kQScaleRegion = 4096;
 constexpr int kQLds = 2 * kQStages * kSlotBytes + 4 * kQScaleRegion;
 static_assert(kQLds <= 160 * 1024, "LDS budget");
 
-template <int NFA>
+// EPI_SILU_GLU: B tile rows 0..127 gate, 128..255 the matching up rows, 128
+// h columns out; EPI_STORE: 256 rows of one weight matrix, 256 columns out.
+// QOUT (SiLU-GLU only): h leaves as MX-FP8 codes and MFMA-layout scales.
+template <int EPI, bool QOUT, int NFA>
 __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
+  constexpr bool kGlu = EPI == EPI_SILU_GLU;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -150,7 +159,7 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
 
   const uint8_t* a_tile = ta.A + (long long)(ta.row0 + m0) * ta.lda;
   const uint8_t* b_lo = ta.Bg + (long long)n0 * Kdim;
-  const uint8_t* b_hi = ta.Bu + (long long)n0 * Kdim;
+  const uint8_t* b_hi = kGlu ? ta.Bu + (long long)n0 * Kdim : b_lo;
   const int a_last = ta.rows - 1 - m0;
   const int b_last = N - 1 - n0;
   // Per-lane source offsets; B instructions 4..7 fill tile rows 128..255, the
@@ -161,7 +170,7 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
     const int r = (j * kQWaves + wave) * (1024 / kRowBytes) + lane / 8;
     const int lchunk = (lane & 7) ^ swz(r);
     if (j < NA) offa[j] = (uint32_t)(min(r, a_last) * ta.lda + lchunk * 16);
-    const int br = j < kQDmaB / 2 ? r : r - kQNOut;
+    const int br = (kGlu && j >= kQDmaB / 2) ? r - kQNOut : r;
     offb[j] = (uint32_t)(min(br, b_last) * Kdim + lchunk * 16);
   }
 
@@ -198,7 +207,7 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
     if (q < 8) {
       soff[t] = (uint32_t)(ta.row0 + min(m0 + r, ta.rows - 1)) * 2 + (lane & 1);
     } else {
-      const int n = r < kQNOut ? r : r - kQNOut;
+      const int n = (kGlu && r >= kQNOut) ? r - kQNOut : r;
       soff[t] = (uint32_t)(ta.brow0 + min(n0 + n, N - 1)) * 2 + (lane & 1);
     }
   }
@@ -212,7 +221,7 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const uint32_t* src = t < 2 ? as32 + (uint32_t)(2 * g + d) * a_gs
-                                  : (t == 2 ? bgs32 : bus32) + (uint32_t)(2 * g + d) * b_gs;
+                                  : (t == 2 || !kGlu ? bgs32 : bus32) + (uint32_t)(2 * g + d) * b_gs;
       __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + soff[t]),
                                        (lds_ptr_t)(region + (wave + 4 * t) * 256), 4, 0, 0);
     }
@@ -274,6 +283,11 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
   read_scales(0, 0, sca, scb);
   load_qfrags<NFA, 0>(a_slots, b_slots, abase, bbase, f0);
 
+  // There is at least one group (Kdim >= 512).  Telling the compiler so in
+  // the plain-store variant removes the zero-trip path that kept its zeroed
+  // accumulators alive across the loop (246 registers spilled); the SiLU
+  // variant allocates better without it.
+  if constexpr (!kGlu) __builtin_assume(ng > 0);
   for (int g = 0; g < ng; ++g) {
     auto ktile = [&](auto Jc) {
       constexpr int J = decltype(Jc)::value;
@@ -322,32 +336,75 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
 #pragma unroll
   for (int i = 0; i < NFA; ++i) {
     const int m = m0 + wm * kWaveRows + i * 32 + row_l;
-    if (m >= ta.rows) continue;
-    uint16_t* crow = ta.C + (long long)(ta.row0 + m) * ta.ldc;
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq)
+    if (m >= ta.rows) continue;  // lanes l and l ^ 32 share the row
+    const long long row = ta.row0 + m;
+    if constexpr (QOUT) {
+      // A 32-column block of h is one row of a 32 x 32 MFMA block, 16 values
+      // in each of lanes l and l ^ 32: its MX-FP8 scale from their common
+      // maximum (the encoding rule of the dispatch), 16 codes per lane written
+      // as 4 dwords, the scale byte by the h = 0 lane.  I is a multiple of
+      // 512, so every block is whole.
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * 64 + j * 32 + gq * 8 + col_l;
-        if (n < N) {
-          float v[4];
+        const int nb = n0 + wn * 64 + j * 32;  // first column of the block
+        float v[16];
+        float mx = 0.f;
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            v[q] = silu_f(acc[i][j][4 * gq + q]) * acc[i][j + 2][4 * gq + q];
-          store_bf16x4(crow + n, v);
+        for (int q = 0; q < 16; ++q) {
+          v[q] = silu_f(acc[i][j][q]) * acc[i][j + 2][q];
+          mx = fmaxf(mx, fabsf(v[q]));
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const int ef = (int)((__float_as_uint(mx) >> 23) & 0xff);
+        const int sc = min(127, max(-127, ef - 127 - 8));
+        const float inv = __uint_as_float((uint32_t)(127 - sc) << 23);
+        uint8_t* crow = ta.Cq + row * ta.ldc + nb;
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          float e[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) e[q] = fminf(448.f, fmaxf(-448.f, v[4 * gq + q] * inv));
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+          w = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], w, true);
+          *reinterpret_cast<uint32_t*>(crow + gq * 8 + col_l) = (uint32_t)w;
+        }
+        if (col_l == 0) {
+          const int qb = nb / 32, g = qb >> 4, mm = qb & 15;
+          const int d = mm >> 3, b = ((mm >> 2) & 1) * 2 + ((mm >> 1) & 1), hh = mm & 1;
+          ta.Cs[(((long long)(2 * g + d) * ta.rows_as + row) * 2 + hh) * 4 + b] =
+              (uint8_t)(sc + 127);
         }
       }
+    } else {
+      uint16_t* crow = ta.C + row * ta.ldc;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+        for (int j = 0; j < (kGlu ? 2 : kQBF); ++j) {
+          const int n = n0 + (j >> 1) * 128 + wn * 64 + (j & 1) * 32 + gq * 8 + col_l;
+          if (n < N) {
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              v[q] = kGlu ? silu_f(acc[i][j][4 * gq + q]) * acc[i][j + 2][4 * gq + q]
+                          : acc[i][j][4 * gq + q];
+            store_bf16x4(crow + n, v);
+          }
+        }
+    }
   }
 }
 
-__global__ __launch_bounds__(kQThreads, 1) void gemm_mxfp8_glu_kernel(
+template <int EPI, bool QOUT>
+__global__ __launch_bounds__(kQThreads, 1) void gemm_mxfp8_kernel(
     const uint8_t* __restrict__ A, int lda, const uint8_t* __restrict__ As, long long rows_as,
     const uint8_t* __restrict__ Bg, const uint8_t* __restrict__ Bu, long long strideB_group,
     const uint8_t* __restrict__ Bgs, const uint8_t* __restrict__ Bus, long long rows_bs,
-    uint16_t* __restrict__ C, int ldc, const int32_t* __restrict__ offsets, int n_groups, int N,
-    int Kdim) {
+    uint16_t* __restrict__ C, uint8_t* __restrict__ Cq, uint8_t* __restrict__ Cs, int ldc,
+    const int32_t* __restrict__ offsets, int n_groups, int N, int Kdim) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kQLds];
-  const int nN = (N + kQNOut - 1) / kQNOut;
+  constexpr int kNOut = EPI == EPI_SILU_GLU ? kQNOut : kBN;  // output columns per tile
+  const int nN = (N + kNOut - 1) / kNOut;
   Tile tl;
   if (!find_tile(offsets, n_groups, 0, 0, 0, kBM, nN, tl)) return;
   QTileArgs ta;
@@ -358,6 +415,8 @@ __global__ __launch_bounds__(kQThreads, 1) void gemm_mxfp8_glu_kernel(
   ta.Bgs = Bgs;
   ta.Bus = Bus;
   ta.C = C;
+  ta.Cq = Cq;
+  ta.Cs = Cs;
   ta.rows_as = rows_as;
   ta.rows_bs = rows_bs;
   ta.lda = lda;
@@ -366,38 +425,63 @@ __global__ __launch_bounds__(kQThreads, 1) void gemm_mxfp8_glu_kernel(
   ta.row0 = tl.row0;
   ta.rows = tl.rows;
   ta.m0 = tl.m_tile * kBM;
-  ta.n0 = tl.n_tile * kQNOut;
+  ta.n0 = tl.n_tile * kNOut;
   ta.N = N;
   ta.Kdim = Kdim;
   const int left = tl.rows - ta.m0;
   if (left > 3 * kBM / 4)
-    qgemm_tile<4>(ta, lds);
+    qgemm_tile<EPI, QOUT, 4>(ta, lds);
   else if (left > kBM / 2)
-    qgemm_tile<3>(ta, lds);
+    qgemm_tile<EPI, QOUT, 3>(ta, lds);
   else if (left > kBM / 4)
-    qgemm_tile<2>(ta, lds);
+    qgemm_tile<EPI, QOUT, 2>(ta, lds);
   else
-    qgemm_tile<1>(ta, lds);
+    qgemm_tile<EPI, QOUT, 1>(ta, lds);
 }
 
 }  // namespace
+
+size_t mlp_mxfp8_h_offset(const moe_config_t& c) {
+  return align_up((size_t)c.num_tokens * c.top_k * c.intermediate, 256);
+}
 
 hipError_t launch_expert_mlp_mxfp8(const moe_config_t& c, const uint8_t* xq, const uint8_t* xq_scales,
                                    const int32_t* offsets, const uint8_t* wq_gate,
                                    const uint8_t* wq_gate_scales, const uint8_t* wq_up,
                                    const uint8_t* wq_up_scales, const void* w_down,
+                                   const uint8_t* wq_down, const uint8_t* wq_down_scales,
                                    void* y_sorted, void* workspace, hipStream_t s) {
   const int T = c.num_tokens, K = c.top_k, d = c.hidden, I = c.intermediate;
   const int n_loc = c.expert_end - c.expert_begin;
   const int row_bound = ceil_div(T * K, kBM) + n_loc;
-  const dim3 grid(grid_for(row_bound, ceil_div(I, kQNOut)));
-  uint16_t* h = static_cast<uint16_t*>(workspace);
-  hipLaunchKernelGGL(gemm_mxfp8_glu_kernel, grid, dim3(kQThreads), 0, s, xq, d, xq_scales,
-                     (long long)T * K, wq_gate, wq_up, (long long)I * d, wq_gate_scales,
-                     wq_up_scales, (long long)n_loc * I, h, I, offsets, n_loc, I, d);
+  const long long rows = (long long)T * K;
+  if (wq_down == nullptr) {  // gate/up in fp8, h and the down projection in bf16
+    uint16_t* h = static_cast<uint16_t*>(workspace);
+    hipLaunchKernelGGL((gemm_mxfp8_kernel<EPI_SILU_GLU, false>),
+                       dim3(grid_for(row_bound, ceil_div(I, kQNOut))), dim3(kQThreads), 0, s, xq,
+                       d, xq_scales, rows, wq_gate, wq_up, (long long)I * d, wq_gate_scales,
+                       wq_up_scales, (long long)n_loc * I, h, nullptr, nullptr, I, offsets, n_loc,
+                       I, d);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_grouped_down_bf16(c, h, offsets, w_down, y_sorted, s);
+  }
+  // Both projections in fp8: h leaves the gate/up kernel as MX-FP8 codes
+  // [T*K, I] and MFMA-layout scales (T*K rows), the down kernel's A operand.
+  uint8_t* hq = static_cast<uint8_t*>(workspace);
+  uint8_t* hs = hq + mlp_mxfp8_h_offset(c);
+  hipLaunchKernelGGL((gemm_mxfp8_kernel<EPI_SILU_GLU, true>),
+                     dim3(grid_for(row_bound, ceil_div(I, kQNOut))), dim3(kQThreads), 0, s, xq, d,
+                     xq_scales, rows, wq_gate, wq_up, (long long)I * d, wq_gate_scales,
+                     wq_up_scales, (long long)n_loc * I, nullptr, hq, hs, I, offsets, n_loc, I, d);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_grouped_down_bf16(c, h, offsets, w_down, y_sorted, s);
+  hipLaunchKernelGGL((gemm_mxfp8_kernel<EPI_STORE, false>),
+                     dim3(grid_for(row_bound, ceil_div(d, kBN))), dim3(kQThreads), 0, s, hq, I, hs,
+                     rows, wq_down, wq_down, (long long)d * I, wq_down_scales, wq_down_scales,
+                     (long long)n_loc * d, static_cast<uint16_t*>(y_sorted), nullptr, nullptr, d,
+                     offsets, n_loc, d, I);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -377,20 +377,47 @@ moe_status_t moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t dtype, const
                                                scales, static_cast<hipStream_t>(stream)));
 }
 
-moe_status_t moe_expert_mlp_mxfp8(const moe_config_t* cfg, const uint8_t* xq_sorted,
-                                  const uint8_t* xq_scales, const int32_t* expert_offsets,
-                                  const uint8_t* wq_gate, const uint8_t* wq_gate_scales,
-                                  const uint8_t* wq_up, const uint8_t* wq_up_scales,
-                                  const void* w_down, void* y_sorted, void* workspace,
-                                  size_t workspace_bytes, moe_stream_t stream) {
+// Host checks shared by the block-scaled MLP and layer: configuration,
+// down-projection weights (exactly one of bf16 w_down and MX-FP8 wq_down +
+// scales) and the 32-bit scale indexing of the kernels.
+moe_status_t check_mxfp8_common(const moe_config_t* cfg, const void* w_down,
+                                const uint8_t* wq_down, const uint8_t* wq_down_scales) {
   moe_status_t st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (cfg->dtype != MOE_BF16 || cfg->num_shared != 0 || cfg->hidden % 512 != 0)
     return MOE_ERR_UNSUPPORTED;
-  if (!xq_sorted || !xq_scales || !expert_offsets || !wq_gate || !wq_gate_scales || !wq_up ||
-      !wq_up_scales || !w_down || !y_sorted || !workspace)
+  const bool fp8_down = wq_down != nullptr || wq_down_scales != nullptr;
+  if (fp8_down == (w_down != nullptr) || (fp8_down && (!wq_down || !wq_down_scales)))
     return MOE_ERR_INVALID_ARGUMENT;
-  for (const void* p : {(const void*)xq_sorted, (const void*)wq_gate, (const void*)wq_up, w_down,
+  if (w_down && !aligned(w_down, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (fp8_down && (!aligned(wq_down, 16) || !aligned(wq_down_scales, 4)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (fp8_down && cfg->intermediate % 512 != 0) return MOE_ERR_UNSUPPORTED;
+  // Each scale array is indexed in 32-bit dwords.
+  const int64_t n_loc = cfg->expert_end - cfg->expert_begin;
+  const int64_t rows = (int64_t)cfg->num_tokens * cfg->top_k;
+  const int64_t lim = int64_t(1) << 31;
+  if (rows * (cfg->hidden / 128) >= lim || n_loc * cfg->intermediate * (cfg->hidden / 128) >= lim)
+    return MOE_ERR_UNSUPPORTED;
+  if (fp8_down && (rows * (cfg->intermediate / 128) >= lim ||
+                   n_loc * cfg->hidden * (cfg->intermediate / 128) >= lim))
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status_t moe_expert_mlp_mxfp8(const moe_config_t* cfg, const uint8_t* xq_sorted,
+                                  const uint8_t* xq_scales, const int32_t* expert_offsets,
+                                  const uint8_t* wq_gate, const uint8_t* wq_gate_scales,
+                                  const uint8_t* wq_up, const uint8_t* wq_up_scales,
+                                  const void* w_down, const uint8_t* wq_down,
+                                  const uint8_t* wq_down_scales, void* y_sorted, void* workspace,
+                                  size_t workspace_bytes, moe_stream_t stream) {
+  moe_status_t st = check_mxfp8_common(cfg, w_down, wq_down, wq_down_scales);
+  if (st != MOE_OK) return st;
+  if (!xq_sorted || !xq_scales || !expert_offsets || !wq_gate || !wq_gate_scales || !wq_up ||
+      !wq_up_scales || !y_sorted || !workspace)
+    return MOE_ERR_INVALID_ARGUMENT;
+  for (const void* p : {(const void*)xq_sorted, (const void*)wq_gate, (const void*)wq_up,
                         (const void*)y_sorted})
     if (!aligned(p, 16)) return MOE_ERR_INVALID_ARGUMENT;
   for (const void* p : {(const void*)xq_scales, (const void*)wq_gate_scales,
@@ -398,15 +425,9 @@ moe_status_t moe_expert_mlp_mxfp8(const moe_config_t* cfg, const uint8_t* xq_sor
     if (!aligned(p, 4)) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < moe::mlp_workspace_bytes(*cfg)) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  // The kernel indexes each scale array in 32-bit dwords.
-  const int64_t n_loc = cfg->expert_end - cfg->expert_begin;
-  const int64_t kdw = cfg->hidden / 128;  // scale dwords per row
-  if ((int64_t)cfg->num_tokens * cfg->top_k * kdw >= (int64_t(1) << 31) ||
-      n_loc * cfg->intermediate * kdw >= (int64_t(1) << 31))
-    return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_expert_mlp_mxfp8(
       *cfg, xq_sorted, xq_scales, expert_offsets, wq_gate, wq_gate_scales, wq_up, wq_up_scales,
-      w_down, y_sorted, workspace, static_cast<hipStream_t>(stream)));
+      w_down, wq_down, wq_down_scales, y_sorted, workspace, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_forward(const moe_config_t* cfg, const moe_layer_tensors_t* tensors,
@@ -424,25 +445,19 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_layer_tensors_t* ten
 // enqueued).
 moe_status_t check_forward_mxfp8(const moe_config_t* cfg, const moe_layer_tensors_mxfp8_t* t,
                                  const void* workspace, size_t workspace_bytes) {
-  moe_status_t st = check_config(cfg);
+  if (!t) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status_t st = check_mxfp8_common(cfg, t->w_down, t->wq_down, t->wq_down_scales);
   if (st != MOE_OK) return st;
-  if (cfg->dtype != MOE_BF16 || cfg->num_shared != 0 || cfg->hidden % 512 != 0)
-    return MOE_ERR_UNSUPPORTED;
-  if (!t || !t->x || !t->w_router || !t->wq_gate || !t->wq_gate_scales || !t->wq_up ||
-      !t->wq_up_scales || !t->w_down || !t->out || !t->topk_ids || !t->topk_weights)
+  if (!t->x || !t->w_router || !t->wq_gate || !t->wq_gate_scales || !t->wq_up ||
+      !t->wq_up_scales || !t->out || !t->topk_ids || !t->topk_weights)
     return MOE_ERR_INVALID_ARGUMENT;
   for (const void* p : {t->x, t->w_router, (const void*)t->wq_gate, (const void*)t->wq_up,
-                        t->w_down, (const void*)t->out})
+                        (const void*)t->out})
     if (!aligned(p, 16)) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(t->wq_gate_scales, 4) || !aligned(t->wq_up_scales, 4))
     return MOE_ERR_INVALID_ARGUMENT;
   if (!workspace || !aligned(workspace, 256)) return MOE_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < layer_scratch(*cfg, nullptr, nullptr)) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  const int64_t n_loc = cfg->expert_end - cfg->expert_begin;
-  const int64_t kdw = cfg->hidden / 128;
-  if ((int64_t)cfg->num_tokens * cfg->top_k * kdw >= (int64_t(1) << 31) ||
-      n_loc * cfg->intermediate * kdw >= (int64_t(1) << 31))
-    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -462,7 +477,8 @@ moe_status_t enqueue_forward_mxfp8(const moe_config_t& c, const moe_layer_tensor
                            sc.row_of, sc.dispatch_ws, s, xq, reinterpret_cast<uint32_t*>(xs));
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = moe::launch_expert_mlp_mxfp8(c, xq, xs, sc.offsets, t.wq_gate, t.wq_gate_scales, t.wq_up,
-                                   t.wq_up_scales, t.w_down, sc.y_sorted, sc.mlp_ws, s);
+                                   t.wq_up_scales, t.w_down, t.wq_down, t.wq_down_scales,
+                                   sc.y_sorted, sc.mlp_ws, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(moe::launch_combine(c, sc.y_sorted, sc.row_of, t.topk_weights, nullptr, t.out, s));
 }

@@ -54,27 +54,36 @@ class MoELayer:
         self.mx: Optional[dict] = None  # MX-FP8 gate / up weights (quantize_weights)
 
     # ---- block-scaled (MX-FP8) path ------------------------------------------
-    def quantize_weights(self) -> dict:
-        """MX-FP8 encodings of the gate and up stacks in the MFMA scale layout
-        (done once, like an offline weight conversion)."""
+    def quantize_weights(self, down: bool = False) -> dict:
+        """MX-FP8 encodings of the gate and up stacks (and, with down=True, of
+        the down stack) in the MFMA scale layout, done once like an offline
+        weight conversion."""
         c = self.cfg
         n_loc, I, d = c.num_local, c.intermediate, c.hidden
         mx = {}
-        for name, w in (("gate", self.w_gate), ("up", self.w_up)):
-            codes = torch.empty(n_loc, I, d, dtype=torch.uint8, device=self.device)
-            scales = torch.empty(n_loc * I * d // 32, dtype=torch.uint8, device=self.device)
-            B.moe_quantize_mxfp8(w.view(n_loc * I, d), codes.view(n_loc * I, d), scales,
+        mats = [("gate", self.w_gate, I, d), ("up", self.w_up, I, d)]
+        if down:
+            mats.append(("down", self.w_down, d, I))
+        for name, w, rows, cols in mats:
+            codes = torch.empty(n_loc, rows, cols, dtype=torch.uint8, device=self.device)
+            scales = torch.empty(n_loc * rows * cols // 32, dtype=torch.uint8, device=self.device)
+            B.moe_quantize_mxfp8(w.view(n_loc * rows, cols), codes.view(n_loc * rows, cols), scales,
                                  B.MOE_MX_MFMA)
             mx["wq_" + name], mx["wq_" + name + "_scales"] = codes, scales
         self.mx = mx
         return mx
 
     def tensors_mxfp8(self, out: Optional[torch.Tensor] = None) -> dict:
+        """Tensors of the block-scaled layer: the down projection in MX-FP8 when
+        quantize_weights(down=True) was called, else in bf16."""
         if self.mx is None:
             self.quantize_weights()
-        return dict(x=self.x, w_router=self.w_router, bias=self.bias, w_down=self.w_down,
-                    out=self.out if out is None else out, topk_ids=self.topk_ids,
-                    topk_weights=self.topk_weights, **self.mx)
+        t = dict(x=self.x, w_router=self.w_router, bias=self.bias,
+                 out=self.out if out is None else out, topk_ids=self.topk_ids,
+                 topk_weights=self.topk_weights, **self.mx)
+        if "wq_down" not in self.mx:
+            t["w_down"] = self.w_down
+        return t
 
     def forward_mxfp8(self, stream=None, out: Optional[torch.Tensor] = None):
         if self._ws_forward is None:

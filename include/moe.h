@@ -243,18 +243,22 @@ moe_status_t moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t dtype, const
                                 uint8_t* scales, moe_stream_t stream);
 
 /*
- * moe_expert_mlp_mxfp8 -- moe_expert_mlp with the gate/up projection on
- * MX-FP8 operands: the dispatched payload reaches the grouped GEMM with block
- * scaling factors ([PPLX] Dispatch) and the expert outputs return in 16 bits
- * ([PPLX] Combine).  For each local expert e and each of its rows,
+ * moe_expert_mlp_mxfp8 -- moe_expert_mlp with MX-FP8 operands: the dispatched
+ * payload reaches the grouped GEMM with block scaling factors ([PPLX]
+ * Dispatch) and the expert outputs return in 16 bits ([PPLX] Combine).  For
+ * each local expert e and each of its rows,
  *   h = SiLU(D(xq) D(gq_e)^T) * (D(xq) D(uq_e)^T)   accumulated in fp32,
+ *   y = h' W'_e^T                                   accumulated in fp32,
  *                                                   rounded to bf16,
- *   y = h W_down[e]^T                               bf16 operands, fp32
- *                                                   accumulation, rounded,
  * with D() the decoding of moe_quantize_mxfp8 (every product of two decoded
- * elements is exact in fp32).  Requires cfg->dtype == MOE_BF16,
- * cfg->num_shared == 0 and cfg->hidden a multiple of 512
- * (MOE_ERR_UNSUPPORTED otherwise).
+ * elements is exact in fp32) and, for the down projection, either
+ *   - bf16 weights (w_down given): h' = h rounded to bf16, W'_e = w_down[e]; or
+ *   - MX-FP8 weights (wq_down and wq_down_scales given): h' = D(MX-FP8 encoding
+ *     of h, blocks of 32 along I, from the fp32 values), W'_e = D(wq_down[e]);
+ *     requires cfg->intermediate to be a multiple of 512.
+ * Exactly one of the two must be given.  Requires cfg->dtype == MOE_BF16,
+ * cfg->num_shared == 0 and cfg->hidden a multiple of 512 (MOE_ERR_UNSUPPORTED
+ * otherwise).
  * Arguments (T = num_tokens, K = top_k, d = hidden, I = intermediate,
  * E_loc = expert_end - expert_begin):
  *   xq_sorted       [T*K, d] E4M3 codes of the dispatched rows
@@ -264,7 +268,10 @@ moe_status_t moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t dtype, const
  *   wq_gate_scales, wq_up_scales
  *                   scales of the [E_loc * I, d] stacks, MOE_MX_MFMA layout
  *                   with rows = E_loc * I
- *   w_down          [E_loc, d, I] bf16
+ *   w_down          [E_loc, d, I] bf16, or NULL
+ *   wq_down         [E_loc, d, I] E4M3 codes, or NULL
+ *   wq_down_scales  scales of the [E_loc * d, I] stack, MOE_MX_MFMA layout with
+ *                   rows = E_loc * d, or NULL
  *   y_sorted        [T*K, d] bf16 (out); rows past the local count untouched
  *   workspace       >= moe_workspace_bytes(cfg, MOE_WS_EXPERT_MLP) bytes,
  *                   256-byte aligned
@@ -274,7 +281,8 @@ moe_status_t moe_expert_mlp_mxfp8(const moe_config_t* cfg, const uint8_t* xq_sor
                                   const uint8_t* xq_scales, const int32_t* expert_offsets,
                                   const uint8_t* wq_gate, const uint8_t* wq_gate_scales,
                                   const uint8_t* wq_up, const uint8_t* wq_up_scales,
-                                  const void* w_down, void* y_sorted, void* workspace,
+                                  const void* w_down, const uint8_t* wq_down,
+                                  const uint8_t* wq_down_scales, void* y_sorted, void* workspace,
                                   size_t workspace_bytes, moe_stream_t stream);
 
 /*
@@ -332,7 +340,9 @@ typedef struct moe_layer_tensors_mxfp8 {
   const uint8_t* wq_gate_scales;/* MOE_MX_MFMA scales of the [E_loc*I, d] stack     */
   const uint8_t* wq_up;         /* [E_loc, I, d] E4M3 codes                         */
   const uint8_t* wq_up_scales;  /* MOE_MX_MFMA scales of the [E_loc*I, d] stack     */
-  const void* w_down;           /* [E_loc, d, I] bf16                               */
+  const void* w_down;           /* [E_loc, d, I] bf16, or NULL                      */
+  const uint8_t* wq_down;       /* [E_loc, d, I] E4M3 codes, or NULL                */
+  const uint8_t* wq_down_scales;/* MOE_MX_MFMA scales of the [E_loc*d, I] stack     */
   void* out;                    /* [T, d] bf16 (out)                                */
   int32_t* topk_ids;            /* [T, K] int32 (out)                               */
   float* topk_weights;          /* [T, K] fp32 (out)                                */
@@ -344,8 +354,9 @@ typedef struct moe_layer_tensors_mxfp8 {
  * the intermediates carved from a workspace of at least
  * moe_workspace_bytes(cfg, MOE_WS_FORWARD) bytes (256-byte aligned).  The
  * gate and up weights are passed encoded (moe_quantize_mxfp8 of the
- * [E_loc*I, d] stacks, MOE_MX_MFMA layout, done once, offline).  Same
- * requirements as moe_expert_mlp_mxfp8.
+ * [E_loc*I, d] stacks, MOE_MX_MFMA layout, done once, offline), the down
+ * weights either in bf16 (w_down) or encoded too (wq_down, wq_down_scales;
+ * the other NULL), as for moe_expert_mlp_mxfp8, with the same requirements.
  */
 moe_status_t moe_forward_mxfp8(const moe_config_t* cfg,
                                const moe_layer_tensors_mxfp8_t* tensors, void* workspace,

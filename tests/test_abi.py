@@ -172,25 +172,37 @@ def test_expert_mlp_mxfp8_rejects_bad_arguments_on_host(lib):
     f = lib.moe_expert_mlp_mxfp8
     cfg = W.CONFIGS["dsv3_prefill_ep"]
     big = 1 << 30
+    # xq, xs, offsets, wq_gate, sg, wq_up, su, w_down, wq_down, sd, y, workspace
+    BF16_DOWN = [P] * 8 + [None, None] + [P, P]
+    FP8_DOWN = [P] * 7 + [None, P, P] + [P, P]
 
-    def call(c, ptrs=None, ws=big):
-        p = ptrs or [P] * 10
-        return f(ctypes.byref(B.config_struct(c)), *p, ws, None)
+    def call(c, ptrs=BF16_DOWN, ws=big):
+        return f(ctypes.byref(B.config_struct(c)), *ptrs, ws, None)
 
-    assert call(cfg.replace(dtype="f32")) == B.MOE_ERR_UNSUPPORTED
-    assert call(cfg.replace(num_shared=1)) == B.MOE_ERR_UNSUPPORTED
-    assert call(cfg.replace(hidden=7168 - 256)) == B.MOE_ERR_UNSUPPORTED  # d % 512 != 0
-    for k in range(10):  # every pointer is required
-        p = [P] * 10
-        p[k] = None
-        assert call(cfg, p) == B.MOE_ERR_INVALID_ARGUMENT, k
-    p = [P] * 10
+    inv, uns = B.MOE_ERR_INVALID_ARGUMENT, B.MOE_ERR_UNSUPPORTED
+    assert call(cfg.replace(dtype="f32")) == uns
+    assert call(cfg.replace(num_shared=1)) == uns
+    assert call(cfg.replace(hidden=7168 - 256)) == uns  # d % 512 != 0
+    assert call(cfg.replace(intermediate=2048 - 64), FP8_DOWN) == uns  # fp8 down: I % 512 != 0
+    for k in (0, 1, 2, 3, 4, 5, 6, 10, 11):  # always required
+        for base in (BF16_DOWN, FP8_DOWN):
+            p = list(base)
+            p[k] = None
+            assert call(cfg, p) == inv, k
+    assert call(cfg, [P] * 12) == inv  # bf16 and fp8 down weights both given
+    assert call(cfg, [P] * 7 + [None, None, None, P, P]) == inv  # neither
+    assert call(cfg, [P] * 7 + [None, P, None, P, P]) == inv  # fp8 codes without scales
+    p = list(FP8_DOWN)
+    p[9] = P + 2  # down scales must be 4-byte aligned
+    assert call(cfg, p) == inv
+    p = list(BF16_DOWN)
     p[1] = P + 2  # scales must be 4-byte aligned
-    assert call(cfg, p) == B.MOE_ERR_INVALID_ARGUMENT
-    p = [P] * 10
+    assert call(cfg, p) == inv
+    p = list(BF16_DOWN)
     p[0] = P + 4  # codes must be 16-byte aligned
-    assert call(cfg, p) == B.MOE_ERR_INVALID_ARGUMENT
+    assert call(cfg, p) == inv
     assert call(cfg, ws=1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert call(cfg, FP8_DOWN, ws=1) == B.MOE_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_block_scaled_forward_and_capture_reject_bad_arguments_on_host(lib):
@@ -209,8 +221,11 @@ def test_block_scaled_forward_and_capture_reject_bad_arguments_on_host(lib):
                                                ctypes.byref(h)) == uns
     assert h.value is None
     P = 0x10000
-    full = B.LayerTensorsMxfp8Struct(*([P] * 11))
+    full = B.LayerTensorsMxfp8Struct(*([P] * 13))
+    full.wq_down = full.wq_down_scales = None  # bf16 down weights
     assert lib.moe_forward_mxfp8(ctypes.byref(cs), ctypes.byref(full), P, 1, None) == \
         B.MOE_ERR_WORKSPACE_TOO_SMALL
+    both = B.LayerTensorsMxfp8Struct(*([P] * 13))  # bf16 and fp8 down weights both given
+    assert lib.moe_forward_mxfp8(ctypes.byref(cs), ctypes.byref(both), P, 1 << 40, None) == inv
     full.wq_gate_scales = P + 2  # scales must be 4-byte aligned
     assert lib.moe_forward_mxfp8(ctypes.byref(cs), ctypes.byref(full), P, 1 << 40, None) == inv

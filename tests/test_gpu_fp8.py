@@ -170,40 +170,40 @@ def _mlp_case(n_loc, counts, d, I, seed):
     return x, wg, wu, wd, offsets, cap
 
 
-def _run_mlp_mxfp8(cfg, x, wg, wu, wd, offsets):
+def _encode(w2d: torch.Tensor):
+    rows, cols = w2d.shape
+    q = torch.empty(rows, cols, dtype=torch.uint8, device="cuda")
+    s_ = torch.empty(rows * cols // 32, dtype=torch.uint8, device="cuda")
+    B.moe_quantize_mxfp8(w2d.cuda(), q, s_.view(rows, cols // 32), B.MOE_MX_MFMA)
+    return q, s_
+
+
+def _run_mlp_mxfp8(cfg, x, wg, wu, wd, offsets, down=False):
     n_loc, I, d = wg.shape
     rows = x.shape[0]
-    dev = lambda t: t.cuda()
-    xq = torch.empty(rows, d, dtype=torch.uint8, device="cuda")
-    xs = torch.empty(rows * d // 32, dtype=torch.uint8, device="cuda")
-    B.moe_quantize_mxfp8(dev(x), xq, xs.view(rows, d // 32), B.MOE_MX_MFMA)
-    wq, ws = [], []
-    for w in (wg, wu):
-        q = torch.empty(n_loc * I, d, dtype=torch.uint8, device="cuda")
-        s_ = torch.empty(n_loc * I * d // 32, dtype=torch.uint8, device="cuda")
-        B.moe_quantize_mxfp8(dev(w.reshape(n_loc * I, d)), q, s_.view(n_loc * I, d // 32),
-                             B.MOE_MX_MFMA)
-        wq.append(q)
-        ws.append(s_)
+    xq, xs = _encode(x)
+    gq, gs = _encode(wg.reshape(n_loc * I, d))
+    uq, us = _encode(wu.reshape(n_loc * I, d))
     y = torch.full((rows, d), float("nan"), dtype=torch.bfloat16, device="cuda")
     work = B.alloc_workspace(cfg, B.MOE_WS_EXPERT_MLP)
-    B.moe_expert_mlp_mxfp8(cfg, xq, xs, dev(offsets), wq[0], ws[0], wq[1], ws[1], dev(wd), y, work)
+    if down:
+        dq_, ds_ = _encode(wd.reshape(n_loc * d, I))
+        B.moe_expert_mlp_mxfp8(cfg, xq, xs, offsets.cuda(), gq, gs, uq, us, None, y, work,
+                               wq_down=dq_, wq_down_scales=ds_)
+    else:
+        B.moe_expert_mlp_mxfp8(cfg, xq, xs, offsets.cuda(), gq, gs, uq, us, wd.cuda(), y, work)
     torch.cuda.synchronize()
     return y.cpu()
 
 
-def _oracle_rows(rows, row_expert, x, wg, wu, wd):
-    """fp64 MLP of the given x_sorted rows on the oracle-decoded operands."""
-    n_loc, I, d = wg.shape
+def _oracle_rows(rows, row_expert, x, wg, wu, wd, down=False):
+    """The oracle's block-scaled MLP on the given x_sorted rows, with the stacks
+    of the experts they use."""
     used = sorted(set(row_expert.tolist()))
     remap = {e: k for k, e in enumerate(used)}
-    deq = lambda t: oracle.mxfp8_dequantize(*oracle.mxfp8_quantize(t))
-    xd = deq(x[rows])
-    gd = torch.stack([deq(wg[e]) for e in used])
-    ud = torch.stack([deq(wu[e]) for e in used])
-    dd = torch.stack([wd[e].double() for e in used])
     re = torch.tensor([remap[int(e)] for e in row_expert], dtype=torch.int32)
-    return oracle.expert_mlp(xd, re, gd, ud, dd)
+    pick = lambda w: w[used].contiguous()
+    return oracle.expert_mlp_mxfp8(x[rows].contiguous(), re, pick(wg), pick(wu), pick(wd), down)
 
 
 def _rel_l2(got, want):
@@ -216,28 +216,35 @@ MLP_CASES = {
     "ragged_small": (6, [300, 0, 77, 193, 64, 1], 512, 320),
     "deep_k": (3, [257, 130, 511], 2048, 256),
     "one_expert": (1, [700], 1024, 192),
+    # I a multiple of 512, so the down projection can run in fp8 too; d = 1536
+    # leaves a partial 256-column tile in the fp8 down kernel
+    "ragged_i512": (6, [300, 0, 77, 193, 64, 1], 1536, 512),
+    "deep_i1024": (3, [257, 130, 511], 1024, 1024),
 }
+MLP_PARAMS = [(n, False) for n in MLP_CASES] + \
+    [(n, True) for n, c in MLP_CASES.items() if c[3] % 512 == 0]
 
 
-@pytest.mark.parametrize("name", list(MLP_CASES))
-def test_expert_mlp_mxfp8_matches_oracle(name):
+@pytest.mark.parametrize("name,down", MLP_PARAMS)
+def test_expert_mlp_mxfp8_matches_oracle(name, down):
     n_loc, counts, d, I = MLP_CASES[name]
     x, wg, wu, wd, offsets, cap = _mlp_case(n_loc, counts, d, I, seed=len(name))
     K = 1
     cfg = W.MoEConfig(name, cap, d, max(n_loc, 1), K, I, 0, n_loc, 0, "softmax", True, "bf16",
                       "normal")
-    y = _run_mlp_mxfp8(cfg, x, wg, wu, wd, offsets)
+    y = _run_mlp_mxfp8(cfg, x, wg, wu, wd, offsets, down)
     total = int(offsets[-1])
     row_expert = torch.repeat_interleave(torch.arange(n_loc), (offsets[1:] - offsets[:-1]).long())
-    want = _oracle_rows(torch.arange(total), row_expert, x, wg, wu, wd)
+    want = _oracle_rows(torch.arange(total), row_expert, x, wg, wu, wd, down)
     err = _rel_l2(y[:total], want)
-    print(f"{name}: rel-L2 {err:.2e}", file=sys.stderr)
+    print(f"{name} (fp8 down: {down}): rel-L2 {err:.2e}", file=sys.stderr)
     assert torch.isfinite(y[:total].float()).all()
     assert err <= 1e-2
     assert torch.isnan(y[total:].float()).all()  # rows past the local count untouched
 
 
-def test_expert_mlp_mxfp8_full_size_sampled_rows():
+@pytest.mark.parametrize("down", [False, True])
+def test_expert_mlp_mxfp8_full_size_sampled_rows(down):
     """The DeepSeek-V3 expert share at full size (T=4096, d=7168, 32 local
     experts, I=2048) with the routing of its seeded workload: sampled rows of
     every fourth expert against the oracle."""
@@ -254,7 +261,7 @@ def test_expert_mlp_mxfp8_full_size_sampled_rows():
     wd = (torch.randn(n_loc, d, I, generator=g) * 0.02).to(torch.bfloat16)
     offsets = torch.zeros(n_loc + 1, dtype=torch.int32)
     offsets[1:] = counts.cumsum(0).to(torch.int32)
-    y = _run_mlp_mxfp8(cfg, x, wg, wu, wd, offsets)
+    y = _run_mlp_mxfp8(cfg, x, wg, wu, wd, offsets, down)
     rows, row_expert = [], []
     for e in range(0, n_loc, 4):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
@@ -263,9 +270,10 @@ def test_expert_mlp_mxfp8_full_size_sampled_rows():
             rows += pick.tolist()
             row_expert += [e] * len(pick)
     rows_t = torch.tensor(rows)
-    want = _oracle_rows(rows_t, torch.tensor(row_expert), x, wg, wu, wd)
+    want = _oracle_rows(rows_t, torch.tensor(row_expert), x, wg, wu, wd, down)
     err = _rel_l2(y[rows_t], want)
-    print(f"dsv3 full size, {len(rows)} sampled rows: rel-L2 {err:.2e}", file=sys.stderr)
+    print(f"dsv3 full size (fp8 down: {down}), {len(rows)} sampled rows: rel-L2 {err:.2e}",
+          file=sys.stderr)
     assert err <= 1e-2
 
 
@@ -402,4 +410,45 @@ def test_graph_replay_of_the_block_scaled_layer():
     g.launch()
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref2.view(torch.int16))
+    g.destroy()
+
+
+MX_DOWN_LAYERS = {
+    # the block-scaled layer with the down projection in fp8 too (I % 512 == 0)
+    "dsv3_mxd_small": W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=300, hidden=512,
+                                                           intermediate=512),
+    "mixtral_mxd_small": W.CONFIGS["mixtral_bf16"].replace(num_tokens=257, hidden=1024,
+                                                           intermediate=1536),
+}
+
+
+@pytest.mark.parametrize("name", list(MX_DOWN_LAYERS))
+def test_forward_mxfp8_with_fp8_down_matches_oracle(name):
+    cfg = MX_DOWN_LAYERS[name]
+    inp = W.make_inputs(cfg, 0)
+    L = MoELayer(cfg, inp)
+    L.quantize_weights(down=True)
+    L.forward_mxfp8()
+    torch.cuda.synchronize()
+    out_o, ids_o, _, _ = oracle.forward_mxfp8(cfg, inp, down=True)
+    ids_g = L.topk_ids.cpu()
+    bad = (ids_g != ids_o).any(1).nonzero().flatten().tolist()
+    if bad:
+        z_or = oracle.router_logits(inp["x"], inp["w_router"], inp["bias"])
+        L.route()
+        torch.cuda.synchronize()
+        eps = float((L.logits.cpu().double() - z_or).abs().max())
+        for t in bad:
+            zs = torch.sort(z_or[t], descending=True).values
+            assert float(zs[cfg.top_k - 1] - zs[cfg.top_k]) <= 2 * eps, f"token {t}"
+    keep = torch.tensor([t for t in range(cfg.num_tokens) if t not in set(bad)])
+    err = _rel_l2(L.out.cpu()[keep], out_o[keep])
+    print(f"{name}: rel-L2 {err:.2e}, near-tie tokens {bad}", file=sys.stderr)
+    assert err <= 1e-2
+    g = L.capture_forward_mxfp8()  # and a graph of it replays the same bits
+    ref = L.out.clone()
+    L.out.zero_()
+    g.launch()
+    torch.cuda.synchronize()
+    assert torch.equal(L.out.view(torch.int16), ref.view(torch.int16))
     g.destroy()
