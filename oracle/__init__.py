@@ -56,7 +56,8 @@ def lib():
             "oracle_e4m3_decode": (ctypes.c_double, [ctypes.c_uint8]),
             "oracle_mxfp8_quantize": (None, [_I, _I, _I, _P, _LL, _P, _P]),
             "oracle_mxfp8_dequantize": (None, [_I, _I, _P, _P, _P]),
-            "oracle_forward_mxfp8": (_I, [_I] * 10 + [_P] * 10),
+            "oracle_forward_mxfp8": (_I, [_I] * 10 + [_P] * 6 + [_I] + [_P] * 4),
+            "oracle_expert_mlp_mxfp8": (None, [_I] * 5 + [_P] * 5 + [_I, _P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -190,9 +191,26 @@ def forward(cfg, inp: dict, x=None):
     return out, ids, w, counts
 
 
-def forward_mxfp8(cfg, inp: dict):
+def expert_mlp_mxfp8(x_rows, row_expert, w_gate, w_up, w_down, down: bool = False):
+    """y [n, d] fp64 of the block-scaled expert MLP on rows x_rows [n, d]
+    (row r uses expert row_expert[r] of the stacks)."""
+    n, d = x_rows.shape
+    n_exp, I = w_gate.shape[0], w_gate.shape[1]
+    y = torch.empty(n, d, dtype=torch.float64)
+    if n == 0:
+        return y
+    assert x_rows.dtype == w_gate.dtype == w_up.dtype == w_down.dtype
+    lib().oracle_expert_mlp_mxfp8(n, d, I, n_exp, _dt(x_rows), _ptr(x_rows.contiguous()),
+                                  _ptr(row_expert.to(torch.int32).contiguous()),
+                                  _ptr(w_gate.contiguous()), _ptr(w_up.contiguous()),
+                                  _ptr(w_down.contiguous()), int(down), _ptr(y))
+    return y
+
+
+def forward_mxfp8(cfg, inp: dict, down: bool = False):
     """Whole layer with the MX-FP8 payload: the dispatched rows and the gate /
-    up weights decoded from their MX-FP8 encodings; returns like forward."""
+    up weights decoded from their MX-FP8 encodings (with down=True also h and
+    the down weights); returns like forward."""
     x = inp["x"]
     T, d = x.shape
     K, E = cfg.top_k, cfg.num_experts
@@ -204,8 +222,8 @@ def forward_mxfp8(cfg, inp: dict):
     lib().oracle_forward_mxfp8(T, d, E, K, cfg.intermediate, cfg.expert_begin, cfg.expert_end,
                                SCORE[cfg.score], int(cfg.renormalize), _dt(x), _ptr(x),
                                _ptr(inp["w_router"]), _ptr(inp["bias"]), _ptr(inp["w_gate"]),
-                               _ptr(inp["w_up"]), _ptr(inp["w_down"]), _ptr(out), _ptr(ids),
-                               _ptr(w), _ptr(counts))
+                               _ptr(inp["w_up"]), _ptr(inp["w_down"]), int(down), _ptr(out),
+                               _ptr(ids), _ptr(w), _ptr(counts))
     return out, ids, w, counts
 
 

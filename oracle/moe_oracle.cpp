@@ -327,18 +327,79 @@ void oracle_mxfp8_quantize(int rows, int cols, int dt, const void* in, long long
 void oracle_mxfp8_dequantize(int rows, int cols, const uint8_t* codes, const uint8_t* scales,
                              double* out);
 
+// The expert MLP of the block-scaled layer on n_rows rows x_rows [n_rows, d]
+// (dtype dt; row r uses expert row_expert[r] of the n_exp in the stacks):
+// the rows and every row of the gate / up stacks [n_exp*I, d] replaced by
+// their MX-FP8 decodings, then as oracle_expert_mlp, with the down projection
+// either on the fp64 h and the dtype-dt down weights (down_mx = 0) or on the
+// decodings of h (32-element blocks along I) and of the down stack
+// [n_exp*d, I] (down_mx = 1).  y [n_rows, d] fp64.
+void oracle_expert_mlp_mxfp8(int n_rows, int d, int I, int n_exp, int dt, const void* x_rows,
+                             const int32_t* row_expert, const void* w_gate, const void* w_up,
+                             const void* w_down, int down_mx, double* y) {
+  // The MX-FP8 decoding of a rows x cols matrix of element type t.
+  auto decoded = [&](int rows, int cols, int t, const void* m) {
+    std::vector<uint8_t> codes((size_t)rows * cols), scales((size_t)rows * (cols / 32));
+    std::vector<double> v((size_t)rows * cols);
+    oracle_mxfp8_quantize(rows, cols, t, m, cols, codes.data(), scales.data());
+    oracle_mxfp8_dequantize(rows, cols, codes.data(), scales.data(), v.data());
+    return v;
+  };
+  const std::vector<double> xq = decoded(n_rows, d, dt, x_rows);
+  const std::vector<double> gq = decoded(n_exp * I, d, dt, w_gate);
+  const std::vector<double> uq = decoded(n_exp * I, d, dt, w_up);
+  if (!down_mx) {
+    std::vector<double> wd((size_t)n_exp * d * I);
+    for (size_t i = 0; i < wd.size(); ++i) wd[i] = value_at(w_down, i, dt);
+    oracle_expert_mlp(n_rows, d, I, ODT_F64, xq.data(), row_expert, ODT_F64, gq.data(),
+                      uq.data(), wd.data(), y);
+    return;
+  }
+  // h of every row as in oracle_expert_mlp, then its decoding, then the down
+  // projection on the decoded h and the decoded down weights.
+  std::vector<double> hh((size_t)n_rows * I);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int r = 0; r < n_rows; ++r) {
+    const size_t e = (size_t)row_expert[r];
+    for (int j = 0; j < I; ++j) {
+      double g = 0.0, u = 0.0;
+      const size_t base = (e * I + j) * (size_t)d;
+      for (int i = 0; i < d; ++i) {
+        g += xq[(size_t)r * d + i] * gq[base + i];
+        u += xq[(size_t)r * d + i] * uq[base + i];
+      }
+      hh[(size_t)r * I + j] = silu(g) * u;
+    }
+  }
+  const std::vector<double> hq = decoded(n_rows, I, ODT_F64, hh.data());
+  const std::vector<double> wdq = decoded(n_exp * d, I, dt, w_down);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int r = 0; r < n_rows; ++r) {
+    const size_t e = (size_t)row_expert[r];
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      const size_t base = (e * d + c) * (size_t)I;
+      for (int j = 0; j < I; ++j) acc += hq[(size_t)r * I + j] * wdq[base + j];
+      y[(size_t)r * d + c] = acc;
+    }
+  }
+}
+
 // Whole layer with a block-scaled 8-bit payload ("Efficient and portable
 // mixture-of-experts communication", Dispatch: tokens travel to the experts
 // with block scaling factors; Combine: the expert outputs travel back
 // unquantized): as oracle_forward, except that every dispatched row and every
 // row of the gate and up weight stacks is replaced by its MX-FP8 decoding
 // (oracle_mxfp8_quantize, then oracle_mxfp8_dequantize) before the expert
-// MLP.  The router sees the original tokens; the down weights and the combine
-// stay in dtype dt.  No shared experts.  Same outputs as oracle_forward.
+// MLP.  The router sees the original tokens; the combine stays in dtype dt.
+// down_mx = 0: the down projection on the fp64 h and the dtype-dt down weights.
+// down_mx = 1: the down projection encoded too -- every row of h (32-element
+// blocks along I) and every row of the [E_loc*d, I] down stack replaced by
+// its MX-FP8 decoding.  No shared experts.  Same outputs as oracle_forward.
 int oracle_forward_mxfp8(int T, int d, int E, int K, int I, int e_begin, int e_end, int score,
                          int renorm, int dt, const void* x, const void* w_router,
                          const float* bias, const void* w_gate, const void* w_up,
-                         const void* w_down, double* out, int32_t* ids_out,
+                         const void* w_down, int down_mx, double* out, int32_t* ids_out,
                          double* weights_out, int32_t* counts_out) {
   const int n_loc = e_end - e_begin;
   std::vector<int32_t> ids((size_t)T * K), counts(E), offsets(n_loc + 1),
@@ -354,24 +415,10 @@ int oracle_forward_mxfp8(int T, int d, int E, int K, int I, int e_begin, int e_e
   std::vector<int32_t> row_expert(std::max(n_rows, 1));
   for (int j = 0; j < n_loc; ++j)
     for (int r = offsets[j]; r < offsets[j + 1]; ++r) row_expert[r] = j;
-  // The MX-FP8 decodings of the dispatched rows and of the gate / up stacks.
-  auto decoded = [&](int rows, const void* m) {
-    std::vector<uint8_t> codes((size_t)rows * d), scales((size_t)rows * (d / 32));
-    std::vector<double> v((size_t)rows * d);
-    oracle_mxfp8_quantize(rows, d, dt, m, d, codes.data(), scales.data());
-    oracle_mxfp8_dequantize(rows, d, codes.data(), scales.data(), v.data());
-    return v;
-  };
   std::vector<double> y((size_t)std::max(n_rows, 1) * d);
-  if (n_rows > 0) {
-    const std::vector<double> xq = decoded(n_rows, xs.data());
-    const std::vector<double> gq = decoded(n_loc * I, w_gate);
-    const std::vector<double> uq = decoded(n_loc * I, w_up);
-    std::vector<double> wd((size_t)n_loc * d * I);
-    for (size_t i = 0; i < wd.size(); ++i) wd[i] = value_at(w_down, i, dt);
-    oracle_expert_mlp(n_rows, d, I, ODT_F64, xq.data(), row_expert.data(), ODT_F64, gq.data(),
-                      uq.data(), wd.data(), y.data());
-  }
+  if (n_rows > 0)
+    oracle_expert_mlp_mxfp8(n_rows, d, I, n_loc, dt, xs.data(), row_expert.data(), w_gate, w_up,
+                            w_down, down_mx, y.data());
   oracle_combine(T, d, K, ODT_F64, y.data(), row_of.data(), ODT_F64, w.data(), 0, nullptr, out);
   if (ids_out) std::memcpy(ids_out, ids.data(), sizeof(int32_t) * ids.size());
   if (weights_out) std::memcpy(weights_out, w.data(), sizeof(double) * w.size());

@@ -611,3 +611,33 @@ def test_mxfp8_forward_quantizes_payload_and_gate_up_only():
                           inp["w_down"].double())
     want = oracle.combine(y, disp["row_of"], w, cfg.num_tokens, cfg.top_k)
     assert torch.equal(out8, want)
+
+
+def test_mxfp8_forward_with_encoded_down_encodes_h_per_row():
+    """Identity down weights (d = I) and top-1 routing (weight exactly 1): the
+    layer's output for a token is the MX-FP8 decoding of its h row, h taken
+    from the oracle's own MLP on the decoded payload and gate / up weights."""
+    cfg = W.MoEConfig("mxd", 24, 64, 4, 1, 64, 0, 4, 0, "softmax", True, "bf16", "normal")
+    inp = W.make_inputs(cfg, 3)
+    eye = torch.eye(64).to(torch.bfloat16)
+    inp["w_down"] = torch.stack([eye] * 4).contiguous()
+    out8, ids, w, _ = oracle.forward_mxfp8(cfg, inp, down=True)
+    assert bool((w == 1.0).all())
+    dq = lambda t: oracle.mxfp8_dequantize(*oracle.mxfp8_quantize(t))
+    h = oracle.expert_mlp(dq(inp["x"]), ids[:, 0], dq(inp["w_gate"].reshape(-1, 64)).view(4, 64, 64),
+                          dq(inp["w_up"].reshape(-1, 64)).view(4, 64, 64), inp["w_down"].double())
+    assert torch.equal(out8, dq(h))
+    assert not torch.equal(dq(h), h)  # the encoding of h is visible in this case
+
+
+def test_mxfp8_forward_with_encoded_down_stays_close():
+    """Encoding h and the down weights too moves the output by about the E4M3
+    rounding and keeps the routing."""
+    cfg, inp = _mx_layer(4, lossless=False)
+    cfg = cfg.replace(intermediate=64)
+    inp = W.make_inputs(cfg, 4)
+    a, ids_a, _, _ = oracle.forward_mxfp8(cfg, inp, down=True)
+    b, ids_b, _, _ = oracle.forward_mxfp8(cfg, inp, down=False)
+    assert torch.equal(ids_a, ids_b)
+    rel = float((a - b).norm() / b.norm())
+    assert 1e-4 < rel < 0.1

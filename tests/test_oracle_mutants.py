@@ -50,8 +50,11 @@ MUTANTS = [
     ("mx_no_clamp", "        codes[(size_t)r * cols + b * 32 + i] = oracle_e4m3_encode(std::min(448.0, std::max(-448.0, v)));",
      "        codes[(size_t)r * cols + b * 32 + i] = oracle_e4m3_encode(v);"),
     ("mx_forward_payload_not_encoded",
-     "    oracle_mxfp8_dequantize(rows, d, codes.data(), scales.data(), v.data());",
-     "    for (size_t i = 0; i < v.size(); ++i) v[i] = value_at(m, i, dt);"),
+     "    oracle_mxfp8_dequantize(rows, cols, codes.data(), scales.data(), v.data());",
+     "    for (size_t i = 0; i < v.size(); ++i) v[i] = value_at(m, i, t);"),
+    ("mx_forward_h_not_encoded",
+     "  const std::vector<double> hq = decoded(n_rows, I, ODT_F64, hh.data());",
+     "  const std::vector<double> hq = hh;"),
 ]
 
 
