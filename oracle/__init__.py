@@ -56,7 +56,7 @@ def lib():
             "oracle_e4m3_decode": (ctypes.c_double, [ctypes.c_uint8]),
             "oracle_mxfp8_quantize": (None, [_I, _I, _I, _P, _LL, _P, _P]),
             "oracle_mxfp8_dequantize": (None, [_I, _I, _P, _P, _P]),
-            "oracle_forward_mxfp8": (_I, [_I] * 10 + [_P] * 6 + [_I] + [_P] * 4),
+            "oracle_forward_mxfp8": (_I, [_I] * 11 + [_P] * 9 + [_I] + [_P] * 4),
             "oracle_expert_mlp_mxfp8": (None, [_I] * 5 + [_P] * 5 + [_I, _P]),
         }
         for name, (res, args) in sig.items():
@@ -208,22 +208,26 @@ def expert_mlp_mxfp8(x_rows, row_expert, w_gate, w_up, w_down, down: bool = Fals
 
 
 def forward_mxfp8(cfg, inp: dict, down: bool = False):
-    """Whole layer with the MX-FP8 payload: the dispatched rows and the gate /
-    up weights decoded from their MX-FP8 encodings (with down=True also h and
-    the down weights); returns like forward."""
+    """Whole layer with the MX-FP8 payload: the dispatched rows (and, for the
+    shared experts, the tokens) and the gate / up weights decoded from their
+    MX-FP8 encodings (with down=True also h and the down weights); returns
+    like forward."""
     x = inp["x"]
     T, d = x.shape
     K, E = cfg.top_k, cfg.num_experts
-    assert cfg.num_shared == 0 and d % 32 == 0
+    assert d % 32 == 0
     out = torch.empty(T, d, dtype=torch.float64)
     ids = torch.empty(T, K, dtype=torch.int32)
     w = torch.empty(T, K, dtype=torch.float64)
     counts = torch.empty(E, dtype=torch.int32)
-    lib().oracle_forward_mxfp8(T, d, E, K, cfg.intermediate, cfg.expert_begin, cfg.expert_end,
+    S = cfg.num_shared
+    sh = lambda k: _ptr(inp.get(k)) if S > 0 else None
+    lib().oracle_forward_mxfp8(T, d, E, K, cfg.intermediate, cfg.expert_begin, cfg.expert_end, S,
                                SCORE[cfg.score], int(cfg.renormalize), _dt(x), _ptr(x),
                                _ptr(inp["w_router"]), _ptr(inp["bias"]), _ptr(inp["w_gate"]),
-                               _ptr(inp["w_up"]), _ptr(inp["w_down"]), int(down), _ptr(out),
-                               _ptr(ids), _ptr(w), _ptr(counts))
+                               _ptr(inp["w_up"]), _ptr(inp["w_down"]), sh("ws_gate"),
+                               sh("ws_up"), sh("ws_down"), int(down), _ptr(out), _ptr(ids),
+                               _ptr(w), _ptr(counts))
     return out, ids, w, counts
 
 

@@ -395,11 +395,14 @@ void oracle_expert_mlp_mxfp8(int n_rows, int d, int I, int n_exp, int dt, const 
 // down_mx = 0: the down projection on the fp64 h and the dtype-dt down weights.
 // down_mx = 1: the down projection encoded too -- every row of h (32-element
 // blocks along I) and every row of the [E_loc*d, I] down stack replaced by
-// its MX-FP8 decoding.  No shared experts.  Same outputs as oracle_forward.
-int oracle_forward_mxfp8(int T, int d, int E, int K, int I, int e_begin, int e_end, int score,
-                         int renorm, int dt, const void* x, const void* w_router,
+// its MX-FP8 decoding.  Shared experts (n_shared > 0, stacks ws_*) run the
+// same block-scaled MLP on every token, the token encoded like a dispatched
+// row.  Same outputs as oracle_forward.
+int oracle_forward_mxfp8(int T, int d, int E, int K, int I, int e_begin, int e_end, int n_shared,
+                         int score, int renorm, int dt, const void* x, const void* w_router,
                          const float* bias, const void* w_gate, const void* w_up,
-                         const void* w_down, int down_mx, double* out, int32_t* ids_out,
+                         const void* w_down, const void* ws_gate, const void* ws_up,
+                         const void* ws_down, int down_mx, double* out, int32_t* ids_out,
                          double* weights_out, int32_t* counts_out) {
   const int n_loc = e_end - e_begin;
   std::vector<int32_t> ids((size_t)T * K), counts(E), offsets(n_loc + 1),
@@ -419,7 +422,20 @@ int oracle_forward_mxfp8(int T, int d, int E, int K, int I, int e_begin, int e_e
   if (n_rows > 0)
     oracle_expert_mlp_mxfp8(n_rows, d, I, n_loc, dt, xs.data(), row_expert.data(), w_gate, w_up,
                             w_down, down_mx, y.data());
-  oracle_combine(T, d, K, ODT_F64, y.data(), row_of.data(), ODT_F64, w.data(), 0, nullptr, out);
+  // Shared experts: the same block-scaled MLP on every token (its input, the
+  // token, encoded like a dispatched row), weight one in the combine.
+  std::vector<double> ysh;
+  if (n_shared > 0) {
+    ysh.resize((size_t)n_shared * T * d);
+    std::vector<int32_t> sh_expert(T);
+    for (int s = 0; s < n_shared; ++s) {
+      for (int t = 0; t < T; ++t) sh_expert[t] = s;
+      oracle_expert_mlp_mxfp8(T, d, I, n_shared, dt, x, sh_expert.data(), ws_gate, ws_up, ws_down,
+                              down_mx, ysh.data() + (size_t)s * T * d);
+    }
+  }
+  oracle_combine(T, d, K, ODT_F64, y.data(), row_of.data(), ODT_F64, w.data(), n_shared,
+                 n_shared > 0 ? ysh.data() : nullptr, out);
   if (ids_out) std::memcpy(ids_out, ids.data(), sizeof(int32_t) * ids.size());
   if (weights_out) std::memcpy(weights_out, w.data(), sizeof(double) * w.size());
   if (counts_out) std::memcpy(counts_out, counts.data(), sizeof(int32_t) * counts.size());

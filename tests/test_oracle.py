@@ -641,3 +641,26 @@ def test_mxfp8_forward_with_encoded_down_stays_close():
     assert torch.equal(ids_a, ids_b)
     rel = float((a - b).norm() / b.norm())
     assert 1e-4 < rel < 0.1
+
+
+def test_mxfp8_forward_shared_experts_add_their_block_scaled_mlp():
+    """Shared experts in the block-scaled layer: the output minus the routed-only
+    layer is the sum over shared experts of the oracle's block-scaled MLP on
+    every token (weight one), and on exactly encodable inputs the whole layer
+    equals the plain one."""
+    cfg = W.MoEConfig("mxs", 30, 96, 8, 2, 64, 1, 6, 2, "softmax", False, "bf16", "normal")
+    inp = W.make_inputs(cfg, 5)
+    full, ids, _, _ = oracle.forward_mxfp8(cfg, inp)
+    routed, ids_r, _, _ = oracle.forward_mxfp8(cfg.replace(num_shared=0), inp)
+    assert torch.equal(ids, ids_r)
+    sh = sum(oracle.expert_mlp_mxfp8(inp["x"], torch.full((30,), s, dtype=torch.int32),
+                                     inp["ws_gate"], inp["ws_up"], inp["ws_down"])
+             for s in range(2))
+    np.testing.assert_allclose((full - routed).numpy(), sh.numpy(), rtol=1e-12, atol=1e-12)
+    g = torch.Generator().manual_seed(77)
+    for k, lo, hi in (("x", -4, 0), ("w_gate", -9, -5), ("w_up", -9, -5), ("ws_gate", -9, -5),
+                      ("ws_up", -9, -5)):
+        inp[k] = _mx_lossless(inp[k].shape, g, lo, hi)
+    a, _, _, _ = oracle.forward_mxfp8(cfg, inp)
+    b, _, _, _ = oracle.forward(cfg, inp)
+    assert torch.equal(a, b)
