@@ -47,7 +47,8 @@ class ConfigStruct(ctypes.Structure):
 class LayerTensorsMxfp8Struct(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "x", "w_router", "bias", "wq_gate", "wq_gate_scales", "wq_up", "wq_up_scales", "w_down",
-        "wq_down", "wq_down_scales", "out", "topk_ids", "topk_weights")]
+        "wq_down", "wq_down_scales", "wsq_gate", "wsq_gate_scales", "wsq_up", "wsq_up_scales",
+        "ws_down", "wsq_down", "wsq_down_scales", "out", "topk_ids", "topk_weights")]
 
 
 class LayerTensorsStruct(ctypes.Structure):
@@ -406,6 +407,7 @@ def layer_tensors_mxfp8(cfg, t: dict) -> LayerTensorsMxfp8Struct:
     c = _cs(cfg)
     T, d, E, K, I = c.num_tokens, c.hidden, c.num_experts, c.top_k, c.intermediate
     n_loc = c.expert_end - c.expert_begin
+    S = c.num_shared
     u8, bf = torch.uint8, torch.bfloat16
     return LayerTensorsMxfp8Struct(
         _p(t["x"], "x", (T, d), bf), _p(t["w_router"], "w_router", (E, d), bf),
@@ -417,6 +419,13 @@ def layer_tensors_mxfp8(cfg, t: dict) -> LayerTensorsMxfp8Struct:
         _p(t.get("w_down"), "w_down", (n_loc, d, I), bf),
         _p(t.get("wq_down"), "wq_down", (n_loc, d, I), u8),
         _p(t.get("wq_down_scales"), "wq_down_scales", (n_loc * d * I // 32,), u8),
+        _p(t.get("wsq_gate"), "wsq_gate", (S, I, d), u8),
+        _p(t.get("wsq_gate_scales"), "wsq_gate_scales", (S * I * d // 32,), u8),
+        _p(t.get("wsq_up"), "wsq_up", (S, I, d), u8),
+        _p(t.get("wsq_up_scales"), "wsq_up_scales", (S * I * d // 32,), u8),
+        _p(t.get("ws_down"), "ws_down", (S, d, I), bf),
+        _p(t.get("wsq_down"), "wsq_down", (S, d, I), u8),
+        _p(t.get("wsq_down_scales"), "wsq_down_scales", (S * d * I // 32,), u8),
         _p(t["out"], "out", (T, d), bf),
         _p(t["topk_ids"], "topk_ids", (T, K), torch.int32),
         _p(t["topk_weights"], "topk_weights", (T, K), torch.float32))

@@ -524,15 +524,18 @@ hipError_t launch_expert_mlp(const moe_config_t& c, const void* x_sorted, const 
 }
 
 // The down projection alone (bf16 h and weights), for the block-scaled gate/up
-// path: the same launch as the routed part of launch_expert_mlp's second GEMM.
+// path: the same launch as launch_expert_mlp's second GEMM, the S shared
+// experts (h_sh [S, T, I], ws_down, y_shared) as extra groups.
 hipError_t launch_grouped_down_bf16(const moe_config_t& c, const void* h, const int32_t* offsets,
-                                    const void* w_down, void* y_sorted, hipStream_t s) {
+                                    const void* w_down, void* y_sorted, hipStream_t s,
+                                    const void* h_sh, const void* ws_down, void* y_shared, int S) {
   const int T = c.num_tokens, K = c.top_k, d = c.hidden, I = c.intermediate;
   const int n_loc = c.expert_end - c.expert_begin;
-  const int row_bound = ceil_div(T * K, kBM) + n_loc;
+  const int row_bound = ceil_div(T * K, kBM) + n_loc + S * ceil_div(T, kBM);
   GemmArgs down{h, I, 0, w_down, nullptr, (long long)d * I, 0, y_sorted, d, 0,
                 offsets, n_loc, 0, row_bound, d, I, 1,
-                nullptr, 0, nullptr, nullptr, 0, nullptr, 0, 0, 0};
+                h_sh, (long long)T * I, ws_down, nullptr, (long long)d * I, y_shared,
+                (long long)T * d, S, T};
   return run_gemm<EPI_STORE>(MOE_BF16, down, s);
 }
 

@@ -40,7 +40,8 @@
 namespace moe {
 
 hipError_t launch_grouped_down_bf16(const moe_config_t& c, const void* h, const int32_t* offsets,
-                                    const void* w_down, void* y_sorted, hipStream_t s);
+                                    const void* w_down, void* y_sorted, hipStream_t s,
+                                    const void* h_sh, const void* ws_down, void* y_shared, int S);
 
 namespace {
 
@@ -395,34 +396,70 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
   }
 }
 
+// Groups: the local experts (rows from the offsets), then n_extra extra
+// groups of extra_rows rows each with operands of their own (the shared
+// experts: A2 + e * strideA2 rows from 0, B2 stacks, C2 + e * strideC2).
+struct QExtra {
+  const uint8_t* A;   // codes, advanced by e * strideA per group
+  const uint8_t* As;  // scales (MFMA layout over rows_as rows), + e * strideAs
+  long long strideA, strideAs, rows_as;
+  const uint8_t* Bg;  // weight codes [n_extra, N, Kdim] (gate; up in Bu)
+  const uint8_t* Bu;
+  const uint8_t* Bgs;  // scales of the [n_extra * N, Kdim] stacks
+  const uint8_t* Bus;
+  long long strideB, rows_bs;
+  uint16_t* C;        // bf16 output (or Cq / Cs), + e * strideC elements or bytes
+  uint8_t* Cq;
+  uint8_t* Cs;
+  long long strideC, strideCs;
+  int n_extra, extra_rows;
+};
+
 template <int EPI, bool QOUT>
 __global__ __launch_bounds__(kQThreads, 1) void gemm_mxfp8_kernel(
     const uint8_t* __restrict__ A, int lda, const uint8_t* __restrict__ As, long long rows_as,
     const uint8_t* __restrict__ Bg, const uint8_t* __restrict__ Bu, long long strideB_group,
     const uint8_t* __restrict__ Bgs, const uint8_t* __restrict__ Bus, long long rows_bs,
     uint16_t* __restrict__ C, uint8_t* __restrict__ Cq, uint8_t* __restrict__ Cs, int ldc,
-    const int32_t* __restrict__ offsets, int n_groups, int N, int Kdim) {
+    const int32_t* __restrict__ offsets, int n_groups, int N, int Kdim, QExtra ex) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kQLds];
   constexpr int kNOut = EPI == EPI_SILU_GLU ? kQNOut : kBN;  // output columns per tile
   const int nN = (N + kNOut - 1) / kNOut;
   Tile tl;
-  if (!find_tile(offsets, n_groups, 0, 0, 0, kBM, nN, tl)) return;
+  if (!find_tile(offsets, n_groups, ex.n_extra, ex.extra_rows, 0, kBM, nN, tl)) return;
   QTileArgs ta;
-  ta.A = A;
-  ta.As = As;
-  ta.Bg = Bg + (long long)tl.group * strideB_group;
-  ta.Bu = Bu + (long long)tl.group * strideB_group;
-  ta.Bgs = Bgs;
-  ta.Bus = Bus;
-  ta.C = C;
-  ta.Cq = Cq;
-  ta.Cs = Cs;
-  ta.rows_as = rows_as;
-  ta.rows_bs = rows_bs;
+  if (tl.group < n_groups) {
+    ta.A = A;
+    ta.As = As;
+    ta.rows_as = rows_as;
+    ta.Bg = Bg + (long long)tl.group * strideB_group;
+    ta.Bu = Bu + (long long)tl.group * strideB_group;
+    ta.Bgs = Bgs;
+    ta.Bus = Bus;
+    ta.rows_bs = rows_bs;
+    ta.brow0 = tl.group * N;
+    ta.C = C;
+    ta.Cq = Cq;
+    ta.Cs = Cs;
+    ta.row0 = tl.row0;
+  } else {  // an extra group: its own operands, rows from 0
+    const int e = tl.group - n_groups;
+    ta.A = ex.A + (long long)e * ex.strideA;
+    ta.As = ex.As + (long long)e * ex.strideAs;
+    ta.rows_as = ex.rows_as;
+    ta.Bg = ex.Bg + (long long)e * ex.strideB;
+    ta.Bu = ex.Bu + (long long)e * ex.strideB;
+    ta.Bgs = ex.Bgs;
+    ta.Bus = ex.Bus;
+    ta.rows_bs = ex.rows_bs;
+    ta.brow0 = e * N;
+    ta.C = ex.C ? ex.C + (long long)e * ex.strideC : nullptr;
+    ta.Cq = ex.Cq ? ex.Cq + (long long)e * ex.strideC : nullptr;
+    ta.Cs = ex.Cs ? ex.Cs + (long long)e * ex.strideCs : nullptr;
+    ta.row0 = 0;
+  }
   ta.lda = lda;
   ta.ldc = ldc;
-  ta.brow0 = tl.group * N;
-  ta.row0 = tl.row0;
   ta.rows = tl.rows;
   ta.m0 = tl.m_tile * kBM;
   ta.n0 = tl.n_tile * kNOut;
@@ -441,46 +478,92 @@ __global__ __launch_bounds__(kQThreads, 1) void gemm_mxfp8_kernel(
 
 }  // namespace
 
-size_t mlp_mxfp8_h_offset(const moe_config_t& c) {
-  return align_up((size_t)c.num_tokens * c.top_k * c.intermediate, 256);
-}
-
 hipError_t launch_expert_mlp_mxfp8(const moe_config_t& c, const uint8_t* xq, const uint8_t* xq_scales,
                                    const int32_t* offsets, const uint8_t* wq_gate,
                                    const uint8_t* wq_gate_scales, const uint8_t* wq_up,
                                    const uint8_t* wq_up_scales, const void* w_down,
                                    const uint8_t* wq_down, const uint8_t* wq_down_scales,
-                                   void* y_sorted, void* workspace, hipStream_t s) {
+                                   void* y_sorted, void* workspace, hipStream_t s,
+                                   const MxfpShared* sh) {
   const int T = c.num_tokens, K = c.top_k, d = c.hidden, I = c.intermediate;
   const int n_loc = c.expert_end - c.expert_begin;
-  const int row_bound = ceil_div(T * K, kBM) + n_loc;
+  const int S = sh ? c.num_shared : 0;
+  const int row_bound = ceil_div(T * K, kBM) + n_loc + S * ceil_div(T, kBM);
   const long long rows = (long long)T * K;
-  if (wq_down == nullptr) {  // gate/up in fp8, h and the down projection in bf16
-    uint16_t* h = static_cast<uint16_t*>(workspace);
+  // Workspace: h of the routed rows, then of the shared experts ([S, T, I]):
+  // bf16, or MX-FP8 codes followed by their scales (per shared expert a
+  // [T, I] matrix with its own MFMA layout).
+  const size_t h_bytes = align_up((size_t)T * K * I * 2, 256);
+  char* ws = static_cast<char*>(workspace);
+  const bool fp8_down = wq_down != nullptr;
+  QExtra up{};
+  up.n_extra = S;
+  up.extra_rows = T;
+  if (S > 0) {
+    up.A = sh->xq;
+    up.As = sh->xq_scales;
+    up.rows_as = T;
+    up.Bg = sh->wq_gate;
+    up.Bu = sh->wq_up;
+    up.Bgs = sh->wq_gate_scales;
+    up.Bus = sh->wq_up_scales;
+    up.strideB = (long long)I * d;
+    up.rows_bs = (long long)S * I;
+    up.strideC = (long long)T * I;
+    up.strideCs = (long long)T * I / 32;
+  }
+  char* hsh = ws + h_bytes;
+  if (!fp8_down) {  // gate/up in fp8, h and the down projection in bf16
+    uint16_t* h = reinterpret_cast<uint16_t*>(ws);
+    if (S > 0) up.C = reinterpret_cast<uint16_t*>(hsh);
     hipLaunchKernelGGL((gemm_mxfp8_kernel<EPI_SILU_GLU, false>),
                        dim3(grid_for(row_bound, ceil_div(I, kQNOut))), dim3(kQThreads), 0, s, xq,
                        d, xq_scales, rows, wq_gate, wq_up, (long long)I * d, wq_gate_scales,
                        wq_up_scales, (long long)n_loc * I, h, nullptr, nullptr, I, offsets, n_loc,
-                       I, d);
+                       I, d, up);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch_grouped_down_bf16(c, h, offsets, w_down, y_sorted, s);
+    return launch_grouped_down_bf16(c, h, offsets, w_down, y_sorted, s, S > 0 ? hsh : nullptr,
+                                    S > 0 ? sh->w_down : nullptr, S > 0 ? sh->y : nullptr, S);
   }
   // Both projections in fp8: h leaves the gate/up kernel as MX-FP8 codes
   // [T*K, I] and MFMA-layout scales (T*K rows), the down kernel's A operand.
-  uint8_t* hq = static_cast<uint8_t*>(workspace);
-  uint8_t* hs = hq + mlp_mxfp8_h_offset(c);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(ws);
+  uint8_t* hs = hq + align_up((size_t)T * K * I, 256);
+  uint8_t* hshq = reinterpret_cast<uint8_t*>(hsh);
+  uint8_t* hshs = hshq + align_up((size_t)S * T * I, 256);
+  if (S > 0) {
+    up.Cq = hshq;
+    up.Cs = hshs;
+  }
   hipLaunchKernelGGL((gemm_mxfp8_kernel<EPI_SILU_GLU, true>),
                      dim3(grid_for(row_bound, ceil_div(I, kQNOut))), dim3(kQThreads), 0, s, xq, d,
                      xq_scales, rows, wq_gate, wq_up, (long long)I * d, wq_gate_scales,
-                     wq_up_scales, (long long)n_loc * I, nullptr, hq, hs, I, offsets, n_loc, I, d);
+                     wq_up_scales, (long long)n_loc * I, nullptr, hq, hs, I, offsets, n_loc, I, d,
+                     up);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  QExtra dn{};
+  dn.n_extra = S;
+  dn.extra_rows = T;
+  if (S > 0) {
+    dn.A = hshq;
+    dn.As = hshs;
+    dn.strideA = (long long)T * I;
+    dn.strideAs = (long long)T * I / 32;
+    dn.rows_as = T;
+    dn.Bg = dn.Bu = sh->wq_down;
+    dn.Bgs = dn.Bus = sh->wq_down_scales;
+    dn.strideB = (long long)d * I;
+    dn.rows_bs = (long long)S * d;
+    dn.C = static_cast<uint16_t*>(sh->y);
+    dn.strideC = (long long)T * d;
+  }
   hipLaunchKernelGGL((gemm_mxfp8_kernel<EPI_STORE, false>),
                      dim3(grid_for(row_bound, ceil_div(d, kBN))), dim3(kQThreads), 0, s, hq, I, hs,
                      rows, wq_down, wq_down, (long long)d * I, wq_down_scales, wq_down_scales,
                      (long long)n_loc * d, static_cast<uint16_t*>(y_sorted), nullptr, nullptr, d,
-                     offsets, n_loc, d, I);
+                     offsets, n_loc, d, I, dn);
   return hipGetLastError();
 }
 

@@ -379,12 +379,15 @@ moe_status_t moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t dtype, const
 
 // Host checks shared by the block-scaled MLP and layer: configuration,
 // down-projection weights (exactly one of bf16 w_down and MX-FP8 wq_down +
-// scales) and the 32-bit scale indexing of the kernels.
+// scales) and the 32-bit scale indexing of the kernels.  Shared experts only
+// where the caller handles them (the layer).
 moe_status_t check_mxfp8_common(const moe_config_t* cfg, const void* w_down,
-                                const uint8_t* wq_down, const uint8_t* wq_down_scales) {
+                                const uint8_t* wq_down, const uint8_t* wq_down_scales,
+                                bool allow_shared) {
   moe_status_t st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (cfg->dtype != MOE_BF16 || cfg->num_shared != 0 || cfg->hidden % 512 != 0)
+  if (cfg->dtype != MOE_BF16 || (cfg->num_shared != 0 && !allow_shared) ||
+      cfg->hidden % 512 != 0)
     return MOE_ERR_UNSUPPORTED;
   const bool fp8_down = wq_down != nullptr || wq_down_scales != nullptr;
   if (fp8_down == (w_down != nullptr) || (fp8_down && (!wq_down || !wq_down_scales)))
@@ -402,6 +405,10 @@ moe_status_t check_mxfp8_common(const moe_config_t* cfg, const void* w_down,
   if (fp8_down && (rows * (cfg->intermediate / 128) >= lim ||
                    n_loc * cfg->hidden * (cfg->intermediate / 128) >= lim))
     return MOE_ERR_UNSUPPORTED;
+  const int64_t S = cfg->num_shared;
+  if (S * cfg->intermediate * (cfg->hidden / 128) >= lim ||
+      (fp8_down && S * cfg->hidden * (cfg->intermediate / 128) >= lim))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -412,7 +419,7 @@ moe_status_t moe_expert_mlp_mxfp8(const moe_config_t* cfg, const uint8_t* xq_sor
                                   const void* w_down, const uint8_t* wq_down,
                                   const uint8_t* wq_down_scales, void* y_sorted, void* workspace,
                                   size_t workspace_bytes, moe_stream_t stream) {
-  moe_status_t st = check_mxfp8_common(cfg, w_down, wq_down, wq_down_scales);
+  moe_status_t st = check_mxfp8_common(cfg, w_down, wq_down, wq_down_scales, false);
   if (st != MOE_OK) return st;
   if (!xq_sorted || !xq_scales || !expert_offsets || !wq_gate || !wq_gate_scales || !wq_up ||
       !wq_up_scales || !y_sorted || !workspace)
@@ -446,11 +453,24 @@ moe_status_t moe_forward(const moe_config_t* cfg, const moe_layer_tensors_t* ten
 moe_status_t check_forward_mxfp8(const moe_config_t* cfg, const moe_layer_tensors_mxfp8_t* t,
                                  const void* workspace, size_t workspace_bytes) {
   if (!t) return MOE_ERR_INVALID_ARGUMENT;
-  moe_status_t st = check_mxfp8_common(cfg, t->w_down, t->wq_down, t->wq_down_scales);
+  moe_status_t st = check_mxfp8_common(cfg, t->w_down, t->wq_down, t->wq_down_scales, true);
   if (st != MOE_OK) return st;
   if (!t->x || !t->w_router || !t->wq_gate || !t->wq_gate_scales || !t->wq_up ||
       !t->wq_up_scales || !t->out || !t->topk_ids || !t->topk_weights)
     return MOE_ERR_INVALID_ARGUMENT;
+  // Shared experts: encoded gate / up stacks, and down weights of the routed
+  // experts' kind; all seven pointers NULL without shared experts.
+  const bool sh = cfg->num_shared > 0;
+  const bool fp8_down = t->wq_down != nullptr;
+  const void* shp[7] = {t->wsq_gate, t->wsq_gate_scales, t->wsq_up, t->wsq_up_scales,
+                        t->ws_down, t->wsq_down, t->wsq_down_scales};
+  const bool want[7] = {sh, sh, sh, sh, sh && !fp8_down, sh && fp8_down, sh && fp8_down};
+  for (int i = 0; i < 7; ++i)
+    if ((shp[i] != nullptr) != want[i]) return MOE_ERR_INVALID_ARGUMENT;
+  for (const void* p : {shp[0], shp[2], shp[4], shp[5]})
+    if (!aligned(p, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  for (const void* p : {shp[1], shp[3], shp[6]})
+    if (!aligned(p, 4)) return MOE_ERR_INVALID_ARGUMENT;
   for (const void* p : {t->x, t->w_router, (const void*)t->wq_gate, (const void*)t->wq_up,
                         (const void*)t->out})
     if (!aligned(p, 16)) return MOE_ERR_INVALID_ARGUMENT;
@@ -476,11 +496,26 @@ moe_status_t enqueue_forward_mxfp8(const moe_config_t& c, const moe_layer_tensor
   e = moe::launch_dispatch(c, t.x, t.topk_ids, sc.counts, sc.offsets, nullptr, sc.src_index,
                            sc.row_of, sc.dispatch_ws, s, xq, reinterpret_cast<uint32_t*>(xs));
   if (e != hipSuccess) return MOE_ERR_HIP;
+  // Shared experts read every token, encoded once more (T rows, MFMA layout)
+  // into the y_sorted region: the gate/up kernel is its last reader and the
+  // down kernel, after it on the stream, the first writer of y_sorted.
+  moe::MxfpShared sh{};
+  if (c.num_shared > 0) {
+    uint8_t* tq = static_cast<uint8_t*>(sc.y_sorted);
+    uint8_t* ts = tq + align_up((size_t)c.num_tokens * c.hidden, 256);
+    e = moe::launch_mxfp8_quantize(c.num_tokens, c.hidden, MOE_BF16, t.x, c.hidden, MOE_MX_MFMA,
+                                   tq, ts, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    sh = moe::MxfpShared{tq,          ts,          t.wsq_gate, t.wsq_gate_scales,
+                         t.wsq_up,    t.wsq_up_scales,         t.ws_down,
+                         t.wsq_down,  t.wsq_down_scales,       sc.y_shared};
+  }
   e = moe::launch_expert_mlp_mxfp8(c, xq, xs, sc.offsets, t.wq_gate, t.wq_gate_scales, t.wq_up,
                                    t.wq_up_scales, t.w_down, t.wq_down, t.wq_down_scales,
-                                   sc.y_sorted, sc.mlp_ws, s);
+                                   sc.y_sorted, sc.mlp_ws, s, c.num_shared > 0 ? &sh : nullptr);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(moe::launch_combine(c, sc.y_sorted, sc.row_of, t.topk_weights, nullptr, t.out, s));
+  return hip_status(
+      moe::launch_combine(c, sc.y_sorted, sc.row_of, t.topk_weights, sc.y_shared, t.out, s));
 }
 
 moe_status_t moe_forward_mxfp8(const moe_config_t* cfg,

@@ -57,15 +57,33 @@ hipError_t launch_expert_mlp(const moe_config_t& c, const void* x_sorted, const 
 hipError_t launch_mxfp8_quantize(int rows, int cols, int dtype, const void* in, long long ld,
                                  int layout, uint8_t* codes, uint8_t* scales, hipStream_t s);
 
+// Shared experts of the block-scaled MLP: the tokens encoded (T rows, MFMA
+// layout), their encoded gate / up stacks, down weights in the form of the
+// routed ones (bf16 w_down, or wq_down + scales), and y_shared [S, T, d].
+struct MxfpShared {
+  const uint8_t* xq;
+  const uint8_t* xq_scales;
+  const uint8_t* wq_gate;
+  const uint8_t* wq_gate_scales;
+  const uint8_t* wq_up;
+  const uint8_t* wq_up_scales;
+  const void* w_down;
+  const uint8_t* wq_down;
+  const uint8_t* wq_down_scales;
+  void* y;
+};
+
 // wq_down == nullptr: the down projection in bf16 (w_down); else in fp8
-// (wq_down, wq_down_scales), h encoded as MX-FP8 in the workspace.
+// (wq_down, wq_down_scales), h encoded as MX-FP8 in the workspace.  sh: the
+// shared experts (c.num_shared of them), or nullptr.
 hipError_t launch_expert_mlp_mxfp8(const moe_config_t& c, const uint8_t* xq,
                                    const uint8_t* xq_scales, const int32_t* offsets,
                                    const uint8_t* wq_gate, const uint8_t* wq_gate_scales,
                                    const uint8_t* wq_up, const uint8_t* wq_up_scales,
                                    const void* w_down, const uint8_t* wq_down,
                                    const uint8_t* wq_down_scales, void* y_sorted,
-                                   void* workspace, hipStream_t s);
+                                   void* workspace, hipStream_t s,
+                                   const MxfpShared* sh = nullptr);
 
 hipError_t launch_combine(const moe_config_t& c, const void* y_sorted, const int32_t* row_of,
                           const float* weights, const void* y_shared, void* out, hipStream_t s);

@@ -56,20 +56,25 @@ class MoELayer:
     # ---- block-scaled (MX-FP8) path ------------------------------------------
     def quantize_weights(self, down: bool = False) -> dict:
         """MX-FP8 encodings of the gate and up stacks (and, with down=True, of
-        the down stack) in the MFMA scale layout, done once like an offline
-        weight conversion."""
+        the down stack), routed and shared, in the MFMA scale layout, done once
+        like an offline weight conversion."""
         c = self.cfg
-        n_loc, I, d = c.num_local, c.intermediate, c.hidden
+        n_loc, I, d, S = c.num_local, c.intermediate, c.hidden, c.num_shared
         mx = {}
-        mats = [("gate", self.w_gate, I, d), ("up", self.w_up, I, d)]
+        mats = [("wq_gate", self.w_gate, I, d), ("wq_up", self.w_up, I, d)]
         if down:
-            mats.append(("down", self.w_down, d, I))
+            mats.append(("wq_down", self.w_down, d, I))
+        if S > 0:
+            mats += [("wsq_gate", self.ws_gate, I, d), ("wsq_up", self.ws_up, I, d)]
+            if down:
+                mats.append(("wsq_down", self.ws_down, d, I))
         for name, w, rows, cols in mats:
-            codes = torch.empty(n_loc, rows, cols, dtype=torch.uint8, device=self.device)
-            scales = torch.empty(n_loc * rows * cols // 32, dtype=torch.uint8, device=self.device)
-            B.moe_quantize_mxfp8(w.view(n_loc * rows, cols), codes.view(n_loc * rows, cols), scales,
+            n = w.shape[0]
+            codes = torch.empty(n, rows, cols, dtype=torch.uint8, device=self.device)
+            scales = torch.empty(n * rows * cols // 32, dtype=torch.uint8, device=self.device)
+            B.moe_quantize_mxfp8(w.view(n * rows, cols), codes.view(n * rows, cols), scales,
                                  B.MOE_MX_MFMA)
-            mx["wq_" + name], mx["wq_" + name + "_scales"] = codes, scales
+            mx[name], mx[name + "_scales"] = codes, scales
         self.mx = mx
         return mx
 
@@ -83,6 +88,8 @@ class MoELayer:
                  topk_weights=self.topk_weights, **self.mx)
         if "wq_down" not in self.mx:
             t["w_down"] = self.w_down
+            if self.cfg.num_shared > 0:
+                t["ws_down"] = self.ws_down
         return t
 
     def forward_mxfp8(self, stream=None, out: Optional[torch.Tensor] = None):

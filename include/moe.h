@@ -343,6 +343,15 @@ typedef struct moe_layer_tensors_mxfp8 {
   const void* w_down;           /* [E_loc, d, I] bf16, or NULL                      */
   const uint8_t* wq_down;       /* [E_loc, d, I] E4M3 codes, or NULL                */
   const uint8_t* wq_down_scales;/* MOE_MX_MFMA scales of the [E_loc*d, I] stack     */
+  /* Shared experts (cfg->num_shared = S > 0; all NULL when S == 0): encoded
+   * like the routed ones, the down weights in the routed experts' form.     */
+  const uint8_t* wsq_gate;       /* [S, I, d] E4M3 codes                             */
+  const uint8_t* wsq_gate_scales;/* MOE_MX_MFMA scales of the [S*I, d] stack         */
+  const uint8_t* wsq_up;         /* [S, I, d] E4M3 codes                             */
+  const uint8_t* wsq_up_scales;  /* MOE_MX_MFMA scales of the [S*I, d] stack         */
+  const void* ws_down;           /* [S, d, I] bf16 (with w_down), else NULL          */
+  const uint8_t* wsq_down;       /* [S, d, I] E4M3 codes (with wq_down), else NULL   */
+  const uint8_t* wsq_down_scales;/* MOE_MX_MFMA scales of the [S*d, I] stack         */
   void* out;                    /* [T, d] bf16 (out)                                */
   int32_t* topk_ids;            /* [T, K] int32 (out)                               */
   float* topk_weights;          /* [T, K] fp32 (out)                                */
@@ -356,7 +365,15 @@ typedef struct moe_layer_tensors_mxfp8 {
  * gate and up weights are passed encoded (moe_quantize_mxfp8 of the
  * [E_loc*I, d] stacks, MOE_MX_MFMA layout, done once, offline), the down
  * weights either in bf16 (w_down) or encoded too (wq_down, wq_down_scales;
- * the other NULL), as for moe_expert_mlp_mxfp8, with the same requirements.
+ * the other NULL), as for moe_expert_mlp_mxfp8, with the same requirements
+ * except that shared experts are allowed (as in moe_expert_mlp: [DBO]
+ * Introduction's shared expert, applied to every token with weight one).
+ * A shared expert s reads the token rows encoded by the same rule (D(xq)
+ * below is the decoding of x's moe_quantize_mxfp8; wsq_* are its weights):
+ *   h_s = SiLU(D(xq) D(gsq_s)^T) * (D(xq) D(usq_s)^T)   in fp32,
+ *   y_s = h_s' W'_s^T                                   in fp32, to bf16,
+ * with h_s' and W'_s as for the routed experts (ws_down, or the encoded h_s
+ * and wsq_down); the combine adds the y_s as moe_combine adds y_shared.
  */
 moe_status_t moe_forward_mxfp8(const moe_config_t* cfg,
                                const moe_layer_tensors_mxfp8_t* tensors, void* workspace,

@@ -215,17 +215,54 @@ def test_block_scaled_forward_and_capture_reject_bad_arguments_on_host(lib):
                                                ctypes.byref(h)) == inv
     assert lib.moe_graph_capture_forward_mxfp8(ctypes.byref(cs), ctypes.byref(lt), None, 0,
                                                None) == inv
-    shared = B.config_struct(W.CONFIGS["dsv2lite_decode"])  # shared experts: not on this path
-    assert lib.moe_forward_mxfp8(ctypes.byref(shared), ctypes.byref(lt), None, 0, None) == uns
-    assert lib.moe_graph_capture_forward_mxfp8(ctypes.byref(shared), ctypes.byref(lt), None, 0,
-                                               ctypes.byref(h)) == uns
-    assert h.value is None
     P = 0x10000
-    full = B.LayerTensorsMxfp8Struct(*([P] * 13))
-    full.wq_down = full.wq_down_scales = None  # bf16 down weights
+    nf = len(B.LayerTensorsMxfp8Struct._fields_)
+    SHARED = ("wsq_gate", "wsq_gate_scales", "wsq_up", "wsq_up_scales", "ws_down", "wsq_down",
+              "wsq_down_scales")
+
+    def tensors(fp8_down: bool, shared: bool):
+        t = B.LayerTensorsMxfp8Struct(*([P] * nf))
+        for f in (("w_down", "ws_down") if fp8_down else ("wq_down", "wq_down_scales", "wsq_down",
+                                                           "wsq_down_scales")):
+            setattr(t, f, None)
+        if not shared:
+            for f in SHARED:
+                setattr(t, f, None)
+        return t
+
+    full = tensors(fp8_down=False, shared=False)
     assert lib.moe_forward_mxfp8(ctypes.byref(cs), ctypes.byref(full), P, 1, None) == \
         B.MOE_ERR_WORKSPACE_TOO_SMALL
-    both = B.LayerTensorsMxfp8Struct(*([P] * 13))  # bf16 and fp8 down weights both given
+    # shared-expert weights are given exactly when the layer has shared experts
+    assert lib.moe_forward_mxfp8(ctypes.byref(cs), ctypes.byref(tensors(False, True)), P,
+                                 1 << 40, None) == inv
+    shared = B.config_struct(W.CONFIGS["dsv2lite_decode"])
+    for fp8_down in (False, True):
+        cfg = B.config_struct(W.CONFIGS["dsv2lite_decode"].replace(intermediate=1536)) \
+            if fp8_down else shared
+        ok = tensors(fp8_down, shared=True)
+        assert lib.moe_forward_mxfp8(ctypes.byref(cfg), ctypes.byref(ok), P, 1, None) == \
+            B.MOE_ERR_WORKSPACE_TOO_SMALL
+        assert lib.moe_forward_mxfp8(ctypes.byref(cfg), ctypes.byref(tensors(fp8_down, False)),
+                                     P, 1 << 40, None) == inv
+        for f in SHARED:  # each one missing, or the down weights of the other kind added
+            t = tensors(fp8_down, shared=True)
+            setattr(t, f, None if getattr(t, f) else P)
+            assert lib.moe_forward_mxfp8(ctypes.byref(cfg), ctypes.byref(t), P, 1 << 40,
+                                         None) == inv, f
+        t = tensors(fp8_down, shared=True)
+        t.wsq_up_scales = P + 2  # scales must be 4-byte aligned
+        assert lib.moe_forward_mxfp8(ctypes.byref(cfg), ctypes.byref(t), P, 1 << 40, None) == inv
+        t = tensors(fp8_down, shared=True)
+        t.wsq_gate = P + 4  # codes must be 16-byte aligned
+        assert lib.moe_forward_mxfp8(ctypes.byref(cfg), ctypes.byref(t), P, 1 << 40, None) == inv
+    # a rejected capture makes no graph
+    assert lib.moe_graph_capture_forward_mxfp8(ctypes.byref(shared), ctypes.byref(lt), None, 0,
+                                               ctypes.byref(h)) == inv
+    assert h.value is None
+    both = B.LayerTensorsMxfp8Struct(*([P] * nf))  # bf16 and fp8 down weights both given
+    both.wsq_gate = both.wsq_gate_scales = both.wsq_up = both.wsq_up_scales = None
+    both.ws_down = both.wsq_down = both.wsq_down_scales = None
     assert lib.moe_forward_mxfp8(ctypes.byref(cs), ctypes.byref(both), P, 1 << 40, None) == inv
     full.wq_gate_scales = P + 2  # scales must be 4-byte aligned
     assert lib.moe_forward_mxfp8(ctypes.byref(cs), ctypes.byref(full), P, 1 << 40, None) == inv

@@ -280,13 +280,21 @@ def test_expert_mlp_mxfp8_full_size_sampled_rows(down):
 # ---------------------------------------------------------------- dispatch and layer
 
 MX_LAYERS = {
-    # reduced widths with the real routing structure; no shared experts (the
-    # block-scaled path has none); hidden a multiple of 512
+    # reduced widths with the real routing structure; hidden a multiple of 512
     "dsv3_mx_small": W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=300, hidden=512,
                                                           intermediate=256),
     "mixtral_mx_small": W.CONFIGS["mixtral_bf16"].replace(num_tokens=257, hidden=1024,
                                                           intermediate=384),
     "dsv2lite_mx_decode": W.CONFIGS["dsv2lite_decode"].replace(num_shared=0),
+}
+
+MX_SHARED_LAYERS = {
+    # the block-scaled layer with shared experts: DeepSeek-V2-Lite as it is
+    # (two shared experts, I = 1408, so the down projection stays bf16) and a
+    # reduced DeepSeek-V3 share with one shared expert
+    "dsv2lite_mx_decode_shared": W.CONFIGS["dsv2lite_decode"],
+    "dsv3_mx_small_shared": W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=300, hidden=512,
+                                                                 intermediate=256, num_shared=1),
 }
 
 
@@ -357,14 +365,16 @@ def test_dispatch_mxfp8_full_size_sampled_rows():
     _check_dispatch_mx(cfg, inp, L, rows)
 
 
-@pytest.mark.parametrize("name", list(MX_LAYERS))
-def test_forward_mxfp8_matches_oracle(name):
-    cfg = MX_LAYERS[name]
+def _check_forward_mx(name, cfg, down: bool):
+    """The block-scaled layer against the oracle: routing equal up to the
+    router's near-ties, output within the bf16 bar, a second call and a graph
+    replay bit-equal to the first call."""
     inp = W.make_inputs(cfg, 0)
     L = MoELayer(cfg, inp)
+    L.quantize_weights(down=down)
     L.forward_mxfp8()
     torch.cuda.synchronize()
-    out_o, ids_o, w_o, _ = oracle.forward_mxfp8(cfg, inp)
+    out_o, ids_o, _, _ = oracle.forward_mxfp8(cfg, inp, down=down)
     ids_g = L.topk_ids.cpu()
     bad = (ids_g != ids_o).any(1).nonzero().flatten().tolist()
     if bad:  # near-ties of the router: allowed only within the measured logit error
@@ -377,13 +387,24 @@ def test_forward_mxfp8_matches_oracle(name):
             assert float(zs[cfg.top_k - 1] - zs[cfg.top_k]) <= 2 * eps, f"token {t}"
     keep = torch.tensor([t for t in range(cfg.num_tokens) if t not in set(bad)])
     err = _rel_l2(L.out.cpu()[keep], out_o[keep])
-    print(f"{name}: rel-L2 {err:.2e}, near-tie tokens {bad}", file=sys.stderr)
+    print(f"{name} (fp8 down: {down}): rel-L2 {err:.2e}, near-tie tokens {bad}",
+          file=sys.stderr)
     assert err <= 1e-2
-    # the same layer twice gives the same bits
     first = L.out.clone()
-    L.forward_mxfp8()
+    L.forward_mxfp8()  # the same layer twice gives the same bits
     torch.cuda.synchronize()
     assert torch.equal(first.view(torch.int16), L.out.view(torch.int16))
+    g = L.capture_forward_mxfp8()  # and a graph of it replays them
+    L.out.zero_()
+    g.launch()
+    torch.cuda.synchronize()
+    assert torch.equal(L.out.view(torch.int16), first.view(torch.int16))
+    g.destroy()
+
+
+@pytest.mark.parametrize("name", list(MX_LAYERS))
+def test_forward_mxfp8_matches_oracle(name):
+    _check_forward_mx(name, MX_LAYERS[name], down=False)
 
 
 def test_graph_replay_of_the_block_scaled_layer():
@@ -424,31 +445,23 @@ MX_DOWN_LAYERS = {
 
 @pytest.mark.parametrize("name", list(MX_DOWN_LAYERS))
 def test_forward_mxfp8_with_fp8_down_matches_oracle(name):
-    cfg = MX_DOWN_LAYERS[name]
-    inp = W.make_inputs(cfg, 0)
-    L = MoELayer(cfg, inp)
-    L.quantize_weights(down=True)
-    L.forward_mxfp8()
-    torch.cuda.synchronize()
-    out_o, ids_o, _, _ = oracle.forward_mxfp8(cfg, inp, down=True)
-    ids_g = L.topk_ids.cpu()
-    bad = (ids_g != ids_o).any(1).nonzero().flatten().tolist()
-    if bad:
-        z_or = oracle.router_logits(inp["x"], inp["w_router"], inp["bias"])
-        L.route()
-        torch.cuda.synchronize()
-        eps = float((L.logits.cpu().double() - z_or).abs().max())
-        for t in bad:
-            zs = torch.sort(z_or[t], descending=True).values
-            assert float(zs[cfg.top_k - 1] - zs[cfg.top_k]) <= 2 * eps, f"token {t}"
-    keep = torch.tensor([t for t in range(cfg.num_tokens) if t not in set(bad)])
-    err = _rel_l2(L.out.cpu()[keep], out_o[keep])
-    print(f"{name}: rel-L2 {err:.2e}, near-tie tokens {bad}", file=sys.stderr)
-    assert err <= 1e-2
-    g = L.capture_forward_mxfp8()  # and a graph of it replays the same bits
-    ref = L.out.clone()
-    L.out.zero_()
-    g.launch()
-    torch.cuda.synchronize()
-    assert torch.equal(L.out.view(torch.int16), ref.view(torch.int16))
-    g.destroy()
+    _check_forward_mx(name, MX_DOWN_LAYERS[name], down=True)
+
+
+MX_SHARED_DOWN_LAYERS = {
+    # shared experts with both projections in fp8 (I % 512 == 0): two shared
+    # experts on a DeepSeek-V2-Lite-shaped decode, one on a DeepSeek-V3 share
+    "dsv2lite_mxd_decode_shared": W.CONFIGS["dsv2lite_decode"].replace(intermediate=1536),
+    "dsv3_mxd_small_shared": W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=300, hidden=512,
+                                                                  intermediate=512, num_shared=1),
+}
+
+
+@pytest.mark.parametrize("name", list(MX_SHARED_LAYERS))
+def test_forward_mxfp8_with_shared_experts_matches_oracle(name):
+    _check_forward_mx(name, MX_SHARED_LAYERS[name], down=False)
+
+
+@pytest.mark.parametrize("name", list(MX_SHARED_DOWN_LAYERS))
+def test_forward_mxfp8_with_shared_experts_and_fp8_down_matches_oracle(name):
+    _check_forward_mx(name, MX_SHARED_DOWN_LAYERS[name], down=True)
