@@ -457,6 +457,27 @@ MX_SHARED_DOWN_LAYERS = {
 }
 
 
+MX_EDGE = [
+    # (name, config, fp8 down)
+    ("mx_one_token", W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=1, hidden=512,
+                                                          intermediate=256), False),
+    ("mxd_one_token_shared", W.CONFIGS["dsv3_prefill_ep"].replace(
+        num_tokens=1, hidden=512, intermediate=512, num_shared=1), True),
+    # no token reaches the least popular experts: the output is the shared
+    # experts' alone, the routed groups all empty
+    ("mx_no_local_rows_shared", W.CONFIGS["dsv3_prefill_ep"].replace(
+        num_tokens=64, hidden=512, intermediate=256, expert_begin=248, expert_end=256,
+        num_shared=2), False),
+    ("mxd_max_shared", W.CONFIGS["dsv2lite_decode"].replace(num_tokens=77, hidden=512,
+                                                            intermediate=512, num_shared=4), True),
+]
+
+
+@pytest.mark.parametrize("name,cfg,down", MX_EDGE, ids=[e[0] for e in MX_EDGE])
+def test_forward_mxfp8_edge_cases(name, cfg, down):
+    _check_forward_mx(name, cfg, down)
+
+
 @pytest.mark.parametrize("name", list(MX_SHARED_LAYERS))
 def test_forward_mxfp8_with_shared_experts_matches_oracle(name):
     _check_forward_mx(name, MX_SHARED_LAYERS[name], down=False)

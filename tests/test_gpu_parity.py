@@ -341,6 +341,9 @@ EDGE = [
     ("fp32_shared", W.CONFIGS["tiny_f32"].replace(num_tokens=70, num_shared=2, renormalize=False)),
     ("bf16_unaligned_tiles", W.CONFIGS["mixtral_bf16"].replace(num_tokens=515, hidden=320,
                                                                intermediate=448)),
+    # the most shared experts a layer may have, on a ragged token count
+    ("max_shared", W.CONFIGS["dsv2lite_decode"].replace(num_tokens=77, hidden=256,
+                                                        intermediate=192, num_shared=4)),
     # the Zipf bias keeps every token off the least popular experts: no local
     # rows at all, so the expert MLP has nothing to do and the output is zero
     ("no_local_rows", W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=64, hidden=256,
