@@ -501,8 +501,11 @@ moe_status_t enqueue_forward_mxfp8(const moe_config_t& c, const moe_layer_tensor
   // down kernel, after it on the stream, the first writer of y_sorted.
   moe::MxfpShared sh{};
   if (c.num_shared > 0) {
+    // T*d + T*d/32 bytes; y_sorted holds T*K*d*2 (d is a multiple of 512)
+    const size_t n_tok = (size_t)c.num_tokens * c.hidden;
+    if (align_up(n_tok, 256) + n_tok / 32 > n_tok * c.top_k * 2) return MOE_ERR_UNSUPPORTED;
     uint8_t* tq = static_cast<uint8_t*>(sc.y_sorted);
-    uint8_t* ts = tq + align_up((size_t)c.num_tokens * c.hidden, 256);
+    uint8_t* ts = tq + align_up(n_tok, 256);
     e = moe::launch_mxfp8_quantize(c.num_tokens, c.hidden, MOE_BF16, t.x, c.hidden, MOE_MX_MFMA,
                                    tq, ts, s);
     if (e != hipSuccess) return MOE_ERR_HIP;

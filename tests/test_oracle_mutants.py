@@ -55,6 +55,9 @@ MUTANTS = [
     ("mx_forward_h_not_encoded",
      "  const std::vector<double> hq = decoded(n_rows, I, ODT_F64, hh.data());",
      "  const std::vector<double> hq = hh;"),
+    ("mx_shared_first_stack_only",
+     "      for (int t = 0; t < T; ++t) sh_expert[t] = s;\n      oracle_expert_mlp_mxfp8(",
+     "      for (int t = 0; t < T; ++t) sh_expert[t] = 0;\n      oracle_expert_mlp_mxfp8("),
 ]
 
 
