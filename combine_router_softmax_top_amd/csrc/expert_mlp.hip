@@ -94,8 +94,12 @@ struct TileArgs {
 // x 64 columns.  NFA = 4 for full tiles; 1..3 for the last row tile of an
 // expert with at most 192 rows (that fraction of the A staging and of the
 // MFMAs).  The k order of every output element is the same at every height.
-template <int EPI, int NFA>
+// DEEP (64-row tiles only): a tile that little more than streams its weights
+// keeps more of them in flight -- rings of 4 slots for both operands (A slots
+// of 8 KB), each k-tile's A and B loads issued together three k-tiles ahead.
+template <int EPI, int NFA, bool DEEP = false>
 __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
+  static_assert(!DEEP || NFA == 1, "the deep ring holds 64-row activation tiles");
   constexpr int kNOut = EPI == EPI_SILU_GLU ? kBN / 2 : kBN;
   constexpr int kWaveRows = NFA * 32;
   const int tid = threadIdx.x;
@@ -177,32 +181,54 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
   constexpr int kMaxStages = kAStages > kBStages ? kAStages : kBStages;
   // Loads issued after tile 0's in the prologue (A1, B1); after tile kt+1's
   // by barrier kt (the B(kt+2) loads of iteration kt, issued after A(kt+1)).
-  constexpr int kVmPrologue = (kAStages - 1) * NA + (kBStages - 2) * kDmaB;
-  constexpr int kVmBarrier = kDmaB;
+  // DEEP: k-tiles kt+2 and kt+3 in both cases.
+  constexpr int kDeep = 4;                                   // DEEP ring slots
+  constexpr int kASlot = DEEP ? kSlotBytes / 4 : kSlotBytes;  // A slot bytes
+  constexpr int kVmPrologue =
+      DEEP ? 2 * (NA + kDmaB) : (kAStages - 1) * NA + (kBStages - 2) * kDmaB;
+  constexpr int kVmBarrier = DEEP ? 2 * (NA + kDmaB) : kDmaB;
   static_assert(kAStages == 2 && kBStages == 3 && kVmPrologue < 64, "vmcnt immediates");
+  static_assert(!DEEP || kDeep * (kASlot + kSlotBytes) <= (kAStages + kBStages) * kSlotBytes,
+                "LDS budget");
   uint8_t* a_slots = lds;
-  uint8_t* b_slots = lds + kAStages * kSlotBytes;
+  uint8_t* b_slots = lds + (DEEP ? kDeep * kASlot : kAStages * kSlotBytes);
   const int nk = Kdim / kBK;
   const int last = (nk - 1) * kRowBytes;
+  if constexpr (DEEP) {
 #pragma unroll
-  for (int t = 0; t < kMaxStages; ++t) {
-    if (t < kAStages) stage_a<NA>(a_slots + t * kSlotBytes, a_tile, off, wave, min(t * kRowBytes, last));
-    if (t < kBStages - 1)  // B2 comes in iteration 0
+    for (int t = 0; t < kDeep - 1; ++t) {
+      stage_a<NA>(a_slots + t * kASlot, a_tile, off, wave, min(t * kRowBytes, last));
       stage_b(b_slots + t * kSlotBytes, b_lo, b_hi, off, wave, min(t * kRowBytes, last));
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < kMaxStages; ++t) {
+      if (t < kAStages) stage_a<NA>(a_slots + t * kSlotBytes, a_tile, off, wave, min(t * kRowBytes, last));
+      if (t < kBStages - 1)  // B2 comes in iteration 0
+        stage_b(b_slots + t * kSlotBytes, b_lo, b_hi, off, wave, min(t * kRowBytes, last));
+    }
   }
   wait_loads_and_barrier<kVmPrologue>();  // tile 0 landed
   Frags f0, f1;
   load_frags<NFA>(a_slots, b_slots, 0, a_row0, b_row, xa, xb, f0);
+  constexpr int kAS = DEEP ? kDeep : kAStages, kBS = DEEP ? kDeep : kBStages;
   for (int kt = 0; kt < nk; ++kt) {
-    uint8_t* sa = a_slots + (kt % kAStages) * kSlotBytes;
-    uint8_t* sb = b_slots + (kt % kBStages) * kSlotBytes;
-    const uint8_t* na = a_slots + ((kt + 1) % kAStages) * kSlotBytes;
-    const uint8_t* nb = b_slots + ((kt + 1) % kBStages) * kSlotBytes;
+    uint8_t* sa = a_slots + (kt % kAS) * kASlot;
+    uint8_t* sb = b_slots + (kt % kBS) * kSlotBytes;
+    const uint8_t* na = a_slots + ((kt + 1) % kAS) * kASlot;
+    const uint8_t* nb = b_slots + ((kt + 1) % kBS) * kSlotBytes;
     load_frags<NFA>(sa, sb, 1, a_row0, b_row, xa, xb, f1);
-    stage_b(b_slots + ((kt + kBStages - 1) % kBStages) * kSlotBytes, b_lo, b_hi, off, wave,
-            min((kt + kBStages - 1) * kRowBytes, last));
+    if constexpr (DEEP) {  // k-tile kt+3 into the slots of kt-1, free since barrier kt-1
+      const int t3 = (kt + kDeep - 1) % kDeep;
+      stage_a<NA>(a_slots + t3 * kASlot, a_tile, off, wave, min((kt + kDeep - 1) * kRowBytes, last));
+      stage_b(b_slots + t3 * kSlotBytes, b_lo, b_hi, off, wave,
+              min((kt + kDeep - 1) * kRowBytes, last));
+    } else {
+      stage_b(b_slots + ((kt + kBStages - 1) % kBStages) * kSlotBytes, b_lo, b_hi, off, wave,
+              min((kt + kBStages - 1) * kRowBytes, last));
+    }
     mma_step<NFA>(f0, acc);
-    pin_kstep_schedule<kMfma, kReads, kDmaB>();
+    pin_kstep_schedule<kMfma, kReads, DEEP ? NA + kDmaB : kDmaB>();
     load_frags<NFA>(sa, sb, 2, a_row0, b_row, xa, xb, f0);
     mma_step<NFA>(f1, acc);
     pin_kstep_schedule<kMfma, kReads, 0>();
@@ -211,9 +237,9 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
     pin_kstep_schedule<kMfma, kReads, 0>();
     wait_loads_and_barrier<kVmBarrier>();  // tile kt+1 landed; tile kt's slots free
     load_frags<NFA>(na, nb, 0, a_row0, b_row, xa, xb, f0);
-    stage_a<NA>(sa, a_tile, off, wave, min((kt + kAStages) * kRowBytes, last));
+    if constexpr (!DEEP) stage_a<NA>(sa, a_tile, off, wave, min((kt + kAStages) * kRowBytes, last));
     mma_step<NFA>(f1, acc);
-    pin_kstep_schedule<kMfma, kReads, NA>();
+    pin_kstep_schedule<kMfma, kReads, DEEP ? 0 : NA>();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -309,7 +335,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
   else if (left > kBM / 4)
     gemm_tile<EPI, 2>(ta, lds);
   else
-    gemm_tile<EPI, 1>(ta, lds);
+    gemm_tile<EPI, 1, true>(ta, lds);
 }
 
 // ------------------------------------------------------------------ fp32 VALU GEMM
