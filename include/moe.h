@@ -257,7 +257,8 @@ moe_status_t moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t dtype, const
  *     of h, blocks of 32 along I, from the fp32 values), W'_e = D(wq_down[e]);
  *     requires cfg->intermediate to be a multiple of 512.
  * Exactly one of the two must be given.  Requires cfg->dtype == MOE_BF16,
- * cfg->num_shared == 0 and cfg->hidden a multiple of 512 (MOE_ERR_UNSUPPORTED
+ * cfg->num_shared == 0 (the block-scaled shared experts run inside
+ * moe_forward_mxfp8) and cfg->hidden a multiple of 512 (MOE_ERR_UNSUPPORTED
  * otherwise).
  * Arguments (T = num_tokens, K = top_k, d = hidden, I = intermediate,
  * E_loc = expert_end - expert_begin):
