@@ -22,13 +22,14 @@ MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_UNSUPPORT
 MOE_F32, MOE_BF16 = 0, 1
 MOE_MX_ROWS, MOE_MX_MFMA = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_WEIGHTS_ROW_MAJOR, MOE_WEIGHTS_PACKED = 0, 1
 MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_EXPERT_MLP, MOE_WS_FORWARD, MOE_WS_FORWARD_DBO = range(5)
 
 EXPORTED = ["moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_forward",
             "moe_forward_dbo", "moe_forward_dbo_at", "moe_graph_capture_forward",
             "moe_graph_capture_forward_dbo", "moe_graph_launch", "moe_graph_destroy",
             "moe_workspace_bytes", "moe_dbo_split_point", "moe_dbo_plan_split",
-            "moe_quantize_mxfp8", "moe_expert_mlp_mxfp8", "moe_dispatch_mxfp8",
+            "moe_quantize_mxfp8", "moe_expert_mlp_mxfp8", "moe_dispatch_mxfp8", "moe_pack_weights",
             "moe_forward_mxfp8", "moe_graph_capture_forward_mxfp8", "moe_status_string"]
 
 
@@ -41,7 +42,7 @@ class MoEError(RuntimeError):
 class ConfigStruct(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_tokens", "hidden", "num_experts", "top_k", "intermediate", "expert_begin",
-        "expert_end", "num_shared", "score", "renormalize", "dtype")]
+        "expert_end", "num_shared", "score", "renormalize", "dtype", "weight_layout")]
 
 
 class LayerTensorsMxfp8Struct(ctypes.Structure):
@@ -85,6 +86,7 @@ def lib() -> ctypes.CDLL:
             "moe_graph_launch": [P, P],
             "moe_graph_destroy": [P],
             "moe_quantize_mxfp8": [I32, I32, I32, P, ctypes.c_int64, I32, P, P, P],
+            "moe_pack_weights": [I32, I32, I32, P, P, P],
             "moe_expert_mlp_mxfp8": [C, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
             "moe_dispatch_mxfp8": [C, P, P, P, P, P, P, P, P, P, SZ, P],
             "moe_forward_mxfp8": [C, ctypes.POINTER(LayerTensorsMxfp8Struct), P, SZ, P],
@@ -116,7 +118,8 @@ def config_struct(cfg: MoEConfig, num_tokens: Optional[int] = None) -> ConfigStr
         int(cfg.num_tokens if num_tokens is None else num_tokens), cfg.hidden, cfg.num_experts,
         cfg.top_k, cfg.intermediate, cfg.expert_begin, cfg.expert_end, cfg.num_shared,
         MOE_SCORE_SIGMOID if cfg.score == "sigmoid" else MOE_SCORE_SOFTMAX,
-        int(cfg.renormalize), MOE_BF16 if cfg.dtype == "bf16" else MOE_F32)
+        int(cfg.renormalize), MOE_BF16 if cfg.dtype == "bf16" else MOE_F32,
+        MOE_WEIGHTS_PACKED if cfg.packed_weights else MOE_WEIGHTS_ROW_MAJOR)
 
 
 def _cs(cfg) -> ConfigStruct:
@@ -338,6 +341,17 @@ def dbo_plan_split(num_tokens: int, has_prefill: bool, decode_threshold: int,
                    prefill_threshold: int, uniform_query_len: int = 1) -> int:
     return int(lib().moe_dbo_plan_split(int(num_tokens), int(has_prefill), int(decode_threshold),
                                         int(prefill_threshold), int(uniform_query_len)))
+
+
+def moe_pack_weights(w, packed, stream=None):
+    """w [n, rows, cols] bf16 (row-major) -> packed (same shape and size) in the
+    layout of MOE_WEIGHTS_PACKED: [n, rows/128, cols/64, 128, 64]."""
+    if w.dim() != 3:
+        raise ValueError("w: expected [n, rows, cols]")
+    n, rows, cols = w.shape
+    _check("moe_pack_weights", lib().moe_pack_weights(
+        n, rows, cols, _p(w, "w", None, torch.bfloat16),
+        _p(packed, "packed", tuple(w.shape), torch.bfloat16), _stream(stream)))
 
 
 def moe_quantize_mxfp8(x, codes, scales, scale_layout: int = 0, stream=None):

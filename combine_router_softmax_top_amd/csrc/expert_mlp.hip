@@ -88,6 +88,7 @@ struct TileArgs {
   uint16_t* C;
   int ldc;
   int row0, rows, m0, n0, N, Kdim;
+  int b_packed;  // weights in the packed layout (16 KB k-tile blocks of 128 rows)
 };
 
 // One output tile of NFA * 64 rows: the 8 waves as 2 x 4, each NFA * 32 rows
@@ -129,8 +130,12 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
       off[j] = (uint32_t)(min(r, a_last) * ta.lda * 2 + lchunk * 16);
     } else {
       // r is the B-tile row; rows 128.. come from b_hi
-      const int br = EPI == EPI_SILU_GLU ? (r & (kNOut - 1)) : r;
-      off[j] = (uint32_t)(min(br, b_last) * Kdim * 2 + lchunk * 16);
+      const int br = min(EPI == EPI_SILU_GLU ? (r & (kNOut - 1)) : r, b_last);
+      // packed: row br is row br % 128 of the tile's row block br / 128, whose
+      // k-tiles are 16 KB apart (a row block takes 128 * Kdim * 2 bytes in
+      // either layout, so the tile's base is the same)
+      off[j] = (uint32_t)(ta.b_packed ? (br & ~127) * Kdim * 2 + (br & 127) * kRowBytes
+                                      : br * Kdim * 2) + lchunk * 16;
     }
   }
 
@@ -194,18 +199,21 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
   uint8_t* b_slots = lds + (DEEP ? kDeep * kASlot : kAStages * kSlotBytes);
   const int nk = Kdim / kBK;
   const int last = (nk - 1) * kRowBytes;
+  // The weights' k-tile step: 128 bytes along a row, or a packed 16 KB block.
+  const int b_step = ta.b_packed ? 128 * kRowBytes : kRowBytes;
+  const int b_lastk = (nk - 1) * b_step;
   if constexpr (DEEP) {
 #pragma unroll
     for (int t = 0; t < kDeep - 1; ++t) {
       stage_a<NA>(a_slots + t * kASlot, a_tile, off, wave, min(t * kRowBytes, last));
-      stage_b(b_slots + t * kSlotBytes, b_lo, b_hi, off, wave, min(t * kRowBytes, last));
+      stage_b(b_slots + t * kSlotBytes, b_lo, b_hi, off, wave, min(t * b_step, b_lastk));
     }
   } else {
 #pragma unroll
     for (int t = 0; t < kMaxStages; ++t) {
       if (t < kAStages) stage_a<NA>(a_slots + t * kSlotBytes, a_tile, off, wave, min(t * kRowBytes, last));
       if (t < kBStages - 1)  // B2 comes in iteration 0
-        stage_b(b_slots + t * kSlotBytes, b_lo, b_hi, off, wave, min(t * kRowBytes, last));
+        stage_b(b_slots + t * kSlotBytes, b_lo, b_hi, off, wave, min(t * b_step, b_lastk));
     }
   }
   wait_loads_and_barrier<kVmPrologue>();  // tile 0 landed
@@ -222,10 +230,10 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
       const int t3 = (kt + kDeep - 1) % kDeep;
       stage_a<NA>(a_slots + t3 * kASlot, a_tile, off, wave, min((kt + kDeep - 1) * kRowBytes, last));
       stage_b(b_slots + t3 * kSlotBytes, b_lo, b_hi, off, wave,
-              min((kt + kDeep - 1) * kRowBytes, last));
+              min((kt + kDeep - 1) * b_step, b_lastk));
     } else {
       stage_b(b_slots + ((kt + kBStages - 1) % kBStages) * kSlotBytes, b_lo, b_hi, off, wave,
-              min((kt + kBStages - 1) * kRowBytes, last));
+              min((kt + kBStages - 1) * b_step, b_lastk));
     }
     mma_step<NFA>(f0, acc);
     pin_kstep_schedule<kMfma, kReads, DEEP ? NA + kDmaB : kDmaB>();
@@ -293,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
     const int32_t* __restrict__ offsets, int n_groups, int fixed_rows, int N, int Kdim,
     const uint16_t* __restrict__ A2, long long strideA2, const uint16_t* __restrict__ B2_0,
     const uint16_t* __restrict__ B2_1, long long strideB2, uint16_t* __restrict__ C2,
-    long long strideC2, int n_extra, int extra_rows) {
+    long long strideC2, int n_extra, int extra_rows, int b_packed) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[(kAStages + kBStages) * kSlotBytes];
 
   // Output columns per tile: EPI_STORE 256, EPI_SILU_GLU 128 (gate and up 128 each).
@@ -325,6 +333,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(
   ta.n0 = tl.n_tile * kNOut;
   ta.N = N;
   ta.Kdim = Kdim;
+  ta.b_packed = b_packed;
   // Height of the tile: its rows rounded up to 64 (a full tile when more
   // than 192), as find_tile classed it.
   const int left = tl.rows - ta.m0;
@@ -478,6 +487,7 @@ struct GemmArgs {
   // and strides per group, and their common row count.
   const void* A2; long long strideA2; const void* B2_0; const void* B2_1; long long strideB2;
   void* C2; long long strideC2; int n_extra; int extra_rows;
+  int b_packed;  // bf16 weights in the packed layout (moe_pack_weights)
 };
 
 template <int EPI>
@@ -494,7 +504,7 @@ hipError_t run_gemm(int dtype, const GemmArgs& g, hipStream_t s) {
                        static_cast<const uint16_t*>(g.A2), g.strideA2,
                        static_cast<const uint16_t*>(g.B2_0), static_cast<const uint16_t*>(g.B2_1),
                        g.strideB2, static_cast<uint16_t*>(g.C2), g.strideC2, g.n_extra,
-                       g.extra_rows);
+                       g.extra_rows, g.b_packed);
   } else {
     const int rt = g.offsets ? g.max_row_tiles_bound : ceil_div(g.fixed_rows, kFM);
     const dim3 grid(grid_for(rt, ceil_div(g.N, kFN)), 1, g.batch);
@@ -539,13 +549,14 @@ hipError_t launch_expert_mlp(const moe_config_t& c, const void* x_sorted, const 
 
   GemmArgs up{x_sorted, d, 0, w_gate, w_up, (long long)I * d, 0, h, I, 0,
               offsets, n_loc, 0, row_bound, I, d, 1,
-              x, 0, ws_gate, ws_up, (long long)I * d, h_sh, (long long)T * I, S, T};
+              x, 0, ws_gate, ws_up, (long long)I * d, h_sh, (long long)T * I, S, T,
+              c.weight_layout == MOE_WEIGHTS_PACKED};
   hipError_t err = run_gemm<EPI_SILU_GLU>(c.dtype, up, s);
   if (err != hipSuccess) return err;
   GemmArgs down{h, I, 0, w_down, nullptr, (long long)d * I, 0, y_sorted, d, 0,
                 offsets, n_loc, 0, row_bound, d, I, 1,
                 h_sh, (long long)T * I, ws_down, nullptr, (long long)d * I, y_shared,
-                (long long)T * d, S, T};
+                (long long)T * d, S, T, c.weight_layout == MOE_WEIGHTS_PACKED};
   return run_gemm<EPI_STORE>(c.dtype, down, s);
 }
 
@@ -561,7 +572,7 @@ hipError_t launch_grouped_down_bf16(const moe_config_t& c, const void* h, const 
   GemmArgs down{h, I, 0, w_down, nullptr, (long long)d * I, 0, y_sorted, d, 0,
                 offsets, n_loc, 0, row_bound, d, I, 1,
                 h_sh, (long long)T * I, ws_down, nullptr, (long long)d * I, y_shared,
-                (long long)T * d, S, T};
+                (long long)T * d, S, T, c.weight_layout == MOE_WEIGHTS_PACKED};
   return run_gemm<EPI_STORE>(MOE_BF16, down, s);
 }
 

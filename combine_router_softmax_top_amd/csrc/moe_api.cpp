@@ -31,9 +31,14 @@ moe_status_t check_config(const moe_config_t* c) {
     return MOE_ERR_INVALID_ARGUMENT;
   if (c->renormalize != 0 && c->renormalize != 1) return MOE_ERR_INVALID_ARGUMENT;
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (c->weight_layout != MOE_WEIGHTS_ROW_MAJOR && c->weight_layout != MOE_WEIGHTS_PACKED)
+    return MOE_ERR_INVALID_ARGUMENT;
   if ((int64_t)c->num_tokens * c->top_k >= (int64_t(1) << 31)) return MOE_ERR_INVALID_ARGUMENT;
   const int q = c->dtype == MOE_BF16 ? 64 : 16;
   if (c->hidden % q != 0 || c->intermediate % q != 0) return MOE_ERR_UNSUPPORTED;
+  if (c->weight_layout == MOE_WEIGHTS_PACKED &&
+      (c->dtype != MOE_BF16 || c->hidden % 128 != 0 || c->intermediate % 128 != 0))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -359,6 +364,19 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y_sorted, const in
                                         static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_pack_weights(int32_t n, int32_t rows, int32_t cols, const void* in, void* packed,
+                              moe_stream_t stream) {
+  if (n < 0 || rows < 1 || cols < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (rows % 128 != 0 || cols % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (n == 0) return MOE_OK;
+  if (!in || !packed || !aligned(in, 16) || !aligned(packed, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(in), b = reinterpret_cast<uintptr_t>(packed);
+  const uintptr_t bytes = (uintptr_t)n * rows * cols * 2;
+  if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARGUMENT;  // overlapping
+  return hip_status(
+      moe::launch_pack_weights(n, rows, cols, in, packed, static_cast<hipStream_t>(stream)));
+}
+
 moe_status_t moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t dtype, const void* in,
                                 int64_t ld, int32_t scale_layout, uint8_t* codes,
                                 uint8_t* scales, moe_stream_t stream) {
@@ -387,7 +405,7 @@ moe_status_t check_mxfp8_common(const moe_config_t* cfg, const void* w_down,
   moe_status_t st = check_config(cfg);
   if (st != MOE_OK) return st;
   if (cfg->dtype != MOE_BF16 || (cfg->num_shared != 0 && !allow_shared) ||
-      cfg->hidden % 512 != 0)
+      cfg->hidden % 512 != 0 || cfg->weight_layout != MOE_WEIGHTS_ROW_MAJOR)
     return MOE_ERR_UNSUPPORTED;
   const bool fp8_down = wq_down != nullptr || wq_down_scales != nullptr;
   if (fp8_down == (w_down != nullptr) || (fp8_down && (!wq_down || !wq_down_scales)))

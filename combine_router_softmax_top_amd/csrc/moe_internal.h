@@ -54,6 +54,10 @@ hipError_t launch_expert_mlp(const moe_config_t& c, const void* x_sorted, const 
                              const void* ws_up, const void* ws_down, void* y_shared,
                              void* workspace, hipStream_t s);
 
+// moe_pack_weights: [n, rows, cols] bf16 -> [n, rows/128, cols/64, 128, 64].
+hipError_t launch_pack_weights(int n, int rows, int cols, const void* in, void* out,
+                               hipStream_t s);
+
 hipError_t launch_mxfp8_quantize(int rows, int cols, int dtype, const void* in, long long ld,
                                  int layout, uint8_t* codes, uint8_t* scales, hipStream_t s);
 

@@ -34,6 +34,14 @@ class MoELayer:
         self.ws_gate = to_dev(host_inputs.get("ws_gate"))
         self.ws_up = to_dev(host_inputs.get("ws_up"))
         self.ws_down = to_dev(host_inputs.get("ws_down"))
+        if cfg.packed_weights:  # the bf16 stacks rearranged once, like an offline conversion
+            for name in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
+                w = getattr(self, name)
+                if w is not None:
+                    packed = torch.empty_like(w)
+                    B.moe_pack_weights(w, packed)
+                    setattr(self, name, packed)
+            torch.cuda.synchronize(dev)
 
         self.topk_ids = torch.empty(T, K, dtype=torch.int32, device=dev)
         self.topk_weights = torch.empty(T, K, dtype=torch.float32, device=dev)

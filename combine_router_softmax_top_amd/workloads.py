@@ -55,6 +55,7 @@ class MoEConfig:
     zipf_s: Optional[float] = None   # router bias b_e = -s ln(e+1)
     dual_microbatch: bool = False
     description: str = ""
+    packed_weights: bool = False     # bf16 weight stacks in the MOE_WEIGHTS_PACKED layout
 
     @property
     def num_local(self) -> int:

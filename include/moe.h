@@ -56,6 +56,8 @@ typedef enum {
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
 /* Router score functions. */
 enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+/* Layouts of the bf16 expert weight stacks (moe_config_t.weight_layout). */
+enum { MOE_WEIGHTS_ROW_MAJOR = 0, MOE_WEIGHTS_PACKED = 1 };
 /* Workspace kinds for moe_workspace_bytes. */
 enum { MOE_WS_ROUTE = 0, MOE_WS_DISPATCH = 1, MOE_WS_EXPERT_MLP = 2, MOE_WS_FORWARD = 3,
        MOE_WS_FORWARD_DBO = 4 };
@@ -70,8 +72,10 @@ enum { MOE_WS_ROUTE = 0, MOE_WS_DISPATCH = 1, MOE_WS_EXPERT_MLP = 2, MOE_WS_FORW
  *   0 <= expert_begin < expert_end <= num_experts;
  *   0 <= num_shared <= MOE_MAX_SHARED; score in MOE_SCORE_*; dtype in MOE_F32/MOE_BF16;
  *   hidden and intermediate >= 1.
+ *   weight_layout in MOE_WEIGHTS_*.
  * Shapes the kernels do not cover return MOE_ERR_UNSUPPORTED:
- *   bf16: hidden and intermediate multiples of 64;  f32: multiples of 4. */
+ *   bf16: hidden and intermediate multiples of 64;  f32: multiples of 4;
+ *   MOE_WEIGHTS_PACKED: bf16 only, hidden and intermediate multiples of 128. */
 typedef struct moe_config {
   int32_t num_tokens;    /* T: tokens in this call                                    */
   int32_t hidden;        /* d: model width                                            */
@@ -84,6 +88,9 @@ typedef struct moe_config {
   int32_t score;         /* MOE_SCORE_SOFTMAX or MOE_SCORE_SIGMOID                    */
   int32_t renormalize;   /* 1: weights = selected scores / their sum; 0: raw scores   */
   int32_t dtype;         /* MOE_F32 or MOE_BF16, for activations and weights          */
+  int32_t weight_layout; /* MOE_WEIGHTS_ROW_MAJOR, or MOE_WEIGHTS_PACKED: every bf16
+                            expert weight stack (w_gate, w_up, w_down, ws_*) passed in
+                            the layout moe_pack_weights writes                        */
 } moe_config_t;
 
 /* A hipStream_t handle; NULL means the default (null) stream. */
@@ -208,6 +215,28 @@ moe_status_t moe_combine(const moe_config_t* cfg, const void* y_sorted, const in
 
 /* Scale layouts of moe_quantize_mxfp8. */
 enum { MOE_MX_ROWS = 0, MOE_MX_MFMA = 1 };
+
+/*
+ * moe_pack_weights -- rearranges a stack of bf16 expert weight matrices once
+ * (offline, like a checkpoint conversion) into the layout the expert GEMM
+ * streams in order.  The grouped GEMM ([PPLX] Dispatch: the expert-contiguous
+ * rows feed a grouped GEMM) reads each weight matrix as k-tiles of 64
+ * columns over blocks of 128 rows; row-major storage spreads such a k-tile
+ * over 128 rows 2*cols bytes apart, the packed layout stores it as 16 KB in
+ * a row, the k-tiles of a row block one after another:
+ *   in [n, rows, cols] bf16 (row-major)  ->  packed [n, rows/128, cols/64, 128, 64] bf16,
+ *   packed element (m, r / 128, c / 64, r % 128, c % 64) = in[m, r, c].
+ * The packed stack has the same size; layers whose config has weight_layout
+ * = MOE_WEIGHTS_PACKED take w_gate and w_up ([E_loc, I, d]: rows = I,
+ * cols = d), w_down ([E_loc, d, I]: rows = d, cols = I) and the shared
+ * stacks in this layout; results are bit-identical to the row-major layer's
+ * (the same products in the same order).
+ * Requirements: n >= 0 (0: nothing to do), rows a multiple of 128, cols a
+ * multiple of 64 (else MOE_ERR_UNSUPPORTED); in and packed 16-byte aligned,
+ * not overlapping (MOE_ERR_INVALID_ARGUMENT otherwise).
+ */
+moe_status_t moe_pack_weights(int32_t n, int32_t rows, int32_t cols, const void* in, void* packed,
+                              moe_stream_t stream);
 
 /*
  * moe_quantize_mxfp8 -- block-scaled 8-bit encoding of the rows of a matrix,

@@ -266,3 +266,35 @@ def test_block_scaled_forward_and_capture_reject_bad_arguments_on_host(lib):
     assert lib.moe_forward_mxfp8(ctypes.byref(cs), ctypes.byref(both), P, 1 << 40, None) == inv
     full.wq_gate_scales = P + 2  # scales must be 4-byte aligned
     assert lib.moe_forward_mxfp8(ctypes.byref(cs), ctypes.byref(full), P, 1 << 40, None) == inv
+
+
+def test_packed_layout_is_validated_on_host(lib):
+    P = 0x10000
+    inv, uns = B.MOE_ERR_INVALID_ARGUMENT, B.MOE_ERR_UNSUPPORTED
+    f = lib.moe_pack_weights
+    assert f(-1, 128, 64, P, P * 64, None) == inv
+    assert f(1, 0, 64, P, P * 64, None) == inv
+    assert f(1, 192, 64, P, P * 64, None) == uns          # rows not a multiple of 128
+    assert f(1, 128, 96, P, P * 64, None) == uns          # cols not a multiple of 64
+    assert f(0, 128, 64, None, None, None) == B.MOE_OK    # nothing to do
+    assert f(1, 128, 64, None, P * 64, None) == inv
+    assert f(1, 128, 64, P + 8, P * 64, None) == inv      # not 16-byte aligned
+    assert f(1, 128, 64, P, P + 128 * 64, None) == inv    # overlapping
+    cfg = W.CONFIGS["dsv3_prefill_ep"]
+    bad = B.config_struct(cfg)
+    bad.weight_layout = 2
+    assert lib.moe_workspace_bytes(ctypes.byref(bad), B.MOE_WS_FORWARD) == 0
+    ok = B.config_struct(cfg.replace(packed_weights=True))
+    assert ok.weight_layout == B.MOE_WEIGHTS_PACKED
+    assert lib.moe_workspace_bytes(ctypes.byref(ok), B.MOE_WS_FORWARD) == \
+        lib.moe_workspace_bytes(ctypes.byref(B.config_struct(cfg)), B.MOE_WS_FORWARD)
+    # fp32 layers and widths that are not multiples of 128 have no packed form
+    mlp = lib.moe_expert_mlp
+    for c in (W.CONFIGS["tiny_f32"].replace(packed_weights=True),
+              cfg.replace(intermediate=2048 - 64, packed_weights=True)):
+        # x_sorted, offsets, w_gate, w_up, w_down, y_sorted; no shared experts; workspace
+        assert mlp(ctypes.byref(B.config_struct(c)), *([P] * 6), *([None] * 5), P, 1 << 40,
+                   None) == uns
+    # nor does the block-scaled path (its weights are MX-FP8 encoded)
+    lt = B.LayerTensorsMxfp8Struct(*([P] * len(B.LayerTensorsMxfp8Struct._fields_)))
+    assert lib.moe_forward_mxfp8(ctypes.byref(ok), ctypes.byref(lt), P, 1 << 40, None) == uns
