@@ -55,6 +55,13 @@ MUTANTS = [
     ("mx_forward_h_not_encoded",
      "  const std::vector<double> hq = decoded(n_rows, I, ODT_F64, hh.data());",
      "  const std::vector<double> hq = hh;"),
+    ("dbo_boundary_ties_high",
+     "    split = (split - below <= above - split) ? below : above;",
+     "    split = (split - below < above - split) ? below : above;"),
+    ("e4m3_subnormal_step", "  if (ef == 0) return sign * std::ldexp((double)m, -9);",
+     "  if (ef == 0) return sign * std::ldexp((double)m, -8);"),
+    ("invalid_ids_not_counted", "    if (e < 0 || e >= E) ++bad;\n    else ++counts[e];",
+     "    if (e < 0 || e >= E) (void)bad;\n    else ++counts[e];"),
     ("mx_shared_first_stack_only",
      "      for (int t = 0; t < T; ++t) sh_expert[t] = s;\n      oracle_expert_mlp_mxfp8(",
      "      for (int t = 0; t < T; ++t) sh_expert[t] = 0;\n      oracle_expert_mlp_mxfp8("),
