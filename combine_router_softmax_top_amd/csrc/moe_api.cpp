@@ -368,6 +368,8 @@ moe_status_t moe_pack_weights(int32_t n, int32_t rows, int32_t cols, const void*
                               moe_stream_t stream) {
   if (n < 0 || rows < 1 || cols < 1) return MOE_ERR_INVALID_ARGUMENT;
   if (rows % 128 != 0 || cols % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  // one thread per 16 bytes, 256 per workgroup, in a 1-D grid
+  if ((int64_t)n * rows * cols / 8 / 256 >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
   if (n == 0) return MOE_OK;
   if (!in || !packed || !aligned(in, 16) || !aligned(packed, 16)) return MOE_ERR_INVALID_ARGUMENT;
   const uintptr_t a = reinterpret_cast<uintptr_t>(in), b = reinterpret_cast<uintptr_t>(packed);

@@ -232,7 +232,7 @@ enum { MOE_MX_ROWS = 0, MOE_MX_MFMA = 1 };
  * stacks in this layout; results are bit-identical to the row-major layer's
  * (the same products in the same order).
  * Requirements: n >= 0 (0: nothing to do), rows a multiple of 128, cols a
- * multiple of 64 (else MOE_ERR_UNSUPPORTED); in and packed 16-byte aligned,
+ * multiple of 64, n*rows*cols < 2^42 (else MOE_ERR_UNSUPPORTED); in and packed 16-byte aligned,
  * not overlapping (MOE_ERR_INVALID_ARGUMENT otherwise).
  */
 moe_status_t moe_pack_weights(int32_t n, int32_t rows, int32_t cols, const void* in, void* packed,

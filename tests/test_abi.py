@@ -276,6 +276,7 @@ def test_packed_layout_is_validated_on_host(lib):
     assert f(1, 0, 64, P, P * 64, None) == inv
     assert f(1, 192, 64, P, P * 64, None) == uns          # rows not a multiple of 128
     assert f(1, 128, 96, P, P * 64, None) == uns          # cols not a multiple of 64
+    assert f(1 << 16, 1 << 13, 1 << 14, P, P * 64, None) == uns  # 2^43 elements: grid too large
     assert f(0, 128, 64, None, None, None) == B.MOE_OK    # nothing to do
     assert f(1, 128, 64, None, P * 64, None) == inv
     assert f(1, 128, 64, P + 8, P * 64, None) == inv      # not 16-byte aligned
