@@ -54,6 +54,9 @@ def parse():
                    help="no GPU work: read the rocprofv3 counter CSVs under DIR (pmc_FETCH_SIZE, "
                         "pmc_WRITE_SIZE, pmc_copy_FETCH_SIZE, pmc_copy_WRITE_SIZE) and write the "
                         "expert-MLP HBM traffic record for the current kernel source")
+    p.add_argument("--packed-weights", action="store_true",
+                   help="expert weights in the packed layout (moe_pack_weights, "
+                        "MOE_WEIGHTS_PACKED); the block-scaled leg is skipped")
     p.add_argument("--dbo", action="store_true",
                    help="time the two-microbatch forward (moe_forward_dbo, compute + comm "
                         "streams) against the unsplit moe_forward on the same tokens")
@@ -232,6 +235,8 @@ def main():
         return
 
     cfg = W.CONFIGS[args.workload]
+    if args.packed_weights:
+        cfg = cfg.replace(packed_weights=True)
     t_gen = time.perf_counter()
     inp = W.make_inputs(cfg, seed=0)
     t_gen = time.perf_counter() - t_gen
@@ -291,7 +296,7 @@ def main():
     peak = BF16_MFMA_PEAK_TFLOPS if bf16 else FP32_VALU_PEAK_TFLOPS
     gemm_tflops = alg["gemm_flops"] / (stage["expert_mlp"] * 1e-3) / 1e12
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    if os.path.exists(TRAFFIC_FILE) and not cfg.packed_weights:  # counted on row-major weights
         rec = json.load(open(TRAFFIC_FILE))
         if rec.get("source_digest") == source_digest() and rec.get("workload") == cfg.name:
             traffic = rec.get("hbm_bytes_per_launch")
@@ -313,7 +318,8 @@ def main():
                    "local_experts": f"{cfg.expert_begin}-{cfg.expert_end - 1}",
                    "top_k": cfg.top_k, "intermediate": cfg.intermediate,
                    "shared_experts": cfg.num_shared, "local_rows": n_loc,
-                   "tokens_touching_local_experts": t_touch, "parallelism": "none (1 GPU)"},
+                   "tokens_touching_local_experts": t_touch, "parallelism": "none (1 GPU)",
+                   "weights": "packed" if cfg.packed_weights else "row-major"},
         "stages_us": {k: round(v * 1e3, 2) for k, v in stage.items()},
         "dispatch_combine": {
             "tokens_per_s": T / (dc_ms * 1e-3),
@@ -337,7 +343,7 @@ def main():
         result["graph_replay"] = graph_replay(args, layer, stream, torch)
     if not args.no_cold:
         result["dispatch_combine_cold"] = cold_dispatch_combine(layer, stream, torch, alg)
-    if not args.no_mxfp8 and cfg.dtype == "bf16" and cfg.num_shared == 0 and cfg.hidden % 512 == 0:
+    if not args.no_mxfp8 and not cfg.packed_weights and cfg.dtype == "bf16" and cfg.num_shared == 0 and cfg.hidden % 512 == 0:
         result["mxfp8"] = mxfp8_leg(args, layer, stream, torch, alg, n_loc, t_touch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
