@@ -522,6 +522,24 @@ hipError_t run_gemm(int dtype, const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
+// The launch grids of launch_expert_mlp, in 64-bit: grid_for over the row-tile
+// bound and the column tiles of each pass, times the threads per workgroup.
+long long expert_mlp_max_workitems(const moe_config_t& c) {
+  const bool bf16 = c.dtype == MOE_BF16;
+  const long long T = c.num_tokens, K = c.top_k, S = c.num_shared;
+  const long long n_loc = c.expert_end - c.expert_begin;
+  const long long bm = bf16 ? kBM : kFM;
+  const long long rt = ceil_div_ll(T * K, bm) + n_loc + S * ceil_div_ll(T, bm);
+  auto workitems = [&](long long col_tiles) {
+    const long long rx = xcd_row_groups(col_tiles >= 4 ? 4 : (int)col_tiles), cx = 8 / rx;
+    const long long per_xcd = ceil_div_ll(col_tiles, cx) * (ceil_div_ll(rt, rx) + 1);
+    return 8 * per_xcd * (bf16 ? kThreads : 256);
+  };
+  const long long up = workitems(ceil_div_ll(c.intermediate, bf16 ? kBN / 2 : kFN));
+  const long long down = workitems(ceil_div_ll(c.hidden, bf16 ? kBN : kFN));
+  return up > down ? up : down;
+}
+
 // Workspace: h for the routed rows [T*K, I] and for the shared experts [S, T, I].
 size_t mlp_workspace_bytes(const moe_config_t& c) {
   const size_t elem = c.dtype == MOE_BF16 ? 2 : 4;

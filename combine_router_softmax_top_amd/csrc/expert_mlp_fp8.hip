@@ -140,7 +140,9 @@ struct QTileArgs {
 // halves, then 256 weight rows x 2 halves).
 constexpr int kQStages = 2;
 constexpr int kQScaleRegion = 4096;
-constexpr int kQLds = 2 * kQStages * kSlotBytes + 4 * kQScaleRegion;
+// Scale regions: (group parity, dword) x 4, then 2 pad regions that take the
+// last group's surplus scale loads (see the k-loop).
+constexpr int kQLds = 2 * kQStages * kSlotBytes + 6 * kQScaleRegion;
 static_assert(kQLds <= 160 * 1024, "LDS budget");
 
 // EPI_SILU_GLU: B tile rows 0..127 gate, 128..255 the matching up rows, 128
@@ -214,11 +216,11 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
   }
   const uint32_t a_gs = (uint32_t)ta.rows_as * 2, b_gs = (uint32_t)ta.rows_bs * 2;
   uint8_t* regions = lds + 2 * kQStages * kSlotBytes;
-  // Dword d of group g into region (g % 2, d) (t = 0, 1: activations; 2, 3:
-  // weights; waves 0..3 fill weight rows 0..127 (gate) for t = 2, 128..255
-  // (up) for t = 3).
-  auto stage_scales = [&](int g, int d) {
-    uint8_t* region = regions + ((g & 1) * 2 + d) * kQScaleRegion;
+  // Dword d of group g into `region` (t = 0, 1: activations; 2, 3: weights;
+  // waves 0..3 fill weight rows 0..127 (gate) for t = 2, 128..255 (up) for
+  // t = 3).  Region (g % 2, d) holds the group's dword d.
+  auto scale_region = [&](int g, int d) { return regions + ((g & 1) * 2 + d) * kQScaleRegion; };
+  auto stage_scales = [&](int g, int d, uint8_t* region) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const uint32_t* src = t < 2 ? as32 + (uint32_t)(2 * g + d) * a_gs
@@ -268,8 +270,8 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
   const int nk = Kdim / kQK;  // a multiple of kQGroupTiles
   const int ng = nk / kQGroupTiles;
   const int last = (nk - 1) * kRowBytes;
-  stage_scales(0, 0);
-  stage_scales(0, 1);
+  stage_scales(0, 0, scale_region(0, 0));
+  stage_scales(0, 1, scale_region(0, 1));
 #pragma unroll
   for (int t = 0; t < kQStages; ++t) {
     qstage<NA>(a_slots + t * kSlotBytes, a_tile, a_tile, NA, offa, wave, min(t * kRowBytes, last));
@@ -307,11 +309,15 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
       qstage<NA>(sa, a_tile, a_tile, NA, offa, wave, kb);
       qstage<kQDmaB>(sb, b_lo, b_hi, kQDmaB / 2, offb, wave, kb);
       if constexpr (J == 0) {
-        // In the last group this reloads the group's own scales into its own
-        // buffer: the same bytes, so a read racing the load sees them either
-        // way; the load count stays the one the barrier waits assume.
-        stage_scales(min(g + 1, ng - 1), 0);
-        stage_scales(min(g + 1, ng - 1), 1);
+        // Group g+1's scales into the regions group g-1 used.  The last group
+        // has no successor: it issues the same loads (so the counts the
+        // barrier waits assume hold in every group) from its own scales into
+        // the two pad regions, which nothing reads; no load ever writes a
+        // region that is being read.
+        const bool more = g + 1 < ng;
+        const int gs = more ? g + 1 : g;
+        stage_scales(gs, 0, more ? scale_region(gs, 0) : regions + 4 * kQScaleRegion);
+        stage_scales(gs, 1, more ? scale_region(gs, 1) : regions + 5 * kQScaleRegion);
       }
       qmma_step<NFA, 2 * (J % 2) + 1>(f1, sca, scb, acc);
       // After the last MFMA of the pair that uses them, the scale registers

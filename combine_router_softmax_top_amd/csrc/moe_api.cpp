@@ -39,6 +39,10 @@ moe_status_t check_config(const moe_config_t* c) {
   if (c->weight_layout == MOE_WEIGHTS_PACKED &&
       (c->dtype != MOE_BF16 || c->hidden % 128 != 0 || c->intermediate % 128 != 0))
     return MOE_ERR_UNSUPPORTED;
+  // A launch holds fewer than 2^32 work-items: one wave per token in the
+  // router, scatter and combine; the grouped GEMMs' grids.
+  if (c->num_tokens >= MOE_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+  if (moe::expert_mlp_max_workitems(*c) >= moe::kMaxWorkItems) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -368,8 +372,8 @@ moe_status_t moe_pack_weights(int32_t n, int32_t rows, int32_t cols, const void*
                               moe_stream_t stream) {
   if (n < 0 || rows < 1 || cols < 1) return MOE_ERR_INVALID_ARGUMENT;
   if (rows % 128 != 0 || cols % 64 != 0) return MOE_ERR_UNSUPPORTED;
-  // one thread per 16 bytes, 256 per workgroup, in a 1-D grid
-  if ((int64_t)n * rows * cols / 8 / 256 >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  // one work-item per 16 bytes, 256 per workgroup, fewer than 2^32 in all
+  if ((int64_t)n * rows * cols / 8 + 255 >= moe::kMaxWorkItems) return MOE_ERR_UNSUPPORTED;
   if (n == 0) return MOE_OK;
   if (!in || !packed || !aligned(in, 16) || !aligned(packed, 16)) return MOE_ERR_INVALID_ARGUMENT;
   const uintptr_t a = reinterpret_cast<uintptr_t>(in), b = reinterpret_cast<uintptr_t>(packed);
@@ -387,12 +391,12 @@ moe_status_t moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t dtype, const
   if (scale_layout != MOE_MX_ROWS && scale_layout != MOE_MX_MFMA) return MOE_ERR_INVALID_ARGUMENT;
   if (scale_layout == MOE_MX_MFMA && cols % 512 != 0) return MOE_ERR_INVALID_ARGUMENT;
   if (rows == 0) return MOE_OK;
+  // One work-item per 8 elements, 256 per workgroup, fewer than 2^32 in all.
+  if ((int64_t)rows * (cols / 8) + 255 >= moe::kMaxWorkItems) return MOE_ERR_UNSUPPORTED;
   if (!in || !codes || !scales) return MOE_ERR_INVALID_ARGUMENT;
   const int elem = dtype == MOE_BF16 ? 2 : 4;
   if (!aligned(in, 16) || (ld * elem) % 16 != 0 || !aligned(codes, 8) || !aligned(scales, 4))
     return MOE_ERR_INVALID_ARGUMENT;
-  // One lane per 8 elements, 256 lanes per workgroup: the grid must fit.
-  if ((int64_t)rows * (cols / 8) > (int64_t)0x7fffffff * 256) return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_mxfp8_quantize(rows, cols, dtype, in, ld, scale_layout, codes,
                                                scales, static_cast<hipStream_t>(stream)));
 }

@@ -31,6 +31,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 }
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline long long ceil_div_ll(long long a, long long b) { return (a + b - 1) / b; }
+
+// HIP launches hold fewer work-items than this in each grid dimension.
+constexpr long long kMaxWorkItems = 0xffffffffLL;
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // ---- launchers (each returns the launch status) ----
@@ -48,6 +52,10 @@ hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* 
                            uint8_t* xq = nullptr, uint32_t* xs = nullptr);
 
 size_t mlp_workspace_bytes(const moe_config_t& c);
+// Work-items of the largest grouped-GEMM launch of a layer with this shape
+// (bf16 or fp32; the block-scaled launches use the same tile grids with fewer
+// threads per workgroup).
+long long expert_mlp_max_workitems(const moe_config_t& c);
 hipError_t launch_expert_mlp(const moe_config_t& c, const void* x_sorted, const int32_t* offsets,
                              const void* w_gate, const void* w_up, const void* w_down,
                              void* y_sorted, const void* x, const void* ws_gate,

@@ -65,6 +65,7 @@ enum { MOE_WS_ROUTE = 0, MOE_WS_DISPATCH = 1, MOE_WS_EXPERT_MLP = 2, MOE_WS_FORW
 #define MOE_MAX_EXPERTS 512
 #define MOE_MAX_TOPK 16
 #define MOE_MAX_SHARED 4
+#define MOE_MAX_TOKENS (1 << 26)
 
 /* One layer's shape.  Limits (else MOE_ERR_INVALID_ARGUMENT):
  *   1 <= num_tokens, num_tokens * top_k < 2^31;
@@ -74,8 +75,11 @@ enum { MOE_WS_ROUTE = 0, MOE_WS_DISPATCH = 1, MOE_WS_EXPERT_MLP = 2, MOE_WS_FORW
  *   hidden and intermediate >= 1.
  *   weight_layout in MOE_WEIGHTS_*.
  * Shapes the kernels do not cover return MOE_ERR_UNSUPPORTED:
- *   bf16: hidden and intermediate multiples of 64;  f32: multiples of 4;
- *   MOE_WEIGHTS_PACKED: bf16 only, hidden and intermediate multiples of 128. */
+ *   bf16: hidden and intermediate multiples of 64;  f32: multiples of 16;
+ *   MOE_WEIGHTS_PACKED: bf16 only, hidden and intermediate multiples of 128;
+ *   num_tokens >= MOE_MAX_TOKENS (the router, scatter and combine run one
+ *   64-lane wave per token, and a launch holds fewer than 2^32 work-items);
+ *   shapes whose grouped expert GEMM launch would reach 2^32 work-items. */
 typedef struct moe_config {
   int32_t num_tokens;    /* T: tokens in this call                                    */
   int32_t hidden;        /* d: model width                                            */
@@ -232,8 +236,9 @@ enum { MOE_MX_ROWS = 0, MOE_MX_MFMA = 1 };
  * stacks in this layout; results are bit-identical to the row-major layer's
  * (the same products in the same order).
  * Requirements: n >= 0 (0: nothing to do), rows a multiple of 128, cols a
- * multiple of 64, n*rows*cols < 2^42 (else MOE_ERR_UNSUPPORTED); in and packed 16-byte aligned,
- * not overlapping (MOE_ERR_INVALID_ARGUMENT otherwise).
+ * multiple of 64, n*rows*cols < 2^35 (one work-item per 8 elements, fewer
+ * than 2^32 in the launch; else MOE_ERR_UNSUPPORTED); in and packed 16-byte
+ * aligned, not overlapping (MOE_ERR_INVALID_ARGUMENT otherwise).
  */
 moe_status_t moe_pack_weights(int32_t n, int32_t rows, int32_t cols, const void* in, void* packed,
                               moe_stream_t stream);
@@ -265,7 +270,8 @@ moe_status_t moe_pack_weights(int32_t n, int32_t rows, int32_t cols, const void*
  *   codes         [rows, cols] uint8 E4M3 (out), 8-byte aligned
  *   scales        uint8 E8M0 (out), 4-byte aligned
  * The result is bit-exact and independent of the launch.  rows == 0 enqueues
- * nothing and reads no pointer.
+ * nothing and reads no pointer.  rows * cols / 8 must stay below 2^32 - 256
+ * (one work-item per 8 elements; MOE_ERR_UNSUPPORTED otherwise).
  */
 moe_status_t moe_quantize_mxfp8(int32_t rows, int32_t cols, int32_t dtype, const void* in,
                                 int64_t ld, int32_t scale_layout, uint8_t* codes,

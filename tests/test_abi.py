@@ -299,3 +299,77 @@ def test_packed_layout_is_validated_on_host(lib):
     # nor does the block-scaled path (its weights are MX-FP8 encoded)
     lt = B.LayerTensorsMxfp8Struct(*([P] * len(B.LayerTensorsMxfp8Struct._fields_)))
     assert lib.moe_forward_mxfp8(ctypes.byref(ok), ctypes.byref(lt), P, 1 << 40, None) == uns
+
+
+# ------------------------------------------------------------------ launch-size limits
+
+def _route_status(lib, cs):
+    P = ctypes.c_void_p
+    # a NULL token pointer: INVALID_ARGUMENT once the shape is accepted, so no
+    # kernel is ever launched on these fake pointers
+    return lib.moe_route(ctypes.byref(cs), None, P(16), None, P(16), P(16), None, P(256),
+                         1 << 40, None)
+
+
+@pytest.mark.parametrize("width,status", [(20, B.MOE_ERR_UNSUPPORTED),   # 4 x odd
+                                          (100, B.MOE_ERR_UNSUPPORTED),
+                                          (48, B.MOE_ERR_INVALID_ARGUMENT),
+                                          (16, B.MOE_ERR_INVALID_ARGUMENT)])
+@pytest.mark.parametrize("field", ["hidden", "intermediate"])
+def test_fp32_widths_are_multiples_of_16(lib, field, width, status):
+    # include/moe.h: fp32 hidden and intermediate must be multiples of 16
+    cs = B.config_struct(W.CONFIGS["tiny_f32"])
+    setattr(cs, field, width)
+    assert _route_status(lib, cs) == status
+    assert (lib.moe_workspace_bytes(ctypes.byref(cs), B.MOE_WS_FORWARD) == 0) == \
+        (status == B.MOE_ERR_UNSUPPORTED)
+
+
+def test_token_count_limit(lib):
+    # one 64-lane wave per token: T = MOE_MAX_TOKENS would need 2^32 work-items
+    cs = B.config_struct(W.CONFIGS["dsv3_prefill_ep"].replace(hidden=64, intermediate=64,
+                                                              top_k=1))
+    cs.num_tokens = (1 << 26) - 1
+    assert _route_status(lib, cs) == B.MOE_ERR_INVALID_ARGUMENT
+    cs.num_tokens = 1 << 26
+    assert _route_status(lib, cs) == B.MOE_ERR_UNSUPPORTED
+
+
+def _gemm_workitems(T, K, n_loc, S, d, I):
+    """Work-items of the larger bf16 grouped-GEMM launch (256x256 tiles, 512
+    threads; gate/up tiles 128 columns wide, down 256), as the launcher sizes
+    its grid: 8 XCDs x (column tiles per XCD x (row tiles per XCD + 1))."""
+    rt = -(-T * K // 256) + n_loc + S * -(-T // 256)
+
+    def wi(col_tiles):
+        rx = 2 if col_tiles >= 4 else 8
+        cx = 8 // rx
+        return 8 * -(-col_tiles // cx) * (-(-rt // rx) + 1) * 512
+    return max(wi(-(-I // 128)), wi(-(-d // 256)))
+
+
+def test_grouped_gemm_grid_limit(lib):
+    # the largest hidden size (a multiple of 64) whose down-projection grid
+    # stays under 2^32 work-items is accepted, the next one is not
+    T, K = 1 << 20, 8
+    cfg = W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=T, top_k=K, intermediate=64)
+    d = 64
+    while _gemm_workitems(T, K, cfg.num_local, 0, d + 64, 64) < 0xffffffff:
+        d += 64
+    for width, status in [(d, B.MOE_ERR_INVALID_ARGUMENT), (d + 64, B.MOE_ERR_UNSUPPORTED)]:
+        cs = B.config_struct(cfg.replace(hidden=width))
+        assert _route_status(lib, cs) == status, width
+
+
+def test_pack_and_quantize_launch_limits(lib):
+    P = ctypes.c_void_p
+    # pack: one work-item per 8 elements; 2^22 stacks of 128 x 64 need 2^32
+    assert lib.moe_pack_weights((1 << 22) - 1, 128, 64, None, P(256), None) == \
+        B.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_pack_weights(1 << 22, 128, 64, P(256), P(4096), None) == B.MOE_ERR_UNSUPPORTED
+    # quantize: rows * cols / 8 work-items, rounded up to workgroups of 256
+    rows_ok = (1 << 30) - 65
+    assert lib.moe_quantize_mxfp8(rows_ok, 32, B.MOE_BF16, None, 32, B.MOE_MX_ROWS, P(256),
+                                  P(256), None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_quantize_mxfp8(rows_ok + 1, 32, B.MOE_BF16, P(256), 32, B.MOE_MX_ROWS,
+                                  P(256), P(256), None) == B.MOE_ERR_UNSUPPORTED

@@ -81,13 +81,30 @@ def test_packed_layer_equals_row_major_and_oracle(name):
 def test_packed_full_size_equals_row_major(name):
     cfg = W.CONFIGS[name]
     inp = W.make_inputs(cfg, 0)
+    # The row-major layer is checked row by row against the oracle at these
+    # sizes (test_gpu_parity.test_full_size); here every row of the packed
+    # layer's expert output and every token of its output must equal it bit for
+    # bit.
     R = MoELayer(cfg, inp)
-    R.forward()
+    R.route()
+    R.dispatch()
+    R.expert_mlp()
+    R.combine()
     torch.cuda.synchronize()
-    ref = R.out.clone()
+    n = R.n_rows()
+    ref, ref_y = R.out.cpu(), R.y_sorted[:n].cpu()
     del R
     torch.cuda.empty_cache()
     P = MoELayer(cfg.replace(packed_weights=True), inp)
-    P.forward()
+    P.route()
+    P.dispatch()
+    P.expert_mlp()
+    P.combine()
     torch.cuda.synchronize()
-    assert torch.equal(bits(P.out), bits(ref))
+    assert P.n_rows() == n
+    assert torch.equal(bits(P.y_sorted[:n].cpu()), bits(ref_y))
+    assert torch.equal(bits(P.out.cpu()), bits(ref))
+    o = torch.empty_like(P.out)
+    P.forward(out=o)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(o.cpu()), bits(ref))
