@@ -30,7 +30,8 @@ EXPORTED = ["moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_f
             "moe_graph_capture_forward_dbo", "moe_graph_launch", "moe_graph_destroy",
             "moe_workspace_bytes", "moe_dbo_split_point", "moe_dbo_plan_split",
             "moe_quantize_mxfp8", "moe_expert_mlp_mxfp8", "moe_dispatch_mxfp8", "moe_pack_weights",
-            "moe_forward_mxfp8", "moe_graph_capture_forward_mxfp8", "moe_status_string"]
+            "moe_forward_mxfp8", "moe_graph_capture_forward_mxfp8", "moe_status_string",
+            "moe_dispatch_noalloc"]
 
 
 class MoEError(RuntimeError):
@@ -76,6 +77,7 @@ def lib() -> ctypes.CDLL:
         sigs = {
             "moe_route": [C, P, P, P, P, P, P, P, SZ, P],
             "moe_dispatch": [C, P, P, P, P, P, P, P, P, SZ, P],
+            "moe_dispatch_noalloc": [C, P, P, P, P, P, P, P, P, P],
             "moe_expert_mlp": [C, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
             "moe_combine": [C, P, P, P, P, P, P],
             "moe_forward": [C, LT, P, SZ, P],
@@ -205,6 +207,24 @@ def moe_dispatch(cfg, x, topk_ids, expert_counts, expert_offsets, x_sorted, src_
                             _p(workspace, "workspace"), workspace.numel() * workspace.element_size(),
                             _stream(stream))
     _check("moe_dispatch", st)
+
+
+def moe_dispatch_noalloc(cfg, x, topk_ids, expert_counts, expert_offsets, x_sorted, src_index,
+                         row_of, n_invalid=None, stream=None):
+    """moe_dispatch without a workspace (the library's own per-GPU scratch)."""
+    c = _cs(cfg)
+    T, d, E, K, dt = c.num_tokens, c.hidden, c.num_experts, c.top_k, _act(c)
+    n_loc = c.expert_end - c.expert_begin
+    st = lib().moe_dispatch_noalloc(ctypes.byref(c), _p(x, "x", (T, d), dt),
+                                    _p(topk_ids, "topk_ids", (T, K), torch.int32),
+                                    _p(expert_counts, "expert_counts", (E,), torch.int32),
+                                    _p(expert_offsets, "expert_offsets", (n_loc + 1,), torch.int32),
+                                    _p(x_sorted, "x_sorted", (T * K, d), dt),
+                                    _p(src_index, "src_index", (T * K,), torch.int32),
+                                    _p(row_of, "row_of", (T * K,), torch.int32),
+                                    _p(n_invalid, "n_invalid", (1,), torch.int32),
+                                    _stream(stream))
+    _check("moe_dispatch_noalloc", st)
 
 
 def moe_expert_mlp(cfg, x_sorted, expert_offsets, w_gate, w_up, w_down, y_sorted, x=None,

@@ -342,13 +342,13 @@ size_t dispatch_workspace_bytes(const moe_config_t& c) {
 hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* ids,
                            int32_t* counts, int32_t* offsets, void* x_sorted, int32_t* src_index,
                            int32_t* row_of, void* workspace, hipStream_t s, uint8_t* xq,
-                           uint32_t* xs) {
+                           uint32_t* xs, int32_t* n_invalid_out) {
   const int T = c.num_tokens, K = c.top_k, E = c.num_experts;
   const int eb = c.expert_begin, ee = c.expert_end, n_loc = ee - eb;
   const int n_assign = T * K;
   const int n_chunks = ceil_div(n_assign, kCA);
   char* ws = static_cast<char*>(workspace);
-  int32_t* n_invalid = reinterpret_cast<int32_t*>(ws);
+  int32_t* n_invalid = n_invalid_out ? n_invalid_out : reinterpret_cast<int32_t*>(ws);
   ws += 256;
   int32_t* hist = reinterpret_cast<int32_t*>(ws);
   ws += align_up((size_t)n_chunks * (E + 1) * 4, 256);

@@ -308,6 +308,28 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const void* x, const int32_t*
                                          static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_dispatch_noalloc(const moe_config_t* cfg, const void* x, const int32_t* topk_ids,
+                                  int32_t* expert_counts, int32_t* expert_offsets, void* x_sorted,
+                                  int32_t* src_index, int32_t* row_of, int32_t* n_invalid,
+                                  moe_stream_t stream) {
+  moe_status_t st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!x || !topk_ids || !expert_counts || !expert_offsets || !x_sorted || !src_index || !row_of)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(x_sorted, 16) || (n_invalid && !aligned(n_invalid, 4)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  // The workspace moe_dispatch would take, here carved from the library's own
+  // array; its first 256 bytes (the count of invalid ids) are not used when
+  // the caller asks for that count.
+  if (moe::dispatch_workspace_bytes(*cfg) > moe::kNoallocScratchBytes) return MOE_ERR_UNSUPPORTED;
+  void* scratch = nullptr;
+  if (moe::noalloc_scratch(&scratch) != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_dispatch(*cfg, x, topk_ids, expert_counts, expert_offsets,
+                                         x_sorted, src_index, row_of, scratch,
+                                         static_cast<hipStream_t>(stream), nullptr, nullptr,
+                                         n_invalid));
+}
+
 moe_status_t moe_dispatch_mxfp8(const moe_config_t* cfg, const void* x, const int32_t* topk_ids,
                                 int32_t* expert_counts, int32_t* expert_offsets,
                                 uint8_t* xq_sorted, uint8_t* xq_scales, int32_t* src_index,

@@ -46,10 +46,19 @@ hipError_t launch_route(const moe_config_t& c, const void* x, const void* w_rout
 size_t dispatch_workspace_bytes(const moe_config_t& c);
 // xq != nullptr: the bf16 rows are encoded as MX-FP8 into codes xq [T*K, d]
 // and scale words xs (MFMA layout, T*K rows); x_sorted is not written.
+// n_invalid_out: where the invalid-id count goes (default: the first int32 of
+// the workspace).
 hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* ids,
                            int32_t* counts, int32_t* offsets, void* x_sorted, int32_t* src_index,
                            int32_t* row_of, void* workspace, hipStream_t s,
-                           uint8_t* xq = nullptr, uint32_t* xs = nullptr);
+                           uint8_t* xq = nullptr, uint32_t* xs = nullptr,
+                           int32_t* n_invalid_out = nullptr);
+
+// The library's own dispatch scratch on the current device (a file-scope
+// device array of kNoallocScratchBytes): its device address, looked up once per
+// device.
+constexpr size_t kNoallocScratchBytes = size_t(4) << 20;
+hipError_t noalloc_scratch(void** ptr);
 
 size_t mlp_workspace_bytes(const moe_config_t& c);
 // Work-items of the largest grouped-GEMM launch of a layer with this shape

@@ -163,6 +163,26 @@ moe_status_t moe_dispatch(const moe_config_t* cfg, const void* x, const int32_t*
                           size_t workspace_bytes, moe_stream_t stream);
 
 /*
+ * moe_dispatch_noalloc -- moe_dispatch for callers that cannot allocate device
+ * memory (code being captured into a HIP graph, tight serving loops, hosts
+ * that forbid hipMalloc): the same kernels and the same results (counts,
+ * offsets, x_sorted, src_index, row_of, bit for bit), with the scratch those
+ * kernels need taken from a 4 MiB array the library holds on each GPU instead
+ * of a workspace argument.  The call allocates nothing.
+ *   n_invalid  [1] int32 (out, device) -- the count of ids outside [0, E), or
+ *              NULL when the caller does not want it
+ * Limits: moe_workspace_bytes(cfg, MOE_WS_DISPATCH) <= 4 MiB (T*K up to about
+ * 900k assignments at E = 256), else MOE_ERR_UNSUPPORTED.  Every call on a GPU
+ * uses that GPU's one array: calls that may overlap on one GPU (different
+ * streams, or graphs replayed concurrently) race and must be serialised by the
+ * caller.  The array needs no clearing: each call writes every entry it reads.
+ */
+moe_status_t moe_dispatch_noalloc(const moe_config_t* cfg, const void* x, const int32_t* topk_ids,
+                                  int32_t* expert_counts, int32_t* expert_offsets, void* x_sorted,
+                                  int32_t* src_index, int32_t* row_of, int32_t* n_invalid,
+                                  moe_stream_t stream);
+
+/*
  * moe_expert_mlp -- grouped SiLU-gated MLP over the expert-contiguous rows,
  * plus optional shared experts over all tokens.
  * [PPLX] Introduction (experts are small MLPs), Dispatch (the contiguous
