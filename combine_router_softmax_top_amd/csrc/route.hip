@@ -13,8 +13,9 @@
 // adds the slices in a fixed order (deterministic).
 // fp32: each wave takes one token and reduces every dot product across its 64
 // lanes with a butterfly.
-// Selection: one wave per token, E/64 candidates per lane in registers, K
-// rounds of a butterfly arg-max ordered by (logit desc, expert id asc).
+// Selection: one wave per token, the partial slices read as 16-byte pieces (4
+// adjacent experts per lane), K rounds of an arg-max ordered by (logit desc,
+// expert id asc), each a DPP reduction into lane 63 read back as a scalar.
 #include <math.h>
 
 #include "moe_internal.h"
@@ -322,36 +323,121 @@ __global__ __launch_bounds__(256, 1) void route_logits_kernel(
       }
 }
 
-// One wave per token: logits = sum of the k-slice partials (ascending) + bias.
-template <int NV>
+// Largest key of the wave, in lane 63 (then read into scalar registers):
+// each row of 16 lanes as in wave_max_key, then row 1 and row 3 take lane 15
+// of the row below (row_bcast:15) and rows 2 and 3 take lane 31
+// (row_bcast:31), all DPP moves, no LDS round trip.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ unsigned long long dpp_max_rows(unsigned long long k) {
+  const int lo0 = (int)(uint32_t)k, hi0 = (int)(uint32_t)(k >> 32);
+  const int lo = __builtin_amdgcn_update_dpp(lo0, lo0, CTRL, ROWS, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(hi0, hi0, CTRL, ROWS, 0xf, false);
+  const unsigned long long o = ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+  return o > k ? o : k;
+}
+__device__ __forceinline__ unsigned long long wave_max_key_uniform(unsigned long long k) {
+  k = dpp_max<0xB1>(k);   // quad_perm [1,0,3,2]
+  k = dpp_max<0x4E>(k);   // quad_perm [2,3,0,1]
+  k = dpp_max<0x124>(k);  // row_ror 4
+  k = dpp_max<0x128>(k);  // row_ror 8
+  k = dpp_max_rows<0x142, 0xa>(k);  // row_bcast:15 into rows 1, 3
+  k = dpp_max_rows<0x143, 0xc>(k);  // row_bcast:31 into rows 2, 3
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// One wave per token: logits = sum of the k-slice partials (ascending) + bias,
+// then the score and the top-K.  Lane l holds experts 4l + r + 256v (r < 4,
+// v < NV4), read as one 16-byte load per slice and v.  K rounds: each lane's
+// best key, the wave's best by DPP into a scalar, which the owning lane then
+// clears.  Keys order by (logit desc, expert asc) (sel_key).
+template <int NV4>
 __global__ __launch_bounds__(256) void route_select_kernel(
     const float* __restrict__ part, int n_slices, int e_pad, const float* __restrict__ bias,
     int T, int E, int K, int score, int renorm, int32_t* __restrict__ ids,
     float* __restrict__ weights, float* __restrict__ logits) {
+  constexpr int NC = 4 * NV4;  // candidates per lane
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   // All slice loads first (at most 8 slices), then the sums in ascending
   // slice order.
-  float p[8][NV];
+  f32x4 p[8][NV4];
 #pragma unroll
   for (int s = 0; s < 8; ++s)
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = min(lane + kWave * i, e_pad - 1);
-      p[s][i] = s < n_slices ? part[((size_t)s * T + t) * e_pad + e] : 0.f;
+    for (int v = 0; v < NV4; ++v) {
+      const int e = min(4 * lane + 256 * v, e_pad - 4);
+      p[s][v] = s < n_slices
+                    ? *reinterpret_cast<const f32x4*>(part + ((size_t)s * T + t) * e_pad + e)
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  float v[NV];
+  float z[NC];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int e = lane + kWave * i;
-    float z = p[0][i];
+  for (int v = 0; v < NV4; ++v) {
+    f32x4 a = p[0][v];
 #pragma unroll
     for (int s = 1; s < 8; ++s)
-      if (s < n_slices) z += p[s][i];
-    v[i] = e < E ? z + (bias ? bias[e] : 0.f) : -INFINITY;
+      if (s < n_slices) a += p[s][v];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int e = 4 * lane + 256 * v + r;
+      z[4 * v + r] = e < E ? a[r] + (bias ? bias[e] : 0.f) : -INFINITY;
+    }
   }
-  select_topk<NV>(v, E, K, score, renorm, t, ids, weights, logits, lane);
+  if (logits) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int e = 4 * lane + 256 * (c / 4) + c % 4;
+      if (e < E) logits[(size_t)t * E + e] = z[c];
+    }
+  }
+  float m = 0.f, denom = 1.f;
+  if (score == MOE_SCORE_SOFTMAX) {
+    float lm = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) lm = fmaxf(lm, z[c]);
+    m = wave_max(lm);
+    float sum = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      if (4 * lane + 256 * (c / 4) + c % 4 < E) sum += __expf(z[c] - m);
+    denom = wave_sum(sum);
+  }
+  unsigned long long kv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int e = 4 * lane + 256 * (c / 4) + c % 4;
+    kv[c] = e < E ? sel_key(z[c], e) : 0ull;
+  }
+  int my_e = 0;
+  float my_s = 0.f, sum_sel = 0.f;
+  for (int k = 0; k < K; ++k) {
+    unsigned long long best = kv[0];
+#pragma unroll
+    for (int c = 1; c < NC; ++c) best = kv[c] > best ? kv[c] : best;
+    best = wave_max_key_uniform(best);
+    const int be = key_expert(best);
+    const float bv = key_value(best);
+    if (((be & 255) >> 2) == lane) {
+      const int slot = (be & 3) + 4 * (be >> 8);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        if (c == slot) kv[c] = 0ull;
+    }
+    const float sc = score == MOE_SCORE_SIGMOID ? 1.f / (1.f + __expf(-bv)) : __expf(bv - m);
+    sum_sel += sc;
+    if (lane == k) { my_e = be; my_s = sc; }
+  }
+  if (lane < K) {
+    float w;
+    if (renorm) w = my_s / sum_sel;
+    else if (score == MOE_SCORE_SOFTMAX) w = my_s / denom;
+    else w = my_s;
+    ids[(size_t)t * K + lane] = my_e;
+    weights[(size_t)t * K + lane] = w;
+  }
 }
 
 template <int NV>
@@ -461,11 +547,9 @@ hipError_t launch_bf16(const moe_config_t& c, const void* x, const void* wr, con
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int nv = ceil_div(c.num_experts, kWave);
-  if (nv <= 1) return launch_select<1>(c, part, ks, e_pad, bias, ids, w, logits, s);
-  if (nv <= 2) return launch_select<2>(c, part, ks, e_pad, bias, ids, w, logits, s);
-  if (nv <= 4) return launch_select<4>(c, part, ks, e_pad, bias, ids, w, logits, s);
-  return launch_select<8>(c, part, ks, e_pad, bias, ids, w, logits, s);
+  // 4 experts per lane and 16-byte load: one or two of them per slice
+  if (e_pad <= 256) return launch_select<1>(c, part, ks, e_pad, bias, ids, w, logits, s);
+  return launch_select<2>(c, part, ks, e_pad, bias, ids, w, logits, s);
 }
 
 template <int NV>
