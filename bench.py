@@ -29,6 +29,7 @@ sys.path.insert(0, _ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0
 FP32_VALU_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "expert_mlp_dsv3_prefill_ep_traffic.json")
 
@@ -58,14 +59,18 @@ def parse():
                    help="expert weights in the packed layout (moe_pack_weights, "
                         "MOE_WEIGHTS_PACKED); the block-scaled leg is skipped")
     p.add_argument("--dbo", action="store_true",
-                   help="time the two-microbatch forward (moe_forward_dbo, compute + comm "
+                   help="only time the two-microbatch forward (moe_forward_dbo, compute + comm "
                         "streams) against the unsplit moe_forward on the same tokens")
+    p.add_argument("--no-dbo", action="store_true",
+                   help="skip the dual-microbatch leg of the default line")
+    p.add_argument("--no-probes", action="store_true",
+                   help="skip the achievable-peak probes (streaming copy, MFMA loops)")
     return p.parse_args()
 
 
-def bench_dbo(args, cfg, layer, torch) -> dict:
-    """Whole-layer time of moe_forward_dbo vs moe_forward (same inputs, same outputs)."""
-    from combine_router_softmax_top_amd import binding as B
+def dbo_timings(args, layer, torch) -> dict:
+    """Whole-layer time of moe_forward_dbo on two streams, on one stream, and of
+    the unsplit moe_forward, on the same tokens (same outputs)."""
     compute, comm = torch.cuda.Stream(), torch.cuda.Stream()
 
     def timed(fn):
@@ -92,17 +97,89 @@ def bench_dbo(args, cfg, layer, torch) -> dict:
         g = layer.capture_forward(dbo=True)
         graph_ms = timed(lambda: g.launch(compute))
         g.destroy()
+    return {"unsplit_ms": unsplit, "split_two_streams_ms": split,
+            "split_one_stream_ms": one_stream, "overlap_gain": unsplit / split - 1.0,
+            "bitwise_equal_to_unsplit": same, "split_graph_replay_ms": graph_ms}
+
+
+def dbo_leg(args, layer, torch) -> dict:
+    """The dual-microbatch workload (8192 tokens of the DeepSeek-V3-shaped share,
+    split at the midpoint into two 4096-token microbatches) on the same device
+    weights as the main workload."""
+    from combine_router_softmax_top_amd import binding as B
+    from combine_router_softmax_top_amd import workloads as W
+    from combine_router_softmax_top_amd.layer import MoELayer
+    cfg5 = W.CONFIGS["dsv3_dual_microbatch"]
+    layer5 = MoELayer(cfg5, {"x": W.make_tokens(cfg5, seed=0)}, share_weights=layer)
+    r = dbo_timings(args, layer5, torch)
+    T = cfg5.num_tokens
+    mid = B.dbo_split_point(T)
+    r.update({"workload": cfg5.name, "tokens": T, "microbatches": [mid, T - mid],
+              "tokens_per_s_two_streams": T / (r["split_two_streams_ms"] * 1e-3),
+              "tokens_per_s_unsplit": T / (r["unsplit_ms"] * 1e-3)})
+    del layer5
+    torch.cuda.empty_cache()
+    return r
+
+
+def bench_dbo(args, cfg, layer, torch) -> dict:
+    """The --dbo line: moe_forward_dbo vs moe_forward on the chosen workload."""
+    from combine_router_softmax_top_amd import binding as B
+    r = dbo_timings(args, layer, torch)
     T = cfg.num_tokens
     return {"metric": "dual-microbatch layer tokens/s (moe_forward_dbo, two HIP streams)",
-            "value": T / (split * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": split, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+            "value": T / (r["split_two_streams_ms"] * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": r["split_two_streams_ms"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
             "data": "synthetic (seeded)",
             "config": {"workload": cfg.name, "tokens": T, "microbatches": [
-                B.dbo_split_point(T), T - B.dbo_split_point(T)]},
-            "unsplit_ms": unsplit, "split_two_streams_ms": split, "split_one_stream_ms": one_stream,
-            "overlap_gain": unsplit / split - 1.0, "bitwise_equal_to_unsplit": same,
-            "split_graph_replay_ms": graph_ms}
+                B.dbo_split_point(T), T - B.dbo_split_point(T)]}, **r}
+
+
+def achievable_peaks(torch, stream) -> dict:
+    """What plain streaming kernels and register-only MFMA loops reach on this
+    GPU (include/moe_probe.h), next to the nominal peaks the roofline uses."""
+    from combine_router_softmax_top_amd import binding as B
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    sink = torch.empty(8192 * 256, dtype=torch.int32, device="cuda")
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    res = {"how": "1 GiB, 16-byte accesses, the best of 512-8192 workgroups of 256; MFMA "
+                  "loops: 256 workgroups of 8 waves, 8 independent register-only MFMAs per round"}
+    grids = (512, 1024, 2048, 4096, 8192)
+    for key, kind, moved in [("copy", B.PROBE_COPY, 2 * n), ("read", B.PROBE_READ, n),
+                             ("write", B.PROBE_WRITE, n)]:
+        best, best_wg = 0.0, 0
+        for g in grids:
+            t = timed(lambda: B.probe_stream(kind, n, dst=b if kind != B.PROBE_READ else None,
+                                             src=a if kind != B.PROBE_WRITE else None,
+                                             sink=sink if kind == B.PROBE_READ else None,
+                                             workgroups=g, stream=stream))
+            if moved / t / 1e9 > best:
+                best, best_wg = moved / t / 1e9, g
+        res[f"{key}_GB_per_s"] = best  # copy: bytes read + bytes written
+        res[f"{key}_workgroups"] = best_wg
+    del a, b
+    out = torch.empty(256 * 512, dtype=torch.float32, device="cuda")
+    for kind, key, iters in [(B.PROBE_MFMA_BF16, "mfma_bf16_TFLOP_per_s", 4000),
+                             (B.PROBE_MFMA_FP8, "mfma_fp8_TFLOP_per_s", 2000)]:
+        t = timed(lambda: B.probe_mfma(kind, 256, iters, out, stream=stream))
+        res[key] = B.probe_mfma_flops(kind, 256, iters) / t / 1e12
+    res["nominal"] = {"hbm_GB_per_s": HBM_PEAK_GBS, "bf16_TFLOP_per_s": BF16_MFMA_PEAK_TFLOPS,
+                      "fp8_TFLOP_per_s": FP8_MFMA_PEAK_TFLOPS}
+    return res
 
 
 def source_digest() -> str:
@@ -132,35 +209,112 @@ def algorithmic(cfg, n_loc: int, t_touch: int) -> dict:
     return dict(route=route, dispatch=dispatch, combine=combine, gemm_flops=flops)
 
 
-def cpu_baseline(cfg, inp, target_s: float) -> dict:
-    import torch
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def cpu_baseline(cfg, inp, target_s: float) -> dict:
+    """The fp64 oracle's whole-layer forward (oracle.forward) on the first n
+    tokens of the workload with every host thread, n grown to about 60 % of
+    target_s; then the same on fewer tokens with one thread; then the oracle's
+    stages one by one (route, dispatch, expert MLP, combine) on a quarter of
+    the sample with every thread."""
     import oracle
     threads = oracle.num_threads()
-    n = 8
-    while True:
+
+    def sample(n):
         sub = cfg.with_tokens(n)
         sub_inp = dict(inp)
         sub_inp["x"] = inp["x"][:n].contiguous()
-        t0 = time.perf_counter()
-        oracle.forward(sub, sub_inp)
-        dt = time.perf_counter() - t0
-        if dt >= target_s * 0.5 or n >= cfg.num_tokens:
-            break
-        n = min(cfg.num_tokens, max(n * 2, int(n * target_s / max(dt, 1e-3))))
+        return sub, sub_inp
+
+    def grow(budget):
+        n = 8
+        while True:
+            sub, sub_inp = sample(n)
+            t0 = time.perf_counter()
+            oracle.forward(sub, sub_inp)
+            dt = time.perf_counter() - t0
+            if dt >= budget * 0.5 or n >= cfg.num_tokens:
+                return n, dt, sub, sub_inp
+            n = min(cfg.num_tokens, max(n * 2, int(n * budget / max(dt, 1e-3))))
+
+    n, dt, sub, sub_inp = grow(0.6 * target_s)
     reps = 1
-    if dt < target_s * 0.5:
-        # The whole workload is quick: repeat it until the target CPU time.
-        reps = max(2, int(target_s / max(dt, 1e-4)))
+    if dt < target_s * 0.3:
+        # The whole workload is quick: repeat it until about the budget.
+        reps = max(2, int(0.6 * target_s / max(dt, 1e-4)))
         t0 = time.perf_counter()
         for _ in range(reps):
             oracle.forward(sub, sub_inp)
         dt = time.perf_counter() - t0
     what = f"first {n} of the {cfg.num_tokens} tokens" if n < cfg.num_tokens else \
         f"all {n} tokens" + (f", {reps} times" if reps > 1 else "")
-    return {"value": n * reps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{what} of the same workload, whole layer (route, dispatch, expert MLP, "
-                      f"combine) in fp64, {dt:.1f} s"}
+    res = {"value": n * reps / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{what} of the same workload, whole layer (route, dispatch, expert MLP, "
+                     f"combine) in fp64, {dt:.1f} s",
+           "cpu_model": _cpu_model(), "host_cpus": len(os.sched_getaffinity(0))}
+    # one thread, about a fifth of the budget
+    budget1 = 0.2 * target_s
+    n1 = max(1, min(n, int(budget1 * (n * reps / dt) / threads)))
+    sub1, inp1 = sample(n1)
+    oracle.set_threads(1)
+    try:
+        reps1, dt1 = 0, 0.0
+        while dt1 < 0.5 * budget1 or reps1 == 0:
+            t0 = time.perf_counter()
+            oracle.forward(sub1, inp1)
+            dt1 += time.perf_counter() - t0
+            reps1 += 1
+    finally:
+        oracle.set_threads(threads)
+    res["one_thread"] = {"value": n1 * reps1 / dt1, "unit": "tokens/s",
+                         "sample": f"first {n1} tokens, whole layer"
+                                   + (f", {reps1} times" if reps1 > 1 else "") + f", {dt1:.1f} s"}
+    # stages, every thread
+    ns = max(1, n // 4)
+    subs, inps = sample(ns)
+    K, E = cfg.top_k, cfg.num_experts
+    st = {}
+    t0 = time.perf_counter()
+    ids, w, _ = oracle.route(inps["x"], inps["w_router"], inps["bias"], K, cfg.score,
+                             cfg.renormalize)
+    t1 = time.perf_counter()
+    d = oracle.dispatch(ids, E, cfg.expert_begin, cfg.expert_end, x=inps["x"])
+    t2 = time.perf_counter()
+    off = d["offsets"]
+    row_expert = oracle_row_experts(off, cfg.num_local)
+    y = oracle.expert_mlp(d["x_sorted"], row_expert, inps["w_gate"], inps["w_up"], inps["w_down"])
+    ysh = None
+    if cfg.num_shared:
+        import torch
+        ysh = torch.stack([oracle.expert_mlp(inps["x"], torch.full((ns,), s, dtype=torch.int32),
+                                             inps["ws_gate"], inps["ws_up"], inps["ws_down"])
+                           for s in range(cfg.num_shared)])
+    t3 = time.perf_counter()
+    padded = y.new_zeros(ns * K, y.shape[1])
+    padded[:y.shape[0]] = y
+    oracle.combine(padded, d["row_of"], w, ns, K, y_shared=ysh)
+    t4 = time.perf_counter()
+    res["stages_s"] = {"tokens": ns, "route": t1 - t0, "dispatch": t2 - t1,
+                       "expert_mlp": t3 - t2, "combine": t4 - t3}
+    return res
+
+
+def oracle_row_experts(offsets, n_loc: int):
+    """Local expert index of every dispatched row, from the expert offsets."""
+    import torch
+    n = int(offsets[n_loc])
+    re = torch.empty(n, dtype=torch.int32)
+    for j in range(n_loc):
+        re[int(offsets[j]):int(offsets[j + 1])] = j
+    return re
 
 
 def write_traffic_record(d: str, out_path: str = TRAFFIC_FILE) -> dict:
@@ -345,6 +499,14 @@ def main():
         result["dispatch_combine_cold"] = cold_dispatch_combine(layer, stream, torch, alg)
     if not args.no_mxfp8 and not cfg.packed_weights and cfg.dtype == "bf16" and cfg.num_shared == 0 and cfg.hidden % 512 == 0:
         result["mxfp8"] = mxfp8_leg(args, layer, stream, torch, alg, n_loc, t_touch)
+    if not args.no_dbo and cfg.name == "dsv3_prefill_ep" and not cfg.packed_weights:
+        result["dbo"] = dbo_leg(args, layer, torch)
+    if not args.no_probes:
+        peaks = achievable_peaks(torch, stream)
+        peaks["expert_gemm_frac_of_mfma_loop"] = (
+            gemm_tflops / peaks["mfma_bf16_TFLOP_per_s"] if bf16 else None)
+        peaks["dispatch_combine_frac_of_copy"] = gbs(dc_bytes, dc_ms) / peaks["copy_GB_per_s"]
+        result["achievable_peaks"] = peaks
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)

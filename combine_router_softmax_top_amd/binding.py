@@ -23,6 +23,7 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_MX_ROWS, MOE_MX_MFMA = 0, 1
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_WEIGHTS_ROW_MAJOR, MOE_WEIGHTS_PACKED = 0, 1
+MOE_SHARED_FUSED, MOE_SHARED_BESIDE_COMBINE = 0, 1
 MOE_WS_ROUTE, MOE_WS_DISPATCH, MOE_WS_EXPERT_MLP, MOE_WS_FORWARD, MOE_WS_FORWARD_DBO = range(5)
 
 EXPORTED = ["moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_forward",
@@ -32,6 +33,8 @@ EXPORTED = ["moe_route", "moe_dispatch", "moe_expert_mlp", "moe_combine", "moe_f
             "moe_quantize_mxfp8", "moe_expert_mlp_mxfp8", "moe_dispatch_mxfp8", "moe_pack_weights",
             "moe_forward_mxfp8", "moe_graph_capture_forward_mxfp8", "moe_status_string",
             "moe_dispatch_noalloc"]
+# include/moe_probe.h: achievable-peak probes (measurement only)
+PROBE_EXPORTED = ["moe_probe_stream", "moe_probe_mfma", "moe_probe_mfma_flops"]
 
 
 class MoEError(RuntimeError):
@@ -43,7 +46,8 @@ class MoEError(RuntimeError):
 class ConfigStruct(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_tokens", "hidden", "num_experts", "top_k", "intermediate", "expert_begin",
-        "expert_end", "num_shared", "score", "renormalize", "dtype", "weight_layout")]
+        "expert_end", "num_shared", "score", "renormalize", "dtype", "weight_layout",
+        "shared_placement")]
 
 
 class LayerTensorsMxfp8Struct(ctypes.Structure):
@@ -99,6 +103,12 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.argtypes = args
             f.restype = ctypes.c_int
+        L.moe_probe_stream.argtypes = [I32, P, P, SZ, P, I32, P]
+        L.moe_probe_stream.restype = ctypes.c_int
+        L.moe_probe_mfma.argtypes = [I32, I32, I32, P, P]
+        L.moe_probe_mfma.restype = ctypes.c_int
+        L.moe_probe_mfma_flops.argtypes = [I32, I32, I32]
+        L.moe_probe_mfma_flops.restype = ctypes.c_double
         L.moe_workspace_bytes.argtypes = [C, I32]
         L.moe_workspace_bytes.restype = SZ
         L.moe_dbo_split_point.argtypes = [I32]
@@ -121,7 +131,8 @@ def config_struct(cfg: MoEConfig, num_tokens: Optional[int] = None) -> ConfigStr
         cfg.top_k, cfg.intermediate, cfg.expert_begin, cfg.expert_end, cfg.num_shared,
         MOE_SCORE_SIGMOID if cfg.score == "sigmoid" else MOE_SCORE_SOFTMAX,
         int(cfg.renormalize), MOE_BF16 if cfg.dtype == "bf16" else MOE_F32,
-        MOE_WEIGHTS_PACKED if cfg.packed_weights else MOE_WEIGHTS_ROW_MAJOR)
+        MOE_WEIGHTS_PACKED if cfg.packed_weights else MOE_WEIGHTS_ROW_MAJOR,
+        MOE_SHARED_BESIDE_COMBINE if cfg.shared_beside_combine else MOE_SHARED_FUSED)
 
 
 def _cs(cfg) -> ConfigStruct:
@@ -481,3 +492,27 @@ def alloc_workspace(cfg, kind: int, device="cuda") -> Optional[torch.Tensor]:
         raise MoEError("moe_workspace_bytes", MOE_ERR_INVALID_ARGUMENT)
     # torch's caching allocator returns 256-byte (or larger) aligned blocks.
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+# ---- achievable-peak probes (include/moe_probe.h) ------------------------------
+
+PROBE_COPY, PROBE_READ, PROBE_WRITE = 0, 1, 2
+PROBE_MFMA_BF16, PROBE_MFMA_FP8 = 0, 1
+
+
+def probe_stream(kind: int, nbytes: int, dst=None, src=None, sink=None, workgroups: int = 2048,
+                 stream=None):
+    st = lib().moe_probe_stream(int(kind), _p(dst, "dst"), _p(src, "src"), int(nbytes),
+                                _p(sink, "sink", (workgroups * 256,), torch.int32),
+                                int(workgroups), _stream(stream))
+    _check("moe_probe_stream", st)
+
+
+def probe_mfma(kind: int, workgroups: int, iters: int, out, stream=None):
+    st = lib().moe_probe_mfma(int(kind), int(workgroups), int(iters),
+                              _p(out, "out", (workgroups * 512,), torch.float32), _stream(stream))
+    _check("moe_probe_mfma", st)
+
+
+def probe_mfma_flops(kind: int, workgroups: int, iters: int) -> float:
+    return float(lib().moe_probe_mfma_flops(int(kind), int(workgroups), int(iters)))

@@ -83,7 +83,9 @@ __device__ __forceinline__ void gather_batch(const u32x4* __restrict__ base, lon
 // min(K, 8); K <= 16, so at most two batches); the shared-expert rows (at most
 // 4) form one batch of their own.  NT: stream the routed rows (see
 // launch_combine).
-template <typename T, int KB, bool NT>
+// SUMS: no shared rows and no rounding; the fp32 sums go to `out` as floats
+// ([T, d] fp32, N floats per 16-byte input piece).
+template <typename T, int KB, bool NT, bool SUMS = false>
 __global__ __launch_bounds__(256) void combine_kernel(
     const u32x4* __restrict__ y_sorted, const int32_t* __restrict__ row_of,
     const float* __restrict__ weights, const u32x4* __restrict__ y_shared, int num_tokens, int K,
@@ -124,6 +126,16 @@ __global__ __launch_bounds__(256) void combine_kernel(
       gather_batch<T, KB, NT>(y_sorted, row_vecs, v, rows0, w0, dummy, acc);
       if (second) gather_batch<T, KB, NT>(y_sorted, row_vecs, v, rows1, w1, dummy, acc);
     }
+    if (SUMS) {
+      if (v0 + lane < row_vecs) {
+        u32x4* o = out + ((size_t)t * row_vecs + v) * (N / 4);
+#pragma unroll
+        for (int q = 0; q < N / 4; ++q)
+          o[q] = u32x4{__float_as_uint(acc[4 * q]), __float_as_uint(acc[4 * q + 1]),
+                       __float_as_uint(acc[4 * q + 2]), __float_as_uint(acc[4 * q + 3])};
+      }
+      continue;
+    }
     if (n_shared > 0) {
       constexpr int SB = MOE_MAX_SHARED;
       int rows[SB];
@@ -138,6 +150,36 @@ __global__ __launch_bounds__(256) void combine_kernel(
     }
     if (v0 + lane < row_vecs) out[(size_t)t * row_vecs + v] = Vec<T>::store(acc);
   }
+}
+
+// out = round(sums + y_shared[0] + ... ): one thread per 16-byte piece of the
+// output rows; the shared rows are added in ascending s as fmaf(1, y, acc),
+// the very operations of combine_kernel's shared-row batch, so the result is
+// bit for bit the fused combine's.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_finish_kernel(const float* __restrict__ sums,
+                                                             const u32x4* __restrict__ y_shared,
+                                                             int n_shared, long long pieces,
+                                                             long long shared_stride,
+                                                             u32x4* __restrict__ out) {
+  constexpr int N = Vec<T>::N;
+  const long long p = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (p >= pieces) return;
+  float acc[N];
+  const f32x4* sp = reinterpret_cast<const f32x4*>(sums) + p * (N / 4);
+#pragma unroll
+  for (int q = 0; q < N / 4; ++q) {
+    const f32x4 a = sp[q];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[4 * q + i] = a[i];
+  }
+  for (int sh = 0; sh < n_shared; ++sh) {
+    float f[N];
+    Vec<T>::load(y_shared[sh * shared_stride + p], f);
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = fmaf(1.f, f[i], acc[i]);
+  }
+  out[p] = Vec<T>::store(acc);
 }
 
 }  // namespace
@@ -172,6 +214,55 @@ static void launch_t(const moe_config_t& c, const void* y_sorted, const int32_t*
     launch_kb<T, 4>(c, y_sorted, row_of, weights, y_shared, n_sh, row_vecs, out, s);
   else
     launch_kb<T, 8>(c, y_sorted, row_of, weights, y_shared, n_sh, row_vecs, out, s);
+}
+
+template <typename T>
+static hipError_t launch_sums_t(const moe_config_t& c, const void* y_sorted,
+                                const int32_t* row_of, const float* weights, float* sums,
+                                int row_vecs, hipStream_t s) {
+  const int n_loc = c.expert_end - c.expert_begin;
+  const double routed_bytes = (double)c.num_tokens * (c.top_k < n_loc ? c.top_k : n_loc) *
+                              row_vecs * 16.0;
+  const bool nt = routed_bytes > kStreamBytes;
+  void (*kern)(const u32x4*, const int32_t*, const float*, const u32x4*, int, int, int, int,
+               u32x4*);
+  if (c.top_k <= 2)
+    kern = nt ? combine_kernel<T, 2, true, true> : combine_kernel<T, 2, false, true>;
+  else if (c.top_k <= 4)
+    kern = nt ? combine_kernel<T, 4, true, true> : combine_kernel<T, 4, false, true>;
+  else
+    kern = nt ? combine_kernel<T, 8, true, true> : combine_kernel<T, 8, false, true>;
+  hipLaunchKernelGGL(kern, dim3(ceil_div(c.num_tokens, 4)), dim3(256), 0, s,
+                     static_cast<const u32x4*>(y_sorted), row_of, weights, nullptr, c.num_tokens,
+                     c.top_k, 0, row_vecs, reinterpret_cast<u32x4*>(sums));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_sums(const moe_config_t& c, const void* y_sorted, const int32_t* row_of,
+                               const float* weights, float* sums, hipStream_t s) {
+  const int elem = c.dtype == MOE_BF16 ? 2 : 4;
+  const int row_vecs = c.hidden * elem / 16;
+  if (c.dtype == MOE_BF16)
+    return launch_sums_t<uint16_t>(c, y_sorted, row_of, weights, sums, row_vecs, s);
+  return launch_sums_t<float>(c, y_sorted, row_of, weights, sums, row_vecs, s);
+}
+
+hipError_t launch_combine_finish(const moe_config_t& c, const float* sums, const void* y_shared,
+                                 void* out, hipStream_t s) {
+  const int elem = c.dtype == MOE_BF16 ? 2 : 4;
+  const long long row_vecs = (long long)c.hidden * elem / 16;
+  const long long pieces = (long long)c.num_tokens * row_vecs;
+  const dim3 grid((unsigned)((pieces + 255) / 256));
+  const int n_sh = y_shared ? c.num_shared : 0;
+  if (c.dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_finish_kernel<uint16_t>, grid, dim3(256), 0, s, sums,
+                       static_cast<const u32x4*>(y_shared), n_sh, pieces, pieces,
+                       static_cast<u32x4*>(out));
+  else
+    hipLaunchKernelGGL(combine_finish_kernel<float>, grid, dim3(256), 0, s, sums,
+                       static_cast<const u32x4*>(y_shared), n_sh, pieces, pieces,
+                       static_cast<u32x4*>(out));
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const moe_config_t& c, const void* y_sorted, const int32_t* row_of,

@@ -552,18 +552,21 @@ hipError_t launch_expert_mlp(const moe_config_t& c, const void* x_sorted, const 
                              const void* w_gate, const void* w_up, const void* w_down,
                              void* y_sorted, const void* x, const void* ws_gate,
                              const void* ws_up, const void* ws_down, void* y_shared,
-                             void* workspace, hipStream_t s) {
+                             void* workspace, hipStream_t s, int parts) {
   const int T = c.num_tokens, K = c.top_k, d = c.hidden, I = c.intermediate;
-  const int n_loc = c.expert_end - c.expert_begin;
   const size_t elem = c.dtype == MOE_BF16 ? 2 : 4;
   char* ws = static_cast<char*>(workspace);
   void* h = ws;
   void* h_sh = ws + align_up((size_t)T * K * I * elem, 256);
   const int bm = c.dtype == MOE_BF16 ? kBM : kFM;
-  const int S = c.num_shared;
+  // Routed groups (the local experts, rows from the offsets) unless only the
+  // shared experts are asked for; shared experts unless only the routed ones.
+  const int n_loc = (parts & kMlpRouted) ? c.expert_end - c.expert_begin : 0;
+  const int S = (parts & kMlpShared) ? c.num_shared : 0;
   // The shared experts run in the same launches as the routed ones, as extra
   // groups of T rows, so their tiles fill the routed launches' last rounds.
-  const int row_bound = ceil_div(T * K, bm) + n_loc + S * ceil_div(T, bm);
+  const int row_bound = (n_loc > 0 ? ceil_div(T * K, bm) + n_loc : 0) + S * ceil_div(T, bm);
+  if (row_bound == 0) return hipSuccess;
 
   GemmArgs up{x_sorted, d, 0, w_gate, w_up, (long long)I * d, 0, h, I, 0,
               offsets, n_loc, 0, row_bound, I, d, 1,

@@ -33,6 +33,8 @@ moe_status_t check_config(const moe_config_t* c) {
   if (c->dtype != MOE_F32 && c->dtype != MOE_BF16) return MOE_ERR_INVALID_ARGUMENT;
   if (c->weight_layout != MOE_WEIGHTS_ROW_MAJOR && c->weight_layout != MOE_WEIGHTS_PACKED)
     return MOE_ERR_INVALID_ARGUMENT;
+  if (c->shared_placement != MOE_SHARED_FUSED && c->shared_placement != MOE_SHARED_BESIDE_COMBINE)
+    return MOE_ERR_INVALID_ARGUMENT;
   if ((int64_t)c->num_tokens * c->top_k >= (int64_t(1) << 31)) return MOE_ERR_INVALID_ARGUMENT;
   const int q = c->dtype == MOE_BF16 ? 64 : 16;
   if (c->hidden % q != 0 || c->intermediate % q != 0) return MOE_ERR_UNSUPPORTED;
@@ -60,13 +62,18 @@ struct LayerScratch {
   void* y_shared;
   void* dispatch_ws;
   void* mlp_ws;
+  float* sums;  // [T, d] fp32: the routed combine's sums (shared experts beside the combine)
 };
+
+bool shared_beside_combine(const moe_config_t& c) {
+  return c.num_shared > 0 && c.shared_placement == MOE_SHARED_BESIDE_COMBINE;
+}
 
 size_t layer_scratch(const moe_config_t& c, void* base, LayerScratch* out) {
   const size_t T = c.num_tokens, K = c.top_k, d = c.hidden;
   const size_t elem = c.dtype == MOE_BF16 ? 2 : 4;
   const size_t n_loc = c.expert_end - c.expert_begin;
-  const size_t sizes[10] = {
+  const size_t sizes[11] = {
       align_up(moe::route_workspace_bytes(c), 256),
       align_up(c.num_experts * 4, 256),
       align_up((n_loc + 1) * 4, 256),
@@ -76,10 +83,11 @@ size_t layer_scratch(const moe_config_t& c, void* base, LayerScratch* out) {
       align_up(T * K * d * elem, 256),
       align_up((size_t)c.num_shared * T * d * elem, 256),
       align_up(moe::dispatch_workspace_bytes(c), 256),
-      align_up(moe::mlp_workspace_bytes(c), 256)};
-  size_t off[10];
+      align_up(moe::mlp_workspace_bytes(c), 256),
+      shared_beside_combine(c) ? align_up(T * d * 4, 256) : 0};
+  size_t off[11];
   size_t total = 0;
-  for (int i = 0; i < 10; ++i) {
+  for (int i = 0; i < 11; ++i) {
     off[i] = total;
     total += sizes[i];
   }
@@ -95,6 +103,7 @@ size_t layer_scratch(const moe_config_t& c, void* base, LayerScratch* out) {
     out->y_shared = c.num_shared > 0 ? b + off[7] : nullptr;
     out->dispatch_ws = b + off[8];
     out->mlp_ws = b + off[9];
+    out->sums = shared_beside_combine(c) ? reinterpret_cast<float*>(b + off[10]) : nullptr;
   }
   return total;
 }
@@ -132,6 +141,20 @@ moe_status_t enqueue_layer(const moe_config_t& c, const moe_layer_tensors_t& t, 
   e = moe::launch_dispatch(c, t.x, t.topk_ids, sc.counts, sc.offsets, sc.x_sorted, sc.src_index,
                            sc.row_of, sc.dispatch_ws, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
+  if (shared_beside_combine(c)) {
+    // routed MLP, shared MLP, routed combine (its fp32 sums), shared rows added
+    e = moe::launch_expert_mlp(c, sc.x_sorted, sc.offsets, t.w_gate, t.w_up, t.w_down,
+                               sc.y_sorted, t.x, t.ws_gate, t.ws_up, t.ws_down, sc.y_shared,
+                               sc.mlp_ws, s, moe::kMlpRouted);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = moe::launch_expert_mlp(c, sc.x_sorted, sc.offsets, t.w_gate, t.w_up, t.w_down,
+                               sc.y_sorted, t.x, t.ws_gate, t.ws_up, t.ws_down, sc.y_shared,
+                               sc.mlp_ws, s, moe::kMlpShared);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = moe::launch_combine_sums(c, sc.y_sorted, sc.row_of, t.topk_weights, sc.sums, s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(moe::launch_combine_finish(c, sc.sums, sc.y_shared, t.out, s));
+  }
   e = moe::launch_expert_mlp(c, sc.x_sorted, sc.offsets, t.w_gate, t.w_up, t.w_down, sc.y_sorted,
                              t.x, t.ws_gate, t.ws_up, t.ws_down, sc.y_shared, sc.mlp_ws, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
@@ -151,12 +174,12 @@ size_t dbo_workspace(const moe_config_t& c, int32_t split) {
 // parts of the two scratches add up to those of the whole call, the parts
 // that do not depend on the token count (expert counts, offsets, histogram
 // columns) appear twice -- once more than in a one-token call covers -- the
-// chunk counts round up at most once more, and each of the ten 256-byte
+// chunk counts round up at most once more, and each of the eleven 256-byte
 // alignments may add up to 255 bytes per scratch.
 size_t dbo_workspace_bound(const moe_config_t& c) {
   const size_t whole = layer_scratch(c, nullptr, nullptr);
   const size_t one = layer_scratch(with_tokens(c, 1), nullptr, nullptr);
-  return std::max(whole, dbo_workspace(c, moe_dbo_split_point(c.num_tokens))) + one + 20 * 256;
+  return std::max(whole, dbo_workspace(c, moe_dbo_split_point(c.num_tokens))) + one + 22 * 256;
 }
 
 // The tensors of microbatch [t0, t0 + n) of a layer call.
@@ -170,10 +193,46 @@ moe_layer_tensors_t slice(const moe_config_t& c, const moe_layer_tensors_t& t, i
   return r;
 }
 
+// Events of the dual-microbatch schedule.  An eager call takes them from a
+// pool made once per host thread and device (a thread enqueues each call's
+// records and waits in order, and a wait sees the latest record, so reusing
+// them is safe and creates no runtime objects per call); they last until the
+// process ends.  Under stream capture a call makes its own and destroys them
+// once enqueued, as the captured graph keeps the dependencies.
+enum { EV_START, EV_R0, EV_R1, EV_D0, EV_D1, EV_M0, EV_M1, EV_S0, EV_S1, EV_DONE, EV_N };
+constexpr int kMaxEventDevices = 64;
+
+hipError_t pooled_events(hipEvent_t** out) {
+  struct Pool {
+    hipEvent_t ev[EV_N];
+    bool made;
+  };
+  thread_local Pool pools[kMaxEventDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxEventDevices) return hipErrorInvalidDevice;
+  Pool& p = pools[dev];
+  if (!p.made) {
+    for (int i = 0; i < EV_N; ++i) {
+      e = hipEventCreateWithFlags(&p.ev[i], hipEventDisableTiming);
+      if (e != hipSuccess) {
+        for (int j = 0; j < i; ++j) hipEventDestroy(p.ev[j]);
+        return e;
+      }
+    }
+    p.made = true;
+  }
+  *out = p.ev;
+  return hipSuccess;
+}
+
 // The dual-microbatch schedule for a cut at `split` (0: the unsplit layer on
 // `cs`): route on the compute stream, dispatch on the comm stream, the expert
 // MLPs on compute, the combines on comm, with events between; `cs` then waits
-// for both microbatches.
+// for both microbatches.  With the shared experts beside the combine, each
+// microbatch's shared-expert MLP follows its routed MLP on compute, while its
+// combine runs on comm; the shared rows are added on comm once both are done.
 moe_status_t enqueue_dbo(const moe_config_t& cfg, const moe_layer_tensors_t& tensors,
                          void* workspace, int32_t split, hipStream_t cs, hipStream_t ms) {
   const int32_t T = cfg.num_tokens;
@@ -181,28 +240,52 @@ moe_status_t enqueue_dbo(const moe_config_t& cfg, const moe_layer_tensors_t& ten
 
   const moe_config_t c0 = with_tokens(cfg, split), c1 = with_tokens(cfg, T - split);
   const moe_layer_tensors_t t0 = slice(cfg, tensors, 0), t1 = slice(cfg, tensors, split);
-  LayerScratch s0, s1;
   const size_t first = layer_scratch(c0, nullptr, nullptr);
-  layer_scratch(c0, workspace, &s0);
-  layer_scratch(c1, static_cast<char*>(workspace) + first, &s1);
 
   if (cs == ms) {
     const moe_status_t st = enqueue_layer(c0, t0, workspace, cs);
     if (st != MOE_OK) return st;
     return enqueue_layer(c1, t1, static_cast<char*>(workspace) + first, cs);
   }
+  LayerScratch s0, s1;
+  layer_scratch(c0, workspace, &s0);
+  layer_scratch(c1, static_cast<char*>(workspace) + first, &s1);
 
-  enum { EV_START, EV_R0, EV_R1, EV_D0, EV_D1, EV_M0, EV_M1, EV_DONE, EV_N };
-  hipEvent_t ev[EV_N] = {};
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(cs, &cap) != hipSuccess) return MOE_ERR_HIP;
+  const bool own = cap != hipStreamCaptureStatusNone;
+  hipEvent_t made[EV_N] = {};
+  hipEvent_t* ev = made;
+  if (own) {
+    for (int i = 0; i < EV_N; ++i)
+      if (hipEventCreateWithFlags(&made[i], hipEventDisableTiming) != hipSuccess) {
+        for (int j = 0; j < i; ++j) hipEventDestroy(made[j]);
+        return MOE_ERR_HIP;
+      }
+  } else if (pooled_events(&ev) != hipSuccess) {
+    return MOE_ERR_HIP;
+  }
   moe_status_t result = MOE_OK;
-  for (int i = 0; i < EV_N; ++i)
-    if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) {
-      for (int j = 0; j < i; ++j) hipEventDestroy(ev[j]);
-      return MOE_ERR_HIP;
-    }
   auto ok = [&](hipError_t e) {
     if (e != hipSuccess) result = MOE_ERR_HIP;
     return e == hipSuccess;
+  };
+  const bool beside = shared_beside_combine(cfg);
+  const int parts = beside ? moe::kMlpRouted : moe::kMlpBoth;
+  auto mlp = [&](const moe_config_t& c, const moe_layer_tensors_t& t, const LayerScratch& sc,
+                 int which) {
+    return moe::launch_expert_mlp(c, sc.x_sorted, sc.offsets, t.w_gate, t.w_up, t.w_down,
+                                  sc.y_sorted, t.x, t.ws_gate, t.ws_up, t.ws_down, sc.y_shared,
+                                  sc.mlp_ws, cs, which);
+  };
+  auto combine = [&](const moe_config_t& c, const moe_layer_tensors_t& t, const LayerScratch& sc,
+                     int ev_shared) {
+    if (!beside)
+      return ok(moe::launch_combine(c, sc.y_sorted, sc.row_of, t.topk_weights, sc.y_shared,
+                                    t.out, ms));
+    return ok(moe::launch_combine_sums(c, sc.y_sorted, sc.row_of, t.topk_weights, sc.sums, ms)) &&
+           ok(hipStreamWaitEvent(ms, ev[ev_shared], 0)) &&
+           ok(moe::launch_combine_finish(c, sc.sums, sc.y_shared, t.out, ms));
   };
   // The comm stream must see the caller's earlier work on the compute stream.
   bool good = ok(hipEventRecord(ev[EV_START], cs)) && ok(hipStreamWaitEvent(ms, ev[EV_START], 0));
@@ -221,26 +304,22 @@ moe_status_t enqueue_dbo(const moe_config_t& cfg, const moe_layer_tensors_t& ten
          ok(moe::launch_dispatch(c1, t1.x, t1.topk_ids, s1.counts, s1.offsets, s1.x_sorted,
                                  s1.src_index, s1.row_of, s1.dispatch_ws, ms)) &&
          ok(hipEventRecord(ev[EV_D1], ms));
-  // compute: experts of microbatch 0 (overlapping dispatch 1), then of microbatch 1.
-  good = good && ok(hipStreamWaitEvent(cs, ev[EV_D0], 0)) &&
-         ok(moe::launch_expert_mlp(c0, s0.x_sorted, s0.offsets, t0.w_gate, t0.w_up, t0.w_down,
-                                   s0.y_sorted, t0.x, t0.ws_gate, t0.ws_up, t0.ws_down,
-                                   s0.y_shared, s0.mlp_ws, cs)) &&
-         ok(hipEventRecord(ev[EV_M0], cs)) && ok(hipStreamWaitEvent(cs, ev[EV_D1], 0)) &&
-         ok(moe::launch_expert_mlp(c1, s1.x_sorted, s1.offsets, t1.w_gate, t1.w_up, t1.w_down,
-                                   s1.y_sorted, t1.x, t1.ws_gate, t1.ws_up, t1.ws_down,
-                                   s1.y_shared, s1.mlp_ws, cs)) &&
-         ok(hipEventRecord(ev[EV_M1], cs));
-  // comm: combine 0 (overlapping experts of microbatch 1), then combine 1.
-  good = good && ok(hipStreamWaitEvent(ms, ev[EV_M0], 0)) &&
-         ok(moe::launch_combine(c0, s0.y_sorted, s0.row_of, t0.topk_weights, s0.y_shared, t0.out,
-                                ms)) &&
-         ok(hipStreamWaitEvent(ms, ev[EV_M1], 0)) &&
-         ok(moe::launch_combine(c1, s1.y_sorted, s1.row_of, t1.topk_weights, s1.y_shared, t1.out,
-                                ms)) &&
+  // compute: experts of microbatch 0 (overlapping dispatch 1), then of
+  // microbatch 1; each microbatch's shared experts right after its routed
+  // ones when they sit beside the combine.
+  good = good && ok(hipStreamWaitEvent(cs, ev[EV_D0], 0)) && ok(mlp(c0, t0, s0, parts)) &&
+         ok(hipEventRecord(ev[EV_M0], cs)) &&
+         (!beside || (ok(mlp(c0, t0, s0, moe::kMlpShared)) && ok(hipEventRecord(ev[EV_S0], cs)))) &&
+         ok(hipStreamWaitEvent(cs, ev[EV_D1], 0)) && ok(mlp(c1, t1, s1, parts)) &&
+         ok(hipEventRecord(ev[EV_M1], cs)) &&
+         (!beside || (ok(mlp(c1, t1, s1, moe::kMlpShared)) && ok(hipEventRecord(ev[EV_S1], cs))));
+  // comm: combine 0 (overlapping the experts of microbatch 1), then combine 1.
+  good = good && ok(hipStreamWaitEvent(ms, ev[EV_M0], 0)) && combine(c0, t0, s0, EV_S0) &&
+         ok(hipStreamWaitEvent(ms, ev[EV_M1], 0)) && combine(c1, t1, s1, EV_S1) &&
          ok(hipEventRecord(ev[EV_DONE], ms)) && ok(hipStreamWaitEvent(cs, ev[EV_DONE], 0));
   (void)good;
-  for (int i = 0; i < EV_N; ++i) hipEventDestroy(ev[i]);
+  if (own)
+    for (int i = 0; i < EV_N; ++i) hipEventDestroy(made[i]);
   return result;
 }
 

@@ -65,11 +65,14 @@ size_t mlp_workspace_bytes(const moe_config_t& c);
 // (bf16 or fp32; the block-scaled launches use the same tile grids with fewer
 // threads per workgroup).
 long long expert_mlp_max_workitems(const moe_config_t& c);
+// parts: which groups the two launches hold -- the routed experts (rows from
+// the offsets), the shared experts (T rows each), or both (the default).
+enum { kMlpRouted = 1, kMlpShared = 2, kMlpBoth = 3 };
 hipError_t launch_expert_mlp(const moe_config_t& c, const void* x_sorted, const int32_t* offsets,
                              const void* w_gate, const void* w_up, const void* w_down,
                              void* y_sorted, const void* x, const void* ws_gate,
                              const void* ws_up, const void* ws_down, void* y_shared,
-                             void* workspace, hipStream_t s);
+                             void* workspace, hipStream_t s, int parts = kMlpBoth);
 
 // moe_pack_weights: [n, rows, cols] bf16 -> [n, rows/128, cols/64, 128, 64].
 hipError_t launch_pack_weights(int n, int rows, int cols, const void* in, void* out,
@@ -108,5 +111,13 @@ hipError_t launch_expert_mlp_mxfp8(const moe_config_t& c, const uint8_t* xq,
 
 hipError_t launch_combine(const moe_config_t& c, const void* y_sorted, const int32_t* row_of,
                           const float* weights, const void* y_shared, void* out, hipStream_t s);
+// The routed part of the combine, its fp32 sums (before any shared row and
+// before the rounding) written to sums [T, d] fp32.
+hipError_t launch_combine_sums(const moe_config_t& c, const void* y_sorted, const int32_t* row_of,
+                               const float* weights, float* sums, hipStream_t s);
+// out = round(sums + y_shared[0] + ... + y_shared[S-1]), added in that order
+// exactly as launch_combine adds them.
+hipError_t launch_combine_finish(const moe_config_t& c, const float* sums, const void* y_shared,
+                                 void* out, hipStream_t s);
 
 }  // namespace moe

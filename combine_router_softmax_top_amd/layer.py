@@ -14,7 +14,12 @@ from .workloads import MoEConfig
 
 
 class MoELayer:
-    def __init__(self, cfg: MoEConfig, host_inputs: dict, device: str = "cuda"):
+    WEIGHTS = ("w_router", "bias", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")
+
+    def __init__(self, cfg: MoEConfig, host_inputs: dict, device: str = "cuda",
+                 share_weights: Optional["MoELayer"] = None):
+        """share_weights: another layer of the same shape except the token
+        count, whose device weights this one uses instead of copies."""
         self.cfg = cfg
         self.cs = B.config_struct(cfg)
         dev = torch.device(device)
@@ -26,15 +31,19 @@ class MoELayer:
             return None if t is None else t.to(dev, non_blocking=False).contiguous()
 
         self.x = to_dev(host_inputs["x"])
-        self.w_router = to_dev(host_inputs["w_router"])
-        self.bias = to_dev(host_inputs.get("bias"))
-        self.w_gate = to_dev(host_inputs.get("w_gate"))
-        self.w_up = to_dev(host_inputs.get("w_up"))
-        self.w_down = to_dev(host_inputs.get("w_down"))
-        self.ws_gate = to_dev(host_inputs.get("ws_gate"))
-        self.ws_up = to_dev(host_inputs.get("ws_up"))
-        self.ws_down = to_dev(host_inputs.get("ws_down"))
-        if cfg.packed_weights:  # the bf16 stacks rearranged once, like an offline conversion
+        if share_weights is not None:
+            o = share_weights.cfg
+            keys = ("hidden", "num_experts", "intermediate", "expert_begin", "expert_end",
+                    "num_shared", "dtype", "router_init", "zipf_s", "packed_weights")
+            if any(getattr(o, k) != getattr(cfg, k) for k in keys):
+                raise ValueError("share_weights: the layers' weights differ")
+            for name in self.WEIGHTS:
+                setattr(self, name, getattr(share_weights, name))
+        else:
+            for name in self.WEIGHTS:
+                setattr(self, name, to_dev(host_inputs.get(name)))
+        if cfg.packed_weights and share_weights is None:
+            # the bf16 stacks rearranged once, like an offline conversion
             for name in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"):
                 w = getattr(self, name)
                 if w is not None:

@@ -56,6 +56,7 @@ class MoEConfig:
     dual_microbatch: bool = False
     description: str = ""
     packed_weights: bool = False     # bf16 weight stacks in the MOE_WEIGHTS_PACKED layout
+    shared_beside_combine: bool = False  # MOE_SHARED_BESIDE_COMBINE placement of shared experts
 
     @property
     def num_local(self) -> int:

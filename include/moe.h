@@ -58,6 +58,8 @@ enum { MOE_F32 = 0, MOE_BF16 = 1 };
 enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
 /* Layouts of the bf16 expert weight stacks (moe_config_t.weight_layout). */
 enum { MOE_WEIGHTS_ROW_MAJOR = 0, MOE_WEIGHTS_PACKED = 1 };
+/* Where a whole-layer call runs the shared experts (moe_config_t.shared_placement). */
+enum { MOE_SHARED_FUSED = 0, MOE_SHARED_BESIDE_COMBINE = 1 };
 /* Workspace kinds for moe_workspace_bytes. */
 enum { MOE_WS_ROUTE = 0, MOE_WS_DISPATCH = 1, MOE_WS_EXPERT_MLP = 2, MOE_WS_FORWARD = 3,
        MOE_WS_FORWARD_DBO = 4 };
@@ -95,6 +97,20 @@ typedef struct moe_config {
   int32_t weight_layout; /* MOE_WEIGHTS_ROW_MAJOR, or MOE_WEIGHTS_PACKED: every bf16
                             expert weight stack (w_gate, w_up, w_down, ws_*) passed in
                             the layout moe_pack_weights writes                        */
+  int32_t shared_placement; /* whole-layer calls with shared experts (moe_forward,
+                            moe_forward_dbo, their graph captures):
+                            MOE_SHARED_FUSED: the shared experts are extra groups of
+                              the routed expert-MLP launches and the combine adds
+                              their rows;
+                            MOE_SHARED_BESIDE_COMBINE: [DBO] Introduction's
+                              schedule -- each microbatch's shared-expert MLP is a
+                              launch of its own on the compute stream, beside that
+                              microbatch's routed combine on the communication
+                              stream (which keeps its fp32 sums in the workspace);
+                              a last pass adds the shared rows to those sums in the
+                              same order and rounds once.
+                            Both give the same bits.  The per-stage calls
+                            (moe_expert_mlp, moe_combine) do not read it.           */
 } moe_config_t;
 
 /* A hipStream_t handle; NULL means the default (null) stream. */
@@ -445,8 +461,14 @@ moe_status_t moe_forward_mxfp8(const moe_config_t* cfg,
  *     compute: route0, route1, mlp0, mlp1
  *     comm:    dispatch0, dispatch1, combine0, combine1
  * with events ordering each microbatch's steps, so dispatch1 overlaps mlp0
- * and combine0 overlaps mlp1.  Every output row depends only on its own
- * token, so the result is bitwise equal to moe_forward's.
+ * and combine0 overlaps mlp1.  With shared experts and cfg->shared_placement
+ * = MOE_SHARED_BESIDE_COMBINE the compute stream runs each microbatch's
+ * shared-expert MLP right after its routed MLP, beside its combine:
+ *     compute: route0, route1, mlp0, shared0, mlp1, shared1
+ *     comm:    dispatch0, dispatch1, combine0, finish0, combine1, finish1
+ * (finish = the shared rows added to the combine's sums).  Every output row
+ * depends only on its own token, so the result is bitwise equal to
+ * moe_forward's.
  * If T < min_tokens_to_split (or microbatch 1 is empty) the unsplit forward
  * runs on `compute`.  On return, work enqueued later on `compute` waits for
  * both microbatches; `comm` may be the same stream as `compute`.

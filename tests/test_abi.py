@@ -131,9 +131,12 @@ def test_dbo_plan_split_matches_the_oracle_rule(lib):
                     assert got == oracle.dbo_split(T, prefill, thr, thr + 7, q), (T, prefill, q, thr)
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "dsv2lite_decode", "dsv3_prefill_ep"])
+@pytest.mark.parametrize("name", ["tiny_f32", "dsv2lite_decode", "dsv3_prefill_ep",
+                                  "dsv2lite_decode+beside"])
 def test_dbo_workspace_covers_every_cut(lib, name):
-    cfg = W.CONFIGS[name]
+    cfg = W.CONFIGS[name.split("+")[0]]
+    if name.endswith("+beside"):
+        cfg = cfg.replace(shared_beside_combine=True)
     for T in (2, 3, 97, 256, 700):
         c = cfg.with_tokens(T)
         bound = B.workspace_bytes(c, B.MOE_WS_FORWARD_DBO)
@@ -373,3 +376,39 @@ def test_pack_and_quantize_launch_limits(lib):
                                   P(256), None) == B.MOE_ERR_INVALID_ARGUMENT
     assert lib.moe_quantize_mxfp8(rows_ok + 1, 32, B.MOE_BF16, P(256), 32, B.MOE_MX_ROWS,
                                   P(256), P(256), None) == B.MOE_ERR_UNSUPPORTED
+
+
+def test_probe_header_declares_the_exported_probes(lib):
+    src = open(os.path.join(ROOT, "include", "moe_probe.h")).read()
+    names = sorted(set(re.findall(r"^\S.*?\b(moe_[a-z0-9_]+)\s*\(", src, flags=re.M)))
+    assert names == sorted(B.PROBE_EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    P = ctypes.c_void_p
+    # host checks, nothing launched: bad kind, unaligned size, missing pointers
+    assert lib.moe_probe_stream(3, P(256), P(256), 1024, None, 8, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_probe_stream(0, P(256), P(256), 1000, None, 8, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_probe_stream(1, None, P(256), 1024, None, 8, None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_probe_mfma(2, 1, 1, P(256), None) == B.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_probe_mfma(0, 1, 1, None, None) == B.MOE_ERR_INVALID_ARGUMENT
+    # 8 chains x 8 waves x 32x32x16 MFMAs of 32768 flop each
+    assert lib.moe_probe_mfma_flops(0, 2, 3) == 2 * 3 * 8 * 8 * 32768
+    assert lib.moe_probe_mfma_flops(1, 1, 1) == 8 * 8 * 131072
+
+
+def test_shared_placement_is_validated_on_host(lib):
+    cfg = W.CONFIGS["dsv2lite_decode"]
+    cs = B.config_struct(cfg)
+    fused = lib.moe_workspace_bytes(ctypes.byref(cs), B.MOE_WS_FORWARD)
+    cs.shared_placement = B.MOE_SHARED_BESIDE_COMBINE
+    beside = lib.moe_workspace_bytes(ctypes.byref(cs), B.MOE_WS_FORWARD)
+    # the combine's fp32 sums [T, d] are kept for the shared rows
+    assert beside == fused + cfg.num_tokens * cfg.hidden * 4
+    cs.shared_placement = 2
+    assert lib.moe_workspace_bytes(ctypes.byref(cs), B.MOE_WS_FORWARD) == 0
+    assert _route_status(lib, cs) == B.MOE_ERR_INVALID_ARGUMENT
+    # without shared experts the placement changes nothing
+    c4 = B.config_struct(W.CONFIGS["dsv3_prefill_ep"])
+    a = lib.moe_workspace_bytes(ctypes.byref(c4), B.MOE_WS_FORWARD)
+    c4.shared_placement = B.MOE_SHARED_BESIDE_COMBINE
+    assert lib.moe_workspace_bytes(ctypes.byref(c4), B.MOE_WS_FORWARD) == a

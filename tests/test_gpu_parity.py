@@ -242,6 +242,49 @@ def test_dual_microbatch_at_planned_and_lopsided_cuts():
     assert_close(cfg, got.cpu(), oracle.forward_split_at(cfg, inp, T - 1), "dbo cut vs oracle")
 
 
+def test_shared_experts_beside_the_combine():
+    # [DBO] Introduction's schedule runs a microbatch's shared expert (S) on the
+    # compute stream beside its combine (C) on the communication stream.  With
+    # MOE_SHARED_BESIDE_COMBINE the shared MLP is a launch of its own and the
+    # combine keeps fp32 sums that a last pass completes with the shared rows:
+    # the same operations in the same order, so every variant below gives the
+    # fused layer's bits, and the oracle's value.
+    base = W.CONFIGS["dsv2lite_decode"].replace(num_tokens=600)
+    inp = W.make_inputs(base, seed=12)
+    F = MoELayer(base, inp)
+    F.forward()
+    torch.cuda.synchronize()
+    ref = F.out.clone()
+    del F
+    cfg = base.replace(shared_beside_combine=True)
+    L = MoELayer(cfg, inp)
+    comm = torch.cuda.Stream()
+    runs = {"forward": lambda o: L.forward(out=o),
+            "dbo": lambda o: L.forward_dbo(comm=comm, out=o),
+            "dbo_cut_37": lambda o: L.forward_dbo(comm=comm, out=o, split=37),
+            "dbo_one_stream": lambda o: L.forward_dbo(out=o)}
+    for name, run in runs.items():
+        o = torch.full_like(L.out, float("nan"))
+        run(o)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(o), bits(ref)), name
+    g = L.capture_forward(dbo=True)
+    for rep in range(2):
+        L.out.zero_()
+        torch.cuda.synchronize()
+        g.launch()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(L.out), bits(ref)), f"graph replay {rep}"
+        L.forward(out=torch.empty_like(ref))
+        torch.cuda.synchronize()
+    g.destroy()
+    out_o, ids_o, _, _ = oracle.forward(cfg, inp)
+    same = (L.topk_ids.cpu() == ids_o).all(1)
+    assert int(same.sum()) >= cfg.num_tokens - 1
+    assert_close(cfg, ref.cpu()[same], out_o[same], "out (shared beside combine)")
+    assert_close(cfg, ref.cpu(), oracle.forward_split(cfg, inp), "out vs the oracle's split")
+
+
 def _random_layer(seed: int):
     """A small seeded random layer: every routing option and ragged sizes."""
     g = torch.Generator().manual_seed(10_000 + seed)
@@ -346,6 +389,12 @@ EDGE = [
     # the most shared experts a layer may have, on a ragged token count
     ("max_shared", W.CONFIGS["dsv2lite_decode"].replace(num_tokens=77, hidden=256,
                                                         intermediate=192, num_shared=4)),
+    # router tiles whose k-slice has an odd number of 64-deep chunks (3), and a
+    # single chunk (the second half of the waves has nothing to add)
+    ("router_odd_chunks", W.CONFIGS["dsv2lite_decode"].replace(num_tokens=200, hidden=192,
+                                                               intermediate=128, num_shared=0)),
+    ("router_one_chunk", W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=130, hidden=64,
+                                                              intermediate=64)),
     # the Zipf bias keeps every token off the least popular experts: no local
     # rows at all, so the expert MLP has nothing to do and the output is zero
     ("no_local_rows", W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=64, hidden=256,
