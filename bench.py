@@ -65,6 +65,10 @@ def parse():
                    help="skip the dual-microbatch leg of the default line")
     p.add_argument("--no-probes", action="store_true",
                    help="skip the achievable-peak probes (streaming copy, MFMA loops)")
+    p.add_argument("--tokens", type=int, default=0,
+                   help="override the workload's token count (ad-hoc measurements)")
+    p.add_argument("--shared-beside-combine", action="store_true",
+                   help="run the shared experts beside the combine (MOE_SHARED_BESIDE_COMBINE)")
     return p.parse_args()
 
 
@@ -391,6 +395,10 @@ def main():
     cfg = W.CONFIGS[args.workload]
     if args.packed_weights:
         cfg = cfg.replace(packed_weights=True)
+    if args.tokens:
+        cfg = cfg.with_tokens(args.tokens)
+    if args.shared_beside_combine:
+        cfg = cfg.replace(shared_beside_combine=True)
     t_gen = time.perf_counter()
     inp = W.make_inputs(cfg, seed=0)
     t_gen = time.perf_counter() - t_gen
