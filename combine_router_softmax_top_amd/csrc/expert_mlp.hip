@@ -251,44 +251,63 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& ta, uint8_t* lds) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // Epilogue.  Element r of lane l in a (transposed) 32x32 block is output
-  // row l%32, column (r/4)*8 + (l/32)*4 + r%4: four adjacent bf16 per
-  // (lane, r/4), stored as one 8-byte write.  N is a multiple of 64, so a
-  // group of four columns is either wholly inside or wholly past N.
-  const int row_l = lane & 31;
-  const int col_l = (lane >> 5) * 4;
+  // Epilogue, through LDS.  Element r of lane l in a (transposed) 32x32 block
+  // is output row l%32, column (r/4)*8 + (l/32)*4 + r%4: four adjacent bf16
+  // per (lane, r/4), one 8-byte LDS write, into a row-major copy of the output
+  // tile (row pitch padded by 16 bytes, so the 32 rows of one write share a
+  // bank two rows at most).  Then each lane moves 16 bytes of a row to
+  // memory, the lanes of a wave covering whole rows: a store instruction
+  // writes 2 (or 4) full 512 (256)-byte row segments instead of 16-byte
+  // pieces of 32 rows.  The barrier first waits for every wave's loads and
+  // fragment reads, so the rings are free.
+  constexpr int kOutBytes = kNOut * 2;
+  constexpr int kPitch = kOutBytes + 16;
+  static_assert(kBM * kPitch <= (kAStages + kBStages) * kSlotBytes, "output tile fits the rings");
+  __syncthreads();
+  {
+    const int row_l = lane & 31;
+    const int col_l = (lane >> 5) * 4;
 #pragma unroll
-  for (int i = 0; i < NFA; ++i) {
-    const int m = m0 + wm * kWaveRows + i * 32 + row_l;
-    if (m >= ta.rows) continue;
-    uint16_t* crow = ta.C + (long long)(ta.row0 + m) * ta.ldc;
+    for (int i = 0; i < NFA; ++i) {
+      uint8_t* lrow = lds + (wm * kWaveRows + i * 32 + row_l) * kPitch;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (EPI == EPI_SILU_GLU) {
+      for (int g = 0; g < 4; ++g) {
+        if (EPI == EPI_SILU_GLU) {
 #pragma unroll
-        for (int j = 0; j < kBF / 2; ++j) {
-          const int n = n0 + wn * kWaveCols + j * 32 + g * 8 + col_l;
-          if (n < N) {
+          for (int j = 0; j < kBF / 2; ++j) {
             float v[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
               v[q] = silu_f(acc[i][j][4 * g + q]) * acc[i][j + kBF / 2][4 * g + q];
-            store_bf16x4(crow + n, v);
+            store_bf16x4(reinterpret_cast<uint16_t*>(lrow) + wn * kWaveCols + j * 32 + g * 8 + col_l, v);
           }
-        }
-      } else {
+        } else {
 #pragma unroll
-        for (int j = 0; j < kBF; ++j) {
-          const int n = n0 + wn * kWaveCols + j * 32 + g * 8 + col_l;
-          if (n < N) {
+          for (int j = 0; j < kBF; ++j) {
             float v[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * g + q];
-            store_bf16x4(crow + n, v);
+            store_bf16x4(reinterpret_cast<uint16_t*>(lrow) + wn * kWaveCols + j * 32 + g * 8 + col_l, v);
           }
         }
       }
     }
+  }
+  __syncthreads();
+  // Rows past the group's last one are not stored; N is a multiple of 64, so
+  // a 16-byte piece (8 columns) is either wholly inside or wholly past N.
+  constexpr int kLanesPerRow = kOutBytes / 16;
+  constexpr int kRowsPerPass = kThreads / kLanesPerRow;
+  constexpr int kTileRows = NFA * 64;
+  static_assert(kTileRows % kRowsPerPass == 0, "whole passes");
+  const int piece = tid % kLanesPerRow;
+  const int n = n0 + piece * 8;
+#pragma unroll
+  for (int r = tid / kLanesPerRow; r < kTileRows; r += kRowsPerPass) {
+    const int m = m0 + r;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * kPitch + piece * 16);
+    if (m < ta.rows && n < N)
+      *reinterpret_cast<u32x4*>(ta.C + (long long)(ta.row0 + m) * ta.ldc + n) = v;
   }
 }
 

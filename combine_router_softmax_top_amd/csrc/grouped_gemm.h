@@ -19,15 +19,23 @@ struct Tile {
   int n_tile;   // column tile
 };
 
+// Inclusive prefix sum over the 64 lanes, all in DPP moves (no LDS round
+// trip): shifts of 1, 2, 4 and 8 lanes inside each row of 16 (lanes without a
+// source add 0), then the last lane of rows 0 and 2 is added to rows 1 and 3
+// (row_bcast:15) and the last lane of row 1 -- by then the sum of rows 0-1 --
+// to rows 2 and 3 (row_bcast:31).
 __device__ __forceinline__ int wave_inclusive_sum(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(v, d, 64);
-    if (lane >= d) v += u;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
+
+// Value of lane L (uniform) of v, into a scalar register.
+__device__ __forceinline__ int lane_value(int v, int L) { return __builtin_amdgcn_readlane(v, L); }
 
 // Row tiles of a group of `rows` rows: `full` tiles computed at full height
 // (BM rows, including a last tile of more than 3BM/4 rows) and, when the
@@ -100,9 +108,9 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
       if (c * 64 >= n_all) break;
       int f, q;
       group_row_tiles(g1[c] - g0[c], BM, f, q);
-      n_full += __shfl(wave_inclusive_sum(f), 63, 64);
+      n_full += lane_value(wave_inclusive_sum(f), 63);
 #pragma unroll
-      for (int p = 0; p < 3; ++p) n_part[p] += __shfl(wave_inclusive_sum(q == 3 - p ? 1 : 0), 63, 64);
+      for (int p = 0; p < 3; ++p) n_part[p] += __popcll(__ballot(q == 3 - p));
     }
   } else {
     int q;
@@ -153,13 +161,13 @@ __device__ __forceinline__ bool find_tile(const int32_t* __restrict__ offsets, i
       group_row_tiles(g1[c] - g0[c], BM, f, q);
       const int cnt = is_short ? (q == want ? 1 : 0) : f;
       const int incl = wave_inclusive_sum(cnt);
-      const int chunk = __shfl(incl, 63, 64);
+      const int chunk = lane_value(incl, 63);
       if (rt < chunk) {
         const int L = __builtin_ctzll(__ballot(incl > rt));
-        row0 = __shfl(g0[c], L, 64);
-        rows = __shfl(g1[c], L, 64) - row0;
+        row0 = lane_value(g0[c], L);
+        rows = lane_value(g1[c], L) - row0;
         group = c * 64 + L;
-        m_tile = is_short ? __shfl(f, L, 64) : rt - __shfl(incl - cnt, L, 64);
+        m_tile = is_short ? lane_value(f, L) : rt - lane_value(incl - cnt, L);
         found = true;
       } else {
         rt -= chunk;
