@@ -336,16 +336,21 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
 
   // Epilogue: element r of lane l in a 32 x 32 block is output row l % 32 and
   // column (r / 4) * 8 + (l / 32) * 4 + r % 4; gate block j pairs with up
-  // block j + 2.  N is a multiple of 64, so a run of four columns is wholly
-  // inside or wholly past N.
+  // block j + 2.  N is a multiple of 64, so a run of four (or eight) columns is
+  // wholly inside or wholly past N.
   const int row_l = lane & 31;
   const int col_l = h * 4;
+  if constexpr (QOUT) {
+    // The codes go through LDS as below (row pitch 144 bytes); the scale bytes
+    // straight to memory.
+    constexpr int kPitchQ = kQNOut + 16;
+    __syncthreads();
 #pragma unroll
-  for (int i = 0; i < NFA; ++i) {
-    const int m = m0 + wm * kWaveRows + i * 32 + row_l;
-    if (m >= ta.rows) continue;  // lanes l and l ^ 32 share the row
-    const long long row = ta.row0 + m;
-    if constexpr (QOUT) {
+    for (int i = 0; i < NFA; ++i) {
+      const int r = wm * kWaveRows + i * 32 + row_l;
+      const int m = m0 + r;
+      if (m >= ta.rows) continue;  // lanes l and l ^ 32 share the row
+      const long long row = ta.row0 + m;
       // A 32-column block of h is one row of a 32 x 32 MFMA block, 16 values
       // in each of lanes l and l ^ 32: its MX-FP8 scale from their common
       // maximum (the encoding rule of the dispatch), 16 codes per lane written
@@ -365,7 +370,7 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
         const int ef = (int)((__float_as_uint(mx) >> 23) & 0xff);
         const int sc = min(127, max(-127, ef - 127 - 8));
         const float inv = __uint_as_float((uint32_t)(127 - sc) << 23);
-        uint8_t* crow = ta.Cq + row * ta.ldc + nb;
+        uint8_t* lrow = lds + r * kPitchQ + (nb - n0);
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           float e[4];
@@ -373,7 +378,7 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
           for (int q = 0; q < 4; ++q) e[q] = fminf(448.f, fmaxf(-448.f, v[4 * gq + q] * inv));
           int w = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
           w = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], w, true);
-          *reinterpret_cast<uint32_t*>(crow + gq * 8 + col_l) = (uint32_t)w;
+          *reinterpret_cast<uint32_t*>(lrow + gq * 8 + col_l) = (uint32_t)w;
         }
         if (col_l == 0) {
           const int qb = nb / 32, g = qb >> 4, mm = qb & 15;
@@ -382,22 +387,59 @@ __device__ __forceinline__ void qgemm_tile(const QTileArgs& ta, uint8_t* lds) {
               (uint8_t)(sc + 127);
         }
       }
-    } else {
-      uint16_t* crow = ta.C + row * ta.ldc;
+    }
+    __syncthreads();
+    // 16 bytes per lane, 8 lanes per 128-byte row of codes.
+    constexpr int kRowsPerPass = kQThreads / 8;
+    constexpr int kTileRows = NFA * 64;
+    static_assert(kTileRows % kRowsPerPass == 0, "whole passes");
+    const int piece = tid % 8;
+#pragma unroll
+    for (int r = tid / 8; r < kTileRows; r += kRowsPerPass) {
+      const int m = m0 + r;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * kPitchQ + piece * 16);
+      if (m < ta.rows)
+        *reinterpret_cast<u32x4*>(ta.Cq + (long long)(ta.row0 + m) * ta.ldc + n0 + piece * 16) = v;
+    }
+  } else {
+    // bf16 out, through LDS: four adjacent values per (lane, r / 4) go into a
+    // row-major copy of the tile (row pitch padded by 16 bytes), then each
+    // lane moves 16 bytes of a row to memory, a wave covering whole rows.
+    // The barrier first waits for every wave's loads and fragment reads.
+    constexpr int kNOut = kGlu ? kQNOut : kBN;
+    constexpr int kOutBytes = kNOut * 2;
+    constexpr int kPitch = kOutBytes + 16;
+    static_assert(kBM * kPitch <= kQLds, "output tile fits the rings");
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NFA; ++i) {
+      uint16_t* lrow = reinterpret_cast<uint16_t*>(lds + (wm * kWaveRows + i * 32 + row_l) * kPitch);
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq)
 #pragma unroll
         for (int j = 0; j < (kGlu ? 2 : kQBF); ++j) {
-          const int n = n0 + (j >> 1) * 128 + wn * 64 + (j & 1) * 32 + gq * 8 + col_l;
-          if (n < N) {
-            float v[4];
+          const int c = (j >> 1) * 128 + wn * 64 + (j & 1) * 32 + gq * 8 + col_l;
+          float v[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              v[q] = kGlu ? silu_f(acc[i][j][4 * gq + q]) * acc[i][j + 2][4 * gq + q]
-                          : acc[i][j][4 * gq + q];
-            store_bf16x4(crow + n, v);
-          }
+          for (int q = 0; q < 4; ++q)
+            v[q] = kGlu ? silu_f(acc[i][j][4 * gq + q]) * acc[i][j + 2][4 * gq + q]
+                        : acc[i][j][4 * gq + q];
+          store_bf16x4(lrow + c, v);
         }
+    }
+    __syncthreads();
+    constexpr int kLanesPerRow = kOutBytes / 16;
+    constexpr int kRowsPerPass = kQThreads / kLanesPerRow;
+    constexpr int kTileRows = NFA * 64;
+    static_assert(kTileRows % kRowsPerPass == 0, "whole passes");
+    const int piece = tid % kLanesPerRow;
+    const int n = n0 + piece * 8;
+#pragma unroll
+    for (int r = tid / kLanesPerRow; r < kTileRows; r += kRowsPerPass) {
+      const int m = m0 + r;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * kPitch + piece * 16);
+      if (m < ta.rows && n < N)
+        *reinterpret_cast<u32x4*>(ta.C + (long long)(ta.row0 + m) * ta.ldc + n) = v;
     }
   }
 }
