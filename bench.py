@@ -147,7 +147,7 @@ def achievable_peaks(torch, stream) -> dict:
     n = 1 << 30
     a = torch.ones(n, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
-    sink = torch.empty(8192 * 256, dtype=torch.int32, device="cuda")
+    sink = torch.empty(16384 * 256, dtype=torch.int32, device="cuda")
 
     def timed(fn, reps=5):
         fn()
@@ -160,9 +160,10 @@ def achievable_peaks(torch, stream) -> dict:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e-3 / reps
 
-    res = {"how": "1 GiB, 16-byte accesses, the best of 512-8192 workgroups of 256; MFMA "
-                  "loops: 256 workgroups of 8 waves, 8 independent register-only MFMAs per round"}
-    grids = (512, 1024, 2048, 4096, 8192)
+    res = {"how": "1 GiB, 16-byte accesses in contiguous 16-32 KB blocks per workgroup, the best "
+                  "of 1024-16384 workgroups of 256; MFMA loops: 256 workgroups of 8 waves, 8 "
+                  "independent register-only MFMAs per round"}
+    grids = (1024, 2048, 4096, 8192, 16384)
     for key, kind, moved in [("copy", B.PROBE_COPY, 2 * n), ("read", B.PROBE_READ, n),
                              ("write", B.PROBE_WRITE, n)]:
         best, best_wg = 0.0, 0

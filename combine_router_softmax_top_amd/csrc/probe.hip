@@ -1,5 +1,5 @@
 // Achievable-peak probes of one MI355X: plain streaming copy / read / write
-// kernels (16-byte accesses, several loads in flight per lane) and register-
+// kernels (16-byte accesses in contiguous per-workgroup blocks) and register-
 // only MFMA loops (bf16 v_mfma_f32_32x32x16_bf16 and the block-scaled fp8
 // v_mfma_scale_f32_32x32x64_f8f6f4).  The benchmark reports what they reach
 // beside the nominal peaks (8 TB/s HBM, 2.5 PFLOP/s bf16, 5.0 PFLOP/s fp8),
@@ -11,35 +11,48 @@ namespace moe {
 namespace {
 
 constexpr int kProbeThreads = 256;
-constexpr int kProbeUnroll = 4;  // 16-byte accesses in flight per lane
 
-// kind 0: dst = src; 1: read src (an xor of every word, one dword per thread
-// written so the loads stay live); 2: dst = a pattern.
+// Each workgroup walks the buffer in blocks of UNR * 4 KB (one 16-byte
+// access per lane per KB, all UNR of a block issued before any is used),
+// block b, b + gridDim.x, ...: a workgroup's accesses stay contiguous, which
+// measured 15-20 % faster than a grid-wide stride of 16-byte accesses.  Reads
+// are non-temporal (they are used once).  kind 0: dst = src (8 in flight,
+// non-temporal stores too); 1: read src (8 in flight; an xor of every word,
+// one dword per thread written so the loads stay live); 2: dst = a pattern
+// (4 per block).  A tail shorter than a block is covered 16 bytes per lane.
 template <int KIND>
 __global__ __launch_bounds__(kProbeThreads) void probe_stream_kernel(u32x4* __restrict__ dst,
                                                                       const u32x4* __restrict__ src,
                                                                       long long n,
                                                                       uint32_t* __restrict__ sink) {
-  const long long stride = (long long)gridDim.x * kProbeThreads;
-  long long i = (long long)blockIdx.x * kProbeThreads + threadIdx.x;
+  constexpr int UNR = KIND == 2 ? 4 : 8;
+  constexpr long long kPer = (long long)kProbeThreads * UNR;  // 16-byte elements per block
+  const long long step = (long long)gridDim.x * kPer;
   u32x4 acc = {0u, 0u, 0u, 0u};
-  for (; i + (kProbeUnroll - 1) * stride < n; i += kProbeUnroll * stride) {
-    u32x4 v[kProbeUnroll];
+  long long b = (long long)blockIdx.x * kPer;
+  for (; b + kPer <= n; b += step) {
+    u32x4 v[UNR];
     if constexpr (KIND != 2) {
 #pragma unroll
-      for (int u = 0; u < kProbeUnroll; ++u) v[u] = src[i + u * stride];
+      for (int u = 0; u < UNR; ++u)
+        v[u] = __builtin_nontemporal_load(src + b + u * kProbeThreads + threadIdx.x);
     }
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) {
-      if constexpr (KIND == 0) dst[i + u * stride] = v[u];
+    for (int u = 0; u < UNR; ++u) {
+      const long long i = b + u * kProbeThreads + threadIdx.x;
+      if constexpr (KIND == 0) __builtin_nontemporal_store(v[u], dst + i);
       if constexpr (KIND == 1) acc ^= v[u];
-      if constexpr (KIND == 2) dst[i + u * stride] = u32x4{(uint32_t)u, 1u, 2u, 3u};
+      if constexpr (KIND == 2) dst[i] = u32x4{(uint32_t)u, 1u, 2u, 3u};
     }
   }
-  for (; i < n; i += stride) {
-    if constexpr (KIND == 0) dst[i] = src[i];
-    if constexpr (KIND == 1) acc ^= src[i];
-    if constexpr (KIND == 2) dst[i] = u32x4{0u, 1u, 2u, 3u};
+  // The tail (fewer than kPer elements, past the last whole block), read by
+  // the workgroup whose next block would have started there.
+  if (b < n) {
+    for (long long i = b + threadIdx.x; i < n; i += kProbeThreads) {
+      if constexpr (KIND == 0) dst[i] = src[i];
+      if constexpr (KIND == 1) acc ^= src[i];
+      if constexpr (KIND == 2) dst[i] = u32x4{0u, 1u, 2u, 3u};
+    }
   }
   if constexpr (KIND == 1)
     sink[(long long)blockIdx.x * kProbeThreads + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];

@@ -22,7 +22,9 @@ extern "C" {
 
 /*
  * moe_probe_stream -- one pass over `bytes` bytes (a multiple of 16) with
- * 16-byte accesses, `workgroups` workgroups of 256 threads striding over it:
+ * 16-byte accesses by `workgroups` workgroups of 256 threads, each taking
+ * every workgroups-th contiguous block of 16 KB (kind 2) or 32 KB (kinds 0, 1)
+ * in turn, loads non-temporal:
  *   kind 0: copy src -> dst (reads and writes `bytes` each);
  *   kind 1: read src (sink [workgroups * 256] uint32 receives one word per
  *           thread so the loads stay live; dst unused, may be NULL);

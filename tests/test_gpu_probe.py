@@ -11,9 +11,10 @@ from combine_router_softmax_top_amd import binding as B
 pytestmark = pytest.mark.gpu
 
 
-def test_stream_probes():
-    print("[gpu-case] stream probes", file=sys.stderr, flush=True)
-    n = (1 << 20) + 48  # a ragged tail after the unrolled passes
+@pytest.mark.parametrize("n", [(1 << 20) + 48, 4112])
+def test_stream_probes(n):
+    # (1 << 20) + 48: whole blocks and a ragged tail; 4112: less than one block
+    print(f"[gpu-case] stream probes n={n}", file=sys.stderr, flush=True)
     g = torch.Generator().manual_seed(3)
     a = torch.randint(0, 256, (n,), dtype=torch.uint8, generator=g).cuda()
     b = torch.zeros_like(a)
