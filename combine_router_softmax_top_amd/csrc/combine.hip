@@ -8,11 +8,11 @@
 //
 // One wave per token, four tokens per workgroup.  The row maps and weights of
 // the token are read into lanes 0..K-1 and broadcast with readlane (scalar
-// registers).  Each lane owns 16-byte pieces of the output row; for each piece
-// it issues the gathers of up to 8 expert rows at once (so many rows are in
-// flight per wave), accumulates w_k * y in fp32 in ascending k, adds the
-// shared-expert rows, and rounds once.  Routed rows too many for the Infinity
-// Cache are read with streaming loads.
+// registers).  Each lane owns 16-byte pieces of the output row; it issues the
+// gathers of up to 8 expert rows at once (for top-2 and top-4, of 4 or 2
+// pieces each, so 8 rows' worth are in flight per lane), accumulates w_k * y
+// in fp32 in ascending k, adds the shared-expert rows, and rounds once.
+// Routed rows too many for the Infinity Cache are read with streaming loads.
 #include "moe_internal.h"
 
 namespace moe {
@@ -52,23 +52,28 @@ struct Vec<float> {  // fp32: 4 per 16 bytes
   }
 };
 
-// Accumulates w_j * y[rows[j]] for the NB slots of one batch, in slot order,
-// into acc.
+// Issues the loads of one batch: y[rows[j]] piece v for the NB slots.
 // rows[j] < 0 marks an empty slot: its load reads the valid row `dummy` and
-// the value is discarded by a select (never multiplied by 0, which could turn
-// a non-finite dummy into NaN).  All loads are issued before the first use.
-// NT: streaming loads, which do not allocate in the caches.
-template <typename T, int NB, bool NT>
-__device__ __forceinline__ void gather_batch(const u32x4* __restrict__ base, long long row_stride,
-                                             int v, const int (&rows)[NB], const float (&w)[NB],
-                                             int dummy, float (&acc)[Vec<T>::N]) {
-  constexpr int N = Vec<T>::N;
-  u32x4 buf[NB];
+// the value is discarded by consume_batch's select (never multiplied by 0,
+// which could turn a non-finite dummy into NaN).  NT: streaming loads, which
+// do not allocate in the caches.
+template <int NB, bool NT>
+__device__ __forceinline__ void issue_batch(const u32x4* __restrict__ base, long long row_stride,
+                                            int v, const int (&rows)[NB], int dummy,
+                                            u32x4 (&buf)[NB]) {
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const u32x4* p = base + (long long)(rows[j] >= 0 ? rows[j] : dummy) * row_stride + v;
     buf[j] = NT ? __builtin_nontemporal_load(p) : *p;
   }
+}
+
+// Accumulates w_j * y_j of the NB slots of a loaded batch, in slot order,
+// into acc.
+template <typename T, int NB>
+__device__ __forceinline__ void consume_batch(const u32x4 (&buf)[NB], const int (&rows)[NB],
+                                              const float (&w)[NB], float (&acc)[Vec<T>::N]) {
+  constexpr int N = Vec<T>::N;
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     float f[N];
@@ -77,6 +82,16 @@ __device__ __forceinline__ void gather_batch(const u32x4* __restrict__ base, lon
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = ok ? fmaf(w[j], f[i], acc[i]) : acc[i];
   }
+}
+
+// Both, for one batch: every load issued before the first use.
+template <typename T, int NB, bool NT>
+__device__ __forceinline__ void gather_batch(const u32x4* __restrict__ base, long long row_stride,
+                                             int v, const int (&rows)[NB], const float (&w)[NB],
+                                             int dummy, float (&acc)[Vec<T>::N]) {
+  u32x4 buf[NB];
+  issue_batch<NB, NT>(base, row_stride, v, rows, dummy, buf);
+  consume_batch<T, NB>(buf, rows, w, acc);
 }
 
 // KB = routed rows gathered per batch (2, 4 or 8: the smallest that holds
@@ -117,15 +132,10 @@ __global__ __launch_bounds__(256) void combine_kernel(
     w1[j] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, myw), KB + j));
   }
   const bool second = K > KB;
-  for (int v0 = 0; v0 < row_vecs; v0 += kWave) {
-    const int v = min(v0 + lane, row_vecs - 1);  // lanes past the row re-read its end
-    float acc[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i) acc[i] = 0.f;
-    if (has) {
-      gather_batch<T, KB, NT>(y_sorted, row_vecs, v, rows0, w0, dummy, acc);
-      if (second) gather_batch<T, KB, NT>(y_sorted, row_vecs, v, rows1, w1, dummy, acc);
-    }
+  // The rest of piece v (lanes with v0 + lane >= row_vecs re-read the row's
+  // end and store nothing): fp32 sums out (SUMS), or the shared rows added and
+  // the rounded row written.
+  auto finish = [&](int v0, int v, float (&acc)[N]) {
     if (SUMS) {
       if (v0 + lane < row_vecs) {
         u32x4* o = out + ((size_t)t * row_vecs + v) * (N / 4);
@@ -134,7 +144,7 @@ __global__ __launch_bounds__(256) void combine_kernel(
           o[q] = u32x4{__float_as_uint(acc[4 * q]), __float_as_uint(acc[4 * q + 1]),
                        __float_as_uint(acc[4 * q + 2]), __float_as_uint(acc[4 * q + 3])};
       }
-      continue;
+      return;
     }
     if (n_shared > 0) {
       constexpr int SB = MOE_MAX_SHARED;
@@ -149,6 +159,43 @@ __global__ __launch_bounds__(256) void combine_kernel(
       gather_batch<T, SB, false>(y_shared, row_vecs, v, rows, w, t, acc);
     }
     if (v0 + lane < row_vecs) out[(size_t)t * row_vecs + v] = Vec<T>::store(acc);
+  };
+  // With few routed rows per token (KB = 2 or 4, so a single batch) the loads
+  // of CH column pieces are issued together, 8 rows' worth per lane in flight
+  // as with KB = 8; each piece is then finished in turn.
+  constexpr int CH = KB == 2 ? 4 : KB == 4 ? 2 : 1;
+  if constexpr (CH == 1) {
+    for (int v0 = 0; v0 < row_vecs; v0 += kWave) {
+      const int v = min(v0 + lane, row_vecs - 1);
+      float acc[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[i] = 0.f;
+      if (has) {
+        gather_batch<T, KB, NT>(y_sorted, row_vecs, v, rows0, w0, dummy, acc);
+        if (second) gather_batch<T, KB, NT>(y_sorted, row_vecs, v, rows1, w1, dummy, acc);
+      }
+      finish(v0, v, acc);
+    }
+  } else {
+    for (int v0 = 0; v0 < row_vecs; v0 += CH * kWave) {
+      u32x4 buf[CH][KB];
+      if (has) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+          issue_batch<KB, NT>(y_sorted, row_vecs, min(v0 + c * kWave + lane, row_vecs - 1),
+                              rows0, dummy, buf[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int vc = v0 + c * kWave;
+        if (vc >= row_vecs) break;
+        float acc[N];
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[i] = 0.f;
+        if (has) consume_batch<T, KB>(buf[c], rows0, w0, acc);
+        finish(vc, min(vc + lane, row_vecs - 1), acc);
+      }
+    }
   }
 }
 
