@@ -505,7 +505,10 @@ def main():
     if not args.no_graph:
         result["graph_replay"] = graph_replay(args, layer, stream, torch)
     if not args.no_cold:
-        result["dispatch_combine_cold"] = cold_dispatch_combine(layer, stream, torch, alg)
+        cold = cold_dispatch_combine(layer, stream, torch, alg)
+        w = cold_dispatch_combine(layer, stream, torch, alg, evict="write")
+        cold["evicted_by_writing"] = {k: w[k] for k in ("dispatch_us", "combine_us", "frac_hbm_peak")}
+        result["dispatch_combine_cold"] = cold
     if not args.no_mxfp8 and not cfg.packed_weights and cfg.dtype == "bf16" and cfg.num_shared == 0 and cfg.hidden % 512 == 0:
         result["mxfp8"] = mxfp8_leg(args, layer, stream, torch, alg, n_loc, t_touch)
     if not args.no_dbo and cfg.name == "dsv3_prefill_ep" and not cfg.packed_weights:
@@ -595,20 +598,32 @@ def mxfp8_leg(args, layer, stream, torch, alg, n_loc: int, t_touch: int) -> dict
         "rel_l2_vs_bf16_layer": rel}
 
 
-def cold_dispatch_combine(layer, stream, torch, alg, iters: int = 10) -> dict:
-    """Dispatch and combine with cold caches: 1 GiB is written right before each
-    of them, which evicts L2 and the 256 MB Infinity Cache, so their reads come
-    from HBM (the layer's own sequence leaves part of y_sorted in the cache)."""
+def cold_dispatch_combine(layer, stream, torch, alg, iters: int = 10, evict: str = "read") -> dict:
+    """Dispatch and combine with cold caches: right before each of them 1 GiB
+    of an unrelated buffer is read (evict="read"), which replaces what L2 and
+    the 256 MB Infinity Cache hold with clean lines, so the stage's reads come
+    from HBM (the layer's own sequence leaves part of y_sorted in the cache).
+    evict="write" fills the buffer instead: that leaves the caches full of
+    dirty lines, whose write-back to HBM then runs during the stage."""
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush.fill_(1)
+    sink = torch.empty((), dtype=torch.int64, device="cuda")
+
+    def evict_caches(i):
+        if evict == "read":
+            torch.sum(flush.view(torch.int32), dim=0, out=sink)
+        else:
+            flush.fill_(i & 255)
+
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters)]
     with torch.cuda.stream(stream):
         for i in range(iters):
-            flush.fill_(i & 255)
+            evict_caches(i)
             ev[i][0].record(stream)
             layer.dispatch(stream)
             ev[i][1].record(stream)
             layer.expert_mlp(stream)
-            flush.fill_((i + 1) & 255)
+            evict_caches(i + 1)
             ev[i][2].record(stream)
             layer.combine(stream)
             ev[i][3].record(stream)
@@ -618,9 +633,11 @@ def cold_dispatch_combine(layer, stream, torch, alg, iters: int = 10) -> dict:
     nbytes = alg["dispatch"] + alg["combine"]
     gbs = nbytes / ((d + c) * 1e-3) / 1e9
     del flush
+    how = ("1 GiB of another buffer read before each stage (L2 and Infinity Cache refilled with "
+           "clean lines), HIP events" if evict == "read" else
+           "1 GiB written before each stage (caches left holding dirty lines), HIP events")
     return {"dispatch_us": d * 1e3, "combine_us": c * 1e3, "GB_per_s": gbs,
-            "frac_hbm_peak": gbs / HBM_PEAK_GBS,
-            "how": "1 GiB written before each stage (L2 and Infinity Cache evicted), HIP events"}
+            "frac_hbm_peak": gbs / HBM_PEAK_GBS, "how": how}
 
 
 def graph_replay(args, layer, stream, torch) -> dict:
