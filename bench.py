@@ -187,6 +187,38 @@ def achievable_peaks(torch, stream) -> dict:
     return res
 
 
+def library_dense_gemm(torch, stream, cfg, n_loc: int) -> dict:
+    """The vendor library's bf16 GEMM (torch.nn.functional.linear, i.e. hipBLASLt)
+    on dense matrices with the M x N x K of this layer's two expert GEMMs: the
+    rows (routed, plus T per shared expert) as one [M, d] matrix times the
+    stacked gate and up weights [2I, d], and [M, I] times the down weights
+    [d, I].  One dense product per pass, no expert grouping: a reference for
+    the grouped kernels, same flops."""
+    d, inter = cfg.hidden, cfg.intermediate
+    rows = n_loc + cfg.num_shared * cfg.num_tokens
+    g = torch.Generator(device="cuda").manual_seed(7)
+    out = {}
+    for key, (m, n, k) in (("gate_up", (rows, 2 * inter, d)), ("down", (rows, d, inter))):
+        a = (torch.randn(m, k, device="cuda", generator=g) * 0.5).to(torch.bfloat16)
+        w = (torch.randn(n, k, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                y = torch.nn.functional.linear(a, w)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                y = torch.nn.functional.linear(a, w)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 10 * 1e3
+        out[f"{key}_us"] = us
+        out[f"{key}_TFLOP_per_s"] = 2.0 * m * n * k / (us * 1e-6) / 1e12
+        del a, w, y
+    out["both_us"] = out["gate_up_us"] + out["down_us"]
+    out["shapes"] = {"gate_up": [rows, 2 * inter, d], "down": [rows, d, inter]}
+    return out
+
+
 def source_digest() -> str:
     """Digest of the bf16 expert-MLP kernel's source code (its file and the
     shared grouped-GEMM header): // comments and blank lines are left out, so
@@ -211,7 +243,14 @@ def algorithmic(cfg, n_loc: int, t_touch: int) -> dict:
     dispatch = t_touch * d * b + n_loc * d * b + n_loc * 4 + 2 * T * K * 4 + 2 * E * 4
     combine = n_loc * d * b + T * K * 8 + T * d * b + S * T * d * b
     flops = 6.0 * n_loc * d * I + 6.0 * S * T * d * I
-    return dict(route=route, dispatch=dispatch, combine=combine, gemm_flops=flops)
+    # Expert MLP: every local and shared expert's three weight matrices read
+    # once (every local expert is taken to have rows), the rows read (x),
+    # h written and read back, y written.
+    rows = n_loc + S * T
+    e_loc = cfg.expert_end - cfg.expert_begin
+    gemm_bytes = (e_loc + S) * 3 * I * d * b + rows * (2 * d + 2 * I) * b
+    return dict(route=route, dispatch=dispatch, combine=combine, gemm_flops=flops,
+                gemm_bytes=gemm_bytes)
 
 
 def _cpu_model() -> str:
@@ -458,6 +497,11 @@ def main():
     bf16 = cfg.dtype == "bf16"
     peak = BF16_MFMA_PEAK_TFLOPS if bf16 else FP32_VALU_PEAK_TFLOPS
     gemm_tflops = alg["gemm_flops"] / (stage["expert_mlp"] * 1e-3) / 1e12
+    gemm_gbs = gbs(alg["gemm_bytes"], stage["expert_mlp"])
+    # Arithmetic intensity of the expert MLP against the ridge point of the
+    # roofline (peak flops over 8 TB/s): below it the stage is HBM-bound.
+    ai = alg["gemm_flops"] / alg["gemm_bytes"]
+    ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
     traffic = None
     if os.path.exists(TRAFFIC_FILE) and not cfg.packed_weights:  # counted on row-major weights
         rec = json.load(open(TRAFFIC_FILE))
@@ -495,13 +539,18 @@ def main():
                   "frac_hbm_peak": gbs(alg["route"], stage["route"]) / HBM_PEAK_GBS,
                   "algorithmic_bytes": alg["route"]},
         "expert_gemm": {"TFLOP_per_s": gemm_tflops, "frac_mfma_peak": gemm_tflops / peak,
-                        "flops": alg["gemm_flops"]},
-        "roofline": {"bound": "mfma" if bf16 else "alu", "achieved": gemm_tflops, "peak": peak,
-                     "unit": "TFLOP/s", "frac": gemm_tflops / peak, "traffic": traffic,
-                     "kernel": "moe_expert_mlp (gate/up SiLU GEMM + down GEMM)",
-                     "avg_launch_us": stage["expert_mlp"] * 1e3},
+                        "flops": alg["gemm_flops"], "algorithmic_bytes": alg["gemm_bytes"],
+                        "GB_per_s": gemm_gbs, "flop_per_byte": ai, "ridge_flop_per_byte": ridge},
+        "roofline": ({"bound": "mfma" if bf16 else "alu", "achieved": gemm_tflops, "peak": peak,
+                      "unit": "TFLOP/s", "frac": gemm_tflops / peak}
+                     if ai >= ridge else
+                     {"bound": "hbm", "achieved": gemm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": gemm_gbs / HBM_PEAK_GBS}),
         "input_generation_s": round(t_gen, 1),
     }
+    result["roofline"].update({"traffic": traffic,
+                               "kernel": "moe_expert_mlp (gate/up SiLU GEMM + down GEMM)",
+                               "avg_launch_us": stage["expert_mlp"] * 1e3})
     if not args.no_graph:
         result["graph_replay"] = graph_replay(args, layer, stream, torch)
     if not args.no_cold:
@@ -517,6 +566,10 @@ def main():
         peaks = achievable_peaks(torch, stream)
         peaks["expert_gemm_frac_of_mfma_loop"] = (
             gemm_tflops / peaks["mfma_bf16_TFLOP_per_s"] if bf16 else None)
+        if bf16 and n_loc > 0:
+            lib = library_dense_gemm(torch, stream, cfg, n_loc)
+            lib["expert_mlp_us"] = stage["expert_mlp"] * 1e3
+            peaks["library_dense_gemm_bf16"] = lib
         peaks["dispatch_combine_frac_of_copy"] = gbs(dc_bytes, dc_ms) / peaks["copy_GB_per_s"]
         result["achievable_peaks"] = peaks
     if not args.no_cpu_baseline:
