@@ -8,8 +8,8 @@
 // pages' receive side fills slots in arbitrary order; here the order is fixed
 // (expert ascending, then token ascending), so the layout has one answer.
 //
-// Two kernels (three for very large histograms), no host synchronisation and
-// no memset:
+// Two kernels (one for batches of at most 2048 assignments, see self_count;
+// three for very large histograms), no host synchronisation and no memset:
 //  1. count: one workgroup per chunk of 1024 assignments (t*K + k in
 //     ascending order, one per thread).  Each local expert gets a 1024-bit
 //     mask over the chunk's assignment slots in LDS (64-bit LDS atomic OR);
@@ -190,11 +190,68 @@ __device__ void inline_scan(InlineScan& L, const int32_t* __restrict__ hist, int
   __syncthreads();
 }
 
-// NV = 16-byte pieces of the row each lane holds at once.  INLINE: row
-// numbers from inline_scan (hist), else from the scan kernel (base).
+// Batches of at most kSelfAssign assignments skip the count kernel: every
+// scatter workgroup reads all the ids itself (8 KB at most, from L2), counts
+// them per expert (LDS atomics; invalid ids in an extra column) and counts the
+// local experts' assignments before its own first one, scans the local totals
+// into offsets, and ranks its own assignments among themselves.  A local
+// assignment a to expert e gets row offset(e) + (assignments to e before a),
+// the count kernel's rank plus row base, so the layout is the same.  Workgroup
+// 0 also writes the counts, n_invalid and the offsets.  Every thread of the
+// workgroup takes part (barriers).  Measured: a decode batch (128 tokens x 6)
+// 12.1 -> 9.5 us with cold caches; at 8192 assignments (4096 tokens x 2, 8
+// experts) 23 -> 30 us -- each of 1024 workgroups then counts 8192 ids into 8
+// contended LDS counters -- so larger batches keep the count kernel.
+constexpr int kSelfAssign = 2048;
+
+struct SelfCount {
+  int32_t cnt[MOE_MAX_EXPERTS + 1];  // per expert over the batch; [E] = invalid ids
+  int32_t bef[MOE_MAX_EXPERTS];      // local experts: assignments before the workgroup's first
+  int32_t sc[2][MOE_MAX_EXPERTS];    // scan ping-pong over the local totals
+  int32_t own[4 * MOE_MAX_TOPK];     // the workgroup's own ids
+};
+
+// Returns which sc buffer holds the inclusive scan of the local totals.
+__device__ int self_count(SelfCount& L, const int32_t* __restrict__ ids, int n_assign, int E,
+                          int eb, int n_loc, int a0, int n_own, int32_t* __restrict__ counts,
+                          int32_t* __restrict__ offsets, int32_t* __restrict__ n_invalid) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i <= E; i += 256) L.cnt[i] = 0;
+  for (int i = tid; i < n_loc; i += 256) L.bef[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < n_assign; i += 256) {
+    const int e = ids[i];
+    atomicAdd(&L.cnt[e >= 0 && e < E ? e : E], 1);
+    if (i < a0 && e >= eb && e < eb + n_loc) atomicAdd(&L.bef[e - eb], 1);
+    if (i >= a0 && i < a0 + n_own) L.own[i - a0] = e;
+  }
+  __syncthreads();
+  for (int j = tid; j < n_loc; j += 256) L.sc[0][j] = L.cnt[eb + j];
+  __syncthreads();
+  int cur = 0;
+  for (int off = 1; off < n_loc; off <<= 1) {  // inclusive Hillis-Steele scan
+    for (int j = tid; j < n_loc; j += 256)
+      L.sc[cur ^ 1][j] = L.sc[cur][j] + (j >= off ? L.sc[cur][j - off] : 0);
+    cur ^= 1;
+    __syncthreads();
+  }
+  if (blockIdx.x == 0) {
+    for (int e = tid; e < E; e += 256) counts[e] = L.cnt[e];
+    for (int j = tid; j < n_loc; j += 256) offsets[j + 1] = L.sc[cur][j];
+    if (tid == 0) {
+      *n_invalid = L.cnt[E];
+      offsets[0] = 0;
+    }
+  }
+  return cur;
+}
+
+// NV = 16-byte pieces of the row each lane holds at once.  SELF: row numbers
+// from self_count (no count kernel); else INLINE: from inline_scan (hist),
+// else from the scan kernel (base).
 // Q: encode the (bf16) row as MX-FP8 into codes xq [T*K, d] and scale words
 // xs (MFMA layout over T*K rows) instead of copying it to x_sorted.
-template <int NV, bool INLINE, bool Q>
+template <int NV, bool INLINE, bool Q, bool SELF = false>
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ ids,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ base,
@@ -202,15 +259,24 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
     int row_vecs, u32x4* __restrict__ x_sorted, int32_t* __restrict__ src_index,
     int32_t* __restrict__ row_of, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ n_invalid, uint8_t* __restrict__ xq, uint32_t* __restrict__ xs) {
-  __shared__ typename std::conditional<INLINE, InlineScan, int>::type lds;
+  __shared__ typename std::conditional<
+      SELF, SelfCount, typename std::conditional<INLINE, InlineScan, int>::type>::type lds;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   const bool tok = t < T;  // wave-uniform
   int a = -1, r = -1, j = 0;
   if (tok && lane < K) {
     a = t * K + lane;
-    r = rank[a];
-    if (r >= 0) j = ids[a] - eb;
+    if constexpr (SELF) {  // r >= 0 marks a local assignment; its rank comes below
+      const int e = ids[a];
+      if (e >= eb && e < eb + n_loc) {
+        r = 0;
+        j = e - eb;
+      }
+    } else {
+      r = rank[a];
+      if (r >= 0) j = ids[a] - eb;
+    }
   }
   const bool any = __ballot(r >= 0) != 0ull;  // any local row (wave-uniform)
   // The first piece of the token row does not depend on the row numbers:
@@ -226,7 +292,16 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
   };
   if (tok && any) load_piece(0);
   int myrow = -1;
-  if constexpr (INLINE) {
+  if constexpr (SELF) {
+    const int a0 = blockIdx.x * 4 * K;
+    const int n_own = min(4, T - blockIdx.x * 4) * K;
+    const int cur = self_count(lds, ids, T * K, E, eb, n_loc, a0, n_own, counts, offsets, n_invalid);
+    if (r >= 0) {
+      int rk = lds.bef[j];
+      for (int i = a0; i < a; ++i) rk += lds.own[i - a0] == eb + j ? 1 : 0;
+      myrow = lds.sc[cur][j] - lds.cnt[eb + j] + rk;
+    }
+  } else if constexpr (INLINE) {
     const int c_lo = blockIdx.x * 4 * K / kCA;  // chunk of the workgroup's first assignment
     inline_scan(lds, hist, n_chunks, E, eb, n_loc, c_lo, counts, offsets, n_invalid);
     if (r >= 0) myrow = lds.base[a / kCA - c_lo][j] + r;
@@ -311,15 +386,17 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 }
 
 template <int NV>
-void launch_scatter(bool inl, dim3 grid, hipStream_t s, const void* x, const int32_t* ids,
+void launch_scatter(bool self, bool inl, dim3 grid, hipStream_t s, const void* x, const int32_t* ids,
                     const int32_t* rank, const int32_t* base, const int32_t* hist, int n_chunks,
                     int E, int T, int K, int eb, int n_loc, int row_vecs, void* x_sorted,
                     int32_t* src_index, int32_t* row_of, int32_t* counts, int32_t* offsets,
                     int32_t* n_invalid, uint8_t* xq, uint32_t* xs) {
-  auto kern = xq ? (inl ? dispatch_scatter_kernel<NV, true, true>
-                        : dispatch_scatter_kernel<NV, false, true>)
-                 : (inl ? dispatch_scatter_kernel<NV, true, false>
-                        : dispatch_scatter_kernel<NV, false, false>);
+  auto kern = xq ? (self  ? dispatch_scatter_kernel<NV, false, true, true>
+                   : inl ? dispatch_scatter_kernel<NV, true, true>
+                         : dispatch_scatter_kernel<NV, false, true>)
+                 : (self  ? dispatch_scatter_kernel<NV, false, false, true>
+                   : inl ? dispatch_scatter_kernel<NV, true, false>
+                         : dispatch_scatter_kernel<NV, false, false>);
   hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, static_cast<const u32x4*>(x), ids, rank, base,
                      hist, n_chunks, E, T, K, eb, n_loc, row_vecs,
                      static_cast<u32x4*>(x_sorted), src_index, row_of, counts, offsets,
@@ -356,13 +433,19 @@ hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* 
   ws += align_up((size_t)T * K * 4, 256);
   int32_t* base = reinterpret_cast<int32_t*>(ws);
 
-  hipLaunchKernelGGL(dispatch_count_kernel, dim3(n_chunks), dim3(kCA), 0, s, ids, n_assign, E,
-                     eb, ee, hist, rank);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  // The scan runs inside the scatter when the local chunk counts fit its LDS.
+  // Small batches: the scatter counts for itself (no count kernel).  Else the
+  // count kernel, and the scan inside the scatter when the local chunk counts
+  // fit its LDS.
+  const bool self = n_assign <= kSelfAssign;
+  hipError_t err = hipSuccess;
+  if (!self) {
+    hipLaunchKernelGGL(dispatch_count_kernel, dim3(n_chunks), dim3(kCA), 0, s, ids, n_assign, E,
+                       eb, ee, hist, rank);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   const bool inl = (size_t)n_chunks * n_loc <= (size_t)kInlineScanInts;
-  if (!inl) {
+  if (!self && !inl) {
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, hist, n_chunks,
                        E, eb, ee, counts, offsets, base, n_invalid);
     err = hipGetLastError();
@@ -373,13 +456,13 @@ hipError_t launch_dispatch(const moe_config_t& c, const void* x, const int32_t* 
   const int per_lane = ceil_div(row_vecs, kWave);
   const dim3 grid(ceil_div(T, 4));
   if (per_lane <= 4)
-    launch_scatter<4>(inl, grid, s, x, ids, rank, base, hist, n_chunks, E, T, K, eb, n_loc,
+    launch_scatter<4>(self, inl, grid, s, x, ids, rank, base, hist, n_chunks, E, T, K, eb, n_loc,
                       row_vecs, x_sorted, src_index, row_of, counts, offsets, n_invalid, xq, xs);
   else if (per_lane <= 8)
-    launch_scatter<8>(inl, grid, s, x, ids, rank, base, hist, n_chunks, E, T, K, eb, n_loc,
+    launch_scatter<8>(self, inl, grid, s, x, ids, rank, base, hist, n_chunks, E, T, K, eb, n_loc,
                       row_vecs, x_sorted, src_index, row_of, counts, offsets, n_invalid, xq, xs);
   else
-    launch_scatter<16>(inl, grid, s, x, ids, rank, base, hist, n_chunks, E, T, K, eb, n_loc,
+    launch_scatter<16>(self, inl, grid, s, x, ids, rank, base, hist, n_chunks, E, T, K, eb, n_loc,
                        row_vecs, x_sorted, src_index, row_of, counts, offsets, n_invalid, xq, xs);
   return hipGetLastError();
 }

@@ -447,6 +447,23 @@ def test_dispatch_repeated_experts_in_a_token():
     assert L.n_rows() == cfg.num_tokens * cfg.top_k
 
 
+@pytest.mark.parametrize("tokens", [255, 256, 257])
+def test_dispatch_one_launch_for_small_batches(tokens):
+    # top-8: 2040, 2048 and 2056 assignments.  Up to 2048 the scatter counts
+    # the ids itself (one launch); above, the count kernel runs first.
+    # Invalid, repeated and remote ids on both sides of the boundary, and a
+    # ragged last workgroup of tokens.
+    print(f"[gpu-case] dispatch one launch tokens={tokens}", file=sys.stderr, flush=True)
+    cfg = W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=tokens, hidden=256, intermediate=128)
+    inp = W.make_inputs(cfg, seed=12, with_experts=False)
+    L = MoELayer(cfg, inp)
+    for kw in (dict(invalid_frac=0.03), dict(repeat_pool=5)):
+        ids = W.random_ids(cfg.num_tokens, cfg.num_experts, cfg.top_k, seed=13, **kw)
+        L.dispatch(topk_ids=ids.cuda())
+        torch.cuda.synchronize()
+        check_dispatch(cfg, inp, L, ids=ids)
+
+
 def test_dispatch_scan_fallback_for_large_histograms():
     # 32 chunks x 512 local experts: more per-chunk counts than a scatter
     # workgroup stages, so the separate scan kernel computes the row numbers.
