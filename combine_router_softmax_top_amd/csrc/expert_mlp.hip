@@ -21,6 +21,8 @@
 //     from the activation loads), 160 KB in all; the rows are
 //     XOR-swizzled in 16-byte chunks so the fragment reads are free of bank
 //     conflicts;
+//   * the epilogue stages the rounded tile through LDS, so each store
+//     instruction writes whole row segments;
 //   * ragged groups: the tile list (expert, row tile, column tile) is derived
 //     on the device from the expert offsets; the grid is the host's upper
 //     bound and surplus workgroups exit at once (no host synchronisation); the
@@ -70,7 +72,7 @@ __device__ __forceinline__ void load_frags(const uint8_t* sa, const uint8_t* sb,
 
 // The weights go in the MFMA's first (row) operand, so each 32x32 block holds
 // the transposed output: a lane keeps one output row and runs of 4 adjacent
-// output columns, which the epilogue stores 8 bytes at a time.
+// output columns, which the epilogue writes to LDS 8 bytes at a time.
 template <int NFA>
 __device__ __forceinline__ void mma_step(const Frags& f, f32x16 (&acc)[4][kBF]) {
 #pragma unroll
