@@ -253,6 +253,28 @@ def algorithmic(cfg, n_loc: int, t_touch: int) -> dict:
                 gemm_bytes=gemm_bytes)
 
 
+def mlp_roofline(cfg, alg: dict, mlp_ms: float) -> tuple:
+    """The expert MLP's `expert_gemm` and `roofline` objects for a measured
+    stage time (ms): both rates from the algorithmic flops and bytes, and the
+    bound from the arithmetic intensity against the ridge point of the
+    roofline (peak flops over 8 TB/s) -- below it the stage is HBM-bound."""
+    peak = BF16_MFMA_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_VALU_PEAK_TFLOPS
+    tflops = alg["gemm_flops"] / (mlp_ms * 1e-3) / 1e12
+    gbs = alg["gemm_bytes"] / (mlp_ms * 1e-3) / 1e9
+    ai = alg["gemm_flops"] / alg["gemm_bytes"]
+    ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    expert_gemm = {"TFLOP_per_s": tflops, "frac_mfma_peak": tflops / peak, "flops": alg["gemm_flops"],
+                   "algorithmic_bytes": alg["gemm_bytes"], "GB_per_s": gbs, "flop_per_byte": ai,
+                   "ridge_flop_per_byte": ridge}
+    if ai >= ridge:
+        roofline = {"bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": tflops,
+                    "peak": peak, "unit": "TFLOP/s", "frac": tflops / peak}
+    else:
+        roofline = {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": gbs / HBM_PEAK_GBS}
+    return expert_gemm, roofline
+
+
 def _cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -497,11 +519,7 @@ def main():
     bf16 = cfg.dtype == "bf16"
     peak = BF16_MFMA_PEAK_TFLOPS if bf16 else FP32_VALU_PEAK_TFLOPS
     gemm_tflops = alg["gemm_flops"] / (stage["expert_mlp"] * 1e-3) / 1e12
-    gemm_gbs = gbs(alg["gemm_bytes"], stage["expert_mlp"])
-    # Arithmetic intensity of the expert MLP against the ridge point of the
-    # roofline (peak flops over 8 TB/s): below it the stage is HBM-bound.
-    ai = alg["gemm_flops"] / alg["gemm_bytes"]
-    ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    expert_gemm, roofline = mlp_roofline(cfg, alg, stage["expert_mlp"])
     traffic = None
     if os.path.exists(TRAFFIC_FILE) and not cfg.packed_weights:  # counted on row-major weights
         rec = json.load(open(TRAFFIC_FILE))
@@ -538,14 +556,8 @@ def main():
         "route": {"GB_per_s": gbs(alg["route"], stage["route"]),
                   "frac_hbm_peak": gbs(alg["route"], stage["route"]) / HBM_PEAK_GBS,
                   "algorithmic_bytes": alg["route"]},
-        "expert_gemm": {"TFLOP_per_s": gemm_tflops, "frac_mfma_peak": gemm_tflops / peak,
-                        "flops": alg["gemm_flops"], "algorithmic_bytes": alg["gemm_bytes"],
-                        "GB_per_s": gemm_gbs, "flop_per_byte": ai, "ridge_flop_per_byte": ridge},
-        "roofline": ({"bound": "mfma" if bf16 else "alu", "achieved": gemm_tflops, "peak": peak,
-                      "unit": "TFLOP/s", "frac": gemm_tflops / peak}
-                     if ai >= ridge else
-                     {"bound": "hbm", "achieved": gemm_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": gemm_gbs / HBM_PEAK_GBS}),
+        "expert_gemm": expert_gemm,
+        "roofline": roofline,
         "input_generation_s": round(t_gen, 1),
     }
     result["roofline"].update({"traffic": traffic,
