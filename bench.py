@@ -517,7 +517,6 @@ def main():
     dc_ms = stage["dispatch"] + stage["combine"]
     dc_bytes = alg["dispatch"] + alg["combine"]
     bf16 = cfg.dtype == "bf16"
-    peak = BF16_MFMA_PEAK_TFLOPS if bf16 else FP32_VALU_PEAK_TFLOPS
     gemm_tflops = alg["gemm_flops"] / (stage["expert_mlp"] * 1e-3) / 1e12
     expert_gemm, roofline = mlp_roofline(cfg, alg, stage["expert_mlp"])
     traffic = None
