@@ -15,7 +15,8 @@
 // lanes with a butterfly.
 // Selection: one wave per token, the partial slices read as 16-byte pieces (4
 // adjacent experts per lane), K rounds of an arg-max ordered by (logit desc,
-// expert id asc), each a DPP reduction into lane 63 read back as a scalar.
+// expert id asc): the largest logit by a DPP reduction into lane 63 read back
+// as a scalar, the lowest id holding it by a ballot.
 #include <math.h>
 
 #include "moe_internal.h"
@@ -41,7 +42,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 // logit's bit pattern made order-preserving as an unsigned integer (flip all
 // bits of a negative, the sign bit of a non-negative); the low word is ~id.
 __device__ __forceinline__ unsigned long long sel_key(float v, int e) {
-  const uint32_t u = __float_as_uint(v);
+  const uint32_t u = __float_as_uint(v) == 0x80000000u ? 0u : __float_as_uint(v);  // -0 == +0
   const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ((unsigned long long)o << 32) | (uint32_t)~(uint32_t)e;
 }
@@ -323,35 +324,40 @@ __global__ __launch_bounds__(256, 1) void route_logits_kernel(
       }
 }
 
-// Largest key of the wave, in lane 63 (then read into scalar registers):
-// each row of 16 lanes as in wave_max_key, then row 1 and row 3 take lane 15
-// of the row below (row_bcast:15) and rows 2 and 3 take lane 31
-// (row_bcast:31), all DPP moves, no LDS round trip.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ unsigned long long dpp_max_rows(unsigned long long k) {
-  const int lo0 = (int)(uint32_t)k, hi0 = (int)(uint32_t)(k >> 32);
-  const int lo = __builtin_amdgcn_update_dpp(lo0, lo0, CTRL, ROWS, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(hi0, hi0, CTRL, ROWS, 0xf, false);
-  const unsigned long long o = ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
-  return o > k ? o : k;
+// The larger of v and the value DPP control CTRL moves into this lane (lanes
+// outside ROWS keep their own value); no NaN handling, the values are finite
+// or -inf.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_fmax(float v) {
+  const int b = __float_as_int(v);
+  // A pattern that writes every lane needs no old value.
+  const float o = __int_as_float(ROWS == 0xf ? __builtin_amdgcn_update_dpp(0, b, CTRL, ROWS, 0xf, false)
+                                             : __builtin_amdgcn_update_dpp(b, b, CTRL, ROWS, 0xf, false));
+  return o > v ? o : v;
 }
-__device__ __forceinline__ unsigned long long wave_max_key_uniform(unsigned long long k) {
-  k = dpp_max<0xB1>(k);   // quad_perm [1,0,3,2]
-  k = dpp_max<0x4E>(k);   // quad_perm [2,3,0,1]
-  k = dpp_max<0x124>(k);  // row_ror 4
-  k = dpp_max<0x128>(k);  // row_ror 8
-  k = dpp_max_rows<0x142, 0xa>(k);  // row_bcast:15 into rows 1, 3
-  k = dpp_max_rows<0x143, 0xc>(k);  // row_bcast:31 into rows 2, 3
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, 63);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
-  return ((unsigned long long)hi << 32) | lo;
+
+// Largest value of the wave as a scalar: within each row
+// of 16 lanes (swap neighbours, swap pairs, rotate by 4, rotate by 8), then
+// row 1 and row 3 take lane 15 of the row below (row_bcast:15) and rows 2 and
+// 3 take lane 31 (row_bcast:31), which leaves the maximum in lane 63.
+__device__ __forceinline__ float wave_fmax_uniform(float v) {
+  v = dpp_fmax<0xB1>(v);       // quad_perm [1,0,3,2]
+  v = dpp_fmax<0x4E>(v);       // quad_perm [2,3,0,1]
+  v = dpp_fmax<0x124>(v);      // row_ror 4
+  v = dpp_fmax<0x128>(v);      // row_ror 8
+  v = dpp_fmax<0x142, 0xa>(v);  // row_bcast:15 into rows 1, 3
+  v = dpp_fmax<0x143, 0xc>(v);  // row_bcast:31 into rows 2, 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // One wave per token: logits = sum of the k-slice partials (ascending) + bias,
 // then the score and the top-K.  Lane l holds experts 4l + r + 256v (r < 4,
-// v < NV4), read as one 16-byte load per slice and v.  K rounds: each lane's
-// best key, the wave's best by DPP into a scalar, which the owning lane then
-// clears.  Keys order by (logit desc, expert asc) (sel_key).
+// v < NV4), read as one 16-byte load per slice and v.  K rounds: the wave's
+// largest remaining logit M by DPP into a scalar; of the candidates equal to
+// M the lowest expert id wins -- within a block of 256 ids the lowest lane
+// holding one (a ballot), in that lane the lowest slot -- and is then marked
+// taken (-inf, like the slots past E; the logits of finite inputs are finite,
+// and K <= E).  This is the order (logit desc, expert asc) of sel_key.
 template <int NV4>
 __global__ __launch_bounds__(256) void route_select_kernel(
     const float* __restrict__ part, int n_slices, int e_pad, const float* __restrict__ bias,
@@ -405,26 +411,32 @@ __global__ __launch_bounds__(256) void route_select_kernel(
       if (4 * lane + 256 * (c / 4) + c % 4 < E) sum += __expf(z[c] - m);
     denom = wave_sum(sum);
   }
-  unsigned long long kv[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int e = 4 * lane + 256 * (c / 4) + c % 4;
-    kv[c] = e < E ? sel_key(z[c], e) : 0ull;
-  }
+  const float kTaken = -INFINITY;  // the slots past E already hold it
   int my_e = 0;
   float my_s = 0.f, sum_sel = 0.f;
   for (int k = 0; k < K; ++k) {
-    unsigned long long best = kv[0];
+    float lm = z[0];
 #pragma unroll
-    for (int c = 1; c < NC; ++c) best = kv[c] > best ? kv[c] : best;
-    best = wave_max_key_uniform(best);
-    const int be = key_expert(best);
-    const float bv = key_value(best);
-    if (((be & 255) >> 2) == lane) {
-      const int slot = (be & 3) + 4 * (be >> 8);
+    for (int c = 1; c < NC; ++c) lm = z[c] > lm ? z[c] : lm;
+    const float bv = wave_fmax_uniform(lm);
+    // The lowest block holding bv, its lowest lane, that lane's lowest slot.
+    int L = 0, slot = 0;
+#pragma unroll
+    for (int v = NV4 - 1; v >= 0; --v) {
+      const bool h0 = z[4 * v] == bv, h1 = z[4 * v + 1] == bv, h2 = z[4 * v + 2] == bv;
+      const bool h3 = z[4 * v + 3] == bv;
+      const unsigned long long mask = __ballot(h0 || h1 || h2 || h3);
+      if (mask) {
+        L = __builtin_ctzll(mask);
+        const int r = h0 ? 0 : h1 ? 1 : h2 ? 2 : 3;
+        slot = 4 * v + __builtin_amdgcn_readlane(r, L);
+      }
+    }
+    const int be = 4 * L + (slot & 3) + 256 * (slot >> 2);
+    if (lane == L) {
 #pragma unroll
       for (int c = 0; c < NC; ++c)
-        if (c == slot) kv[c] = 0ull;
+        if (c == slot) z[c] = kTaken;
     }
     const float sc = score == MOE_SCORE_SIGMOID ? 1.f / (1.f + __expf(-bv)) : __expf(bv - m);
     sum_sel += sc;

@@ -415,6 +415,49 @@ def test_edge_cases(name, cfg):
         assert L.n_rows() == 0 and not bool(L.out.any())
 
 
+TIES = [
+    ("sigmoid_bias_256", W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=300, hidden=512,
+                                                              intermediate=128)),
+    ("softmax_8", W.CONFIGS["mixtral_bf16"].replace(num_tokens=300, hidden=512, intermediate=128)),
+    ("softmax_64_no_renorm", W.CONFIGS["dsv2lite_decode"].replace(hidden=512, intermediate=128,
+                                                                  num_shared=0)),
+    ("two_blocks_512", W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=130, hidden=128,
+                                                            intermediate=64, num_experts=512,
+                                                            top_k=16, expert_begin=100,
+                                                            expert_end=400)),
+    ("fp32", W.CONFIGS["tiny_f32"].replace(num_tokens=70)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", TIES, ids=[t[0] for t in TIES])
+def test_router_exact_ties(name, cfg):
+    """Exact ties in the router: expert e + E/2 gets the router row (and bias)
+    of expert e, so every logit has an equal partner (across the two blocks of
+    256 ids at E = 512), and every 7th token is zero (all its logits equal the
+    bias, or 0).  Ids are compared bit for bit with the oracle's selection on
+    the GPU's own logits: equal logits go to the lower id ("Efficient and
+    portable mixture-of-experts communication", Introduction: the K best
+    experts of each token)."""
+    inp = W.make_inputs(cfg, seed=5)
+    E, h = cfg.num_experts, cfg.num_experts // 2
+    inp["w_router"][h:2 * h] = inp["w_router"][:h]
+    if inp["bias"] is not None:
+        inp["bias"][h:2 * h] = inp["bias"][:h]
+    inp["x"][::7] = 0
+    L = MoELayer(cfg, inp)
+    L.route()
+    torch.cuda.synchronize()
+    z = L.logits.cpu()
+    assert torch.equal(z[:, h:2 * h], z[:, :h]), "duplicated router rows gave different logits"
+    ids_o, w_o = oracle.topk(z.double(), cfg.top_k, cfg.score, cfg.renormalize)
+    ids = L.topk_ids.cpu()
+    assert torch.equal(ids, ids_o), "top-K ids differ on exact ties"
+    assert float((L.topk_weights.cpu().double() - w_o).abs().max()) <= WEIGHT_TOL
+    # a zero token without bias: every logit 0, so the K lowest ids in order
+    if inp["bias"] is None:
+        assert torch.equal(ids[0], torch.arange(cfg.top_k, dtype=torch.int32))
+
+
 def test_dispatch_invalid_ids_are_skipped_and_counted():
     cfg = W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=700, hidden=256, intermediate=128)
     inp = W.make_inputs(cfg, seed=4, with_experts=False)
