@@ -430,7 +430,7 @@ def main():
         print(json.dumps(write_traffic_record(args.write_traffic_record)), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
 

@@ -72,8 +72,9 @@ def lib() -> ctypes.CDLL:
     if _LIB is None:
         path = library_path()
         if not os.path.exists(path):
-            raise RuntimeError(f"{path} is not built: run __graft_entry__.build() "
-                               "(the MoE path has no non-HIP fallback)")
+            raise RuntimeError(f"{path} is not built: run python -m "
+                               "combine_router_softmax_top_amd.build (the MoE path has no non-HIP "
+                               "fallback)")
         L = ctypes.CDLL(path)
         P, I32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         C = ctypes.POINTER(ConfigStruct)
