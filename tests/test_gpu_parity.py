@@ -507,6 +507,30 @@ def test_dispatch_one_launch_for_small_batches(tokens):
         check_dispatch(cfg, inp, L, ids=ids)
 
 
+@pytest.mark.parametrize("tokens,top_k", [(513, 4), (4096, 4), (4097, 4), (4096, 2)])
+def test_dispatch_mid_batches_few_experts(tokens, top_k):
+    # 16 experts, 4..11 local, 2052 to 16388 assignments (the count kernel,
+    # then the scan inside the scatter): a ragged last workgroup of tokens,
+    # several count chunks and a ragged last chunk.  Distinct, invalid,
+    # repeated and all-remote ids.
+    print(f"[gpu-case] dispatch mid batch tokens={tokens} top_k={top_k}", file=sys.stderr,
+          flush=True)
+    cfg = W.CONFIGS["mixtral_bf16"].replace(num_tokens=tokens, hidden=256, intermediate=128,
+                                            num_experts=16, top_k=top_k, expert_begin=4,
+                                            expert_end=12)
+    inp = W.make_inputs(cfg, seed=14, with_experts=False)
+    L = MoELayer(cfg, inp)
+    cases = [W.random_ids(tokens, 16, top_k, seed=15),
+             W.random_ids(tokens, 16, top_k, seed=16, invalid_frac=0.03),
+             W.random_ids(tokens, 16, top_k, seed=17, repeat_pool=6),
+             (torch.arange(top_k, dtype=torch.int32) + 12).repeat(tokens, 1).contiguous()]
+    for ids in cases:
+        L.dispatch(topk_ids=ids.cuda())
+        torch.cuda.synchronize()
+        r = check_dispatch(cfg, inp, L, ids=ids)
+    assert r["n_rows"] == 0
+
+
 def test_dispatch_scan_fallback_for_large_histograms():
     # 32 chunks x 512 local experts: more per-chunk counts than a scatter
     # workgroup stages, so the separate scan kernel computes the row numbers.
