@@ -179,9 +179,19 @@ def test_end_to_end_forward(name):
         eps = float((L.logits.cpu().double() - z_or).abs().max())
         assert eps <= LOGIT_TOL, f"logit error {eps}"
         for t in bad:
-            zs = torch.sort(z_or[t], descending=True).values
-            gap = float(zs[cfg.top_k - 1] - zs[cfg.top_k]) if cfg.top_k < cfg.num_experts else 0.0
-            assert gap <= 2 * eps, f"token {t}: ids differ with logit gap {gap} > 2*{eps}"
+            # The GPU's choice must be a valid top-K of the exact logits up to
+            # the rounding of its own: no unselected logit above a selected
+            # one by more than 2 eps, and the selected ones in descending
+            # order up to the same allowance.
+            z = z_or[t]
+            sel = ids_g[t].long()
+            rest = torch.ones(cfg.num_experts, dtype=torch.bool)
+            rest[sel] = False
+            if bool(rest.any()):
+                over = float(z[rest].max() - z[sel].min())
+                assert over <= 2 * eps, f"token {t}: an unselected logit is {over} above a selected one"
+            zs = z[sel]
+            assert bool((zs[:-1] >= zs[1:] - 2 * eps).all()), f"token {t}: selection out of order"
         print(f"near-tie swaps at tokens {bad}", file=sys.stderr)
     keep = torch.tensor([t for t in range(cfg.num_tokens) if t not in set(bad)])
     assert_close(cfg, L.out.cpu()[keep], out_o[keep], "out (end to end)")
