@@ -52,6 +52,9 @@ typedef enum {
   MOE_ERR_HIP = 4                 /* a HIP runtime call or launch failed       */
 } moe_status_t;
 
+/* The configuration's enumerated fields are int32_t holding these constants
+ * (the size of a C enum type is up to the compiler; a field of fixed width
+ * keeps moe_config_t's layout the same for every caller). */
 /* Element types of activations and weights. */
 enum { MOE_F32 = 0, MOE_BF16 = 1 };
 /* Router score functions. */
