@@ -575,6 +575,65 @@ def test_dispatch_skewed_and_all_remote():
     assert L.n_rows() == cfg.num_tokens
 
 
+# Expert row counts on both sides of every tile height of the expert GEMM (full
+# 256-row tiles; an expert's last tile run at 64, 128, 192 or 256 rows), an
+# empty expert, and 18 experts whose 26 row tiles span two bands of 16.
+TILE_COUNTS = [1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 0, 511, 512, 513, 320]
+
+
+def test_expert_mlp_every_tile_height():
+    # Row-major and packed weights: the same bits, run to run and between the
+    # layouts; every row within the per-row bound of the oracle; the rows past
+    # the count (NaN-filled) never written, so no padding row of a short tile
+    # lands in the buffer.
+    print("[gpu-case] expert MLP every tile height", file=sys.stderr, flush=True)
+    n_loc, total = len(TILE_COUNTS), sum(TILE_COUNTS)
+    d, I, K = 512, 384, 2
+    T = (total + 40 + K - 1) // K
+    base = W.CONFIGS["mixtral_bf16"].replace(num_tokens=T, hidden=d, intermediate=I,
+                                             num_experts=n_loc, top_k=K, expert_begin=0,
+                                             expert_end=n_loc)
+    g = torch.Generator().manual_seed(21)
+    x = torch.randn(T * K, d, generator=g).to(torch.bfloat16)
+    wg = (torch.randn(n_loc, I, d, generator=g) * 0.02).to(torch.bfloat16)
+    wu = (torch.randn(n_loc, I, d, generator=g) * 0.02).to(torch.bfloat16)
+    wd = (torch.randn(n_loc, d, I, generator=g) * 0.02).to(torch.bfloat16)
+    counts = torch.tensor(TILE_COUNTS, dtype=torch.int32)
+    offsets = torch.zeros(n_loc + 1, dtype=torch.int32)
+    offsets[1:] = counts.cumsum(0)
+
+    def packed(w):
+        p_ = torch.empty_like(w)
+        B.moe_pack_weights(w, p_)
+        return p_
+
+    outs = []
+    for layout in ("row_major", "packed"):
+        cfg = base.replace(packed_weights=layout == "packed")
+        ws = [w.cuda() for w in (wg, wu, wd)]
+        if layout == "packed":
+            ws = [packed(w) for w in ws]
+        y = torch.empty(T * K, d, dtype=torch.bfloat16, device="cuda")
+        work = B.alloc_workspace(cfg, B.MOE_WS_EXPERT_MLP)
+        for _ in range(2):
+            y.fill_(float("nan"))
+            B.moe_expert_mlp(cfg, x.cuda(), offsets.cuda(), *ws, y, workspace=work)
+            torch.cuda.synchronize()
+            outs.append(y.cpu())
+    for o in outs[1:]:
+        assert torch.equal(bits(o), bits(outs[0])), "runs or layouts differ"
+    got = outs[0]
+    assert bool(torch.isnan(got[total:].float()).all()), "a row past the count was written"
+    row_expert = torch.repeat_interleave(torch.arange(n_loc, dtype=torch.int32), counts.long())
+    y_o = oracle.expert_mlp(x[:total], row_expert, wg, wu, wd)
+    row_err, num, den = _row_errors(got[:total], y_o)
+    worst = int(row_err.argmax())
+    print(f"tile heights: rel-L2 {(num / den) ** 0.5:.2e}, worst row {worst} "
+          f"(expert {int(row_expert[worst])}) {float(row_err[worst]):.2e}", file=sys.stderr)
+    assert (num / den) ** 0.5 <= 1e-2
+    assert float(row_err[worst]) <= ROW_REL_L2
+
+
 # ------------------------------------------------------------------ full sizes
 
 # Per-row bound at full size, on top of the per-tensor rel-L2: a single
