@@ -634,6 +634,52 @@ def test_expert_mlp_every_tile_height():
     assert float(row_err[worst]) <= ROW_REL_L2
 
 
+@pytest.mark.parametrize("K,dtype,S", [(2, "bf16", 0), (3, "bf16", 0), (4, "bf16", 0),
+                                       (8, "bf16", 2), (16, "bf16", 0), (8, "f32", 1)])
+def test_combine_hand_built_maps(K, dtype, S):
+    # Row maps built by hand: about 40 % of the slots remote (-1), a token
+    # with no local row, a token with all slots local, zero and negative
+    # weights, a ragged last workgroup of tokens and ragged row pieces.  The
+    # rows no slot names, row 0 among them, hold NaN: the loads of empty
+    # slots read a dummy row and must never reach the output.  Bound per
+    # element, from the oracle alone: one rounding of the output (2^-8 of the
+    # value in bf16) plus the fp32 accumulation of K + S terms, priced on the
+    # oracle's sum of the terms' magnitudes.
+    print(f"[gpu-case] combine hand-built maps K={K} {dtype} S={S}", file=sys.stderr, flush=True)
+    T, d = 301, 576
+    cfg = W.CONFIGS["mixtral_bf16" if dtype == "bf16" else "tiny_f32"].replace(
+        num_tokens=T, hidden=d, intermediate=64, num_experts=32, top_k=K, expert_begin=0,
+        expert_end=32, num_shared=S)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator().manual_seed(100 + K + S)
+    local = torch.rand(T, K, generator=g) < 0.6
+    local[5] = False
+    local[6] = True
+    n_rows = int(local.sum())
+    row_of = torch.full((T, K), -1, dtype=torch.int32)
+    row_of[local] = (torch.randperm(n_rows, generator=g) + 1).to(torch.int32)  # row 0 unused
+    w = torch.rand(T, K, generator=g) * 2 - 1
+    w[torch.rand(T, K, generator=g) < 0.1] = 0.0
+    y = torch.full((T * K, d), float("nan")).to(dt)
+    y[1:n_rows + 1] = torch.randn(n_rows, d, generator=g).to(dt)
+    ysh = torch.randn(S, T, d, generator=g).to(dt) if S else None
+    out = torch.empty(T, d, dtype=dt, device="cuda")
+    B.moe_combine(cfg, y.cuda(), row_of.flatten().cuda(), w.cuda(), None if ysh is None else ysh.cuda(),
+                  out)
+    torch.cuda.synchronize()
+    got = out.cpu().double()
+    o = oracle.combine(y, row_of.flatten(), w, T, K, y_shared=ysh)
+    mag = oracle.combine(y.abs(), row_of.flatten(), w.abs(), T, K,
+                         y_shared=None if ysh is None else ysh.abs())
+    assert bool(torch.isfinite(got).all()), "a dummy row's NaN reached the output"
+    rnd = 2.0 ** -8 if dtype == "bf16" else 0.0
+    bound = rnd * o.abs() + (K + S + 1) * 2.0 ** -24 * mag * (1 + rnd)
+    excess = float(((got - o).abs() - bound).max())
+    assert excess <= 0.0, f"an element is {excess:.3g} past its bound"
+    if S == 0:
+        assert bool((got[5] == 0).all()), "a token with no local row must give zeros"
+
+
 # ------------------------------------------------------------------ full sizes
 
 # Per-row bound at full size, on top of the per-tensor rel-L2: a single
