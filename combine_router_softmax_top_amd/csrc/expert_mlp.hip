@@ -18,9 +18,11 @@
 //     memory into LDS (global_load_lds, 16 B per lane): the activations in a
 //     ring of two slots (one tile ahead), the weights in a ring of three (close
 //     to two tiles ahead, they miss L2 more often, and issued a k-step apart
-//     from the activation loads), 160 KB in all; the rows are
-//     XOR-swizzled in 16-byte chunks so the fragment reads are free of bank
-//     conflicts;
+//     from the activation loads), 160 KB in all; tiles of at most 64 rows,
+//     which mostly stream their weights, run a ring of four slots for each
+//     operand instead, every k-tile's loads issued three k-tiles ahead; the
+//     rows are XOR-swizzled in 16-byte chunks so the fragment reads are free
+//     of bank conflicts;
 //   * the epilogue stages the rounded tile through LDS, so each store
 //     instruction writes whole row segments;
 //   * ragged groups: the tile list (expert, row tile, column tile) is derived

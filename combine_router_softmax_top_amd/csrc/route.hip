@@ -9,8 +9,9 @@
 //
 // bf16: a logits GEMM (16x16x32 bf16 MFMA, fp32 accumulation) over tiles of
 // 64 tokens x up to 256 experts x one slice of the reduction dimension, its
-// operands streamed into LDS four chunks ahead, then a selection kernel that
-// adds the slices in a fixed order (deterministic).
+// operands streamed through a four-slot LDS ring (each chunk loaded three
+// chunks ahead), then a selection kernel that adds the slices in a fixed
+// order (deterministic).
 // fp32: each wave takes one token and reduces every dot product across its 64
 // lanes with a butterfly.
 // Selection: one wave per token, the partial slices read as 16-byte pieces (4
