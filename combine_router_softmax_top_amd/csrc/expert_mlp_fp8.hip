@@ -19,15 +19,16 @@
 //     in the register file); an expert's last row tile of at most 192 rows
 //     runs at its rows rounded up to 64, as in the bf16 kernel;
 //   * k-tiles of 128 (128-byte rows, the same bytes as the bf16 kernel's
-//     64-deep tiles) go straight from global memory into the shared swizzled
-//     LDS rings (activations two slots, weights three); a lane's operand for
-//     64-deep k-step s is two 16-byte chunks of its row, 4s + h and 4s + 2 + h
-//     (h = lane / 32);
-//   * the scales bypass LDS: they are stored pre-arranged for the MFMA (the
-//     MFMA scale layout of moe_quantize_mxfp8) so that one 8-byte load per
-//     lane and fragment brings every scale that lane needs for four k-tiles;
-//     the loads for the next four k-tiles are issued with the activation loads
-//     and complete by the same barrier;
+//     64-deep tiles) go straight from global memory into swizzled LDS rings
+//     of two slots per operand; a lane's operand for 64-deep k-step s is two
+//     16-byte chunks of its row, 4s + h and 4s + 2 + h (h = lane / 32);
+//   * the scales are stored pre-arranged for the MFMA (the MFMA scale layout
+//     of moe_quantize_mxfp8) and reach LDS the same way, by 4-byte
+//     global->LDS loads, a group of four k-tiles at a time into a
+//     double-buffered area issued two k-tiles ahead; each lane then reads one
+//     dword per fragment, whose bytes serve the group's k-steps through the
+//     MFMA's op_sel (register loads mixed with the LDS loads made the
+//     compiler wait for every load in flight before their first use);
 //   * tile list, XCD band order and a fixed k order as in the bf16 kernel.
 // The down projection runs either on bf16 h with the bf16 grouped GEMM, or,
 // with MX-FP8 down weights, on h encoded in the gate/up epilogue (the
