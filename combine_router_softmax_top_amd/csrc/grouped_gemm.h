@@ -72,8 +72,9 @@ __host__ __device__ inline int tiles_per_xcd_bound(int row_tiles, int nN) {
 // group's full-height tiles in group order, then the short last tiles of 3, 2
 // and 1 quarters, each kind in group order -- cut into bands of kBandRows row
 // tiles.  The 8 XCDs (workgroup ids go round-robin over them, XCD x running
-// ids x, x+8, ...) all work on the same band at a time: they form a grid of row groups x column groups over it, and XCD x
-// takes its block of the band column by column.  An XCD thus holds a few
+// ids x, x+8, ...) all work on the same band at a time: they form a grid of
+// row groups x column groups over it, and XCD x takes its block of the band
+// column by column.  An XCD thus holds a few
 // weight column tiles across half the band's rows: a weight tile streams
 // from memory once or twice per band, an activation row tile is shared by
 // the few XCDs of its row group (the Infinity Cache serves the repeats), and
