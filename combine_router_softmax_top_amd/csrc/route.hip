@@ -78,6 +78,21 @@ __device__ __forceinline__ unsigned long long wave_max_key(unsigned long long k)
   return xor_max(k, 32);
 }
 
+// Score of a selected logit z: softmax numerator exp(z - m) (m the largest
+// logit), or sigmoid.  Renormalised sigmoid weights are ratios of scores.
+// When the first (largest) selected logit is at most -17 they are taken from
+// exp(z - first): there sigmoid(z) = e^z (1 + O(e^z)), so the ratios agree to
+// a relative 4e-8, where the plain scores would lose about 1e-6 near -50 (an
+// exponential of a large fp32 argument) and underflow to 0 below about -88
+// (0/0 when every selected one does).  Above -17 the plain scores lose less
+// than 7e-7, and a selected logit whose score underflows weighs less than
+// e^-71 against the first.
+__device__ __forceinline__ float score_of(float z, int score, int renorm, float m, float first) {
+  if (score != MOE_SCORE_SIGMOID) return __expf(z - m);
+  if (renorm && first <= -17.f) return __expf(z - first);
+  return 1.f / (1.f + __expf(-z));
+}
+
 // v[i] holds the logit of expert lane + 64*i (bias included), -inf past E.
 template <int NV>
 __device__ __forceinline__ void select_topk(float (&v)[NV], int E, int K, int score, int renorm,
@@ -112,7 +127,7 @@ __device__ __forceinline__ void select_topk(float (&v)[NV], int E, int K, int sc
     kv[i] = e < E ? sel_key(v[i], e) : 0ull;
   }
   int my_e = 0;
-  float my_s = 0.f, sum_sel = 0.f;
+  float my_s = 0.f, sum_sel = 0.f, first = 0.f;
   for (int k = 0; k < K; ++k) {
     unsigned long long best = kv[0];
 #pragma unroll
@@ -125,7 +140,8 @@ __device__ __forceinline__ void select_topk(float (&v)[NV], int E, int K, int sc
       for (int i = 0; i < NV; ++i)
         if (i == (be >> 6)) kv[i] = 0ull;
     }
-    const float sc = score == MOE_SCORE_SIGMOID ? 1.f / (1.f + __expf(-bv)) : __expf(bv - m);
+    if (k == 0) first = bv;
+    const float sc = score_of(bv, score, renorm, m, first);
     sum_sel += sc;
     if (lane == k) { my_e = be; my_s = sc; }
   }
@@ -414,7 +430,7 @@ __global__ __launch_bounds__(256) void route_select_kernel(
   }
   const float kTaken = -INFINITY;  // the slots past E already hold it
   int my_e = 0;
-  float my_s = 0.f, sum_sel = 0.f;
+  float my_s = 0.f, sum_sel = 0.f, first = 0.f;
   for (int k = 0; k < K; ++k) {
     float lm = z[0];
 #pragma unroll
@@ -439,7 +455,8 @@ __global__ __launch_bounds__(256) void route_select_kernel(
       for (int c = 0; c < NC; ++c)
         if (c == slot) z[c] = kTaken;
     }
-    const float sc = score == MOE_SCORE_SIGMOID ? 1.f / (1.f + __expf(-bv)) : __expf(bv - m);
+    if (k == 0) first = bv;
+    const float sc = score_of(bv, score, renorm, m, first);
     sum_sel += sc;
     if (lane == k) { my_e = be; my_s = sc; }
   }

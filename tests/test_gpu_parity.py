@@ -468,6 +468,53 @@ def test_router_exact_ties(name, cfg):
         assert torch.equal(ids[0], torch.arange(cfg.top_k, dtype=torch.int32))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("bias_kind", ["all_far", "steps"])
+def test_router_sigmoid_renorm_far_below_zero(dtype, bias_kind):
+    # Renormalised sigmoid weights are ratios of scores; the fp32 sigmoid of a
+    # logit below about -88 underflows, and that of a logit near -50 carries
+    # ~1e-6 of relative error.  Token rows at 0.1x, 1x and 400x with biases of
+    # -300 for every expert (the selected logits of the small rows all far
+    # below zero: the ratios come from exp(z - first)), or K/2 experts at
+    # -10, then -100 up to E/2, then -300 (plain scores, the first selected
+    # near -10 and the other half of the selection's scores underflowing).  ids bit-exact against the
+    # oracle's top-K on the GPU's logits; weights finite and within
+    # WEIGHT_TOL of the oracle's fp64 ratios.
+    print(f"[gpu-case] router far below zero {dtype} {bias_kind}", file=sys.stderr, flush=True)
+    if dtype == "bf16":
+        cfg = W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=130, hidden=256, intermediate=64)
+    else:
+        cfg = W.CONFIGS["tiny_f32"].replace(num_tokens=130, score="sigmoid", num_experts=16,
+                                            top_k=4, expert_end=16)
+    E, K = cfg.num_experts, cfg.top_k
+    inp = W.make_inputs(cfg, seed=31, with_experts=False)
+    scale = torch.tensor([0.1, 1.0, 400.0])[torch.arange(cfg.num_tokens) % 3]
+    x = (inp["x"].double() * scale[:, None]).to(inp["x"].dtype)
+    if bias_kind == "all_far":
+        bias = torch.full((E,), -300.0)
+    else:
+        e = torch.arange(E)
+        bias = torch.where(e < K // 2, -10.0, torch.where(e < E // 2, -100.0, -300.0))
+    inp = dict(inp, x=x, bias=bias.float())
+    L = MoELayer(cfg, inp)
+    L.route()
+    torch.cuda.synchronize()
+    z = L.logits.cpu().double()
+    ids_o, w_o = oracle.topk(z, K, cfg.score, cfg.renormalize)
+    assert torch.equal(L.topk_ids.cpu(), ids_o), "top-K ids differ (stage-chained)"
+    w = L.topk_weights.cpu().double()
+    assert bool(torch.isfinite(w).all()), "non-finite weights"
+    assert bool(torch.isfinite(w_o).all())
+    err = float((w - w_o).abs().max())
+    assert err <= WEIGHT_TOL, f"weights max-abs {err}"
+    top = torch.sort(z, 1, descending=True).values[:, :K]
+    first = top[:, 0]
+    if bias_kind == "all_far":  # both regimes reached
+        assert bool((first <= -17).any()) and bool((first > -17).any())
+    else:  # a selected score underflows beside a first one above -17
+        assert bool(((first > -17) & (top[:, -1] < -88)).any())
+
+
 def test_dispatch_invalid_ids_are_skipped_and_counted():
     cfg = W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=700, hidden=256, intermediate=128)
     inp = W.make_inputs(cfg, seed=4, with_experts=False)
