@@ -403,6 +403,12 @@ EDGE = [
     # the most shared experts a layer may have, on a ragged token count
     ("max_shared", W.CONFIGS["dsv2lite_decode"].replace(num_tokens=77, hidden=256,
                                                         intermediate=192, num_shared=4)),
+    # every expert local at the maximum count, plus the maximum shared experts:
+    # 516 groups in the expert GEMMs' tile lookup, most of them empty
+    ("max_groups", W.CONFIGS["dsv3_prefill_ep"].replace(num_tokens=130, hidden=128,
+                                                        intermediate=64, num_experts=512,
+                                                        top_k=16, expert_begin=0,
+                                                        expert_end=512, num_shared=4)),
     # router tiles whose k-slice has an odd number of 64-deep chunks (3), and a
     # single chunk (the second half of the waves has nothing to add)
     ("router_odd_chunks", W.CONFIGS["dsv2lite_decode"].replace(num_tokens=200, hidden=192,
