@@ -62,6 +62,15 @@ MUTANTS = [
      "  if (ef == 0) return sign * std::ldexp((double)m, -8);"),
     ("invalid_ids_not_counted", "    if (e < 0 || e >= E) ++bad;\n    else ++counts[e];",
      "    if (e < 0 || e >= E) (void)bad;\n    else ++counts[e];"),
+    ("dispatch_slot_major",
+     "    for (int t = 0; t < T; ++t) {\n      for (int k = 0; k < K; ++k) {\n        if (ids[(size_t)t * K + k] != e) continue;",
+     "    for (int k = 0; k < K; ++k) {\n      for (int t = 0; t < T; ++t) {\n        if (ids[(size_t)t * K + k] != e) continue;"),
+    ("softmax_without_max_shift",
+     "  for (int e = 0; e < E; ++e) denom += std::exp(z[e] - m);\n  for (int e = 0; e < E; ++e) s[e] = std::exp(z[e] - m) / denom;",
+     "  for (int e = 0; e < E; ++e) denom += std::exp(z[e]);\n  for (int e = 0; e < E; ++e) s[e] = std::exp(z[e]) / denom;"),
+    ("combine_weights_shared_rows",
+     "        acc += value_at(y_shared, ((size_t)s * T + t) * d + c, dt_y);",
+     "        acc += value_at(weights, t * K, dt_w) * value_at(y_shared, ((size_t)s * T + t) * d + c, dt_y);"),
     ("mx_shared_first_stack_only",
      "      for (int t = 0; t < T; ++t) sh_expert[t] = s;\n      oracle_expert_mlp_mxfp8(",
      "      for (int t = 0; t < T; ++t) sh_expert[t] = 0;\n      oracle_expert_mlp_mxfp8("),
