@@ -71,6 +71,10 @@ MUTANTS = [
     ("combine_weights_shared_rows",
      "        acc += value_at(y_shared, ((size_t)s * T + t) * d + c, dt_y);",
      "        acc += value_at(weights, t * K, dt_w) * value_at(y_shared, ((size_t)s * T + t) * d + c, dt_y);"),
+    ("select_on_scores", "    topk_of_row(key.data(), E, K, ids + (size_t)t * K);",
+     "    topk_of_row(s.data(), E, K, ids + (size_t)t * K);"),
+    ("score_kind_ignored", "  if (score == OSCORE_SIGMOID) {\n    for (int e = 0; e < E; ++e) s[e] = 1.0 / (1.0 + std::exp(-z[e]));",
+     "  if (score != OSCORE_SIGMOID) {\n    for (int e = 0; e < E; ++e) s[e] = 1.0 / (1.0 + std::exp(-z[e]));"),
     ("mx_shared_first_stack_only",
      "      for (int t = 0; t < T; ++t) sh_expert[t] = s;\n      oracle_expert_mlp_mxfp8(",
      "      for (int t = 0; t < T; ++t) sh_expert[t] = 0;\n      oracle_expert_mlp_mxfp8("),
