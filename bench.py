@@ -10,7 +10,9 @@ dispatch+combine tokens/s and HBM GB/s against the 8 TB/s peak, and the
 expert GEMM's TFLOP/s against the 2.5 PFLOP/s dense bf16 MFMA peak.  The
 `roofline` object is for the expert MLP (the dominant kernel pair), timed with
 HIP events recorded on its own stream around every call inside the timed
-region.  `cpu_baseline` is the fp64 CPU oracle timed on a bounded sample of
+region; its bound follows from the MLP's flops per algorithmic byte against
+the ridge point (MFMA-bound above it, HBM-bound below, as the weight-streaming
+decode shape is).  `cpu_baseline` is the fp64 CPU oracle timed on a bounded sample of
 the same workload's tokens.
 
 Usage: python bench.py [--gpus 1] [--steps 30] [--warmup 5] [--workload dsv3_prefill_ep]
